@@ -1,0 +1,175 @@
+"""Python names of the C ABI in include/dsa.h (argument marshalling only).
+
+Each function checks dtypes/devices/shapes of torch tensors, allocates any
+output the caller did not pass (torch provides device memory), and calls the
+HIP library on torch's current stream. Every step of the computation runs in
+libdsa.so; there is no Python or CPU implementation behind these names.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+DSA_F32, DSA_BF16 = 0, 1
+_STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARGUMENT", 2: "DSA_ERR_UNSUPPORTED",
+           3: "DSA_ERR_WORKSPACE_TOO_SMALL", 4: "DSA_ERR_HIP"}
+
+
+class DsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+def _check(status: int):
+    if status != 0:
+        msg = _lib.load().dsa_last_error()
+        raise DsaError(status, msg.decode() if msg else "")
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, name, dtype):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def abi_version() -> int:
+    return _lib.load().dsa_abi_version()
+
+
+def quantize_fp8(x: torch.Tensor, out: torch.Tensor | None = None,
+                 scale: torch.Tensor | None = None):
+    """Hadamard + e4m3fn quantisation of each last-axis vector (dim 64 or 128)."""
+    _dev(x, "x", torch.float32)
+    d = x.shape[-1]
+    nvec = x.numel() // d if d else 0
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    _check(_lib.load().dsa_quantize_fp8(_p(x), nvec, d, _p(out), _p(scale), _stream()))
+    return out, scale
+
+
+def index_score(q_fp8, q_scale, w, k_fp8, k_scale, q_row_offsets, kv_row_offsets,
+                max_q_rows: int, max_kv_len: int, scores: torch.Tensor | None = None):
+    """Indexer scores [T, score_ld]; entries past each row's visible prefix are untouched."""
+    _dev(q_fp8, "q_fp8", torch.uint8)
+    _dev(k_fp8, "k_fp8", torch.uint8)
+    for n, t in (("q_scale", q_scale), ("w", w), ("k_scale", k_scale)):
+        _dev(t, n, torch.float32)
+    _dev(q_row_offsets, "q_row_offsets", torch.int32)
+    _dev(kv_row_offsets, "kv_row_offsets", torch.int64)
+    T, H, D = q_fp8.shape
+    B = q_row_offsets.numel() - 1
+    if scores is None:
+        ld = (max_kv_len + 3) // 4 * 4
+        scores = torch.empty((T, ld), dtype=torch.float32, device=q_fp8.device)
+    _dev(scores, "scores", torch.float32)
+    _check(_lib.load().dsa_index_score(
+        _p(q_fp8), _p(q_scale), _p(w), _p(k_fp8), _p(k_scale), _p(q_row_offsets),
+        _p(kv_row_offsets), B, T, max_q_rows, H, D, max_kv_len, _p(scores), scores.shape[1],
+        _stream()))
+    return scores
+
+
+def topk(scores, q_row_offsets, kv_row_offsets, max_q_rows: int, max_kv_len: int, k: int,
+         out: torch.Tensor | None = None):
+    """Per-row top-k positions [T, k] (ascending, -1 padded)."""
+    _dev(scores, "scores", torch.float32)
+    _dev(q_row_offsets, "q_row_offsets", torch.int32)
+    _dev(kv_row_offsets, "kv_row_offsets", torch.int64)
+    T = scores.shape[0]
+    B = q_row_offsets.numel() - 1
+    if out is None:
+        out = torch.empty((T, k), dtype=torch.int32, device=scores.device)
+    _dev(out, "out", torch.int32)
+    lib = _lib.load()
+    wsb = lib.dsa_topk_workspace_size(T, max_kv_len, k)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=scores.device) if wsb else None
+    _check(lib.dsa_topk(_p(scores), scores.shape[1], _p(q_row_offsets), _p(kv_row_offsets), B, T,
+                        max_q_rows, max_kv_len, k, _p(out), _p(ws), wsb, _stream()))
+    return out
+
+
+def sparse_mla_workspace_size(T: int, H: int, k: int) -> int:
+    return int(_lib.load().dsa_sparse_mla_workspace_size(T, H, k))
+
+
+def sparse_mla_decode(q, kv, topk_idx, q_row_offsets, kv_row_offsets, max_q_rows: int,
+                      sm_scale: float, share_base=None, num_accepted=None, out=None, lse=None,
+                      workspace=None, want_lse: bool = True):
+    """Sparse MLA over the selected latent rows: (out [T,H,512] bf16, lse [T,H] f32)."""
+    _dev(q, "q", torch.bfloat16)
+    _dev(kv, "kv", torch.bfloat16)
+    _dev(topk_idx, "topk", torch.int32)
+    _dev(q_row_offsets, "q_row_offsets", torch.int32)
+    _dev(kv_row_offsets, "kv_row_offsets", torch.int64)
+    if share_base is not None:
+        _dev(share_base, "share_base", torch.int32)
+        _dev(num_accepted, "num_accepted", torch.int32)
+    T, H, dq = q.shape
+    if dq != 576 or kv.shape[-1] != 576:
+        raise ValueError("latent rows must be 576 wide (512 latent + 64 rope)")
+    k = topk_idx.shape[1]
+    B = q_row_offsets.numel() - 1
+    if out is None:
+        out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    lib = _lib.load()
+    need = lib.dsa_sparse_mla_workspace_size(T, H, k)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.dsa_sparse_mla_decode(
+        _p(q), _p(kv), _p(topk_idx), topk_idx.shape[0], _p(share_base), _p(num_accepted), _p(q_row_offsets),
+        _p(kv_row_offsets), B, T, max_q_rows, H, k, float(sm_scale), _p(out), _p(lse),
+        _p(workspace), wsb, _stream()))
+    return out, lse
+
+
+def greedy_accept(logits, draft, K: int, argmax: bool = True, workspace=None):
+    """Greedy acceptance: (num_accepted [B], next_token [B], argmax [B, K+1] or None)."""
+    if not isinstance(logits, torch.Tensor) or not logits.is_cuda or not logits.is_contiguous():
+        raise TypeError("logits must be a contiguous CUDA tensor")
+    if logits.dtype == torch.float32:
+        dt = DSA_F32
+    elif logits.dtype == torch.bfloat16:
+        dt = DSA_BF16
+    else:
+        raise TypeError("logits must be float32 or bfloat16")
+    rows, V = logits.shape
+    B = rows // (K + 1)
+    if B * (K + 1) != rows:
+        raise ValueError("logits rows must be B*(K+1)")
+    if K:
+        _dev(draft, "draft", torch.int32)
+    dev = logits.device
+    n = torch.empty(B, dtype=torch.int32, device=dev)
+    nxt = torch.empty(B, dtype=torch.int32, device=dev)
+    am = torch.empty((B, K + 1), dtype=torch.int32, device=dev) if argmax else None
+    lib = _lib.load()
+    need = lib.greedy_accept_workspace_size(B, K, V)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
+    wsb = workspace.numel() * workspace.element_size()
+    _check(lib.greedy_accept(_p(logits), dt, V, _p(draft) if K else None, B, K, V, _p(n), _p(nxt),
+                             _p(am), _p(workspace), wsb, _stream()))
+    return n, nxt, am

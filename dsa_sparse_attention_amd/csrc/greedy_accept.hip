@@ -1,0 +1,164 @@
+// greedy_accept.hip -- greedy acceptance of a draft chain (split-vocab argmax + prefix scan).
+//
+// "GLM-5.3 推理全链路(十四)", section "接受判定:greedy 与 rejection sampling": the target
+// argmax of verify row i is compared with draft token i; acceptance stops at the first
+// mismatch, so the accepted length is the longest matching prefix. Verify rows are
+// cat(bonus, drafts) ("验证输入是怎么拼出来的"), so logits row b*(K+1)+i follows row i.
+//
+// Pass 1 (HBM-bound): blocks of 256 threads scan a vocabulary slice of one logits row
+// with 16-byte loads and keep (max, first index); ties go to the lower index at every
+// merge, which reproduces "first maximum wins" exactly. Pass 2: one wave per request
+// merges the slices of its K+1 rows in slice order, and a ballot over the K draft
+// comparisons gives the first mismatch.
+#include "common.hpp"
+
+namespace dsa {
+namespace {
+
+constexpr int GA_THREADS = 256;
+constexpr int GA_SLICE = 8192;  // vocabulary entries per block
+
+struct ArgMax {
+  float v;
+  int32_t i;
+};
+
+__device__ __forceinline__ void take(ArgMax& a, float v, int32_t i) {
+  if (v > a.v || (v == a.v && i < a.i)) { a.v = v; a.i = i; }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(GA_THREADS) void argmax_slices_kernel(const void* __restrict__ logits,
+                                                                   int64_t ld, int V, int nslice,
+                                                                   float* __restrict__ ws_v,
+                                                                   int32_t* __restrict__ ws_i) {
+  const int slice = blockIdx.x;
+  const int64_t row = blockIdx.y;
+  const int v0 = slice * GA_SLICE;
+  const int v1 = v0 + GA_SLICE < V ? v0 + GA_SLICE : V;
+  ArgMax best = {-INFINITY, 0x7FFFFFFF};
+  if (BF16) {
+    const uint16_t* lr = static_cast<const uint16_t*>(logits) + row * ld;
+    // 8 bf16 per 16-byte load when the slice start is aligned; scalar tail
+    const bool vec = ((reinterpret_cast<uintptr_t>(lr + v0) & 15) == 0);
+    int v = v0;
+    if (vec) {
+      const int nvec = (v1 - v0) / 8;
+      for (int j = threadIdx.x; j < nvec; j += GA_THREADS) {
+        const i32x4 d = *reinterpret_cast<const i32x4*>(lr + v0 + 8 * j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t w = static_cast<uint32_t>(d[e]);
+          take(best, __uint_as_float(w << 16), v0 + 8 * j + 2 * e);
+          take(best, __uint_as_float(w & 0xFFFF0000u), v0 + 8 * j + 2 * e + 1);
+        }
+      }
+      v = v0 + 8 * nvec;
+    }
+    for (int j = v + threadIdx.x; j < v1; j += GA_THREADS) take(best, bf16_bits_to_f32(lr[j]), j);
+  } else {
+    const float* lr = static_cast<const float*>(logits) + row * ld;
+    const bool vec = ((reinterpret_cast<uintptr_t>(lr + v0) & 15) == 0);
+    int v = v0;
+    if (vec) {
+      const int nvec = (v1 - v0) / 4;
+      for (int j = threadIdx.x; j < nvec; j += GA_THREADS) {
+        const float4 d = *reinterpret_cast<const float4*>(lr + v0 + 4 * j);
+        take(best, d.x, v0 + 4 * j);
+        take(best, d.y, v0 + 4 * j + 1);
+        take(best, d.z, v0 + 4 * j + 2);
+        take(best, d.w, v0 + 4 * j + 3);
+      }
+      v = v0 + 4 * nvec;
+    }
+    for (int j = v + threadIdx.x; j < v1; j += GA_THREADS) take(best, lr[j], j);
+  }
+  // -0.0 == +0.0 compare equal above; wave then block reduction, lower index on ties
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float ov = __shfl_xor(best.v, o);
+    const int32_t oi = __shfl_xor(best.i, o);
+    take(best, ov, oi);
+  }
+  __shared__ float sv[GA_THREADS / 64];
+  __shared__ int32_t si[GA_THREADS / 64];
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  if (lane == 0) { sv[wave] = best.v; si[wave] = best.i; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < GA_THREADS / 64; ++w) take(best, sv[w], si[w]);
+    ws_v[row * nslice + slice] = best.v;
+    ws_i[row * nslice + slice] = best.i;
+  }
+}
+
+__global__ __launch_bounds__(64) void accept_kernel(const float* __restrict__ ws_v,
+                                                    const int32_t* __restrict__ ws_i, int nslice,
+                                                    const int32_t* __restrict__ draft, int K,
+                                                    int32_t* __restrict__ num_accepted,
+                                                    int32_t* __restrict__ next_token,
+                                                    int32_t* __restrict__ argmax) {
+  const int b = blockIdx.x, i = threadIdx.x;
+  int32_t a = -1;
+  bool miss = false;
+  if (i <= K) {
+    const int64_t row = static_cast<int64_t>(b) * (K + 1) + i;
+    ArgMax best = {ws_v[row * nslice], ws_i[row * nslice]};
+    for (int s = 1; s < nslice; ++s) take(best, ws_v[row * nslice + s], ws_i[row * nslice + s]);
+    a = best.i;
+    if (argmax) argmax[row] = a;
+    if (i < K) miss = draft[static_cast<int64_t>(b) * K + i] != a;
+  }
+  const uint64_t mask = __ballot(miss);
+  const int n = mask ? __builtin_ctzll(mask) : K;  // first mismatching draft
+  const int32_t an = __shfl(a, n);
+  if (i == 0) {
+    num_accepted[b] = n;
+    next_token[b] = an;
+  }
+}
+
+}  // namespace
+}  // namespace dsa
+
+extern "C" size_t greedy_accept_workspace_size(int32_t B, int32_t K, int32_t V) {
+  if (B <= 0 || K < 0 || V <= 0) return 0;
+  const int64_t nslice = dsa::ceil_div(V, dsa::GA_SLICE);
+  return static_cast<size_t>(B) * (K + 1) * nslice * (sizeof(float) + sizeof(int32_t));
+}
+
+extern "C" dsa_status greedy_accept(const void* logits, int32_t dtype, int64_t logits_ld,
+                                    const int32_t* draft, int32_t B, int32_t K, int32_t V,
+                                    int32_t* num_accepted, int32_t* next_token, int32_t* argmax,
+                                    void* ws, size_t ws_bytes, void* stream) {
+  using namespace dsa;
+  DSA_REQUIRE(dtype == DSA_F32 || dtype == DSA_BF16, "greedy_accept: dtype must be DSA_F32 or DSA_BF16");
+  DSA_REQUIRE(B >= 0 && K >= 0 && K <= 63, "greedy_accept: need B >= 0 and 0 <= K <= 63");
+  DSA_REQUIRE(V >= 1 && logits_ld >= V, "greedy_accept: need V >= 1 and logits_ld >= V");
+  if (B == 0) return ok();
+  DSA_REQUIRE(logits && num_accepted && next_token && (K == 0 || draft),
+              "greedy_accept: null pointer");
+  const int64_t rows = static_cast<int64_t>(B) * (K + 1);
+  DSA_REQUIRE(rows <= 65535, "greedy_accept: B*(K+1) must be <= 65535");
+  const size_t need = greedy_accept_workspace_size(B, K, V);
+  if (!ws || ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "greedy_accept: workspace needs %zu bytes (got %zu)", need,
+                ws_bytes);
+  DSA_REQUIRE((reinterpret_cast<uintptr_t>(ws) & 3) == 0, "greedy_accept: workspace must be 4-byte aligned");
+  const int nslice = static_cast<int>(ceil_div(V, GA_SLICE));
+  float* ws_v = static_cast<float*>(ws);
+  int32_t* ws_i = reinterpret_cast<int32_t*>(ws_v + rows * nslice);
+  hipStream_t st = as_stream(stream);
+  dim3 grid((unsigned)nslice, (unsigned)rows);
+  if (dtype == DSA_BF16)
+    hipLaunchKernelGGL(argmax_slices_kernel<true>, grid, dim3(GA_THREADS), 0, st, logits, logits_ld,
+                       V, nslice, ws_v, ws_i);
+  else
+    hipLaunchKernelGGL(argmax_slices_kernel<false>, grid, dim3(GA_THREADS), 0, st, logits, logits_ld,
+                       V, nslice, ws_v, ws_i);
+  dsa_status s = check_launch("greedy_accept(argmax)");
+  if (s != DSA_OK) return s;
+  hipLaunchKernelGGL(accept_kernel, dim3((unsigned)B), dim3(64), 0, st, ws_v, ws_i, nslice, draft, K,
+                     num_accepted, next_token, argmax);
+  return check_launch("greedy_accept(accept)");
+}

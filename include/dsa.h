@@ -1,0 +1,199 @@
+/*
+ * dsa.h -- C ABI of libdsa.so: the DSA sparse-attention verify step on one
+ * MI355X (gfx950).
+ *
+ * The step follows the pages' statement of the problem:
+ *   "MAX Pipeline 中的 DeepSeek-V3.2 架构实现解析" (section
+ *   "Indexer 的结构与计算流程"): q/k are Hadamard-rotated, dynamically
+ *   quantised to FP8 (block 128), scored by the lightning indexer, and a
+ *   top-k of shape (total_seq_len, index_topk) selects the positions sparse
+ *   MLA attends to ("稀疏 MLA 的前向路径").
+ *   "GLM-5.3 推理全链路(十四):MTP 的三段前向" (section "验证段"): each
+ *   request contributes k+1 verify rows (bonus + drafts) at consecutive
+ *   positions with a chain-causal mask; every row selects its own top-k;
+ *   greedy acceptance keeps the longest draft prefix equal to the target
+ *   argmax ("接受判定").
+ *   "MAX 中 GLM-5.2 (DeepSeek-V3.2 Sparse) 的统一 MTP 推测解码架构解析"
+ *   (section "阶段 5"): later draft steps reuse the step-0 top-k row at the
+ *   accepted position (index_share_for_mtp_iteration).
+ *   "MAX 推测解码配置指南解读 max.pipelines.speculative" (section
+ *   "Token 合并"): ragged batches are described by exclusive-prefix row
+ *   offsets [B+1].
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers are DEVICE pointers unless documented otherwise; the caller
+ *   owns every buffer (inputs, outputs and workspace). The library never
+ *   allocates, frees, synchronises or reads device memory from the host.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream); every
+ *   call only enqueues kernels on it, so calls are graph-capturable.
+ * - Ragged batch: request b owns query rows [q_row_offsets[b],
+ *   q_row_offsets[b+1]) (R_b rows) and cached positions [kv_row_offsets[b],
+ *   kv_row_offsets[b+1]) (L_b positions, which include its R_b verify rows).
+ *   Row r of request b sits at position p = L_b - R_b + r and sees positions
+ *   0..p (chain-causal). Host scalars (B, T, max_q_rows, max_kv_len) size
+ *   the launch; device offsets bound every access per row. The host scalars
+ *   must be upper bounds of the device values: max_q_rows >= every R_b,
+ *   max_kv_len >= every L_b, T == q_row_offsets[B]; rows longer than the score
+ *   stride are clipped to it.
+ * - Device array CONTENTS (offsets, indices) are trusted for ordering but
+ *   every gather is bounds-checked against its request: out-of-range top-k
+ *   entries are skipped like -1.
+ * - Errors: invalid host arguments are rejected before any launch with a
+ *   dsa_status and a thread-local message (dsa_last_error()). A failed
+ *   launch returns DSA_ERR_HIP. No C++ exception crosses this boundary.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARGUMENT = 1,
+  DSA_ERR_UNSUPPORTED = 2,
+  DSA_ERR_WORKSPACE_TOO_SMALL = 3,
+  DSA_ERR_HIP = 4
+} dsa_status;
+
+typedef enum { DSA_F32 = 0, DSA_BF16 = 1 } dsa_dtype;
+
+/* ABI version of the loaded library (DSA_ABI_VERSION). Host only. */
+int dsa_abi_version(void);
+
+/* Message of the last failed call on this thread ("" if none). Host only;
+ * the string stays valid until the next call on this thread. */
+const char* dsa_last_error(void);
+
+/*
+ * dsa_quantize_fp8 -- Hadamard rotation + dynamic FP8 quantisation.
+ * ("MAX Pipeline 中的 DeepSeek-V3.2 架构实现解析", "Indexer 的结构与计算流程":
+ * hadamard_transform in Sylvester order, then dynamic float8_e4m3fn
+ * quantisation with block size 128 and an fp32 scale.)
+ *
+ * For each of the n_vec vectors x[v, 0:dim] (float32, dim in {64, 128},
+ * one quantisation block per vector):
+ *   y = FWHT(x) in float32 butterflies (a,b)->(a+b,a-b), strides 1,2,4,...
+ *   y = y * RN_f32(1/sqrt(dim))
+ *   scale[v] = amax(|y|) / 448 (float32 division), or 1 when amax == 0
+ *   x_fp8[v, i] = e4m3fn(y[i] / scale[v]), round-to-nearest-even, saturating
+ * Used for indexer queries [T*H_I vectors] and for index-cache keys [N].
+ * Errors: DSA_ERR_INVALID_ARGUMENT (null pointer, n_vec < 0),
+ * DSA_ERR_UNSUPPORTED (dim not 64/128).
+ */
+dsa_status dsa_quantize_fp8(const float* x, int64_t n_vec, int32_t dim, uint8_t* x_fp8,
+                            float* scale, void* stream);
+
+/*
+ * dsa_index_score -- lightning-indexer scores of every verify row against
+ * every visible cached index key.
+ * ("MAX Pipeline 中的 DeepSeek-V3.2 架构实现解析", "Indexer 的结构与计算流程";
+ * index_n_heads / index_head_dim from "配置体系".)
+ *
+ *   scores[t, s] = k_scale[s] * sum_j (w[t,j] * q_scale[t,j]) * ReLU(q_hat[t,j] . k_hat[s])
+ * i.e. sum_j w[t,j] ReLU(q[t,j] . k[s]) with the positive FP8 scales
+ * factored out; FP8 products with float32 accumulation (MFMA), float32
+ * epilogue. Written for s in [0, p_t] only; entries beyond are untouched.
+ *
+ *   q_fp8   [T, H_I, D_I] e4m3fn codes     q_scale, w [T, H_I] float32
+ *   k_fp8   [N, D_I] e4m3fn codes          k_scale    [N] float32
+ *   scores  [T, score_ld] float32, score_ld >= max_kv_len
+ * Supported: D_I = 128 (or 64), H_I a multiple of 8 up to 128.
+ * Errors: DSA_ERR_INVALID_ARGUMENT, DSA_ERR_UNSUPPORTED.
+ */
+dsa_status dsa_index_score(const uint8_t* q_fp8, const float* q_scale, const float* w,
+                           const uint8_t* k_fp8, const float* k_scale,
+                           const int32_t* q_row_offsets, const int64_t* kv_row_offsets,
+                           int32_t B, int32_t T, int32_t max_q_rows, int32_t H_I, int32_t D_I,
+                           int64_t max_kv_len, float* scores, int64_t score_ld, void* stream);
+
+/*
+ * dsa_topk -- per-row top-k selection over the visible scores.
+ * ("MAX Pipeline 中的 DeepSeek-V3.2 架构实现解析", "Indexer 的结构与计算流程": top-k
+ * output of shape (total_seq_len, index_topk); "GLM-5.3 推理全链路(十四)",
+ * "验证段的逐层算子": every verify query selects its own top-k.)
+ *
+ * For each row t, orders positions s in [0, p_t] by (scores[t,s] desc,
+ * s asc) -- -0.0 equals +0.0, scores must not be NaN -- keeps the first
+ * min(k, p_t+1), and writes them ASCENDING to topk[t, 0:k], padding with -1.
+ * Positions are request-local.
+ *   scores [T, score_ld] float32 (as written by dsa_index_score)
+ *   topk   [T, k] int32
+ * Workspace: none (ws may be NULL; ws_bytes ignored).
+ * Errors: DSA_ERR_INVALID_ARGUMENT (k < 1, k > 8192, ...).
+ */
+dsa_status dsa_topk(const float* scores, int64_t score_ld, const int32_t* q_row_offsets,
+                    const int64_t* kv_row_offsets, int32_t B, int32_t T, int32_t max_q_rows,
+                    int64_t max_kv_len, int32_t k, int32_t* topk, void* ws, size_t ws_bytes,
+                    void* stream);
+
+size_t dsa_topk_workspace_size(int32_t T, int64_t max_kv_len, int32_t k);
+
+/*
+ * dsa_sparse_mla_decode -- attention of every query row over only its
+ * selected latent rows.
+ * ("MAX Pipeline 中的 DeepSeek-V3.2 架构实现解析", "稀疏 MLA 的前向路径"; latent row
+ * = kv_lora_rank 512 + qk_rope_head_dim 64 from "GLM-5.3 推理全链路(十四)",
+ * "GLM-5.3 的草稿层到底长什么样".)
+ *
+ * For row t (request b), head h, over the valid indices i of its top-k row
+ * (entries < 0 or >= L_b are skipped):
+ *   z_i = sm_scale * q[t,h,0:576] . kv[kv_row_offsets[b] + idx_i, 0:576]
+ *   out[t,h,0:512] = sum_i softmax(z)_i * kv[., 0:512]   (bf16, fp32 accumulate)
+ *   lse[t,h] = ln sum_i exp(z_i)  (natural log; optional)
+ * No valid index: out = 0, lse = -inf.
+ * Index sharing ("MAX 中 GLM-5.2 ... 统一 MTP 推测解码架构解析", "阶段 5"): when
+ * share_base != NULL, every row of request b reads top-k row
+ * share_base[b] + num_accepted[b] instead of row t (no copy is made).
+ *   q [T, H, 576] bf16; kv [N, 576] bf16; topk [topk_rows, k] int32 (topk_rows >= T
+ *   without a share map; a share map entry outside [0, topk_rows) selects nothing)
+ *   out [T, H, 512] bf16; lse [T, H] float32 or NULL
+ * H must be a multiple of 16, at most 128.
+ * Workspace: dsa_sparse_mla_workspace_size() bytes (split-K partials).
+ * Errors: DSA_ERR_INVALID_ARGUMENT, DSA_ERR_UNSUPPORTED,
+ * DSA_ERR_WORKSPACE_TOO_SMALL.
+ */
+dsa_status dsa_sparse_mla_decode(const uint16_t* q, const uint16_t* kv, const int32_t* topk,
+                                 int32_t topk_rows, const int32_t* share_base, const int32_t* num_accepted,
+                                 const int32_t* q_row_offsets, const int64_t* kv_row_offsets,
+                                 int32_t B, int32_t T, int32_t max_q_rows, int32_t H, int32_t k,
+                                 float sm_scale, uint16_t* out, float* lse, void* ws,
+                                 size_t ws_bytes, void* stream);
+
+size_t dsa_sparse_mla_workspace_size(int32_t T, int32_t H, int32_t k);
+
+/*
+ * greedy_accept -- greedy acceptance of a chain of K drafts per request.
+ * ("GLM-5.3 推理全链路(十四)", "接受判定:greedy 与 rejection sampling": the target
+ * argmax of row i is compared with draft i, stopping at the first mismatch;
+ * "验证输入是怎么拼出来的": verify rows are cat(bonus, drafts).)
+ *
+ * Logits row b*(K+1)+i is the target distribution after verify row i.
+ *   a[b,i] = smallest v attaining max_v logits[b*(K+1)+i, v]  (values, -0 == +0)
+ *   num_accepted[b] = largest n <= K with draft[b,i] == a[b,i] for all i < n
+ *   next_token[b]   = a[b, num_accepted[b]]
+ *   argmax[b*(K+1)+i] = a[b,i] (optional)
+ * accept length (bonus included) is num_accepted + 1.
+ *   logits [B*(K+1), logits_ld] float32 or bf16 (dtype); draft [B, K] int32
+ * Workspace: greedy_accept_workspace_size() bytes. Logits must not be NaN.
+ * Errors: DSA_ERR_INVALID_ARGUMENT, DSA_ERR_WORKSPACE_TOO_SMALL.
+ */
+dsa_status greedy_accept(const void* logits, int32_t dtype, int64_t logits_ld,
+                         const int32_t* draft, int32_t B, int32_t K, int32_t V,
+                         int32_t* num_accepted, int32_t* next_token, int32_t* argmax, void* ws,
+                         size_t ws_bytes, void* stream);
+
+size_t greedy_accept_workspace_size(int32_t B, int32_t K, int32_t V);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H_ */

@@ -187,16 +187,19 @@ ORACLE_API int dsa_oracle_index_score_rows(
   double dec[256];
   for (int c = 0; c < 256; ++c) dec[c] = dsa_oracle_fp8_decode((uint8_t)c);
   int bad = 0;
-#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t i = 0; i < n_rows; ++i)
+    if (row_request(q_off, B, rows[i]) < 0) bad = 1;
+  if (bad) return -1;
+  /* one task per (row, key); rows and keys are independent */
+#pragma omp parallel for collapse(2) schedule(static)
   for (int64_t i = 0; i < n_rows; ++i) {
-    int64_t t = rows[i];
-    int b = row_request(q_off, B, t);
-    double* o = out + i * out_ld;
-    if (b < 0) { bad = 1; continue; }
-    int64_t nv = row_visible(q_off, kv_off, b, t);
-    const uint8_t* qt = q_fp8 + t * (int64_t)H * D;
     for (int64_t s = 0; s < out_ld; ++s) {
+      int64_t t = rows[i];
+      int b = row_request(q_off, B, t);
+      int64_t nv = row_visible(q_off, kv_off, b, t);
+      double* o = out + i * out_ld;
       if (s >= nv) { o[s] = -INFINITY; continue; }
+      const uint8_t* qt = q_fp8 + t * (int64_t)H * D;
       const uint8_t* ks = k_fp8 + (kv_off[b] + s) * (int64_t)D;
       double acc = 0.0;
       for (int j = 0; j < H; ++j) {
@@ -209,7 +212,7 @@ ORACLE_API int dsa_oracle_index_score_rows(
       o[s] = acc * (double)k_scale[kv_off[b] + s];
     }
   }
-  return bad ? -1 : 0;
+  return 0;
 }
 
 /* ------------------------------------------------------------------ */

@@ -1,0 +1,42 @@
+"""The C-ABI library loads and exports every entry point include/dsa.h declares (CPU only).
+
+Only host-side helpers are called here (version and workspace-size queries); no entry
+point that launches work is called without a GPU.
+"""
+import ctypes
+import os
+
+import pytest
+
+from dsa_sparse_attention_amd import _lib
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="libdsa.so not built (run __graft_entry__.build())")
+
+
+def test_header_declares_the_four_calls_and_helpers():
+    names = set(_lib.header_symbols())
+    for n in ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_decode", "greedy_accept",
+              "dsa_quantize_fp8", "dsa_abi_version", "dsa_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    missing = [n for n in _lib.header_symbols() if not hasattr(lib, n)]
+    assert not missing, f"declared but not exported: {missing}"
+    assert set(_lib.SIGNATURES) == set(_lib.header_symbols())
+
+
+def test_version_and_workspace_queries():
+    lib = _lib.load()
+    assert lib.dsa_abi_version() == 1
+    assert lib.dsa_last_error() in (b"", None)
+    assert lib.dsa_topk_workspace_size(192, 65536, 2048) == 0
+    # split-K partials: T * splits * H * (512 + 2) floats, or none when one split suffices
+    ws = lib.dsa_sparse_mla_workspace_size(192, 64, 2048)
+    assert ws == 0 or ws % (192 * 64 * 514 * 4) == 0
+    assert lib.dsa_sparse_mla_workspace_size(1024, 64, 2048) == 0
+    # greedy accept: one (max, index) pair per 8192-entry vocabulary slice per row
+    assert lib.greedy_accept_workspace_size(32, 5, 151552) == 32 * 6 * 19 * 8
+    assert lib.greedy_accept_workspace_size(0, 5, 10) == 0

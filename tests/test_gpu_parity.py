@@ -1,0 +1,246 @@
+"""Parity of the HIP path (through the C ABI) against the CPU oracle, CPU-sized cases.
+
+Bars: quantised codes/scales, top-k sets on shared fp32 scores, accepted lengths and
+argmaxes are bit-exact; indexer scores lie within the bound derived from the FP8 MFMA
+and float32 epilogue arithmetic; end-to-end top-k sets are equal or differ only inside
+that bound around the k-th score; sparse MLA meets max|d| <= 2e-2*max|o| + 1e-2*|o|.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dsa_sparse_attention_amd import api, synth, workloads
+from tests._pipeline import (DEV, Case, check_topk_valid, gpu_indexer, mla_check,
+                             oracle_quant, score_tolerance)
+
+pytestmark = pytest.mark.gpu
+
+W = workloads
+SMALL = {
+    "tiny": W.TINY,
+    "decode_verify@4096": W.scaled(W.DECODE_VERIFY, ctx=4096, batch=3, topk=512),
+    "mtp5_verify@6000": W.scaled(W.MTP5_VERIFY, ctx=6000, batch=3, topk=512),
+    "long_ctx@12800": W.scaled(W.LONG_CTX, ctx=12800, batch=1, topk=64),
+}
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# ---------------------------------------------------------------- quantiser
+@pytest.mark.parametrize("dim", [64, 128])
+def test_quantize_bitexact(dim):
+    _say(f"quantize dim={dim}")
+    g = torch.Generator().manual_seed(dim)
+    x = torch.randn((1027, dim), generator=g) * torch.rand((1027, 1), generator=g) * 100
+    x[0] = 0.0                    # zero vector -> scale 1, codes 0
+    x[1, :] = 1e-30               # underflow to subnormal / zero codes
+    x[2, 5] = 3e4                 # one dominant element
+    codes, scale = api.quantize_fp8(x.to(DEV))
+    rc, rs = oracle.quantize(x.numpy())
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    assert np.array_equal(scale.cpu().numpy(), rs)
+
+
+# ---------------------------------------------------------------- indexer score
+@pytest.mark.parametrize("name", list(SMALL))
+def test_index_score_within_bound(name):
+    w = SMALL[name]
+    _say(f"index_score {name}")
+    case = Case(w, with_mla=False, with_accept=False)
+    gi = gpu_indexer(case)
+    qc, qs, kc, ks, ko = oracle_quant(case)
+    assert np.array_equal(gi["qc"].cpu().numpy(), qc) and np.array_equal(gi["kc"].cpu().numpy(), kc)
+    rows = np.arange(case.T)
+    ref = oracle.index_score(qc, qs, case.host("w_f32"), kc, ks, case.qo.numpy(), ko,
+                             rows=rows, width=case.max_kv)
+    tol = score_tolerance(qc, qs, case.host("w_f32"), kc, ks, rows, case.qo.numpy(), ko,
+                          case.max_kv)
+    got = gi["scores"].cpu().numpy()[:, :case.max_kv].astype(np.float64)
+    worst = 0.0
+    for t in rows:
+        n = case.visible(int(t))
+        err = np.abs(got[t, :n] - ref[t, :n])
+        assert np.all(err <= tol[t, :n]), f"row {t}: score error above bound"
+        worst = max(worst, float((err / np.maximum(tol[t, :n], 1e-300)).max()))
+    _say(f"  worst |err|/bound = {worst:.3e}")
+
+
+def test_index_score_exact_grid_bitexact():
+    # q_hat, k_hat integers in [-4, 4] (exact in e4m3fn), unit scales, w = m/16: every
+    # partial sum is exact in any accumulator, so the HIP scores must equal the oracle's
+    _say("index_score exact grid")
+    rng = np.random.default_rng(11)
+    T, H, D, L = 4, 64, 128, 3000
+    vals = np.array([-4, -3, -2, -1, 0, 1, 2, 3, 4], np.float32)
+    q = oracle.fp8_encode(rng.choice(vals, (T, H, D)))
+    k = oracle.fp8_encode(rng.choice(vals, (L, D)))
+    w = (rng.integers(0, 16, (T, H)) / 16).astype(np.float32)
+    qs = np.ones((T, H), np.float32)
+    ks = np.ones(L, np.float32)
+    qo = np.array([0, T], np.int32)
+    ko = np.array([0, L], np.int64)
+    ref = oracle.index_score(q, qs, w, k, ks, qo, ko)
+    d = lambda a: torch.from_numpy(a).to(DEV)
+    got = api.index_score(d(q), d(qs), d(w), d(k), d(ks), d(qo), d(ko), T, L)
+    got = got.cpu().numpy()[:, :L].astype(np.float64)
+    for t in range(T):
+        n = L - T + t + 1
+        assert np.array_equal(got[t, :n], ref[t, :n])
+
+
+# ---------------------------------------------------------------- top-k
+@pytest.mark.parametrize("levels", [0, 5, 1000])
+def test_topk_bitexact_on_shared_scores(levels):
+    _say(f"topk levels={levels}")
+    lens = [5000, 130, 2049, 4099]
+    R = 3
+    qo = torch.tensor([0, 3, 6, 9, 12], dtype=torch.int32)
+    ko = synth.kv_row_offsets(lens)
+    ld = 5000 + 4 - 5000 % 4
+    s = synth.random_scores(12, ld, seed=levels, tie_levels=levels)
+    s[0, :50] = 0.0
+    s[0, 50:100] = -0.0                # -0 ties +0
+    k = 2048
+    got = api.topk(s.to(DEV), qo.to(DEV), ko.to(DEV), R, max(lens), k).cpu().numpy()
+    for t in range(12):
+        n = oracle.row_visible(qo.numpy(), ko.numpy(), t)
+        ref = oracle.topk(s[t:t + 1].double().numpy(), [n], k)[0]
+        assert np.array_equal(got[t], ref), f"row {t} (visible {n})"
+
+
+def test_topk_small_k_and_padding():
+    _say("topk k=1 and padding")
+    lens = [10, 1, 300]
+    qo = torch.tensor([0, 1, 2, 3], dtype=torch.int32)
+    ko = synth.kv_row_offsets(lens)
+    s = synth.random_scores(3, 300, seed=3, tie_levels=3)
+    for k in (1, 7, 300, 301):
+        got = api.topk(s.to(DEV), qo.to(DEV), ko.to(DEV), 1, 300, k).cpu().numpy()
+        for t in range(3):
+            ref = oracle.topk(s[t:t + 1].double().numpy(), [lens[t]], k)[0]
+            assert np.array_equal(got[t], ref), (k, t)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_end_to_end_topk_sets(name):
+    w = SMALL[name]
+    _say(f"end-to-end top-k {name}")
+    case = Case(w, with_mla=False, with_accept=False)
+    gi = gpu_indexer(case)
+    qc, qs, kc, ks, ko = oracle_quant(case)
+    rows = np.arange(case.T)
+    ref_s = oracle.index_score(qc, qs, case.host("w_f32"), kc, ks, case.qo.numpy(), ko,
+                               rows=rows, width=case.max_kv)
+    nvis = np.array([case.visible(int(t)) for t in rows])
+    ref_k = oracle.topk(ref_s, nvis, w.topk)
+    tol = score_tolerance(qc, qs, case.host("w_f32"), kc, ks, rows, case.qo.numpy(), ko,
+                          case.max_kv)
+    ndiff = check_topk_valid(gi["topk"].cpu().numpy(), ref_k, ref_s, nvis, tol, w.topk)
+    _say(f"  rows with band-only differences: {ndiff}/{len(rows)}")
+    if w.spike_frac:
+        for t in rows:  # planted spikes: closed-form answer, decided purely by position
+            assert list(gi["topk"][t].cpu().numpy()) == list(case.spike_pos[0][:w.topk].numpy())
+
+
+# ---------------------------------------------------------------- sparse MLA
+@pytest.mark.parametrize("heads,pad", [(16, 0.0), (64, 0.1), (128, 0.0), (48, 0.5)])
+def test_sparse_mla_matches_oracle(heads, pad):
+    _say(f"sparse_mla heads={heads} pad={pad}")
+    w = W.replace(W.scaled(W.MTP5_VERIFY, ctx=3000, batch=3, topk=512), mla_heads=heads)
+    lens = synth.context_lengths(w)
+    qo, ko = synth.q_row_offsets(w), synth.kv_row_offsets(lens)
+    m = synth.mla_inputs(w, lens)
+    idx = synth.random_topk(w, lens, qo, w.topk, pad_frac=pad)
+    idx[1, :] = -1                     # a row with nothing selected
+    idx[2, 5] = 10 ** 6                # out-of-range entry is skipped
+    out, lse = api.sparse_mla_decode(m["q"].to(DEV), m["kv"].to(DEV), idx.to(DEV), qo.to(DEV),
+                                     ko.to(DEV), w.rows, w.sm_scale)
+    u16 = lambda x: x.view(torch.uint16).numpy()
+    ref_o, ref_l = oracle.sparse_mla(u16(m["q"]), u16(m["kv"]), idx.numpy(), qo.numpy(),
+                                     ko.numpy(), w.sm_scale)
+    worst = mla_check(out, lse, ref_o, ref_l)
+    assert torch.all(out[1] == 0) and torch.all(torch.isneginf(lse[1]))
+    _say(f"  worst err/bound = {worst:.3f}")
+
+
+def test_sparse_mla_index_share_equals_compacted_copy():
+    _say("sparse_mla index share")
+    w = W.replace(W.scaled(W.DRAFT_SHARE, ctx=3000, batch=5, topk=256), rows=6)
+    lens = synth.context_lengths(w)
+    qo0, ko = synth.q_row_offsets(w), synth.kv_row_offsets(lens)
+    step0 = synth.random_topk(w, lens, qo0, w.topk, pad_frac=0.05)
+    n_acc = synth.accepted_lengths(w)
+    qo1 = torch.arange(w.batch + 1, dtype=torch.int32)
+    m = synth.mla_inputs(w, lens, rows=1, seed_offset=1)
+    d = lambda x: x.to(DEV)
+    o_sh, l_sh = api.sparse_mla_decode(d(m["q"]), d(m["kv"]), d(step0), d(qo1), d(ko), 1, w.sm_scale,
+                                       share_base=d(qo0), num_accepted=d(n_acc))
+    compact = step0[qo0[:-1].long() + n_acc.long()].contiguous()
+    o_cp, l_cp = api.sparse_mla_decode(d(m["q"]), d(m["kv"]), d(compact), d(qo1), d(ko), 1, w.sm_scale)
+    assert torch.equal(o_sh, o_cp) and torch.equal(l_sh, l_cp)
+    u16 = lambda x: x.view(torch.uint16).numpy()
+    ref_o, ref_l = oracle.sparse_mla(u16(m["q"]), u16(m["kv"]), step0.numpy(), qo1.numpy(), ko.numpy(),
+                                     w.sm_scale, share_base=qo0.numpy(), num_accepted=n_acc.numpy())
+    mla_check(o_sh, l_sh, ref_o, ref_l)
+
+
+def test_sparse_mla_dense_equals_full_visible_set():
+    # k >= visible: sparse MLA over every visible position is dense causal attention
+    _say("sparse_mla dense case")
+    w = W.replace(W.scaled(W.MTP5_VERIFY, ctx=700, batch=2, topk=1024), mla_heads=32)
+    lens = [700, 333]
+    qo, ko = synth.q_row_offsets(w), synth.kv_row_offsets(lens)
+    m = synth.mla_inputs(w, lens)
+    idx = synth.random_topk(w, lens, qo, w.topk)
+    out, lse = api.sparse_mla_decode(m["q"].to(DEV), m["kv"].to(DEV), idx.to(DEV), qo.to(DEV),
+                                     ko.to(DEV), w.rows, w.sm_scale)
+    u16 = lambda x: x.view(torch.uint16).numpy()
+    ref_o, ref_l = oracle.sparse_mla(u16(m["q"]), u16(m["kv"]), idx.numpy(), qo.numpy(), ko.numpy(),
+                                     w.sm_scale)
+    mla_check(out, lse, ref_o, ref_l)
+
+
+# ---------------------------------------------------------------- greedy accept
+@pytest.mark.parametrize("name,batch,vocab,K", [("tiny", 1, 1024, 1), ("f32", 7, 5000, 4),
+                                                ("bf16", 32, 151552, 5), ("ragged", 3, 8193, 0)])
+def test_greedy_accept_bitexact(name, batch, vocab, K):
+    _say(f"greedy_accept {name}")
+    base = W.TINY if name in ("tiny", "f32") else W.MTP5_VERIFY
+    w = W.replace(base, batch=batch, vocab=vocab, rows=K + 1)
+    a = synth.accept_inputs(w)
+    logits = a["logits"]
+    if name == "bf16":
+        logits[3, 100] = logits[3].max()   # planted exact tie: lower index must win
+        logits[3, 7] = logits[3, 100]
+    n, nxt, am = api.greedy_accept(logits.to(DEV), a["draft"].to(DEV), K)
+    host = logits.view(torch.uint16).numpy() if logits.dtype == torch.bfloat16 else logits.numpy()
+    rn, rnx, ram = oracle.greedy_accept(host, a["draft"].numpy(), K)
+    assert np.array_equal(n.cpu().numpy(), rn) and np.array_equal(nxt.cpu().numpy(), rnx)
+    assert np.array_equal(am.cpu().numpy(), ram)
+    assert np.array_equal(rn, a["planted_n"].numpy())
+
+
+def test_abi_rejects_bad_arguments_before_launch():
+    _say("abi error paths")
+    x = torch.zeros((4, 96), device=DEV)
+    with pytest.raises(api.DsaError, match="UNSUPPORTED"):
+        api.quantize_fp8(x)
+    s = torch.zeros((2, 64), device=DEV)
+    qo = torch.tensor([0, 2], dtype=torch.int32, device=DEV)
+    ko = torch.tensor([0, 64], dtype=torch.int64, device=DEV)
+    with pytest.raises(api.DsaError, match="INVALID_ARGUMENT"):
+        api.topk(s, qo, ko, 2, 64, 0)
+    q = torch.zeros((2, 20, 576), dtype=torch.bfloat16, device=DEV)
+    kv = torch.zeros((64, 576), dtype=torch.bfloat16, device=DEV)
+    idx = torch.zeros((2, 8), dtype=torch.int32, device=DEV)
+    with pytest.raises(api.DsaError, match="UNSUPPORTED"):
+        api.sparse_mla_decode(q, kv, idx, qo, ko, 2, 0.1)
+    lg = torch.zeros((4, 10), device=DEV)
+    with pytest.raises(api.DsaError, match="WORKSPACE"):
+        api.greedy_accept(lg, torch.zeros((2, 1), dtype=torch.int32, device=DEV), 1,
+                          workspace=torch.zeros(4, dtype=torch.uint8, device=DEV))
