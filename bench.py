@@ -1,0 +1,270 @@
+"""Benchmark of the DSA verify step on one MI355X.
+
+One step = one pass of the whole hot path over a batch of verify rows:
+quantise the indexer queries (Hadamard + e4m3fn), score every visible index key
+(FP8 MFMA), select the per-row top-k, run sparse MLA over the selected latent rows,
+and take the greedy acceptance of the drafts. The index K cache (keys quantised once,
+as at cache-write time), the latent cache and the logits are resident in HBM before
+timing starts; three copies of every input rotate across steps so that no step is
+served from the 256 MB MALL left warm by the previous one.
+
+Prints one JSON line. ``value`` is verify query rows per second (rows of the batch /
+step time). Per-kernel times come from HIP events recorded on the stream the kernels
+run on, over the same timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0      # dense FP8 MFMA
+BF16_PEAK_TFLOPS = 2500.0     # dense BF16 MFMA
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mtp5_verify_64k")
+    ap.add_argument("--copies", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+class Inputs:
+    """One resident copy of the step's inputs (device tensors)."""
+
+    def __init__(self, w, lengths, copy: int):
+        import torch
+
+        from dsa_sparse_attention_amd import api, synth
+
+        dev = "cuda"
+        ix = synth.indexer_inputs(w, lengths, device=dev, seed_offset=copy)
+        self.q_f32 = ix["q"]
+        self.w = ix["w"]
+        # cache-write step: keys are quantised once when the index cache is filled
+        self.k_fp8, self.k_scale = api.quantize_fp8(ix["k"])
+        self.k_f32_sample = ix["k"][: lengths[0]].cpu() if copy == 0 else None
+        del ix
+        m = synth.mla_inputs(w, lengths, device=dev, seed_offset=copy)
+        self.q_mla, self.kv = m["q"], m["kv"]
+        a = synth.accept_inputs(w, device=dev) if copy == 0 else None
+        if a is None:
+            a = Inputs.accept_cache
+        else:
+            Inputs.accept_cache = a
+        self.logits = a["logits"].clone()
+        self.draft = a["draft"].clone()
+        torch.cuda.synchronize()
+
+
+def source_sha(name: str) -> str:
+    p = os.path.join(ROOT, "dsa_sparse_attention_amd", "csrc", name)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def traffic_for(kernel_file: str, launches_key: str):
+    """HBM traffic per launch from the committed rocprofv3 --pmc summary, if still current."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p)).get(launches_key)
+    if not rec or rec.get("source_sha") != source_sha(kernel_file):
+        return None  # counters were taken on a different kernel source
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, lengths, inp0, target_s: float):
+    """Time the oracle (as it stands) on a bounded sample: whole requests of this workload."""
+    import numpy as np
+
+    import oracle
+
+    qo = np.arange(w.batch + 1, dtype=np.int32) * w.rows
+    q_all = inp0.q_f32.cpu().numpy()
+    w_all = inp0.w.cpu().numpy()
+    qm_all = inp0.q_mla.view(__import__("torch").uint16)
+    logits = inp0.logits
+    draft = inp0.draft.cpu().numpy()
+    L = lengths[0]
+    kf = inp0.k_f32_sample.numpy()
+    kv_host = inp0.kv[:L].view(__import__("torch").uint16).cpu().numpy()
+    done_rows, t_total = 0, 0.0
+    b = 0
+    while b < w.batch and (t_total < target_s or b == 0):
+        # every sampled request reuses request 0's caches (same shapes) with its own rows
+        rows = slice(b * w.rows, (b + 1) * w.rows)
+        q = np.ascontiguousarray(q_all[rows])
+        wt = np.ascontiguousarray(w_all[rows])
+        qm = qm_all[rows].cpu().numpy()
+        lg = logits[rows].view(__import__("torch").uint16).cpu().numpy()
+        t0 = time.perf_counter()
+        qc, qs = oracle.quantize(q)
+        kc, ks = oracle.quantize(kf)
+        qo1 = np.array([0, w.rows], np.int32)
+        ko1 = np.array([0, L], np.int64)
+        sc = oracle.index_score(qc, qs, wt, kc, ks, qo1, ko1)
+        nvis = np.array([L - w.rows + r + 1 for r in range(w.rows)])
+        tk = oracle.topk(sc, nvis, w.topk)
+        oracle.sparse_mla(qm, kv_host, tk, qo1, ko1, w.sm_scale)
+        oracle.greedy_accept(lg, draft[b:b + 1], w.drafts)
+        t_total += time.perf_counter() - t0
+        done_rows += w.rows
+        b += 1
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": done_rows / t_total, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": f"{b} request(s) x {w.rows} rows at context {L}: quantise, index score, "
+                      f"top-k, sparse MLA, greedy accept ({t_total:.1f} s)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the verify step is "
+              "data-parallel per request and this build measures one GPU's share.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from dsa_sparse_attention_amd import accounting, api, synth, workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = workloads.ALL[args.workload]
+    lengths = synth.context_lengths(w)
+    T = w.batch * w.rows
+    max_kv = max(lengths)
+    dev = "cuda"
+    print(f"[bench] workload {w.name}: B={w.batch} ctx={max_kv} rows={w.rows} T={T}", file=sys.stderr,
+          flush=True)
+    copies = [Inputs(w, lengths, c) for c in range(args.copies)]
+    qo = synth.q_row_offsets(w).to(dev)
+    ko = synth.kv_row_offsets(lengths).to(dev)
+    ld = (max_kv + 3) // 4 * 4
+    scores = torch.empty((T, ld), dtype=torch.float32, device=dev)
+    topk = torch.empty((T, w.topk), dtype=torch.int32, device=dev)
+    qc = torch.empty((T, w.index_heads, w.index_dim), dtype=torch.uint8, device=dev)
+    qs = torch.empty((T, w.index_heads), dtype=torch.float32, device=dev)
+    out = torch.empty((T, w.mla_heads, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, w.mla_heads), dtype=torch.float32, device=dev)
+    ws_need = api.sparse_mla_workspace_size(T, w.mla_heads, w.topk)
+    ws_mla = torch.empty(max(ws_need, 16), dtype=torch.uint8, device=dev)
+    from dsa_sparse_attention_amd import _lib
+    ga_need = _lib.load().greedy_accept_workspace_size(w.batch, w.drafts, w.vocab)
+    ws_ga = torch.empty(max(ga_need, 16), dtype=torch.uint8, device=dev)
+    print(f"[bench] inputs resident ({args.copies} copies); mla workspace {ws_need/1e6:.1f} MB",
+          file=sys.stderr, flush=True)
+
+    names = ["quantize_q", "index_score", "topk", "sparse_mla", "greedy_accept"]
+    stream = torch.cuda.current_stream()
+
+    def step(inp, ev=None):
+        if ev: ev[0].record(stream)
+        api.quantize_fp8(inp.q_f32, out=qc, scale=qs)
+        if ev: ev[1].record(stream)
+        api.index_score(qc, qs, inp.w, inp.k_fp8, inp.k_scale, qo, ko, w.rows, max_kv, scores=scores)
+        if ev: ev[2].record(stream)
+        api.topk(scores, qo, ko, w.rows, max_kv, w.topk, out=topk)
+        if ev: ev[3].record(stream)
+        api.sparse_mla_decode(inp.q_mla, inp.kv, topk, qo, ko, w.rows, w.sm_scale, out=out, lse=lse,
+                              workspace=ws_mla)
+        if ev: ev[4].record(stream)
+        api.greedy_accept(inp.logits, inp.draft, w.drafts, argmax=False, workspace=ws_ga)
+        if ev: ev[5].record(stream)
+
+    for i in range(args.warmup):
+        step(copies[i % len(copies)])
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(copies[i % len(copies)], evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    per = {n: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)) / args.steps
+           for j, n in enumerate(names)}
+    ms_step = total_ms / args.steps
+    print(f"[bench] {args.steps} steps: {ms_step:.4f} ms/step (wall {wall / args.steps * 1e3:.4f} ms); "
+          + ", ".join(f"{n} {v * 1e3:.1f} us" for n, v in per.items()), file=sys.stderr, flush=True)
+
+    # algorithmic work (bytes / flops the method must move or do)
+    wi = accounting.index_score_work(lengths, w.rows, w.index_heads, w.index_dim)
+    wt = accounting.topk_work(lengths, w.rows, w.topk)
+    wm = accounting.sparse_mla_work(T, w.mla_heads, w.topk)
+    wg = accounting.greedy_accept_work(w.batch, w.drafts, w.vocab, 2)
+    wq = dict(bytes=T * w.index_heads * (w.index_dim * 4 + w.index_dim + 4))
+    kern = {
+        "quantize_q": dict(bytes=wq["bytes"], bound="hbm"),
+        "index_score": dict(bytes=wi["bytes"], flops=wi["flops"], bound="mfma", file="index_score.hip"),
+        "topk": dict(bytes=wt["bytes"], bound="hbm", file="topk.hip"),
+        "sparse_mla": dict(bytes=wm["bytes"], flops=wm["flops"], bound="hbm", file="sparse_mla.hip"),
+        "greedy_accept": dict(bytes=wg["bytes"], bound="hbm", file="greedy_accept.hip"),
+    }
+    kernels = {}
+    for n, kd in kern.items():
+        t_s = per[n] * 1e-3
+        e = {"us": round(per[n] * 1e3, 2), "GB/s": round(kd["bytes"] / t_s / 1e9, 1),
+             "hbm_frac": round(kd["bytes"] / t_s / 1e9 / HBM_PEAK_GBS, 4)}
+        if "flops" in kd:
+            peak = FP8_PEAK_TFLOPS if n == "index_score" else BF16_PEAK_TFLOPS
+            e["TFLOP/s"] = round(kd["flops"] / t_s / 1e12, 1)
+            e["mfma_frac"] = round(kd["flops"] / t_s / 1e12 / peak, 4)
+        kernels[n] = e
+    dom = max(per, key=per.get)
+    kd = kern[dom]
+    t_dom = per[dom] * 1e-3
+    if kd["bound"] == "mfma":
+        peak = FP8_PEAK_TFLOPS
+        ach = kd["flops"] / t_dom / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(ach / peak, 4)}
+    else:
+        ach = kd["bytes"] / t_dom / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    roof["kernel"] = dom
+    roof["traffic"] = traffic_for(kd.get("file", ""), dom) if kd.get("file") else None
+
+    value = T / (ms_step * 1e-3)
+    rec = {
+        "metric": "verify query rows/sec (indexer+top-k+sparse MLA) at 64K ctx; HBM GB/s, MFMA %",
+        "value": round(value, 1), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8+bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "context": max_kv, "rows_per_request": w.rows,
+                   "index_heads": w.index_heads, "index_dim": w.index_dim, "topk": w.topk,
+                   "mla_heads": w.mla_heads, "vocab": w.vocab, "global_batch": T, "seq_len": max_kv,
+                   "parallelism": "single-gpu"},
+        "step_includes": names,
+        "rows_per_s_indexer_topk_mla": round(T / ((per["index_score"] + per["topk"] +
+                                                  per["sparse_mla"]) * 1e-3), 1),
+        "kernels": kernels,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(w, lengths, copies[0], args.cpu_seconds)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec, ensure_ascii=False), flush=True)
+
+
+if __name__ == "__main__":
+    main()
