@@ -5,110 +5,194 @@
 // 512 + qk_rope_head_dim 64 ("GLM-5.3 推理全链路(十四)", "GLM-5.3 的草稿层到底长什么样").
 // Index sharing: "MAX 中 GLM-5.2 ... 统一 MTP 推测解码架构解析", "阶段 5".
 //
-// Work split: a block owns one query row and one slice of its top-k list
-// (split-K); wave w owns heads 16w..16w+15. Per 32-key chunk the block gathers
-// 32 latent rows (1152 B each, 16-byte coalesced loads) into LDS, then
-//   S^T[key, head] = K[32 x 576] . Q^T  (18 x 2 v_mfma_f32_16x16x32_bf16, Q^T
-//                                        fragments held in registers)
-//   online softmax per head in base 2 (one max / sum per lane, lane = head)
-//   O^T[dim, head] += V^T[512 x 32] . P^T (32 MFMAs, P^T taken straight from the
-//                                        S^T accumulator lanes, no shuffle)
-// The transposed O^T layout keeps each head in one lane column, so the
-// softmax rescale of O needs no cross-lane exchange. With more than one split
-// the unnormalised partials (O, max, sum) go to the workspace and a combine
-// kernel merges them.
+// Work split: a block owns one query row and one slice (<= 1024 entries) of its
+// top-k list (split-K); wave w owns heads 16w..16w+15.
+//  1. The slice's valid indices are compacted into LDS in list order (block
+//     prefix sum), so -1 padding and out-of-range entries cost neither HBM
+//     traffic nor MFMA work, and the accumulation order is deterministic.
+//  2. Latent rows stream HBM -> LDS with 16-byte global_load_lds (LDS DMA, no
+//     registers) in 32-row chunks, double-buffered: chunk c+1 is in flight
+//     while chunk c is computed. Rows are stored unpadded (1152 B) with the
+//     16-byte units of each 128-byte group XOR-swizzled by row, which keeps
+//     both read patterns below free of bank conflicts.
+//  3. S^T[key, head] = K[32 x 576] . Q^T with v_mfma_f32_16x16x32_bf16 (Q^T
+//     fragments stay in registers); online softmax per head in base 2, one
+//     head per lane column.
+//  4. O^T[dim, head] += V^T . P^T: P^T is the S^T accumulator itself (no data
+//     movement); the V^T operand comes from ds_read_b64_tr_b16, which
+//     transposes 4x4 blocks of bf16 across lanes while reading, so each 16x32
+//     A operand is two 8-byte LDS reads per lane.
+// With more than one split, unnormalised partials (O, max, sum) go to the
+// workspace and a combine kernel merges them.
 #include "common.hpp"
 
 namespace dsa {
 namespace {
 
 constexpr int DQK = 576, DV = 512;
-constexpr int KC = 32;               // keys per chunk
-constexpr int ROWB = DQK * 2 + 16;   // LDS row stride (bytes), padded against bank conflicts
-constexpr int NCHUNK16 = DQK * 2 / 16;  // 72 16-byte pieces per latent row
+constexpr int KC = 32;                      // latent rows per chunk
+constexpr int ROWB = DQK * 2;               // 1152 bytes per latent row in LDS (unpadded)
+constexpr int UNITS = ROWB / 16;            // 72 16-byte units per row
+constexpr int CHUNK_BYTES = KC * ROWB;      // 36864
+constexpr int BLOCKS = CHUNK_BYTES / 1024;  // 36 wave-wide (64 x 16 B) DMA blocks per chunk
+constexpr int MAX_KPS = 1024;               // top-k entries per split (LDS index staging)
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(i32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Physical position of logical 16-byte unit c of latent row `row` in LDS: the
+// low 3 bits are XORed with a row hash so 16 consecutive rows read at the same
+// logical unit hit 16 different bank groups. An involution: swz(swz(c)) == c.
+__device__ __forceinline__ int swz(int c, int row) {
+  return (c & ~7) | ((c ^ row ^ (row >> 3)) & 7);
+}
+
 template <int NW>
+__device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) tmp[wave] = x;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    before += w < wave ? tmp[w] : 0;
+    tot += tmp[w];
+  }
+  *total = tot;
+  __syncthreads();
+  return before + x - v;
+}
+
 // Two waves per SIMD: caps the kernel at 256 registers per lane (Q^T 72, O^T 128, rest).
+template <int NW>
 __global__ __launch_bounds__(NW * 64, NW == 1 ? 1 : 2) void mla_decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ topk, const int32_t* __restrict__ share_base,
     const int32_t* __restrict__ num_acc, const int32_t* __restrict__ q_off,
     const int64_t* __restrict__ kv_off, int H, int k, int topk_rows, float c2, int nsplit,
-    int keys_per_split,
-    uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o,
-    float* __restrict__ ws_ml) {
+    int keys_per_split, uint16_t* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ ws_o, float* __restrict__ ws_ml) {
   constexpr int NT = NW * 64;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[KC * ROWB];
-  __shared__ int32_t sidx[KC];
+  constexpr int PER_T = (MAX_KPS + NT - 1) / NT;  // index entries per thread
+  __shared__ __attribute__((aligned(1024))) uint8_t kvbuf[2][CHUNK_BYTES];
+  __shared__ int32_t sidx[MAX_KPS];
+  __shared__ int scan_tmp[NW];
 
   const int split = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
   const RowInfo ri = load_row_info(q_off, kv_off, b);
   if (r >= ri.R) return;
   const int64_t t = ri.t0 + r;
   const int64_t trow = share_base ? static_cast<int64_t>(share_base[b]) + num_acc[b] : t;
-  const bool trow_ok = trow >= 0 && trow < topk_rows;  // a bad share map selects nothing
+  const bool trow_ok = trow >= 0 && trow < topk_rows && ri.L > 0;  // else nothing selected
   const int32_t* idx = topk + (trow_ok ? trow : 0) * k;
   const int i_begin = split * keys_per_split;
-  const int i_end = !trow_ok ? i_begin : (i_begin + keys_per_split < k ? i_begin + keys_per_split : k);
+  const int i_end =
+      !trow_ok ? i_begin : (i_begin + keys_per_split < k ? i_begin + keys_per_split : k);
 
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int g = lane / 16, c16 = lane % 16;
   const int head = wave * 16 + c16;
 
-  // Q^T fragments: head `head`, dims 32*ks + 8*g .. +8
+  // Q^T fragments: head `head`, dims 32*ks + 8*g .. +8 (loads overlap the index staging)
   bf16x8 qf[18];
   {
     const uint16_t* qrow = q + (t * H + head) * DQK + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const i32x4*>(qrow + 32 * ks));
+    for (int ks = 0; ks < 18; ++ks)
+      qf[ks] = as_bf16x8(*reinterpret_cast<const i32x4*>(qrow + 32 * ks));
   }
+
+  // 1. compact the valid indices of the slice into sidx, in list order
+  int mine[PER_T];
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < PER_T; ++j) {
+    const int i = i_begin + tid * PER_T + j;
+    int p = i < i_end ? idx[i] : -1;
+    p = (p >= 0 && p < ri.L) ? p : -1;
+    mine[j] = p;
+    cnt += p >= 0;
+  }
+  int nvalid;
+  int pos = block_excl_scan<NW>(cnt, scan_tmp, &nvalid);
+#pragma unroll
+  for (int j = 0; j < PER_T; ++j)
+    if (mine[j] >= 0) sidx[pos++] = mine[j];
+  const int nchunks = (nvalid + KC - 1) / KC;
+  for (int i = nvalid + tid; i < nchunks * KC; i += NT) sidx[i] = -1;
+  __syncthreads();
+
+  // 2. chunk c -> LDS buffer: wave-wide 1 KB DMA blocks; lane fills physical unit u
+  const uint16_t* kvreq = kv + ri.kv_base * DQK;
+  auto issue_chunk = [&](int c, int bufsel) {
+    lds_u8* base = (lds_u8*)&kvbuf[bufsel][0];  // generic -> LDS address space
+#pragma unroll 1
+    for (int m = wave; m < BLOCKS; m += NW) {
+      const int u = m * 64 + lane;
+      const int row = u / UNITS, cu = u % UNITS;
+      const int cl = swz(cu, row);  // logical unit stored at physical unit cu
+      int p = sidx[c * KC + row];
+      p = p < 0 ? 0 : p;            // padding rows load position 0 and are masked below
+      __builtin_amdgcn_global_load_lds(kvreq + static_cast<int64_t>(p) * DQK + cl * 8,
+                                       (lds_void*)(base + m * 1024), 16, 0, 0);
+    }
+  };
+
   f32x4 o[DV / 16];
 #pragma unroll
   for (int dt = 0; dt < DV / 16; ++dt) o[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY;  // running max (base-2 logits) of this head
-  float lsum = 0.0f;    // running sum of this lane's share of the keys
+  float m_run = -INFINITY;  // running max (base-2 logits) of this head
+  float lsum = 0.0f;        // running sum of this lane's share of the keys
 
-  for (int i0 = i_begin; i0 < i_end; i0 += KC) {
-    if (tid < KC) {
-      const int i = i0 + tid;
-      const int p = i < i_end ? idx[i] : -1;
-      sidx[tid] = (p >= 0 && p < ri.L) ? p : -1;
-    }
-    __syncthreads();
-    for (int c = tid; c < KC * NCHUNK16; c += NT) {
-      const int row = c / NCHUNK16, ch = c % NCHUNK16;
-      const int p = sidx[row];
-      i32x4 v = {0, 0, 0, 0};
-      if (p >= 0) v = *reinterpret_cast<const i32x4*>(kv + (ri.kv_base + p) * DQK + ch * 8);
-      *reinterpret_cast<i32x4*>(lds + row * ROWB + ch * 16) = v;
-    }
-    __syncthreads();
+  const int sr = c16 >> 2, sc = c16 & 3;  // transposing-read source row / dim block
+  if (nchunks > 0) issue_chunk(0, 0);
+  for (int c = 0; c < nchunks; ++c) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // chunk c is in LDS for every wave; chunk c-1's buffer is free
+    if (c + 1 < nchunks) issue_chunk(c + 1, (c + 1) & 1);  // in flight during the compute
+    const uint8_t* buf = kvbuf[c & 1];
 
-    // S^T for keys 0..15 (s0) and 16..31 (s1): lane holds keys 4g+i / 16+4g+i of head c16
+    // 3. S^T for keys 0..15 (s0) and 16..31 (s1): lane holds keys 4g+i / 16+4g+i of head c16
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    // logical unit 4*ks + g sits at 128*(ks/2) + 16*((4*(ks&1) + g) ^ h(row)) in its row
+    const uint8_t* k0e = buf + c16 * ROWB + 16 * ((g ^ c16 ^ (c16 >> 3)) & 7);
+    const uint8_t* k0o = buf + c16 * ROWB + 16 * (((4 + g) ^ c16 ^ (c16 >> 3)) & 7);
+    const int r1 = 16 + c16;
+    const uint8_t* k1e = buf + r1 * ROWB + 16 * ((g ^ r1 ^ (r1 >> 3)) & 7);
+    const uint8_t* k1o = buf + r1 * ROWB + 16 * (((4 + g) ^ r1 ^ (r1 >> 3)) & 7);
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) {
-      const bf16x8 a0 = as_bf16x8(*reinterpret_cast<const i32x4*>(lds + c16 * ROWB + ks * 64 + g * 16));
-      const bf16x8 a1 = as_bf16x8(*reinterpret_cast<const i32x4*>(lds + (16 + c16) * ROWB + ks * 64 + g * 16));
+      const int off = 128 * (ks >> 1);
+      const bf16x8 a0 = as_bf16x8(*reinterpret_cast<const i32x4*>((ks & 1 ? k0o : k0e) + off));
+      const bf16x8 a1 = as_bf16x8(*reinterpret_cast<const i32x4*>((ks & 1 ? k1o : k1e) + off));
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks], s1, 0, 0, 0);
     }
+    const int kb = c * KC;
     float z[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      z[i] = sidx[4 * g + i] >= 0 ? s0[i] * c2 : -INFINITY;
-      z[4 + i] = sidx[16 + 4 * g + i] >= 0 ? s1[i] * c2 : -INFINITY;
+      z[i] = kb + 4 * g + i < nvalid ? s0[i] * c2 : -INFINITY;
+      z[4 + i] = kb + 16 + 4 * g + i < nvalid ? s1[i] * c2 : -INFINITY;
     }
     float cm = z[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) cm = fmaxf(cm, z[i]);
     cm = fmaxf(cm, __shfl_xor(cm, 16));
     cm = fmaxf(cm, __shfl_xor(cm, 32));
-    const float mn = fmaxf(m, cm);
-    // all keys so far invalid for this head: nothing to add (p = 0, alpha = 1)
-    const float alpha = (m == -INFINITY) ? (mn == -INFINITY ? 1.0f : 0.0f) : exp2f(m - mn);
+    const float mn = fmaxf(m_run, cm);  // finite: every chunk holds at least one valid key
+    const float alpha = m_run == -INFINITY ? 0.0f : exp2f(m_run - mn);
     uint32_t pw[4];
     float psum = 0.0f;
 #pragma unroll
@@ -120,31 +204,36 @@ __global__ __launch_bounds__(NW * 64, NW == 1 ? 1 : 2) void mla_decode_kernel(
       pw[i] = static_cast<uint32_t>(ha) | (static_cast<uint32_t>(hb) << 16);
     }
     lsum = lsum * alpha + psum;
-    m = mn;
+    m_run = mn;
     if (__any(alpha != 1.0f)) {  // wave-uniform: skip the rescale once the max is stable
 #pragma unroll
       for (int dt = 0; dt < DV / 16; ++dt) o[dt] *= alpha;
     }
     const bf16x8 pf = as_bf16x8((i32x4){(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3]});
-    // V^T fragments: dim 16*dt + c16, keys 4g..4g+3 then 16+4g..16+4g+3 (same slots as pf)
-    const uint8_t* r0 = lds + (4 * g) * ROWB;
-    const uint8_t* r1 = lds + (16 + 4 * g) * ROWB;
+
+    // 4. V^T operand via transposing reads: source lane s of group g points at row
+    // key(g, s/4) and dims 16*dt + 4*(s%4) .. +4; the read hands lane i the value
+    // at dim 16*dt + i of rows key(g, 0..3) -- keys 4g..4g+3, then 16+4g..16+4g+3.
+    // dim tile dt reads logical unit 2*dt + sc/2: at 128*(dt/4) + 16*((2*(dt%4) + sc/2) ^ h(row))
+    const int rowA = 4 * g + sr, rowB = 16 + 4 * g + sr;
+    const int hA = (rowA ^ (rowA >> 3)) & 7, hB = (rowB ^ (rowB >> 3)) & 7;
+    const lds_u8* lbuf = (const lds_u8*)buf;  // generic -> LDS address space
+    const int byte_in = (sc & 1) * 8;
 #pragma unroll
-    for (int dt = 0; dt < DV / 16; ++dt) {
-      const int off = (16 * dt + c16) * 2;
-      uint32_t v[4];
-      v[0] = *reinterpret_cast<const uint16_t*>(r0 + off) |
-             (static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(r0 + ROWB + off)) << 16);
-      v[1] = *reinterpret_cast<const uint16_t*>(r0 + 2 * ROWB + off) |
-             (static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(r0 + 3 * ROWB + off)) << 16);
-      v[2] = *reinterpret_cast<const uint16_t*>(r1 + off) |
-             (static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(r1 + ROWB + off)) << 16);
-      v[3] = *reinterpret_cast<const uint16_t*>(r1 + 2 * ROWB + off) |
-             (static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(r1 + 3 * ROWB + off)) << 16);
-      const bf16x8 vf = as_bf16x8((i32x4){(int)v[0], (int)v[1], (int)v[2], (int)v[3]});
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[dt], 0, 0, 0);
+    for (int dq = 0; dq < 4; ++dq) {
+      const lds_u8* pa = lbuf + rowA * ROWB + 16 * (((2 * dq + (sc >> 1)) ^ hA) & 7) + byte_in;
+      const lds_u8* pb = lbuf + rowB * ROWB + 16 * (((2 * dq + (sc >> 1)) ^ hB) & 7) + byte_in;
+#pragma unroll
+      for (int d4 = 0; d4 < 8; ++d4) {
+        const int dt = 4 * d4 + dq;
+        const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(pa + 128 * d4));
+        const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(pb + 128 * d4));
+        const s16x8 v8 = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v8), pf, o[dt],
+                                                       0, 0, 0);
+      }
     }
-    __syncthreads();
+    // no barrier here: the next iteration's barrier precedes any refill of this buffer
   }
 
   float l = lsum + __shfl_xor(lsum, 16);
@@ -160,7 +249,8 @@ __global__ __launch_bounds__(NW * 64, NW == 1 ? 1 : 2) void mla_decode_kernel(
                           (static_cast<uint32_t>(f32_to_bf16_bits(o[dt][3] * inv)) << 16);
       *reinterpret_cast<uint2*>(orow + 16 * dt) = make_uint2(lo, hi);
     }
-    if (lse && g == 0) lse[t * H + head] = l > 0.0f ? (m + __log2f(l)) * 0.69314718055994531f : -INFINITY;
+    if (lse && g == 0)
+      lse[t * H + head] = l > 0.0f ? (m_run + __log2f(l)) * 0.69314718055994531f : -INFINITY;
   } else {
     const int64_t slot = (t * nsplit + split) * H + head;
     float* orow = ws_o + slot * DV + 4 * g;
@@ -168,7 +258,7 @@ __global__ __launch_bounds__(NW * 64, NW == 1 ? 1 : 2) void mla_decode_kernel(
     for (int dt = 0; dt < DV / 16; ++dt)
       *reinterpret_cast<float4*>(orow + 16 * dt) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
     if (g == 0) {
-      ws_ml[2 * slot] = m;
+      ws_ml[2 * slot] = m_run;
       ws_ml[2 * slot + 1] = l;
     }
   }
@@ -201,13 +291,19 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(const float* __restric
   const uint32_t lo = f32_to_bf16_bits(acc.x * inv) | (static_cast<uint32_t>(f32_to_bf16_bits(acc.y * inv)) << 16);
   const uint32_t hi = f32_to_bf16_bits(acc.z * inv) | (static_cast<uint32_t>(f32_to_bf16_bits(acc.w * inv)) << 16);
   reinterpret_cast<uint2*>(out + (t * H + head) * DV)[threadIdx.x] = make_uint2(lo, hi);
-  if (lse && threadIdx.x == 0) lse[t * H + head] = L > 0.0f ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
+  if (lse && threadIdx.x == 0)
+    lse[t * H + head] = L > 0.0f ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 
-// Split count: enough blocks to cover the chip twice, at least 256 keys per split.
+#ifndef DSA_MLA_TARGET_BLOCKS
+#define DSA_MLA_TARGET_BLOCKS 512
+#endif
+
+// Split count: at least ceil(k / 1024) (LDS index staging), then doubled while the grid
+// is below DSA_MLA_TARGET_BLOCKS blocks and each split keeps >= 256 entries.
 int choose_splits(int64_t rows, int k) {
-  int s = 1;
-  while (s < 8 && rows * s < 512 && (k + 2 * s - 1) / (2 * s) >= 256) s *= 2;
+  int s = static_cast<int>(ceil_div(k, MAX_KPS));
+  while (s < 16 && rows * s < DSA_MLA_TARGET_BLOCKS && ceil_div(k, 2 * s) >= 256) s *= 2;
   return s;
 }
 
@@ -235,13 +331,16 @@ extern "C" dsa_status dsa_sparse_mla_decode(const uint16_t* q, const uint16_t* k
                                             size_t ws_bytes, void* stream) {
   using namespace dsa;
   if (H < 16 || H > 128 || H % 16)
-    return fail(DSA_ERR_UNSUPPORTED, "dsa_sparse_mla_decode: H must be a multiple of 16 in [16, 128] (got %d)", H);
-  DSA_REQUIRE(k >= 1, "dsa_sparse_mla_decode: k must be >= 1 (got %d)", k);
+    return fail(DSA_ERR_UNSUPPORTED,
+                "dsa_sparse_mla_decode: H must be a multiple of 16 in [16, 128] (got %d)", H);
+  DSA_REQUIRE(k >= 1 && k <= 16 * MAX_KPS, "dsa_sparse_mla_decode: k must be in [1, %d] (got %d)",
+              16 * MAX_KPS, k);
   DSA_REQUIRE(topk_rows >= 0, "dsa_sparse_mla_decode: topk_rows must be >= 0");
-  DSA_REQUIRE(share_base || topk_rows >= T, "dsa_sparse_mla_decode: topk needs T rows without a share map");
   DSA_REQUIRE(B >= 0 && T >= 0 && max_q_rows >= 0, "dsa_sparse_mla_decode: negative size");
   DSA_REQUIRE((share_base == nullptr) == (num_accepted == nullptr),
               "dsa_sparse_mla_decode: share_base and num_accepted go together");
+  DSA_REQUIRE(share_base || topk_rows >= T,
+              "dsa_sparse_mla_decode: topk needs T rows without a share map");
   DSA_REQUIRE(sm_scale > 0.0f && sm_scale < 1e30f, "dsa_sparse_mla_decode: sm_scale must be positive");
   if (B == 0 || T == 0 || max_q_rows == 0) return ok();
   DSA_REQUIRE(q && kv && topk && q_row_offsets && kv_row_offsets && out,
@@ -249,12 +348,13 @@ extern "C" dsa_status dsa_sparse_mla_decode(const uint16_t* q, const uint16_t* k
   DSA_REQUIRE((reinterpret_cast<uintptr_t>(q) & 15) == 0 && (reinterpret_cast<uintptr_t>(kv) & 15) == 0 &&
                   (reinterpret_cast<uintptr_t>(out) & 15) == 0,
               "dsa_sparse_mla_decode: q, kv and out must be 16-byte aligned");
-  DSA_REQUIRE(B <= 65535 && max_q_rows <= 65535, "dsa_sparse_mla_decode: B and max_q_rows must be <= 65535");
+  DSA_REQUIRE(B <= 65535 && max_q_rows <= 65535,
+              "dsa_sparse_mla_decode: B and max_q_rows must be <= 65535");
   const int s = choose_splits(T, k);
   const size_t need = dsa_sparse_mla_workspace_size(T, H, k);
   if (ws_bytes < need || (need && !ws))
-    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "dsa_sparse_mla_decode: workspace needs %zu bytes (got %zu)",
-                need, ws_bytes);
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL,
+                "dsa_sparse_mla_decode: workspace needs %zu bytes (got %zu)", need, ws_bytes);
   DSA_REQUIRE(!need || (reinterpret_cast<uintptr_t>(ws) & 15) == 0,
               "dsa_sparse_mla_decode: workspace must be 16-byte aligned");
   const int kps = static_cast<int>(keys_per_split(k, s));
@@ -265,10 +365,10 @@ extern "C" dsa_status dsa_sparse_mla_decode(const uint16_t* q, const uint16_t* k
   hipStream_t st = as_stream(stream);
   dim3 grid((unsigned)nsplit, (unsigned)max_q_rows, (unsigned)B);
   const int nw = H / 16;
-#define DSA_MLA_LAUNCH(NWV)                                                                     \
-  hipLaunchKernelGGL(mla_decode_kernel<NWV>, grid, dim3(NWV * 64), 0, st, q, kv, topk,          \
-                     share_base, num_accepted, q_row_offsets, kv_row_offsets, H, k, topk_rows, c2,  \
-                     nsplit, kps, out, lse, ws_o, ws_ml)
+#define DSA_MLA_LAUNCH(NWV)                                                                    \
+  hipLaunchKernelGGL(mla_decode_kernel<NWV>, grid, dim3(NWV * 64), 0, st, q, kv, topk,         \
+                     share_base, num_accepted, q_row_offsets, kv_row_offsets, H, k, topk_rows, \
+                     c2, nsplit, kps, out, lse, ws_o, ws_ml)
   switch (nw) {
     case 1: DSA_MLA_LAUNCH(1); break;
     case 2: DSA_MLA_LAUNCH(2); break;
