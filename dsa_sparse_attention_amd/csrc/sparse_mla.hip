@@ -296,7 +296,7 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(const float* __restric
 }
 
 #ifndef DSA_MLA_TARGET_BLOCKS
-#define DSA_MLA_TARGET_BLOCKS 512
+#define DSA_MLA_TARGET_BLOCKS 256
 #endif
 
 // Split count: at least ceil(k / 1024) (LDS index staging), then doubled while the grid
