@@ -4,15 +4,28 @@
 // indexer output is a top-k of shape (total_seq_len, index_topk); "GLM-5.3 推理全链路
 // (十四)", section "验证段的逐层算子": each verify query selects its own 2048 keys.
 //
-// Selection order: (score desc, position asc). Scores map to order-preserving
-// 32-bit keys (-0.0 canonicalised to +0.0, so equal values tie on position).
-// One 1024-thread block per row:
-//   1. three LDS histogram passes (11 + 11 + 10 key bits) find the exact k-th
-//      largest key theta and how many keys lie strictly above it;
-//   2. one ordered pass emits every position with key > theta plus the lowest
-//      positions with key == theta, using block prefix sums in position order,
-//      so the output comes out ascending with no sort.
-// The row is read four times; after the first pass it is served from L2/MALL.
+// Selection order: (score desc, position asc). Scores map to order-preserving 32-bit
+// keys (-0.0 canonicalised to +0.0, so equal values tie on position). One 1024-thread
+// block per row.
+// Rows of up to 64K scores (fast path) are read once: the top 16 bits of every key go
+// to LDS (128 KB) together with the row maximum; a histogram of each key's distance
+// below the maximum (keys spread over hundreds of bins, so LDS atomics rarely collide)
+// gives the 16-bit class of the k-th largest key; the positions at or above that class
+// (k plus the class population) are compacted in position order with per-wave ballots;
+// their full keys are gathered and the last 16 bits, the ties and the ascending
+// emission run in LDS. Longer rows, or rows whose candidates overflow, take the
+// general path, three reads of the row:
+//   1. histogram of key bits 31..21 into four privatised LDS histograms (one per
+//      group of four waves: indexer scores pile into a few top-bit bins, and one
+//      shared histogram would serialise its atomics), then the bin B1 holding the
+//      k-th largest key;
+//   2. histogram of bits 20..10 of the keys in B1 only, giving the second digit B2;
+//   3. ordered compaction of every key whose top 22 bits are >= (B1, B2) into LDS, in
+//      position order. There are k + (keys sharing theta's top 22 bits) of them, a
+//      few thousand at most for real score distributions.
+// The last 10 bits, the tie count at theta and the ascending emission then run on
+// the LDS candidates only. If the candidates overflow LDS (massive exact ties), a
+// slow path finishes the select and the emission with further reads of the row.
 #include "common.hpp"
 
 namespace dsa {
@@ -20,6 +33,10 @@ namespace {
 
 constexpr int TK_THREADS = 1024;
 constexpr int TK_WAVES = TK_THREADS / 64;
+constexpr int NSUB = 4;        // privatised level-1 histograms
+constexpr int CAND = 8192;     // slow-path LDS candidate capacity (key + position)
+constexpr int FAST_MAX = 65536;  // rows up to this length keep 16-bit keys in LDS
+constexpr int FCAND = 6016;     // fast-path candidate capacity
 
 __device__ __forceinline__ uint32_t order_key(float x) {
   uint32_t u = __float_as_uint(x == 0.0f ? 0.0f : x);
@@ -53,83 +70,66 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, u
   return before + x - v;
 }
 
-__global__ __launch_bounds__(TK_THREADS) void topk_kernel(const float* __restrict__ scores,
-                                                          int64_t ld,
-                                                          const int32_t* __restrict__ q_off,
-                                                          const int64_t* __restrict__ kv_off,
-                                                          int k, int32_t* __restrict__ topk) {
-  __shared__ uint32_t hist[2048];
-  __shared__ uint32_t tmp[2 * TK_WAVES];
-  __shared__ uint32_t sel_bin, sel_above;
-
-  const int b = blockIdx.y, r = blockIdx.x;
-  const RowInfo ri = load_row_info(q_off, kv_off, b);
-  if (r >= ri.R) return;
-  const int64_t t = ri.t0 + r;
-  int64_t n = visible_count(ri, r);
-  if (n > ld) n = ld;  // device lengths beyond the score stride are clipped
-  int32_t* out = topk + t * k;
+// Visit the row as float4s, UNR loads in flight per thread (the passes are
+// latency-bound otherwise), then the scalar tail.
+template <class F>
+__device__ __forceinline__ void for_each_score(const float* srow, int64_t n, F f) {
+  constexpr int UNR = 16;  // 16 x 16 B per thread: a 64K-score row is read in one sweep
   const int tid = threadIdx.x;
-  if (n <= k) {
-    for (int i = tid; i < k; i += TK_THREADS) out[i] = i < n ? i : -1;
-    return;
-  }
-  const float* srow = scores + t * ld;
   const int64_t n4 = n / 4;
   const float4* srow4 = reinterpret_cast<const float4*>(srow);
-
-  // ---- 1. radix select of the k-th largest key ----
-  uint32_t prefix = 0;       // high bits of theta fixed so far
-  uint32_t need = k;         // keys still to take among those matching prefix
-  const int shifts[3] = {21, 10, 0};
-  const int widths[3] = {11, 11, 10};
-#pragma unroll 1
-  for (int level = 0; level < 3; ++level) {
-    const int sh = shifts[level], nb = 1 << widths[level];
-    const int hi_sh = sh + widths[level];  // bits above this level must equal prefix
-    for (int i = tid; i < nb; i += TK_THREADS) hist[i] = 0;
-    __syncthreads();
-    auto add = [&](float x) {
-      const uint32_t key = order_key(x);
-      if (level == 0 || (key >> hi_sh) == prefix) atomicAdd(&hist[(key >> sh) & (nb - 1)], 1u);
-    };
-    for (int64_t i = tid; i < n4; i += TK_THREADS) {
-      const float4 v = srow4[i];
-      add(v.x); add(v.y); add(v.z); add(v.w);
+  for (int64_t i = tid; i < n4; i += UNR * TK_THREADS) {
+    float4 v[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int64_t j = i + u * TK_THREADS;
+      v[u] = j < n4 ? srow4[j] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    for (int64_t i = n4 * 4 + tid; i < n; i += TK_THREADS) add(srow[i]);
-    __syncthreads();
-    // bins in descending order: thread j covers desc slots 2j, 2j+1
-    const int d0 = 2 * tid, d1 = 2 * tid + 1;
-    const uint32_t c0 = d0 < nb ? hist[nb - 1 - d0] : 0u;
-    const uint32_t c1 = d1 < nb ? hist[nb - 1 - d1] : 0u;
-    uint32_t total;
-    const uint32_t ex = block_excl_scan(c0 + c1, tmp, &total);
-    if (ex < need && need <= ex + c0) {
-      sel_bin = nb - 1 - d0;
-      sel_above = ex;
-    } else if (ex + c0 < need && need <= ex + c0 + c1) {
-      sel_bin = nb - 1 - d1;
-      sel_above = ex + c0;
-    }
-    __syncthreads();
-    prefix = (prefix << widths[level]) | sel_bin;
-    need -= sel_above;
-    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < UNR; ++u)
+      if (i + u * TK_THREADS < n4) {
+        f(v[u].x); f(v[u].y); f(v[u].z); f(v[u].w);
+      }
   }
-  const uint32_t theta = prefix;  // exact key of the k-th largest score
-  // keys > theta: k - need of them; ties at theta: take the `need` lowest positions
+  for (int64_t i = n4 * 4 + tid; i < n; i += TK_THREADS) f(srow[i]);
+}
 
-  // ---- 2. ordered emission ----
+// Find the bin holding the need-th largest key of a histogram of nb (<= 2048) bins.
+// Writes the bin and the number of keys in higher bins to *sel (all threads see it).
+__device__ __forceinline__ void select_bin(const uint32_t* hist, int nb, uint32_t need,
+                                           uint32_t* tmp, uint32_t* sel) {
+  const int d0 = 2 * threadIdx.x, d1 = d0 + 1;  // descending slots
+  const uint32_t c0 = d0 < nb ? hist[nb - 1 - d0] : 0u;
+  const uint32_t c1 = d1 < nb ? hist[nb - 1 - d1] : 0u;
+  uint32_t total;
+  const uint32_t ex = block_excl_scan(c0 + c1, tmp, &total);
+  if (ex < need && need <= ex + c0) {
+    sel[0] = nb - 1 - d0;
+    sel[1] = ex;
+  } else if (ex + c0 < need && need <= ex + c0 + c1) {
+    sel[0] = nb - 1 - d1;
+    sel[1] = ex + c0;
+  }
+  __syncthreads();
+}
+
+// Ordered emission over n keys produced by key_at(i) (position pos_at(i)), i in
+// [0, n) in ascending position order: every key > theta and the first `need` keys
+// == theta. Writes ascending positions to out[0..k).
+template <class KeyAt, class PosAt>
+__device__ __forceinline__ void emit_ordered(int64_t n, uint32_t theta, uint32_t need, int k,
+                                             int32_t* out, uint32_t* tmp, KeyAt key_at,
+                                             PosAt pos_at) {
+  const int tid = threadIdx.x;
   uint32_t eq_seen = 0, emitted = 0;
   for (int64_t base = 0; base < n; base += 4 * TK_THREADS) {
-    const int64_t p0 = base + 4 * tid;
+    const int64_t i0 = base + 4 * tid;
     uint32_t key[4];
     bool live[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      live[j] = p0 + j < n;
-      key[j] = live[j] ? order_key(srow[p0 + j]) : 0u;
+      live[j] = i0 + j < n;
+      key[j] = live[j] ? key_at(i0 + j) : 0u;
     }
     uint32_t eqc = 0;
 #pragma unroll
@@ -150,10 +150,297 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const float* __restric
     uint32_t pos = emitted + block_excl_scan(selc, tmp, &sel_total);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      if (sel[j] && pos < static_cast<uint32_t>(k)) out[pos++] = static_cast<int32_t>(p0 + j);
+      if (sel[j] && pos < static_cast<uint32_t>(k)) out[pos++] = pos_at(i0 + j);
     eq_seen += eq_total;
     emitted += sel_total;
   }
+}
+
+__global__ __launch_bounds__(TK_THREADS) void topk_kernel(const float* __restrict__ scores,
+                                                          int64_t ld,
+                                                          const int32_t* __restrict__ q_off,
+                                                          const int64_t* __restrict__ kv_off,
+                                                          int k, int32_t* __restrict__ topk) {
+  // Region A (128 KB): 16-bit keys of the fast path; reused by both paths afterwards.
+  __shared__ __attribute__((aligned(16))) uint32_t regA[32768];
+  __shared__ uint32_t fhist[2048];
+  __shared__ int32_t fpos[FCAND];
+  __shared__ uint32_t tmp[2 * TK_WAVES];
+  __shared__ uint32_t sel[2];
+  __shared__ uint32_t smax;
+  uint32_t (*hist)[2048] = reinterpret_cast<uint32_t (*)[2048]>(regA);  // slow path: NSUB x 8 KB
+  uint32_t* ckey = regA + NSUB * 2048;                                  // slow path: 32 KB
+  int32_t* cpos = reinterpret_cast<int32_t*>(regA + NSUB * 2048 + CAND);  // slow path: 32 KB
+
+  const int b = blockIdx.y, r = blockIdx.x;
+  const RowInfo ri = load_row_info(q_off, kv_off, b);
+  if (r >= ri.R) return;
+  const int64_t t = ri.t0 + r;
+  int64_t n = visible_count(ri, r);
+  if (n > ld) n = ld;  // device lengths beyond the score stride are clipped
+  int32_t* out = topk + t * k;
+  const int tid = threadIdx.x, wave = tid / 64;
+  if (n <= k) {
+    for (int i = tid; i < k; i += TK_THREADS) out[i] = i < n ? i : -1;
+    return;
+  }
+  const float* srow = scores + t * ld;
+
+  if (n <= FAST_MAX) {
+    // ---- fast path A: one read of the row; top 16 key bits to LDS, row maximum ----
+    uint16_t* k16 = reinterpret_cast<uint16_t*>(regA);
+    if (tid == 0) smax = 0;
+    __syncthreads();
+    uint32_t lmax = 0;
+    {
+      constexpr int UNR = 8;
+      const int64_t n4 = n / 4;
+      const float4* s4 = reinterpret_cast<const float4*>(srow);
+      for (int64_t i = tid; i < n4; i += UNR * TK_THREADS) {
+        float4 v[UNR];
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+          const int64_t j = i + u * TK_THREADS;
+          v[u] = j < n4 ? s4[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+          const int64_t j = i + u * TK_THREADS;
+          if (j < n4) {
+            const uint32_t a = order_key(v[u].x) >> 16, bb = order_key(v[u].y) >> 16;
+            const uint32_t c = order_key(v[u].z) >> 16, d = order_key(v[u].w) >> 16;
+            reinterpret_cast<uint2*>(k16)[j] = make_uint2(a | (bb << 16), c | (d << 16));
+            lmax = max(lmax, max(max(a, bb), max(c, d)));
+          }
+        }
+      }
+      for (int64_t i = n4 * 4 + tid; i < n; i += TK_THREADS) {
+        const uint32_t a = order_key(srow[i]) >> 16;
+        k16[i] = static_cast<uint16_t>(a);
+        lmax = max(lmax, a);
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) lmax = max(lmax, static_cast<uint32_t>(__shfl_xor(lmax, o)));
+    if ((tid & 63) == 0) atomicMax(&smax, lmax);
+    for (int i = tid; i < 2048; i += TK_THREADS) fhist[i] = 0;
+    __syncthreads();
+    const uint32_t m16 = smax;
+
+    // ---- fast path B: histogram of the distance below the maximum (bin 2047 - d) ----
+    {
+      auto bin = [&](uint32_t key16) {
+        const uint32_t d = m16 - key16;
+        atomicAdd(&fhist[2047 - (d < 2047 ? d : 2047)], 1u);
+      };
+      const int64_t n8 = n / 8;  // eight 16-bit keys per 16-byte LDS read
+      for (int64_t i = tid; i < n8; i += TK_THREADS) {
+        const uint4 v = reinterpret_cast<const uint4*>(k16)[i];
+        bin(v.x & 0xFFFFu); bin(v.x >> 16); bin(v.y & 0xFFFFu); bin(v.y >> 16);
+        bin(v.z & 0xFFFFu); bin(v.z >> 16); bin(v.w & 0xFFFFu); bin(v.w >> 16);
+      }
+      for (int64_t i = n8 * 8 + tid; i < n; i += TK_THREADS) bin(k16[i]);
+    }
+    __syncthreads();
+    select_bin(fhist, 2048, k, tmp, sel);
+    const uint32_t D = 2047 - sel[0];     // distance of theta's 16-bit class below the max
+    const uint32_t above = sel[1];        // keys strictly closer to the max
+    const uint32_t ncand = above + fhist[sel[0]];
+    __syncthreads();
+    if (D < 2047 && ncand <= FCAND) {
+      const uint32_t c16 = m16 - D;
+      // ---- fast path C: positions with key16 >= c16, compacted in order. Wave w owns a
+      // contiguous segment; a lane takes 8 consecutive keys per 16-byte LDS read, so a
+      // wave step covers 512 positions: count pass, block offsets, write pass.
+      const int lane = tid & 63;
+      const int64_t seg = ((n + TK_WAVES - 1) / TK_WAVES + 511) / 512 * 512;
+      const int64_t lo = wave * seg, hi = lo + seg < n ? lo + seg : n;
+      auto flags = [&](int64_t p0) -> uint32_t {  // bit j: position p0 + 8*lane + j is a candidate
+        const int64_t q = p0 + 8 * lane;
+        uint32_t f = 0;
+        if (q + 7 < hi) {
+          const uint4 v = *reinterpret_cast<const uint4*>(k16 + q);
+          const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            f |= ((w4[j] & 0xFFFFu) >= c16 ? 1u : 0u) << (2 * j);
+            f |= ((w4[j] >> 16) >= c16 ? 1u : 0u) << (2 * j + 1);
+          }
+        } else {
+          for (int j = 0; j < 8; ++j)
+            if (q + j < hi && k16[q + j] >= c16) f |= 1u << j;
+        }
+        return f;
+      };
+      uint32_t cnt = 0;
+      for (int64_t p0 = lo; p0 < hi; p0 += 512) cnt += __popc(flags(p0));
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o);
+      if (lane == 0) tmp[wave] = cnt;
+      __syncthreads();
+      uint32_t base = 0;
+      for (int w = 0; w < wave; ++w) base += tmp[w];
+      for (int64_t p0 = lo; p0 < hi; p0 += 512) {
+        uint32_t f = flags(p0);
+        const uint32_t c = __popc(f);
+        uint32_t x = c;  // inclusive scan of the lane counts
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t y = __shfl_up(x, o);
+          if (lane >= o) x += y;
+        }
+        uint32_t slot = base + x - c;
+        const int64_t q = p0 + 8 * lane;
+        while (f) {
+          const int j = __ffs(f) - 1;
+          f &= f - 1;
+          fpos[slot++] = static_cast<int32_t>(q + j);
+        }
+        base += __shfl(x, 63);
+      }
+      __syncthreads();
+      // ---- fast path D: full keys of the candidates (region A is free again) ----
+      uint32_t* fkey = regA;
+      for (uint32_t j = tid; j < ncand; j += TK_THREADS) fkey[j] = order_key(srow[fpos[j]]);
+      uint32_t* h3 = regA + FCAND;
+      for (int i = tid; i < 2048; i += TK_THREADS) h3[i] = 0;
+      __syncthreads();
+      // ---- fast path E: bits 15..5, then 4..0, of the keys in theta's class ----
+      uint32_t need = k - above;
+      for (uint32_t j = tid; j < ncand; j += TK_THREADS)
+        if ((fkey[j] >> 16) == c16) atomicAdd(&h3[(fkey[j] >> 5) & 2047], 1u);
+      __syncthreads();
+      select_bin(h3, 2048, need, tmp, sel);
+      const uint32_t p27 = (c16 << 11) | sel[0];
+      need -= sel[1];
+      __syncthreads();
+      if (tid < 32) h3[tid] = 0;
+      __syncthreads();
+      for (uint32_t j = tid; j < ncand; j += TK_THREADS)
+        if ((fkey[j] >> 5) == p27) atomicAdd(&h3[fkey[j] & 31], 1u);
+      __syncthreads();
+      select_bin(h3, 32, need, tmp, sel);
+      const uint32_t theta = (p27 << 5) | sel[0];
+      need -= sel[1];
+      __syncthreads();
+      emit_ordered(ncand, theta, need, k, out, tmp, [&](int64_t i) { return fkey[i]; },
+                   [&](int64_t i) { return fpos[i]; });
+      return;
+    }
+    __syncthreads();  // overflow: fall through to the general path (region A is reused)
+  }
+
+  // ---- 1. level-1 digit (bits 31..21) over privatised histograms ----
+  for (int i = tid; i < NSUB * 2048; i += TK_THREADS) (&hist[0][0])[i] = 0;
+  __syncthreads();
+  {
+    uint32_t* h = hist[wave % NSUB];
+    for_each_score(srow, n, [&](float x) { atomicAdd(&h[order_key(x) >> 21], 1u); });
+  }
+  __syncthreads();
+  for (int i = tid; i < 2048; i += TK_THREADS)
+    hist[0][i] = hist[0][i] + hist[1][i] + hist[2][i] + hist[3][i];
+  __syncthreads();
+  select_bin(hist[0], 2048, k, tmp, sel);
+  const uint32_t b1 = sel[0];
+  uint32_t need = k - sel[1];  // keys still to take inside bin b1
+  __syncthreads();
+
+  // ---- 2. level-2 digit (bits 20..10) of the keys in b1 ----
+  uint32_t* h2 = hist[1];
+  for (int i = tid; i < 2048; i += TK_THREADS) h2[i] = 0;
+  __syncthreads();
+  auto add2 = [&](float x) {
+    const uint32_t key = order_key(x);
+    if ((key >> 21) == b1) atomicAdd(&h2[(key >> 10) & 2047], 1u);
+  };
+  for_each_score(srow, n, add2);
+  __syncthreads();
+  select_bin(h2, 2048, need, tmp, sel);
+  const uint32_t p22 = (b1 << 11) | sel[0];  // top 22 bits of theta
+  need -= sel[1];
+  const uint32_t class_count = h2[sel[0]];    // keys sharing theta's top 22 bits
+  const uint32_t ncand = (k - need) + class_count;
+  __syncthreads();
+
+  if (ncand <= CAND) {
+    // ---- 3. compact candidates (top 22 bits >= p22) into LDS in position order ----
+    uint32_t filled = 0;
+    constexpr int PRE = 8;  // tiles loaded ahead of the ordered scans
+    for (int64_t sbase = 0; sbase < n; sbase += PRE * 4 * TK_THREADS) {
+      float4 v[PRE];
+#pragma unroll
+      for (int u = 0; u < PRE; ++u) {
+        const int64_t p0 = sbase + u * 4 * TK_THREADS + 4 * tid;
+        v[u] = p0 + 3 < n ? *reinterpret_cast<const float4*>(srow + p0) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < PRE; ++u) {
+        const int64_t base = sbase + u * 4 * TK_THREADS;
+        if (base >= n) break;  // block-uniform
+        const int64_t p0 = base + 4 * tid;
+        uint32_t key[4];
+        bool c[4];
+        uint32_t cc = 0;
+        if (p0 + 3 < n) {
+          key[0] = order_key(v[u].x); key[1] = order_key(v[u].y);
+          key[2] = order_key(v[u].z); key[3] = order_key(v[u].w);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) c[j] = (key[j] >> 10) >= p22;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            key[j] = p0 + j < n ? order_key(srow[p0 + j]) : 0u;
+            c[j] = p0 + j < n && (key[j] >> 10) >= p22;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cc += c[j] ? 1u : 0u;
+        uint32_t tot;
+        uint32_t slot = filled + block_excl_scan(cc, tmp, &tot);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (c[j]) {
+            ckey[slot] = key[j];
+            cpos[slot] = static_cast<int32_t>(p0 + j);
+            ++slot;
+          }
+        filled += tot;
+      }
+    }
+    __syncthreads();
+    // level-3 digit (bits 9..0) among candidates of the theta class
+    uint32_t* h3 = hist[2];
+    for (int i = tid; i < 1024; i += TK_THREADS) h3[i] = 0;
+    __syncthreads();
+    for (uint32_t i = tid; i < ncand; i += TK_THREADS)
+      if ((ckey[i] >> 10) == p22) atomicAdd(&h3[ckey[i] & 1023], 1u);
+    __syncthreads();
+    select_bin(h3, 1024, need, tmp, sel);
+    const uint32_t theta = (p22 << 10) | sel[0];
+    need -= sel[1];
+    __syncthreads();
+    emit_ordered(ncand, theta, need, k, out, tmp, [&](int64_t i) { return ckey[i]; },
+                 [&](int64_t i) { return cpos[i]; });
+    return;
+  }
+
+  // ---- slow path: level 3 and the emission read the row again ----
+  uint32_t* h3 = hist[2];
+  for (int i = tid; i < 1024; i += TK_THREADS) h3[i] = 0;
+  __syncthreads();
+  auto add3 = [&](float x) {
+    const uint32_t key = order_key(x);
+    if ((key >> 10) == p22) atomicAdd(&h3[key & 1023], 1u);
+  };
+  for_each_score(srow, n, add3);
+  __syncthreads();
+  select_bin(h3, 1024, need, tmp, sel);
+  const uint32_t theta = (p22 << 10) | sel[0];
+  need -= sel[1];
+  __syncthreads();
+  emit_ordered(n, theta, need, k, out, tmp, [&](int64_t i) { return order_key(srow[i]); },
+               [&](int64_t i) { return static_cast<int32_t>(i); });
 }
 
 }  // namespace
