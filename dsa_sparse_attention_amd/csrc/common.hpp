@@ -42,6 +42,27 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16-byte LDS DMA (global_load_lds_dwordx4): lane l copies 16 bytes from `gsrc` to
+// LDS byte lds_base + 16*l; lds_base must be wave-uniform. Issued from inline asm
+// so the compiler keeps no wait bookkeeping of its own for it (it would otherwise
+// wait for every pending DMA before any LDS read it cannot prove disjoint): the
+// caller retires these loads itself with s_waitcnt vmcnt and a barrier before
+// reading the data. Loads retire in order, so the compiler's own vmcnt waits for
+// its loads stay correct (only stricter) while such DMAs are in flight.
+__device__ __forceinline__ void lds_dma16(const void* gsrc, const lds_void* lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_base)));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gsrc), "s"(m0)
+               : "memory");
+}
+
+// s_waitcnt vmcnt(n) (expcnt and lgkmcnt left alone), n <= 15.
+#define DSA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15))
+
 // Row bookkeeping of the ragged verify batch: request b, row r of R_b rows,
 // L_b cached positions; the row sits at position L_b - R_b + r.
 struct RowInfo {

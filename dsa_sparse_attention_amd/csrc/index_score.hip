@@ -23,6 +23,7 @@ namespace dsa {
 namespace {
 
 constexpr int KT = 64;  // keys per LDS tile
+constexpr int MAX_CHUNK = 4096;  // keys per block (key scales staged in LDS)
 
 template <int D, int HT, int NW>
 __global__ __launch_bounds__(NW * 64) void index_score_kernel(
@@ -35,7 +36,9 @@ __global__ __launch_bounds__(NW * 64) void index_score_kernel(
   constexpr int CH = KT * NCH;                // chunks per tile
   constexpr int NT = NW * 64;
   constexpr int PER = (CH + NT - 1) / NT;     // chunk loads per thread per tile
+  constexpr int NPRE = PER >= 4 ? 1 : 4 / PER;  // tiles in flight per block
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][KT * D];
+  __shared__ float sscale[MAX_CHUNK];
 
   const int b = blockIdx.y;
   const RowInfo ri = load_row_info(q_off, kv_off, b);
@@ -58,17 +61,22 @@ __global__ __launch_bounds__(NW * 64) void index_score_kernel(
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
     const int head = ht * 16 + c16;
-    i32x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (row_live && head < H && 32 * g < D) {
-      const i32x4* p = reinterpret_cast<const i32x4*>(q_fp8 + (t * H + head) * D + 32 * g);
-      i32x4 lo = p[0], hi = p[1];
-      v = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    }
-    qa[ht] = v;
+    // branch-free loads from clamped addresses; invalid lanes are zeroed afterwards
+    const bool qok = row_live && head < H && 32 * g < D;
+    const int64_t tq = row_live ? t : ri.t0;
+    const int hq = head < H ? head : H - 1;
+    const int gq = 32 * g < D ? g : 0;
+    const i32x4* p = reinterpret_cast<const i32x4*>(q_fp8 + (tq * H + hq) * D + 32 * gq);
+    const i32x4 lo = p[0], hi = p[1];
+    const i32x8 v = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    const i32x8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+    qa[ht] = qok ? v : zero8;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int h2 = ht * 16 + 4 * g + i;
-      u[ht][i] = (row_live && h2 < H) ? w[t * H + h2] * q_scale[t * H + h2] : 0.0f;
+      const int64_t o = tq * H + (h2 < H ? h2 : H - 1);
+      const float uu = w[o] * q_scale[o];
+      u[ht][i] = (row_live && h2 < H) ? uu : 0.0f;
     }
   }
 
@@ -76,63 +84,92 @@ __global__ __launch_bounds__(NW * 64) void index_score_kernel(
   const int64_t nkeys = key_end - key0;
   const int ntiles = static_cast<int>((nkeys + KT - 1) / KT);
 
-  i32x4 pre[PER];
-  auto load_tile = [&](int it) {
+  // Key scales of the whole chunk go to LDS once (chunk <= 4096 keys).
+  for (int i0 = 0; i0 < nkeys; i0 += 4 * NT) {  // four independent loads per thread per step
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = i0 + j * NT + static_cast<int>(threadIdx.x);
+      v[j] = k_scale[ri.kv_base + key0 + (i < nkeys ? i : nkeys - 1)];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = i0 + j * NT + static_cast<int>(threadIdx.x);
+      if (i < nkeys) sscale[i] = v[j];
+    }
+  }
+
+  // Register ring: each thread holds its 16-byte pieces of the next NPRE tiles, so
+  // NPRE tiles per block are in flight while one is computed (the loop is unrolled
+  // by NPRE so every ring slot is a fixed register).
+  i32x4 pre[NPRE][PER];
+  auto load_tile = [&](int it, i32x4* dst) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-      const int idx = threadIdx.x + j * NT;
+      // branch-free: keys past the chunk load the last key again (their scores are
+      // never stored); pieces past the tile (idx >= CH) are never written to LDS
+      const int idx = threadIdx.x + j * NT < CH ? threadIdx.x + j * NT : CH - 1;
       const int s = idx / NCH, c = idx % NCH;
-      i32x4 v = {0, 0, 0, 0};
-      if (idx < CH && static_cast<int64_t>(it) * KT + s < nkeys)
-        v = *reinterpret_cast<const i32x4*>(kbase + (static_cast<int64_t>(it) * KT + s) * D + c * 16);
-      pre[j] = v;
+      int64_t key = static_cast<int64_t>(it) * KT + s;
+      key = key < nkeys ? key : nkeys - 1;
+      dst[j] = *reinterpret_cast<const i32x4*>(kbase + key * D + c * 16);
     }
   };
-  auto store_tile = [&](uint8_t* buf) {
+  auto store_tile = [&](uint8_t* buf, const i32x4* src) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int idx = threadIdx.x + j * NT;
       if (idx < CH) {
         const int s = idx / NCH, c = idx % NCH;
-        *reinterpret_cast<i32x4*>(buf + s * D + ((c ^ (s & (NCH - 1))) * 16)) = pre[j];
+        *reinterpret_cast<i32x4*>(buf + s * D + ((c ^ (s & (NCH - 1))) * 16)) = src[j];
       }
     }
   };
 
-  load_tile(0);
-  for (int it = 0; it < ntiles; ++it) {
-    uint8_t* buf = lds[it & 1];
-    store_tile(buf);
-    __syncthreads();
-    if (it + 1 < ntiles) load_tile(it + 1);
-    if (row_live) {
-      float res[4];
 #pragma unroll
-      for (int sub = 0; sub < 4; ++sub) {
-        const int s = sub * 16 + c16;
-        i32x8 bfrag = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (32 * g < D) {
-          const int c0 = 2 * g, c1 = 2 * g + 1;
-          i32x4 lo = *reinterpret_cast<const i32x4*>(buf + s * D + ((c0 ^ (s & (NCH - 1))) * 16));
-          i32x4 hi = *reinterpret_cast<const i32x4*>(buf + s * D + ((c1 ^ (s & (NCH - 1))) * 16));
-          bfrag = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  for (int j = 0; j < NPRE; ++j)
+    if (j < ntiles) load_tile(j, pre[j]);
+  for (int base = 0; base < ntiles; base += NPRE) {
+#pragma unroll
+    for (int jr = 0; jr < NPRE; ++jr) {
+      const int it = base + jr;
+      if (it >= ntiles) break;  // block-uniform
+      uint8_t* buf = lds[it & 1];
+      store_tile(buf, pre[jr]);
+      __syncthreads();  // tile `it` is in LDS; the other buffer (tile it-1) is no longer read
+      if (it + NPRE < ntiles) load_tile(it + NPRE, pre[jr]);
+      if (row_live) {
+        float res[4];
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub) {
+          const int s = sub * 16 + c16;
+          i32x8 bfrag = {0, 0, 0, 0, 0, 0, 0, 0};
+          if (32 * g < D) {
+            const int c0 = 2 * g, c1 = 2 * g + 1;
+            i32x4 lo = *reinterpret_cast<const i32x4*>(buf + s * D + ((c0 ^ (s & (NCH - 1))) * 16));
+            i32x4 hi = *reinterpret_cast<const i32x4*>(buf + s * D + ((c1 ^ (s & (NCH - 1))) * 16));
+            bfrag = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          }
+          float part = 0.0f;
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[ht], bfrag, acc, 0, 0, 0, 0,
+                                                                   0, 0);
+            // ReLU as med3(x, 0, FLT_MAX): one instruction (max(x, 0) for finite x)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              part = fmaf(u[ht][i], __builtin_amdgcn_fmed3f(acc[i], 0.0f, 3.402823466e38f), part);
+          }
+          part += __shfl_xor(part, 16);
+          part += __shfl_xor(part, 32);
+          res[sub] = part;
         }
-        float part = 0.0f;
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[ht], bfrag, acc, 0, 0, 0, 0,
-                                                                 0, 0);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) part = fmaf(u[ht][i], fmaxf(acc[i], 0.0f), part);
-        }
-        part += __shfl_xor(part, 16);
-        part += __shfl_xor(part, 32);
-        res[sub] = part;
+        const float v = g == 0 ? res[0] : g == 1 ? res[1] : g == 2 ? res[2] : res[3];
+        const int sl = it * KT + g * 16 + c16;         // key within the chunk
+        const int64_t s = key0 + sl;                    // request-local position
+        if (s < key_end && s < nvis) scores[t * ld + s] = v * sscale[sl];
       }
-      const float v = g == 0 ? res[0] : g == 1 ? res[1] : g == 2 ? res[2] : res[3];
-      const int64_t s = key0 + static_cast<int64_t>(it) * KT + g * 16 + c16;  // request-local
-      if (s < key_end && s < nvis) scores[t * ld + s] = v * k_scale[ri.kv_base + s];
     }
   }
 }

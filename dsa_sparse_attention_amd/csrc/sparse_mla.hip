@@ -41,7 +41,6 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(i32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -135,8 +134,8 @@ __global__ __launch_bounds__(NW * 64, NW == 1 ? 1 : 2) void mla_decode_kernel(
 
   // 2. chunk c -> LDS buffer: wave-wide 1 KB DMA blocks; lane fills physical unit u
   const uint16_t* kvreq = kv + ri.kv_base * DQK;
-  auto issue_chunk = [&](int c, int bufsel) {
-    lds_u8* base = (lds_u8*)&kvbuf[bufsel][0];  // generic -> LDS address space
+  auto issue_chunk = [&](int c) {
+    const lds_u8* base = (const lds_u8*)kvbuf[c & 1];  // generic -> LDS address space
 #pragma unroll 1
     for (int m = wave; m < BLOCKS; m += NW) {
       const int u = m * 64 + lane;
@@ -144,8 +143,7 @@ __global__ __launch_bounds__(NW * 64, NW == 1 ? 1 : 2) void mla_decode_kernel(
       const int cl = swz(cu, row);  // logical unit stored at physical unit cu
       int p = sidx[c * KC + row];
       p = p < 0 ? 0 : p;            // padding rows load position 0 and are masked below
-      __builtin_amdgcn_global_load_lds(kvreq + static_cast<int64_t>(p) * DQK + cl * 8,
-                                       (lds_void*)(base + m * 1024), 16, 0, 0);
+      lds_dma16(kvreq + static_cast<int64_t>(p) * DQK + cl * 8, (const lds_void*)(base + m * 1024));
     }
   };
 
@@ -156,11 +154,12 @@ __global__ __launch_bounds__(NW * 64, NW == 1 ? 1 : 2) void mla_decode_kernel(
   float lsum = 0.0f;        // running sum of this lane's share of the keys
 
   const int sr = c16 >> 2, sc = c16 & 3;  // transposing-read source row / dim block
-  if (nchunks > 0) issue_chunk(0, 0);
+  if (nchunks > 0) issue_chunk(0);
+#pragma unroll 1
   for (int c = 0; c < nchunks; ++c) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // chunk c is in LDS for every wave; chunk c-1's buffer is free
-    if (c + 1 < nchunks) issue_chunk(c + 1, (c + 1) & 1);  // in flight during the compute
+    DSA_WAIT_VMCNT(0);  // the only loads in flight: chunk c
+    __syncthreads();    // chunk c is in LDS for every wave; chunk c-1's buffer is free
+    if (c + 1 < nchunks) issue_chunk(c + 1);  // in flight during the compute
     const uint8_t* buf = kvbuf[c & 1];
 
     // 3. S^T for keys 0..15 (s0) and 16..31 (s1): lane holds keys 4g+i / 16+4g+i of head c16
@@ -233,7 +232,6 @@ __global__ __launch_bounds__(NW * 64, NW == 1 ? 1 : 2) void mla_decode_kernel(
                                                        0, 0, 0);
       }
     }
-    // no barrier here: the next iteration's barrier precedes any refill of this buffer
   }
 
   float l = lsum + __shfl_xor(lsum, 16);
