@@ -60,8 +60,9 @@ __device__ __forceinline__ void lds_dma16(const void* gsrc, const lds_void* lds_
                : "memory");
 }
 
-// s_waitcnt vmcnt(n) (expcnt and lgkmcnt left alone), n <= 15.
-#define DSA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15))
+// s_waitcnt vmcnt(n) (expcnt and lgkmcnt left alone), constant n <= 63: vmcnt is
+// split over bits 3:0 and 15:14 of the immediate.
+#define DSA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
 
 // Row bookkeeping of the ragged verify batch: request b, row r of R_b rows,
 // L_b cached positions; the row sits at position L_b - R_b + r.

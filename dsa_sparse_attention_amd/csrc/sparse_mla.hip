@@ -17,7 +17,9 @@
 //     both read patterns below free of bank conflicts.
 //  3. S^T[key, head] = K[32 x 576] . Q^T with v_mfma_f32_16x16x32_bf16 (Q^T
 //     fragments stay in registers); online softmax per head in base 2, one
-//     head per lane column.
+//     head per lane column, with a lazy reference max: it moves (and the
+//     accumulators are rescaled) only when a chunk's max exceeds it by more
+//     than 2^8, so P <= 2^8 and the result is unchanged up to rounding.
 //  4. O^T[dim, head] += V^T . P^T: P^T is the S^T accumulator itself (no data
 //     movement); the V^T operand comes from ds_read_b64_tr_b16, which
 //     transposes 4x4 blocks of bf16 across lanes while reading, so each 16x32
@@ -31,11 +33,12 @@ namespace {
 
 constexpr int DQK = 576, DV = 512;
 constexpr int KC = 32;                      // latent rows per chunk
-constexpr int ROWB = DQK * 2;               // 1152 bytes per latent row in LDS (unpadded)
-constexpr int UNITS = ROWB / 16;            // 72 16-byte units per row
-constexpr int CHUNK_BYTES = KC * ROWB;      // 36864
+constexpr int UNITS = DQK * 2 / 16;         // 72 16-byte units (8 dims each) per latent row
+constexpr int UNIT_BYTES = KC * 16;         // 512: one unit of all 32 rows of a chunk
+constexpr int CHUNK_BYTES = UNITS * UNIT_BYTES;  // 36864
 constexpr int BLOCKS = CHUNK_BYTES / 1024;  // 36 wave-wide (64 x 16 B) DMA blocks per chunk
 constexpr int MAX_KPS = 1024;               // top-k entries per split (LDS index staging)
+constexpr float LAZY = 8.0f;                // reference-max slack, log2 units
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -44,12 +47,17 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(i32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Physical position of logical 16-byte unit c of latent row `row` in LDS: the
-// low 3 bits are XORed with a row hash so 16 consecutive rows read at the same
-// logical unit hit 16 different bank groups. An involution: swz(swz(c)) == c.
-__device__ __forceinline__ int swz(int c, int row) {
-  return (c & ~7) | ((c ^ row ^ (row >> 3)) & 7);
-}
+// Chunk layout in LDS, unit-major: byte 512*u + 16*cell(r, u) holds dims 8u..8u+7 of the
+// chunk's row r, with cell(r, u) = r ^ (4 * (u & 1)) (an involution in r).
+//  - A K fragment read (16 lanes = rows 0..15 or 16..31 at one unit) is a contiguous
+//    256-byte block: no bank conflicts.
+//  - A transposing V read (16 lanes = 4 rows 4j..4j+3 x 2 adjacent units 2d, 2d+1)
+//    lands on two disjoint 64-byte runs of the 256-byte bank window, thanks to the
+//    4-row offset of odd units.
+//  - A wave-wide DMA block m (1 KB) is units 2m and 2m+1: lane l writes cell l%32 of
+//    unit 2m + l/32, so it loads chunk row (l%32) ^ (4*(l/32)) for every m -- one row
+//    per lane per chunk, with a per-DMA offset of 32*m bytes in the source row.
+__device__ __forceinline__ int cell(int row, int unit) { return row ^ (4 * (unit & 1)); }
 
 template <int NW>
 __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
@@ -74,6 +82,8 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
 }
 
 // Two waves per SIMD: caps the kernel at 256 registers per lane (Q^T 72, O^T 128, rest).
+// NW is a power of two (1, 2, 4, 8); heads past H are computed on zero queries and
+// never stored.
 template <int NW>
 __global__ __launch_bounds__(NW * 64, NW == 1 ? 1 : 2) void mla_decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
@@ -84,9 +94,24 @@ __global__ __launch_bounds__(NW * 64, NW == 1 ? 1 : 2) void mla_decode_kernel(
     float* __restrict__ ws_o, float* __restrict__ ws_ml) {
   constexpr int NT = NW * 64;
   constexpr int PER_T = (MAX_KPS + NT - 1) / NT;  // index entries per thread
+  constexpr int DTW = (DV / 16) / NW;             // 16-dim output tiles per wave
+  constexpr int DMA_PER = (BLOCKS + NW - 1) / NW; // DMA blocks per wave per chunk
+  static_assert((NW & (NW - 1)) == 0 && NW <= 8, "NW must be 1, 2, 4 or 8");
+  static_assert(DTW % 4 == 0, "a wave's first dim tile is a multiple of 4");
   __shared__ __attribute__((aligned(1024))) uint8_t kvbuf[2][CHUNK_BYTES];
   __shared__ int32_t sidx[MAX_KPS];
   __shared__ int scan_tmp[NW];
+  __shared__ float sh_alpha[NW * 16]; // rescale factor of each head this chunk
+  __shared__ int sh_resc[NW];         // wave h moved its reference this chunk
+  // P^T operands of every wave (NW x 64 lanes x 16 B). Up to 4 KB they live in the rope
+  // units (64..71, the last 4 KB) of the chunk being computed, dead once S^T is done;
+  // 128 heads need a buffer of their own.
+  constexpr bool P_IN_ROPE = NW <= 4;
+  __shared__ i32x4 pbuf_own[P_IN_ROPE ? 1 : NW * 64];
+  auto pslot = [&](const uint8_t* buf, int h, int ln) -> i32x4* {
+    const int sl = h * 64 + ln;
+    return P_IN_ROPE ? (i32x4*)(buf + 64 * UNIT_BYTES + 16 * sl) : &pbuf_own[sl];
+  };
 
   const int split = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
   const RowInfo ri = load_row_info(q_off, kv_off, b);
@@ -99,17 +124,23 @@ __global__ __launch_bounds__(NW * 64, NW == 1 ? 1 : 2) void mla_decode_kernel(
   const int i_end =
       !trow_ok ? i_begin : (i_begin + keys_per_split < k ? i_begin + keys_per_split : k);
 
-  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const int tid = threadIdx.x, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // wave-uniform, kept in an SGPR
   const int g = lane / 16, c16 = lane % 16;
-  const int head = wave * 16 + c16;
+  const int head = wave * 16 + c16;  // head of this lane's column in the S/softmax phase
+  const bool head_ok = head < H;
 
-  // Q^T fragments: head `head`, dims 32*ks + 8*g .. +8 (loads overlap the index staging)
+  // Q^T fragments: head `head`, dims 32*ks + 8*g .. +8 (loads overlap the index staging).
+  // Heads past H read head H-1 and are zeroed.
   bf16x8 qf[18];
   {
-    const uint16_t* qrow = q + (t * H + head) * DQK + 8 * g;
+    const uint16_t* qrow = q + (t * H + (head_ok ? head : H - 1)) * DQK + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks)
-      qf[ks] = as_bf16x8(*reinterpret_cast<const i32x4*>(qrow + 32 * ks));
+    for (int ks = 0; ks < 18; ++ks) {
+      const i32x4 v = *reinterpret_cast<const i32x4*>(qrow + 32 * ks);
+      const i32x4 zero = {0, 0, 0, 0};
+      qf[ks] = as_bf16x8(head_ok ? v : zero);
+    }
   }
 
   // 1. compact the valid indices of the slice into sidx, in list order
@@ -132,52 +163,70 @@ __global__ __launch_bounds__(NW * 64, NW == 1 ? 1 : 2) void mla_decode_kernel(
   for (int i = nvalid + tid; i < nchunks * KC; i += NT) sidx[i] = -1;
   __syncthreads();
 
-  // 2. chunk c -> LDS buffer: wave-wide 1 KB DMA blocks; lane fills physical unit u
+  // 2. chunk c -> LDS slot c&1 in wave-wide 1 KB DMA blocks m = wave + j*NW. Lane l
+  // loads chunk row (l%32) ^ (4*(l/32)) for all of them: dims 8*(2m + l/32) .. +8.
+  // `ln` is an opaque copy of the lane index (recomputed per chunk rather than hoisted
+  // into registers held across the loop).
   const uint16_t* kvreq = kv + ri.kv_base * DQK;
-  auto issue_chunk = [&](int c) {
-    const lds_u8* base = (const lds_u8*)kvbuf[c & 1];  // generic -> LDS address space
-#pragma unroll 1
-    for (int m = wave; m < BLOCKS; m += NW) {
-      const int u = m * 64 + lane;
-      const int row = u / UNITS, cu = u % UNITS;
-      const int cl = swz(cu, row);  // logical unit stored at physical unit cu
-      int p = sidx[c * KC + row];
-      p = p < 0 ? 0 : p;            // padding rows load position 0 and are masked below
-      lds_dma16(kvreq + static_cast<int64_t>(p) * DQK + cl * 8, (const lds_void*)(base + m * 1024));
-    }
+  auto dma_src = [&](int c, int ln) {  // this lane's source for DMA block 0 of chunk c
+    const int p = sidx[c * KC + ((ln & 31) ^ (4 * (ln >> 5)))];
+    // padding rows load position 0 and are masked below
+    return kvreq + static_cast<int64_t>(p < 0 ? 0 : p) * DQK + 8 * (ln >> 5);
+  };
+  auto dma_one = [&](int c, int j, const uint16_t* src) {
+    const int m = wave + j * NW;
+    if (m < BLOCKS)  // wave-uniform
+      lds_dma16(src + 16 * m, (const lds_void*)((const lds_u8*)kvbuf[c & 1] + m * 1024));
   };
 
-  f32x4 o[DV / 16];
+  f32x4 o[DTW][NW];  // O^T tiles: dims 16*(wave*DTW + d) .., heads 16h .. of the block
 #pragma unroll
-  for (int dt = 0; dt < DV / 16; ++dt) o[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;  // running max (base-2 logits) of this head
-  float lsum = 0.0f;        // running sum of this lane's share of the keys
+  for (int d = 0; d < DTW; ++d)
+#pragma unroll
+    for (int h = 0; h < NW; ++h) o[d][h] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY;  // reference max (base-2 logits) of head `head`
+  float lsum = 0.0f;        // running sum of this lane's share of the keys of `head`
 
-  const int sr = c16 >> 2, sc = c16 & 3;  // transposing-read source row / dim block
-  if (nchunks > 0) issue_chunk(0);
+  if (nchunks > 0) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const uint16_t* src = dma_src(0, ln);
+#pragma unroll
+    for (int j = 0; j < DMA_PER; ++j) dma_one(0, j, src);
+  }
 #pragma unroll 1
   for (int c = 0; c < nchunks; ++c) {
     DSA_WAIT_VMCNT(0);  // the only loads in flight: chunk c
-    __syncthreads();    // chunk c is in LDS for every wave; chunk c-1's buffer is free
-    if (c + 1 < nchunks) issue_chunk(c + 1);  // in flight during the compute
+    __syncthreads();    // chunk c is in LDS for every wave; chunk c-1's slot and pbuf are free
+    const bool more = c + 1 < nchunks;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const uint16_t* src = more ? dma_src(c + 1, ln) : kvreq;
     const uint8_t* buf = kvbuf[c & 1];
 
-    // 3. S^T for keys 0..15 (s0) and 16..31 (s1): lane holds keys 4g+i / 16+4g+i of head c16
+    // 3. S^T for keys 0..15 (s0) and 16..31 (s1): lane holds keys 4g+i / 16+4g+i of head
+    // `head`. Chunk c+1's DMAs are spread over this loop, so the wave never stalls on a
+    // burst of them.
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    // logical unit 4*ks + g sits at 128*(ks/2) + 16*((4*(ks&1) + g) ^ h(row)) in its row
-    const uint8_t* k0e = buf + c16 * ROWB + 16 * ((g ^ c16 ^ (c16 >> 3)) & 7);
-    const uint8_t* k0o = buf + c16 * ROWB + 16 * (((4 + g) ^ c16 ^ (c16 >> 3)) & 7);
-    const int r1 = 16 + c16;
-    const uint8_t* k1e = buf + r1 * ROWB + 16 * ((g ^ r1 ^ (r1 >> 3)) & 7);
-    const uint8_t* k1o = buf + r1 * ROWB + 16 * (((4 + g) ^ r1 ^ (r1 >> 3)) & 7);
+    // k-step ks: lane (g, c16) reads unit 4ks + g of rows c16 (s0) and 16 + c16 (s1)
+    const uint8_t* kfrag = buf + g * UNIT_BYTES + 16 * cell(c16, g);
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) {
-      const int off = 128 * (ks >> 1);
-      const bf16x8 a0 = as_bf16x8(*reinterpret_cast<const i32x4*>((ks & 1 ? k0o : k0e) + off));
-      const bf16x8 a1 = as_bf16x8(*reinterpret_cast<const i32x4*>((ks & 1 ? k1o : k1e) + off));
+      if (more) {
+#pragma unroll
+        for (int j = ks * DMA_PER / 18; j < (ks + 1) * DMA_PER / 18; ++j) dma_one(c + 1, j, src);
+      }
+      const uint8_t* kp = kfrag + 4 * ks * UNIT_BYTES;
+      const bf16x8 a0 = as_bf16x8(*reinterpret_cast<const i32x4*>(kp));
+      const bf16x8 a1 = as_bf16x8(*reinterpret_cast<const i32x4*>(kp + 16 * 16));
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks], s1, 0, 0, 0);
     }
+
+    // 4. softmax of this wave's 16 heads with a lazy reference max: it moves (and the
+    // accumulators are rescaled) only when the chunk max exceeds it by more than
+    // 2^LAZY; otherwise P <= 2^LAZY, and the reference cancels between numerator and
+    // denominator.
     const int kb = c * KC;
     float z[8];
 #pragma unroll
@@ -189,75 +238,129 @@ __global__ __launch_bounds__(NW * 64, NW == 1 ? 1 : 2) void mla_decode_kernel(
 #pragma unroll
     for (int i = 1; i < 8; ++i) cm = fmaxf(cm, z[i]);
     cm = fmaxf(cm, __shfl_xor(cm, 16));
-    cm = fmaxf(cm, __shfl_xor(cm, 32));
-    const float mn = fmaxf(m_run, cm);  // finite: every chunk holds at least one valid key
-    const float alpha = m_run == -INFINITY ? 0.0f : exp2f(m_run - mn);
+    cm = fmaxf(cm, __shfl_xor(cm, 32));  // finite: every chunk holds at least one valid key
+    const bool resc = __any(cm > m_ref + LAZY);  // wave-uniform; always on the first chunk
+    if (resc) {
+      const float mn = cm > m_ref + LAZY ? cm : m_ref;
+      const float alpha = exp2f(m_ref - mn);  // 0 on the first chunk, 1 if unchanged
+      lsum *= alpha;
+      m_ref = mn;
+      if (g == 0) sh_alpha[head] = alpha;
+    }
+    if (lane == 0) sh_resc[wave] = resc;
     uint32_t pw[4];
     float psum = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float pa = z[2 * i] == -INFINITY ? 0.0f : exp2f(z[2 * i] - mn);
-      const float pb = z[2 * i + 1] == -INFINITY ? 0.0f : exp2f(z[2 * i + 1] - mn);
-      const uint16_t ha = f32_to_bf16_bits(pa), hb = f32_to_bf16_bits(pb);
+      const uint16_t ha = f32_to_bf16_bits(exp2f(z[2 * i] - m_ref));  // masked keys: 0
+      const uint16_t hb = f32_to_bf16_bits(exp2f(z[2 * i + 1] - m_ref));
       psum += bf16_bits_to_f32(ha) + bf16_bits_to_f32(hb);
       pw[i] = static_cast<uint32_t>(ha) | (static_cast<uint32_t>(hb) << 16);
     }
-    lsum = lsum * alpha + psum;
-    m_run = mn;
-    if (__any(alpha != 1.0f)) {  // wave-uniform: skip the rescale once the max is stable
-#pragma unroll
-      for (int dt = 0; dt < DV / 16; ++dt) o[dt] *= alpha;
-    }
-    const bf16x8 pf = as_bf16x8((i32x4){(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3]});
+    lsum += psum;
+    // The P^T operand of the 16x16x32 MFMA: lane (head c16, group g) holds keys
+    // 4g..4g+3 and 16+4g..16+4g+3 (the K index order shared with the V^T operand).
+    __syncthreads();  // every wave is done reading K (the rope columns take P^T)
+    *pslot(buf, wave, lane) = (i32x4){(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3]};
+    __syncthreads();  // every wave's P^T and rescale factors are in LDS
 
-    // 4. V^T operand via transposing reads: source lane s of group g points at row
-    // key(g, s/4) and dims 16*dt + 4*(s%4) .. +4; the read hands lane i the value
-    // at dim 16*dt + i of rows key(g, 0..3) -- keys 4g..4g+3, then 16+4g..16+4g+3.
-    // dim tile dt reads logical unit 2*dt + sc/2: at 128*(dt/4) + 16*((2*(dt%4) + sc/2) ^ h(row))
-    const int rowA = 4 * g + sr, rowB = 16 + 4 * g + sr;
-    const int hA = (rowA ^ (rowA >> 3)) & 7, hB = (rowB ^ (rowB >> 3)) & 7;
-    const lds_u8* lbuf = (const lds_u8*)buf;  // generic -> LDS address space
-    const int byte_in = (sc & 1) * 8;
+    // 5. O^T[dim, head] += V^T . P^T for this wave's dims and every head of the block. The
+    // V^T operand comes from transposing reads: source lane s of group g points at row
+    // key(g, s/4) and dims 16*dt + 4*(s%4) .. +4; the read hands lane i the value at dim
+    // 16*dt + i of rows key(g, 0..3) -- keys 4g..4g+3, then 16+4g..16+4g+3.
+    // Rescale the tiles of heads whose wave moved its reference this chunk.
 #pragma unroll
-    for (int dq = 0; dq < 4; ++dq) {
-      const lds_u8* pa = lbuf + rowA * ROWB + 16 * (((2 * dq + (sc >> 1)) ^ hA) & 7) + byte_in;
-      const lds_u8* pb = lbuf + rowB * ROWB + 16 * (((2 * dq + (sc >> 1)) ^ hB) & 7) + byte_in;
+    for (int h = 0; h < NW; ++h) {
+      if (sh_resc[h]) {  // block-uniform
+        const float a = sh_alpha[16 * h + c16];
 #pragma unroll
-      for (int d4 = 0; d4 < 8; ++d4) {
-        const int dt = 4 * d4 + dq;
-        const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(pa + 128 * d4));
-        const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(pb + 128 * d4));
-        const s16x8 v8 = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v8), pf, o[dt],
-                                                       0, 0, 0);
+        for (int d = 0; d < DTW; ++d) o[d][h] *= a;
+      }
+    }
+    // Dim tile dt: source lane (group g, s = lane%16) points at row 4g + s/4 (+16 for
+    // the second read), unit 2dt + (s%4)/2, byte 8*(s%2) of the unit cell. `ln` keeps the
+    // lane-dependent base from being hoisted across the loop.
+    const int g2 = ln >> 4, s2 = ln & 15;
+    const int vu = (s2 & 3) >> 1;  // unit parity
+    const lds_u8* vbase = (const lds_u8*)buf + vu * UNIT_BYTES +
+                          16 * cell(4 * g2 + (s2 >> 2), vu) + 8 * (s2 & 1);
+    auto v_operand = [&](int d) {
+      const int dt = wave * DTW + d;
+      const lds_u8* pa = vbase + 2 * dt * UNIT_BYTES;
+      const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)pa);
+      const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(pa + 16 * 16));
+      const s16x4 v8[2] = {va, vb};
+      return __builtin_bit_cast(bf16x8, v8);
+    };
+    if constexpr (NW <= 4) {  // all P^T operands in registers, one V^T operand at a time
+      bf16x8 pf[NW];
+#pragma unroll
+      for (int h = 0; h < NW; ++h) pf[h] = as_bf16x8(*pslot(buf, h, lane));
+#pragma unroll
+      for (int d = 0; d < DTW; ++d) {
+        const bf16x8 aop = v_operand(d);
+#pragma unroll
+        for (int h = 0; h < NW; ++h)
+          o[d][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, pf[h], o[d][h], 0, 0, 0);
+      }
+    } else {  // 128 heads: all V^T operands in registers, one P^T operand at a time
+      bf16x8 aop[DTW];
+#pragma unroll
+      for (int d = 0; d < DTW; ++d) aop[d] = v_operand(d);
+#pragma unroll
+      for (int h = 0; h < NW; ++h) {
+        const bf16x8 pf = as_bf16x8(*pslot(buf, h, lane));
+#pragma unroll
+        for (int d = 0; d < DTW; ++d)
+          o[d][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[d], pf, o[d][h], 0, 0, 0);
       }
     }
   }
 
+  // Row sums of every head, for the waves that store its dims (slot 0 of the ring is
+  // free once every wave is past the loop).
   float l = lsum + __shfl_xor(lsum, 16);
   l += __shfl_xor(l, 32);
-  if (nsplit == 1) {
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    uint16_t* orow = out + (t * H + head) * DV + 4 * g;
-#pragma unroll
-    for (int dt = 0; dt < DV / 16; ++dt) {
-      const uint32_t lo = f32_to_bf16_bits(o[dt][0] * inv) |
-                          (static_cast<uint32_t>(f32_to_bf16_bits(o[dt][1] * inv)) << 16);
-      const uint32_t hi = f32_to_bf16_bits(o[dt][2] * inv) |
-                          (static_cast<uint32_t>(f32_to_bf16_bits(o[dt][3] * inv)) << 16);
-      *reinterpret_cast<uint2*>(orow + 16 * dt) = make_uint2(lo, hi);
-    }
-    if (lse && g == 0)
-      lse[t * H + head] = l > 0.0f ? (m_run + __log2f(l)) * 0.69314718055994531f : -INFINITY;
-  } else {
-    const int64_t slot = (t * nsplit + split) * H + head;
-    float* orow = ws_o + slot * DV + 4 * g;
-#pragma unroll
-    for (int dt = 0; dt < DV / 16; ++dt)
-      *reinterpret_cast<float4*>(orow + 16 * dt) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
-    if (g == 0) {
-      ws_ml[2 * slot] = m_run;
+  float* sh_l = reinterpret_cast<float*>(kvbuf[0]);
+  __syncthreads();
+  if (g == 0) sh_l[head] = l;
+  __syncthreads();
+  if (g == 0 && head_ok) {
+    if (nsplit == 1) {
+      if (lse) lse[t * H + head] = l > 0.0f ? (m_ref + __log2f(l)) * 0.69314718055994531f : -INFINITY;
+    } else {
+      const int64_t slot = (t * nsplit + split) * H + head;
+      ws_ml[2 * slot] = m_ref;
       ws_ml[2 * slot + 1] = l;
+    }
+  }
+  // this lane holds dims 16*dt + 4g .. +4 of head 16h + c16 in o[d][h]
+#pragma unroll
+  for (int h = 0; h < NW; ++h) {
+    const int hd = 16 * h + c16;
+    if (hd >= H) continue;
+    if (nsplit == 1) {
+      const float lh = sh_l[hd];
+      const float inv = lh > 0.0f ? 1.0f / lh : 0.0f;
+      uint16_t* orow = out + (t * H + hd) * DV + 4 * g;
+#pragma unroll
+      for (int d = 0; d < DTW; ++d) {
+        const int dt = wave * DTW + d;
+        const uint32_t lo = f32_to_bf16_bits(o[d][h][0] * inv) |
+                            (static_cast<uint32_t>(f32_to_bf16_bits(o[d][h][1] * inv)) << 16);
+        const uint32_t hi = f32_to_bf16_bits(o[d][h][2] * inv) |
+                            (static_cast<uint32_t>(f32_to_bf16_bits(o[d][h][3] * inv)) << 16);
+        *reinterpret_cast<uint2*>(orow + 16 * dt) = make_uint2(lo, hi);
+      }
+    } else {
+      const int64_t slot = (t * nsplit + split) * H + hd;
+      float* orow = ws_o + slot * DV + 4 * g;
+#pragma unroll
+      for (int d = 0; d < DTW; ++d) {
+        const int dt = wave * DTW + d;
+        *reinterpret_cast<float4*>(orow + 16 * dt) =
+            make_float4(o[d][h][0], o[d][h][1], o[d][h][2], o[d][h][3]);
+      }
     }
   }
 }
@@ -362,7 +465,7 @@ extern "C" dsa_status dsa_sparse_mla_decode(const uint16_t* q, const uint16_t* k
   const float c2 = sm_scale * 1.4426950408889634f;  // natural -> base-2 logits
   hipStream_t st = as_stream(stream);
   dim3 grid((unsigned)nsplit, (unsigned)max_q_rows, (unsigned)B);
-  const int nw = H / 16;
+  const int nw = H <= 16 ? 1 : H <= 32 ? 2 : H <= 64 ? 4 : 8;  // waves of 16 heads, power of 2
 #define DSA_MLA_LAUNCH(NWV)                                                                    \
   hipLaunchKernelGGL(mla_decode_kernel<NWV>, grid, dim3(NWV * 64), 0, st, q, kv, topk,         \
                      share_base, num_accepted, q_row_offsets, kv_row_offsets, H, k, topk_rows, \
@@ -370,11 +473,7 @@ extern "C" dsa_status dsa_sparse_mla_decode(const uint16_t* q, const uint16_t* k
   switch (nw) {
     case 1: DSA_MLA_LAUNCH(1); break;
     case 2: DSA_MLA_LAUNCH(2); break;
-    case 3: DSA_MLA_LAUNCH(3); break;
     case 4: DSA_MLA_LAUNCH(4); break;
-    case 5: DSA_MLA_LAUNCH(5); break;
-    case 6: DSA_MLA_LAUNCH(6); break;
-    case 7: DSA_MLA_LAUNCH(7); break;
     default: DSA_MLA_LAUNCH(8); break;
   }
 #undef DSA_MLA_LAUNCH
