@@ -43,6 +43,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 // 16-byte LDS DMA (global_load_lds_dwordx4): lane l copies 16 bytes from `gsrc` to
 // LDS byte lds_base + 16*l; lds_base must be wave-uniform. Issued from inline asm
@@ -55,6 +56,17 @@ __device__ __forceinline__ void lds_dma16(const void* gsrc, const lds_void* lds_
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_base)));
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gsrc), "s"(m0)
+               : "memory");
+}
+
+// 4-byte LDS DMA (global_load_lds_dword): lane l copies 4 bytes from `gsrc` to LDS byte
+// lds_base + 4*l; same rules as lds_dma16.
+__device__ __forceinline__ void lds_dma4(const void* gsrc, const lds_void* lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_base)));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
                :
                : "v"(gsrc), "s"(m0)
                : "memory");

@@ -6,195 +6,307 @@
 // ("配置体系", 双 KV 缓存). Score of row t against key s:
 //     I[t,s] = k_scale[s] * sum_j (w[t,j] * q_scale[t,j]) * ReLU(q_hat[t,j] . k_hat[s])
 //
-// Work split: a block owns one request's key chunk and up to NW of its query
-// rows (one wave per row). Keys stream HBM -> registers -> LDS in 64-key tiles
-// (double-buffered, 16-byte chunks XOR-swizzled by key so the per-lane 32-byte
-// reads are bank-conflict free); each key byte is fetched from HBM once per
-// request and shared by all of its rows. Per 16-key sub-tile a wave issues one
-// v_mfma_f32_16x16x128_f8f6f4 per 16-head tile (K = 128 = index_head_dim in one
-// instruction): A = q codes [16 heads x 128], B = key codes [128 x 16 keys].
-// The result lane layout (row = 4*(lane/16)+i, col = lane%16) puts 4 heads of
-// one key in each lane, so the ReLU * weight head reduction is 4*HT in-lane
-// FMAs plus two cross-lane adds. The four lane groups then store four
-// different sub-tiles: one coalesced 256-byte store per 64 keys per row.
+// Work split: a block owns one request's 4096-key chunk and up to 7 of its query rows:
+// two compute waves per row (each takes 32 of every 64-key tile, so that 6 rows make
+// 12 waves, 3 per SIMD: the MFMA load is spread evenly over the CU) plus one producer
+// wave. Every key byte is fetched from HBM once per request and shared by all of its
+// rows.
+//  1. The producer wave streams keys HBM -> LDS with LDS DMA (global_load_lds, no
+//     registers) in 64-key tiles through a ring of NBUF slots (NBUF-1 tiles in flight),
+//     together with the tile's 64 key scales. One 16-byte DMA instruction moves 1 KB of
+//     consecutive keys (contiguous in HBM); in LDS a key keeps its row, with its
+//     16-byte pieces XOR-permuted by (key >> 1) so that the MFMA operand reads (16
+//     lanes = 16 keys at one piece) hit 16 distinct bank groups. The producer issues
+//     nothing but these DMAs, so its s_waitcnt vmcnt counts are exact (the counter is
+//     per wave: the compute waves' stores do not enter it).
+//  2. Per 16-key sub-tile a compute wave issues one v_mfma_f32_16x16x128_f8f6f4 per
+//     16-head tile (K = 128 = index_head_dim in one instruction), each into its own
+//     accumulator: A = q codes [16 heads x 128], B = key codes [128 x 16 keys].
+//     The result layout (row = 4*(lane/16)+i, col = lane%16) puts 4 heads of one key
+//     in each lane: the ReLU * weight head sum is in-lane FMAs plus two lane-half
+//     swaps (v_permlane16_swap / v_permlane32_swap, plain VALU).
+//  3. Each compute wave stores its row's 32 scores of the tile (key scale applied)
+//     with one coalesced 128-byte store.
+// One barrier per tile hands a landed tile to the compute waves and the slot of the
+// previous tile back to the producer.
 #include "common.hpp"
 
 namespace dsa {
 namespace {
 
-constexpr int KT = 64;  // keys per LDS tile
-constexpr int MAX_CHUNK = 4096;  // keys per block (key scales staged in LDS)
+#ifndef DSA_IS_CHUNK
+#define DSA_IS_CHUNK 4096
+#endif
+#ifndef DSA_IS_NBUF
+#define DSA_IS_NBUF 8
+#endif
+constexpr int KT = 64;                // keys per tile
+constexpr int CHUNK = DSA_IS_CHUNK;   // keys per block
+constexpr int NBUF = DSA_IS_NBUF;     // tile slots in LDS: NBUF - 1 tiles in flight
+constexpr int MAX_ROWS = 7;           // rows per block: 2 compute waves each, plus a producer
+constexpr int MAX_ROWS_H128 = 3;      // with 8 head tiles (registers: 256 per wave)
 
-template <int D, int HT, int NW>
-__global__ __launch_bounds__(NW * 64) void index_score_kernel(
+int max_rows_for(int ht) { return ht >= 8 ? MAX_ROWS_H128 : MAX_ROWS; }
+
+// s_waitcnt vmcnt(n') for the largest constant n' <= n, n in [0, N] (wave-uniform n:
+// scalar compares only).
+template <int N>
+__device__ __forceinline__ void wait_vm_at_most(int n) {
+  if constexpr (N == 0) {
+    DSA_WAIT_VMCNT(0);
+  } else {
+    if (n >= N) {
+      DSA_WAIT_VMCNT(N);
+    } else {
+      wait_vm_at_most<N - 1>(n);
+    }
+  }
+}
+
+// Piece permutation of key k within its row in LDS (an involution on the piece index):
+// 16 lanes reading keys 16j..16j+15 at one piece then cover all 256 bytes of the LDS
+// bank window (keys alternate 128-byte halves for D = 128).
+template <int NCH>
+__device__ __forceinline__ int kswz(int k) { return (k >> 1) & (NCH - 1); }
+
+// x + x from the lane 16 (xor) away, and from the lane 32 away: the lane-half swaps
+// of gfx950 hand each lane its partner's value without going through LDS.
+__device__ __forceinline__ float sum_xor16_xor32(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+template <int D, int HT, int NR>
+__global__ __launch_bounds__((2 * NR + 1) * 64) void index_score_kernel(
     const uint8_t* __restrict__ q_fp8, const float* __restrict__ q_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ k_fp8,
     const float* __restrict__ k_scale, const int32_t* __restrict__ q_off,
-    const int64_t* __restrict__ kv_off, int H, int64_t chunk, float* __restrict__ scores,
-    int64_t ld) {
-  constexpr int NCH = D / 16;                 // 16-byte chunks per key
-  constexpr int CH = KT * NCH;                // chunks per tile
-  constexpr int NT = NW * 64;
-  constexpr int PER = (CH + NT - 1) / NT;     // chunk loads per thread per tile
-  constexpr int NPRE = PER >= 4 ? 1 : 4 / PER;  // tiles in flight per block
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][KT * D];
-  __shared__ float sscale[MAX_CHUNK];
+    const int64_t* __restrict__ kv_off, int H, float* __restrict__ scores, int64_t ld) {
+  constexpr int NCH = D / 16;                  // 16-byte pieces per key = K DMAs per tile
+  constexpr int KPB = 1024 / D;                // keys per 1 KB DMA block
+  constexpr int TILE_K = KT * D;               // key bytes per tile
+  constexpr int SLOT = TILE_K + KT * 4;        // + the tile's key scales
+  constexpr int DMAS = NCH + 1;                // producer DMAs per tile
+  static_assert((NBUF - 2) * DMAS <= 63, "vmcnt holds at most 63");
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NBUF][SLOT];
 
   const int b = blockIdx.y;
   const RowInfo ri = load_row_info(q_off, kv_off, b);
-  const int64_t key0 = static_cast<int64_t>(blockIdx.x) * chunk;
-  const int row0 = blockIdx.z * NW;
+  const int64_t key0 = static_cast<int64_t>(blockIdx.x) * CHUNK;
+  const int row0 = blockIdx.z * NR;
   if (key0 >= ri.L || row0 >= ri.R) return;  // block-uniform
-  int64_t key_end = key0 + chunk < ri.L ? key0 + chunk : ri.L;
+  int64_t key_end = key0 + CHUNK < ri.L ? key0 + CHUNK : ri.L;
   if (key_end > ld) key_end = ld;  // device lengths beyond the score stride are clipped
+  const int nkeys = static_cast<int>(key_end - key0);
+  const int ntiles = nkeys > 0 ? (nkeys + KT - 1) / KT : 0;
 
-  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int lane = threadIdx.x % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);  // wave-uniform (SGPR)
+
+  if (wave == 2 * NR) {
+    // ---- producer wave: tile `it` -> slot it % NBUF. DMA m < NCH moves keys KPB*m ..
+    // KPB*m + KPB-1 of the tile: lane l writes physical piece l % NCH of key KPB*m + l/NCH,
+    // i.e. loads logical piece (l % NCH) ^ kswz(key); keys past the chunk load its last
+    // key again (their scores are never stored). DMA NCH moves the 64 key scales.
+    // In a full tile, key KPB*m + l/NCH has kswz = (KPB*m/2 + l/(2*NCH)) % NCH, which only
+    // depends on the parity of m (KPB*m/2 is a multiple of NCH for even m and NCH/2 more
+    // for odd m): two per-lane byte offsets serve every DMA of every full tile.
+    const uint8_t* kreq = k_fp8 + (ri.kv_base + key0) * D;
+    const float* sreq = k_scale + ri.kv_base + key0;
+    const int ful = nkeys / KT;  // full tiles
+    auto issue_tile = [&](int it) {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));  // recomputed per tile, not held across the loop
+      const lds_u8* slot = (const lds_u8*)ring[it % NBUF];
+      if (it < ful) {
+        const uint8_t* base = kreq + static_cast<int64_t>(it) * TILE_K + (ln / NCH) * D;
+        const int off0 = 16 * ((ln % NCH) ^ kswz<NCH>(ln / NCH));
+        const int off1 = 16 * ((ln % NCH) ^ kswz<NCH>(KPB + ln / NCH));
+#pragma unroll
+        for (int m = 0; m < NCH; ++m)
+          lds_dma16(base + 1024 * m + ((m & 1) ? off1 : off0), (const lds_void*)(slot + 1024 * m));
+        lds_dma4(sreq + it * KT + ln, (const lds_void*)(slot + TILE_K));
+      } else {
+#pragma unroll
+        for (int m = 0; m < NCH; ++m) {
+          const int kt = KPB * m + ln / NCH;  // key within the tile
+          const int key = it * KT + kt < nkeys ? it * KT + kt : nkeys - 1;
+          lds_dma16(kreq + static_cast<int64_t>(key) * D + 16 * ((ln % NCH) ^ kswz<NCH>(kt)),
+                    (const lds_void*)(slot + 1024 * m));
+        }
+        const int key = it * KT + ln < nkeys ? it * KT + ln : nkeys - 1;
+        lds_dma4(sreq + key, (const lds_void*)(slot + TILE_K));
+      }
+    };
+    // Tile it+NBUF-2 goes into the slot of tile it-2, which every compute wave finished
+    // reading before barrier it-1: the producer issues it before barrier it, overlapped
+    // with the compute of tile it-1, and reaches the barrier as soon as tile it is in.
+    // Retire every load the compiler issued so far: its own wait bookkeeping does not see
+    // the DMAs, and a wait it placed for one of its loads inside the loop would count them
+    // wrongly and drain the whole DMA pipeline.
+    DSA_WAIT_VMCNT(0);
+#pragma unroll 1
+    for (int j = 0; j < NBUF - 2 && j < ntiles; ++j) issue_tile(j);
+#pragma unroll 1
+    for (int it = 0; it < ntiles; ++it) {
+      if (it + NBUF - 2 < ntiles) issue_tile(it + NBUF - 2);
+      // tile `it` has landed when at most the DMAs of the tiles after it are in flight
+      const int after = ntiles - 1 - it < NBUF - 2 ? ntiles - 1 - it : NBUF - 2;
+      wait_vm_at_most<(NBUF - 2) * DMAS>(after * DMAS);
+      __syncthreads();  // hand tile `it` over; every compute wave is done with tile it-1
+    }
+    return;
+  }
+
+  // ---- compute wave: row row0 + wave/2, keys 32*(wave%2) .. +32 of every tile
   const int g = lane / 16, c16 = lane % 16;
-  const int r = row0 + wave;
-  const bool row_live = r < ri.R;             // wave-uniform
+  const int kh = wave & 1;
+  const int r = row0 + (wave >> 1);
+  const bool row_live = r < ri.R;  // wave-uniform
   const int64_t nvis = row_live ? visible_count(ri, r) : 0;
-  const int64_t t = ri.t0 + r;
+  const int64_t t = ri.t0 + (row_live ? r : 0);  // a valid row for the (discarded) loads
+  // scores stored for keys key0 .. key0 + nstore - 1 of this row (visible and in chunk)
+  const int nstore = static_cast<int>(nvis - key0 < nkeys ? (nvis - key0 > 0 ? nvis - key0 : 0) : nkeys);
 
-  // A operands (q codes) and per-output-row weights u = w * q_scale.
+  // A operands (q codes) and per-output-row weights u = w * q_scale; all loads are issued
+  // before any is used. Heads past H read head H-1 and are zeroed.
   i32x8 qa[HT];
   float u[HT][4];
+  {
+    i32x4 qlo[HT], qhi[HT];
+    float wv[HT][4], qs[HT][4];
 #pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-    const int head = ht * 16 + c16;
-    // branch-free loads from clamped addresses; invalid lanes are zeroed afterwards
-    const bool qok = row_live && head < H && 32 * g < D;
-    const int64_t tq = row_live ? t : ri.t0;
-    const int hq = head < H ? head : H - 1;
-    const int gq = 32 * g < D ? g : 0;
-    const i32x4* p = reinterpret_cast<const i32x4*>(q_fp8 + (tq * H + hq) * D + 32 * gq);
-    const i32x4 lo = p[0], hi = p[1];
-    const i32x8 v = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    const i32x8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
-    qa[ht] = qok ? v : zero8;
+    for (int ht = 0; ht < HT; ++ht) {
+      const int head = ht * 16 + c16;
+      const int gq = 32 * g < D ? g : 0;
+      const i32x4* p = reinterpret_cast<const i32x4*>(q_fp8 + (t * H + (head < H ? head : H - 1)) * D + 32 * gq);
+      qlo[ht] = p[0];
+      qhi[ht] = p[1];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h2 = ht * 16 + 4 * g + i;
-      const int64_t o = tq * H + (h2 < H ? h2 : H - 1);
-      const float uu = w[o] * q_scale[o];
-      u[ht][i] = (row_live && h2 < H) ? uu : 0.0f;
-    }
-  }
-
-  const uint8_t* kbase = k_fp8 + (ri.kv_base + key0) * D;
-  const int64_t nkeys = key_end - key0;
-  const int ntiles = static_cast<int>((nkeys + KT - 1) / KT);
-
-  // Key scales of the whole chunk go to LDS once (chunk <= 4096 keys).
-  for (int i0 = 0; i0 < nkeys; i0 += 4 * NT) {  // four independent loads per thread per step
-    float v[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = i0 + j * NT + static_cast<int>(threadIdx.x);
-      v[j] = k_scale[ri.kv_base + key0 + (i < nkeys ? i : nkeys - 1)];
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = i0 + j * NT + static_cast<int>(threadIdx.x);
-      if (i < nkeys) sscale[i] = v[j];
-    }
-  }
-
-  // Register ring: each thread holds its 16-byte pieces of the next NPRE tiles, so
-  // NPRE tiles per block are in flight while one is computed (the loop is unrolled
-  // by NPRE so every ring slot is a fixed register).
-  i32x4 pre[NPRE][PER];
-  auto load_tile = [&](int it, i32x4* dst) {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      // branch-free: keys past the chunk load the last key again (their scores are
-      // never stored); pieces past the tile (idx >= CH) are never written to LDS
-      const int idx = threadIdx.x + j * NT < CH ? threadIdx.x + j * NT : CH - 1;
-      const int s = idx / NCH, c = idx % NCH;
-      int64_t key = static_cast<int64_t>(it) * KT + s;
-      key = key < nkeys ? key : nkeys - 1;
-      dst[j] = *reinterpret_cast<const i32x4*>(kbase + key * D + c * 16);
-    }
-  };
-  auto store_tile = [&](uint8_t* buf, const i32x4* src) {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int idx = threadIdx.x + j * NT;
-      if (idx < CH) {
-        const int s = idx / NCH, c = idx % NCH;
-        *reinterpret_cast<i32x4*>(buf + s * D + ((c ^ (s & (NCH - 1))) * 16)) = src[j];
+      for (int i = 0; i < 4; ++i) {
+        const int h2 = ht * 16 + 4 * g + i;
+        const int64_t o = t * H + (h2 < H ? h2 : H - 1);
+        wv[ht][i] = w[o];
+        qs[ht][i] = q_scale[o];
       }
     }
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const bool qok = row_live && ht * 16 + c16 < H && 32 * g < D;
+      const i32x8 v = {qlo[ht][0], qlo[ht][1], qlo[ht][2], qlo[ht][3],
+                       qhi[ht][0], qhi[ht][1], qhi[ht][2], qhi[ht][3]};
+      const i32x8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+      qa[ht] = qok ? v : zero8;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        u[ht][i] = (row_live && ht * 16 + 4 * g + i < H) ? wv[ht][i] * qs[ht][i] : 0.0f;
+    }
+  }
+  float* srow = scores + t * ld + key0;
+  const int kt = 32 * kh + 16 * g + c16;  // key of the tile this lane stores (lane groups 0, 1)
+
+  // Software pipeline over 16-key sub-tiles (each wave owns sub-tiles 0 and 1 of its
+  // 32-key half of every tile): the MFMAs of the next sub-tile are issued before the
+  // current one is reduced, so the MFMA pipe and the VALU reduction overlap. Every read of
+  // a tile's slot (keys and scale) happens before the barrier that lets the producer
+  // refill it.
+  const bool live = row_live;
+  auto live_tile = [&](int it) { return live && it * KT + 32 * kh < nstore; };  // wave-uniform
+  auto mfma_sub = [&](int it, int sb, f32x4 (&acc)[HT]) {
+    const uint8_t* buf = ring[it % NBUF];
+    const int key = 32 * kh + sb * 16 + c16;
+    i32x8 bfrag = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (32 * g < D) {  // dims 32g..32g+31 = logical pieces 2g, 2g+1
+      const uint8_t* krow = buf + key * D;
+      const int sw = kswz<NCH>(key);
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(krow + 16 * ((2 * g) ^ sw));
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(krow + 16 * ((2 * g + 1) ^ sw));
+      bfrag = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      acc[ht] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[ht], bfrag, zero, 0, 0, 0, 0,
+                                                                 0, 0);
+    }
+  };
+  // ReLU * weight sum over all heads of key (lane column) from one sub-tile's accumulators
+  auto reduce_sub = [&](const f32x4 (&acc)[HT]) {
+    float part = 0.0f;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)  // ReLU as med3(x, 0, FLT_MAX): max(x, 0) in one op
+        part = fmaf(u[ht][i], __builtin_amdgcn_fmed3f(acc[ht][i], 0.0f, 3.402823466e38f), part);
+    return sum_xor16_xor32(part);
   };
 
-#pragma unroll
-  for (int j = 0; j < NPRE; ++j)
-    if (j < ntiles) load_tile(j, pre[j]);
-  for (int base = 0; base < ntiles; base += NPRE) {
-#pragma unroll
-    for (int jr = 0; jr < NPRE; ++jr) {
-      const int it = base + jr;
-      if (it >= ntiles) break;  // block-uniform
-      uint8_t* buf = lds[it & 1];
-      store_tile(buf, pre[jr]);
-      __syncthreads();  // tile `it` is in LDS; the other buffer (tile it-1) is no longer read
-      if (it + NPRE < ntiles) load_tile(it + NPRE, pre[jr]);
-      if (row_live) {
-        float res[4];
-#pragma unroll
-        for (int sub = 0; sub < 4; ++sub) {
-          const int s = sub * 16 + c16;
-          i32x8 bfrag = {0, 0, 0, 0, 0, 0, 0, 0};
-          if (32 * g < D) {
-            const int c0 = 2 * g, c1 = 2 * g + 1;
-            i32x4 lo = *reinterpret_cast<const i32x4*>(buf + s * D + ((c0 ^ (s & (NCH - 1))) * 16));
-            i32x4 hi = *reinterpret_cast<const i32x4*>(buf + s * D + ((c1 ^ (s & (NCH - 1))) * 16));
-            bfrag = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          }
-          float part = 0.0f;
-#pragma unroll
-          for (int ht = 0; ht < HT; ++ht) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[ht], bfrag, acc, 0, 0, 0, 0,
-                                                                   0, 0);
-            // ReLU as med3(x, 0, FLT_MAX): one instruction (max(x, 0) for finite x)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              part = fmaf(u[ht][i], __builtin_amdgcn_fmed3f(acc[i], 0.0f, 3.402823466e38f), part);
-          }
-          part += __shfl_xor(part, 16);
-          part += __shfl_xor(part, 32);
-          res[sub] = part;
-        }
-        const float v = g == 0 ? res[0] : g == 1 ? res[1] : g == 2 ? res[2] : res[3];
-        const int sl = it * KT + g * 16 + c16;         // key within the chunk
-        const int64_t s = key0 + sl;                    // request-local position
-        if (s < key_end && s < nvis) scores[t * ld + s] = v * sscale[sl];
-      }
+  f32x4 acc0[HT], acc1[HT];  // sub-tile 0 / sub-tile 1 of the current tile
+  if (ntiles > 0) {
+    __syncthreads();  // tile 0 is in LDS (the producer waited for it)
+    if (live_tile(0)) mfma_sub(0, 0, acc0);
+  }
+#pragma unroll 1
+  for (int it = 0; it < ntiles; ++it) {
+    const bool lv = live_tile(it);
+    float sc = 0.0f, res0 = 0.0f, res1 = 0.0f;
+    if (lv) {
+      mfma_sub(it, 1, acc1);
+      sc = reinterpret_cast<const float*>(ring[it % NBUF] + TILE_K)[kt];
+      res0 = reduce_sub(acc0);
     }
+    if (it + 1 < ntiles) {
+      __syncthreads();  // tile it+1 is in LDS; every wave is done reading tile it
+      if (live_tile(it + 1)) mfma_sub(it + 1, 0, acc0);
+    }
+    if (lv) {
+      res1 = reduce_sub(acc1);
+      // lane groups 0 and 1 store the two sub-tiles: key 32kh + 16g + c16, scaled
+      if (g < 2 && it * KT + kt < nstore) srow[it * KT + kt] = (g == 0 ? res0 : res1) * sc;
+    }
+  }
+}
+
+template <int D, int HT, int NRV>
+void launch_one(dim3 grid, hipStream_t st, const uint8_t* q, const float* qs, const float* w,
+                const uint8_t* k, const float* ks, const int32_t* qo, const int64_t* ko, int H,
+                float* sc, int64_t ld) {
+  if constexpr (HT >= 8 && NRV > MAX_ROWS_H128) {
+    return;  // never chosen: the host caps rows per block at MAX_ROWS_H128 for 8 head tiles
+  } else {
+    hipLaunchKernelGGL((index_score_kernel<D, HT, NRV>), grid, dim3((2 * NRV + 1) * 64), 0, st, q,
+                       qs, w, k, ks, qo, ko, H, sc, ld);
   }
 }
 
 template <int D, int HT>
-void launch_nw(int nw, dim3 grid, hipStream_t st, const uint8_t* q, const float* qs,
+void launch_nr(int nr, dim3 grid, hipStream_t st, const uint8_t* q, const float* qs,
                const float* w, const uint8_t* k, const float* ks, const int32_t* qo,
-               const int64_t* ko, int H, int64_t chunk, float* sc, int64_t ld) {
-  switch (nw) {
-    case 1: hipLaunchKernelGGL((index_score_kernel<D, HT, 1>), grid, dim3(64), 0, st, q, qs, w, k, ks, qo, ko, H, chunk, sc, ld); break;
-    case 2: hipLaunchKernelGGL((index_score_kernel<D, HT, 2>), grid, dim3(128), 0, st, q, qs, w, k, ks, qo, ko, H, chunk, sc, ld); break;
-    case 4: hipLaunchKernelGGL((index_score_kernel<D, HT, 4>), grid, dim3(256), 0, st, q, qs, w, k, ks, qo, ko, H, chunk, sc, ld); break;
-    default: hipLaunchKernelGGL((index_score_kernel<D, HT, 8>), grid, dim3(512), 0, st, q, qs, w, k, ks, qo, ko, H, chunk, sc, ld); break;
+               const int64_t* ko, int H, float* sc, int64_t ld) {
+  switch (nr) {
+    case 1: launch_one<D, HT, 1>(grid, st, q, qs, w, k, ks, qo, ko, H, sc, ld); break;
+    case 2: launch_one<D, HT, 2>(grid, st, q, qs, w, k, ks, qo, ko, H, sc, ld); break;
+    case 3: launch_one<D, HT, 3>(grid, st, q, qs, w, k, ks, qo, ko, H, sc, ld); break;
+    case 4: launch_one<D, HT, 4>(grid, st, q, qs, w, k, ks, qo, ko, H, sc, ld); break;
+    case 5: launch_one<D, HT, 5>(grid, st, q, qs, w, k, ks, qo, ko, H, sc, ld); break;
+    case 6: launch_one<D, HT, 6>(grid, st, q, qs, w, k, ks, qo, ko, H, sc, ld); break;
+    default: launch_one<D, HT, 7>(grid, st, q, qs, w, k, ks, qo, ko, H, sc, ld); break;
   }
 }
 
 template <int D>
-void launch_ht(int ht, int nw, dim3 grid, hipStream_t st, const uint8_t* q, const float* qs,
+void launch_ht(int ht, int nr, dim3 grid, hipStream_t st, const uint8_t* q, const float* qs,
                const float* w, const uint8_t* k, const float* ks, const int32_t* qo,
-               const int64_t* ko, int H, int64_t chunk, float* sc, int64_t ld) {
+               const int64_t* ko, int H, float* sc, int64_t ld) {
   switch (ht) {
-    case 1: launch_nw<D, 1>(nw, grid, st, q, qs, w, k, ks, qo, ko, H, chunk, sc, ld); break;
-    case 2: launch_nw<D, 2>(nw, grid, st, q, qs, w, k, ks, qo, ko, H, chunk, sc, ld); break;
-    case 4: launch_nw<D, 4>(nw, grid, st, q, qs, w, k, ks, qo, ko, H, chunk, sc, ld); break;
-    default: launch_nw<D, 8>(nw, grid, st, q, qs, w, k, ks, qo, ko, H, chunk, sc, ld); break;
+    case 1: launch_nr<D, 1>(nr, grid, st, q, qs, w, k, ks, qo, ko, H, sc, ld); break;
+    case 2: launch_nr<D, 2>(nr, grid, st, q, qs, w, k, ks, qo, ko, H, sc, ld); break;
+    case 4: launch_nr<D, 4>(nr, grid, st, q, qs, w, k, ks, qo, ko, H, sc, ld); break;
+    default: launch_nr<D, 8>(nr, grid, st, q, qs, w, k, ks, qo, ko, H, sc, ld); break;
   }
 }
 
@@ -231,21 +343,18 @@ extern "C" dsa_status dsa_index_score(const uint8_t* q_fp8, const float* q_scale
               "dsa_index_score: q_fp8 and k_fp8 must be 16-byte aligned");
   DSA_REQUIRE(B <= 65535, "dsa_index_score: B must be <= 65535");
   const int ht = pow2_at_least((H_I + 15) / 16);
-  const int nw = pow2_at_least(max_q_rows < 8 ? max_q_rows : 8);
-  // Key chunk per block: enough blocks to fill the chip (~4 per CU), 256..4096 keys.
-  int64_t chunk = 4096;
-  const int64_t total_keys = static_cast<int64_t>(B) * max_kv_len;
-  while (chunk > 256 && total_keys / chunk < 1024) chunk /= 2;
-  const int64_t gx = ceil_div(max_kv_len, chunk);
-  const int64_t gz = ceil_div(max_q_rows, nw);
+  // row groups of at most max_rows_for(ht), balanced: e.g. 6 rows -> one group of 6, 8 -> 4 + 4
+  const int64_t gz = ceil_div(max_q_rows, max_rows_for(ht));
+  const int nr = static_cast<int>(ceil_div(max_q_rows, gz));  // rows per block
+  const int64_t gx = ceil_div(max_kv_len, CHUNK);
   DSA_REQUIRE(gx <= 0x7FFFFFFF && gz <= 65535, "dsa_index_score: grid too large");
   dim3 grid((unsigned)gx, (unsigned)B, (unsigned)gz);
   hipStream_t st = as_stream(stream);
   if (D_I == 128)
-    launch_ht<128>(ht, nw, grid, st, q_fp8, q_scale, w, k_fp8, k_scale, q_row_offsets,
-                   kv_row_offsets, H_I, chunk, scores, score_ld);
+    launch_ht<128>(ht, nr, grid, st, q_fp8, q_scale, w, k_fp8, k_scale, q_row_offsets,
+                   kv_row_offsets, H_I, scores, score_ld);
   else
-    launch_ht<64>(ht, nw, grid, st, q_fp8, q_scale, w, k_fp8, k_scale, q_row_offsets,
-                  kv_row_offsets, H_I, chunk, scores, score_ld);
+    launch_ht<64>(ht, nr, grid, st, q_fp8, q_scale, w, k_fp8, k_scale, q_row_offsets,
+                  kv_row_offsets, H_I, scores, score_ld);
   return check_launch("dsa_index_score");
 }
