@@ -39,7 +39,24 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (HBM counter calibration) and exit")
     return ap.parse_args()
+
+
+def calibrate_copy():
+    """A plain elementwise kernel that reads and writes exactly 1 GiB each (5 launches): the
+    reference against which rocprofv3 FETCH_SIZE / WRITE_SIZE are converted to bytes."""
+    import torch
+
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print("[bench] calibration copy done (5 x 1 GiB read + 1 GiB write)", file=sys.stderr, flush=True)
 
 
 class Inputs:
@@ -131,6 +148,9 @@ def cpu_baseline(w, lengths, inp0, target_s: float):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the verify step is "
               "data-parallel per request and this build measures one GPU's share.",
