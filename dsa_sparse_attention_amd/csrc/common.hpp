@@ -51,7 +51,8 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 // wait for every pending DMA before any LDS read it cannot prove disjoint): the
 // caller retires these loads itself with s_waitcnt vmcnt and a barrier before
 // reading the data. Loads retire in order, so the compiler's own vmcnt waits for
-// its loads stay correct (only stricter) while such DMAs are in flight.
+// its loads stay correct (only stricter) while such DMAs are in flight. The
+// instruction's offset field is not used: it would move the LDS destination too.
 __device__ __forceinline__ void lds_dma16(const void* gsrc, const lds_void* lds_base) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_base)));

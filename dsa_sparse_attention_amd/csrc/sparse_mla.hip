@@ -5,60 +5,99 @@
 // 512 + qk_rope_head_dim 64 ("GLM-5.3 推理全链路(十四)", "GLM-5.3 的草稿层到底长什么样").
 // Index sharing: "MAX 中 GLM-5.2 ... 统一 MTP 推测解码架构解析", "阶段 5".
 //
-// Work split: a block owns one query row and one slice (<= 1024 entries) of its
-// top-k list (split-K); wave w owns heads 16w..16w+15.
-//  1. The slice's valid indices are compacted into LDS in list order (block
-//     prefix sum), so -1 padding and out-of-range entries cost neither HBM
-//     traffic nor MFMA work, and the accumulation order is deterministic.
-//  2. Latent rows stream HBM -> LDS with 16-byte global_load_lds (LDS DMA, no
-//     registers) in 32-row chunks, double-buffered: chunk c+1 is in flight
-//     while chunk c is computed. Rows are stored unpadded (1152 B) with the
-//     16-byte units of each 128-byte group XOR-swizzled by row, which keeps
-//     both read patterns below free of bank conflicts.
-//  3. S^T[key, head] = K[32 x 576] . Q^T with v_mfma_f32_16x16x32_bf16 (Q^T
-//     fragments stay in registers); online softmax per head in base 2, one
-//     head per lane column, with a lazy reference max: it moves (and the
-//     accumulators are rescaled) only when a chunk's max exceeds it by more
-//     than 2^8, so P <= 2^8 and the result is unchanged up to rounding.
-//  4. O^T[dim, head] += V^T . P^T: P^T is the S^T accumulator itself (no data
-//     movement); the V^T operand comes from ds_read_b64_tr_b16, which
-//     transposes 4x4 blocks of bf16 across lanes while reading, so each 16x32
-//     A operand is two 8-byte LDS reads per lane.
-// With more than one split, unnormalised partials (O, max, sum) go to the
+// Work split: a block owns one query row, one group of 64 heads and one slice (at most
+// 2048 entries) of the row's top-k list; one block per CU, 16 waves in two roles:
+//  - 8 S waves: wave (hq, kt) computes S^T[key, head] for keys 16kt..16kt+15 of a 32-key
+//    chunk and heads 16hq..16hq+15 with v_mfma_f32_16x16x32_bf16 (its Q^T operand,
+//    576 dims, stays in registers), then the online softmax of its heads: the chunk
+//    max combines both key halves through LDS, and the reference max is lazy (it moves,
+//    and the accumulators are rescaled, only when a chunk max exceeds it by more than
+//    2^8, so P <= 2^8 and the result is unchanged up to rounding). P^T goes to LDS in
+//    MFMA operand order, over the rope columns of the chunk (dead once S^T is done).
+//  - 8 O waves: wave ow accumulates O^T[dim, head] for dims 64ow..64ow+63 of all 64
+//    heads (four v_mfma_f32_32x32x16_bf16 tiles), one chunk behind the S waves; the V^T
+//    operand comes from ds_read_b64_tr_b16, which transposes 4x4 blocks of bf16 across
+//    lanes while reading. The O waves also stream the latent rows HBM -> LDS with
+//    16-byte global_load_lds (LDS DMA, no registers), two chunks ahead, into a ring of
+//    four 36 KB chunk buffers.
+// The slice's valid indices are first compacted into LDS in list order (block prefix
+// sum), so -1 padding and out-of-range entries cost neither HBM traffic nor MFMA work.
+// With more than one slice per row, unnormalised partials (O, max, sum) go to the
 // workspace and a combine kernel merges them.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace dsa {
 namespace {
 
 constexpr int DQK = 576, DV = 512;
-constexpr int KC = 32;                      // latent rows per chunk
-constexpr int UNITS = DQK * 2 / 16;         // 72 16-byte units (8 dims each) per latent row
-constexpr int UNIT_BYTES = KC * 16;         // 512: one unit of all 32 rows of a chunk
-constexpr int CHUNK_BYTES = UNITS * UNIT_BYTES;  // 36864
-constexpr int BLOCKS = CHUNK_BYTES / 1024;  // 36 wave-wide (64 x 16 B) DMA blocks per chunk
-constexpr int MAX_KPS = 1024;               // top-k entries per split (LDS index staging)
-constexpr float LAZY = 8.0f;                // reference-max slack, log2 units
+constexpr int KC = 32;                           // latent rows per chunk
+constexpr int UNITS = DQK * 2 / 16;              // 72 16-byte units (8 dims each) per row
+constexpr int CHUNK_BYTES = KC * UNITS * 16;     // 36864
+constexpr int DMA_BLOCKS = CHUNK_BYTES / 1024;   // 36 wave-wide (64 x 16 B) DMAs per chunk
+constexpr int NBUF = 4;                          // chunk ring: S, O, and two in flight
+constexpr int MAX_KPS = 2048;                    // top-k entries per slice (LDS staging)
+constexpr int HPB = 64;                          // heads per block
+constexpr int NSW = 8, NOW = 8, NWAVE = NSW + NOW, NT = NWAVE * 64;
+constexpr int KS = DQK / 32;                     // 18 k-steps of the S product
+constexpr int KPF = 5;                           // K operand reads in flight ahead
+#ifndef DSA_MLA_DMA_A
+#define DSA_MLA_DMA_A 2
+#endif
+constexpr int DMA_A = DSA_MLA_DMA_A;  // O waves: DMA blocks issued before B1, the rest after
+constexpr float LAZY = 8.0f;                     // reference-max slack, log2 units
+constexpr float M_INIT = -1.0e30f;               // reference before any valid key (finite)
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(i32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Chunk layout in LDS, unit-major: byte 512*u + 16*cell(r, u) holds dims 8u..8u+7 of the
-// chunk's row r, with cell(r, u) = r ^ (4 * (u & 1)) (an involution in r).
-//  - A K fragment read (16 lanes = rows 0..15 or 16..31 at one unit) is a contiguous
-//    256-byte block: no bank conflicts.
-//  - A transposing V read (16 lanes = 4 rows 4j..4j+3 x 2 adjacent units 2d, 2d+1)
-//    lands on two disjoint 64-byte runs of the 256-byte bank window, thanks to the
-//    4-row offset of odd units.
-//  - A wave-wide DMA block m (1 KB) is units 2m and 2m+1: lane l writes cell l%32 of
-//    unit 2m + l/32, so it loads chunk row (l%32) ^ (4*(l/32)) for every m -- one row
-//    per lane per chunk, with a per-DMA offset of 32*m bytes in the source row.
-__device__ __forceinline__ int cell(int row, int unit) { return row ^ (4 * (unit & 1)); }
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
 
-template <int NW>
+// max / sum over lanes l, l^16, l^32, l^48 (the four lanes of one S^T column)
+__device__ __forceinline__ float max_xor16_xor32(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float sum_xor16_xor32(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Chunk layout in LDS: 1 KB block 4 ug + rg holds rows 8rg..8rg+7 and dims 64ug..64ug+63
+// (units 8ug..8ug+7 of 8 dims); row rr = r%8 of the block is 128 bytes at 128 rr, its unit
+// uu = u%8 at 16 * (uu ^ rr ^ 2(rg & 1)).
+//  - A DMA block (one wave-wide global_load_lds, 64 x 16 B) fills one block: lane l
+//    copies unit (l%8) ^ (l/8) ^ 2(rg&1) of row 8rg + l/8, so the 8 lanes of a row read
+//    one whole 128-byte line of it (8 lines per instruction, which keeps the address
+//    path of the load unit from limiting the DMA rate).
+//  - A K fragment read: 16 lanes = rows 0..15 or 16..31 at one unit; a transposing V
+//    read: 16 lanes = 4 rows x 2 adjacent units. Measured on gfx950, this XOR keeps both
+//    at the LDS peak for them (about 254 and 127 B/clk per CU).
+// P^T of the chunk (32 keys x 64 heads bf16, 4 KB) overwrites the rope blocks 32..35
+// after the S phase: byte 32768 + 1024 (2 ht + ko) + 16 l is lane l's B operand of head
+// tile ht (32 heads), key step ko (16 keys).
+
 __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
   int x = v;
@@ -71,7 +110,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
   __syncthreads();
   int before = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
+  for (int w = 0; w < NWAVE; ++w) {
     before += w < wave ? tmp[w] : 0;
     tot += tmp[w];
   }
@@ -80,42 +119,28 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
   return before + x - v;
 }
 
-// Two waves per SIMD: caps the kernel at 256 registers per lane (Q^T 72, O^T 128, rest).
-// NW is a power of two (1, 2, 4, 8); heads past H are computed on zero queries and
-// never stored.
-template <int NW>
-__global__ __launch_bounds__(NW * 64, NW == 1 ? 1 : 2) void mla_decode_kernel(
+// Four waves per SIMD: at most 128 registers per lane.
+__global__ __launch_bounds__(NT, 1) void mla_decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ topk, const int32_t* __restrict__ share_base,
     const int32_t* __restrict__ num_acc, const int32_t* __restrict__ q_off,
-    const int64_t* __restrict__ kv_off, int H, int k, int topk_rows, float c2, int nsplit,
-    int keys_per_split, uint16_t* __restrict__ out, float* __restrict__ lse,
+    const int64_t* __restrict__ kv_off, int H, int nhg, int k, int topk_rows, float c2,
+    int nsplit, int keys_per_split, uint16_t* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ ws_o, float* __restrict__ ws_ml) {
-  constexpr int NT = NW * 64;
-  constexpr int PER_T = (MAX_KPS + NT - 1) / NT;  // index entries per thread
-  constexpr int DTW = (DV / 16) / NW;             // 16-dim output tiles per wave
-  constexpr int DMA_PER = (BLOCKS + NW - 1) / NW; // DMA blocks per wave per chunk
-  static_assert((NW & (NW - 1)) == 0 && NW <= 8, "NW must be 1, 2, 4 or 8");
-  static_assert(DTW % 4 == 0, "a wave's first dim tile is a multiple of 4");
-  __shared__ __attribute__((aligned(1024))) uint8_t kvbuf[2][CHUNK_BYTES];
+  constexpr int PER_T = MAX_KPS / NT;  // index entries per thread
+  __shared__ __attribute__((aligned(1024))) uint8_t kvbuf[NBUF][CHUNK_BYTES];
   __shared__ int32_t sidx[MAX_KPS];
-  __shared__ int scan_tmp[NW];
-  __shared__ float sh_alpha[NW * 16]; // rescale factor of each head this chunk
-  __shared__ int sh_resc[NW];         // wave h moved its reference this chunk
-  // P^T operands of every wave (NW x 64 lanes x 16 B). Up to 4 KB they live in the rope
-  // units (64..71, the last 4 KB) of the chunk being computed, dead once S^T is done;
-  // 128 heads need a buffer of their own.
-  constexpr bool P_IN_ROPE = NW <= 4;
-  __shared__ i32x4 pbuf_own[P_IN_ROPE ? 1 : NW * 64];
-  auto pslot = [&](const uint8_t* buf, int h, int ln) -> i32x4* {
-    const int sl = h * 64 + ln;
-    return P_IN_ROPE ? (i32x4*)(buf + 64 * UNIT_BYTES + 16 * sl) : &pbuf_own[sl];
-  };
+  __shared__ int scan_tmp[NWAVE];
+  __shared__ float sh_cm[2][HPB];     // chunk max of each head over one key half
+  __shared__ float sh_alpha[2][HPB];  // rescale factor of each head, chunk parity
+  __shared__ int sh_resc[2][4];       // head quarter moved its reference, chunk parity
+  __shared__ float sh_m[HPB], sh_l[2][HPB];
 
-  const int split = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
+  const int hg = blockIdx.x % nhg, split = blockIdx.x / nhg;
+  const int r_row = blockIdx.y, b = blockIdx.z;
   const RowInfo ri = load_row_info(q_off, kv_off, b);
-  if (r >= ri.R) return;
-  const int64_t t = ri.t0 + r;
+  if (r_row >= ri.R) return;
+  const int64_t t = ri.t0 + r_row;
   const int64_t trow = share_base ? static_cast<int64_t>(share_base[b]) + num_acc[b] : t;
   const bool trow_ok = trow >= 0 && trow < topk_rows && ri.L > 0;  // else nothing selected
   const int32_t* idx = topk + (trow_ok ? trow : 0) * k;
@@ -123,24 +148,9 @@ __global__ __launch_bounds__(NW * 64, NW == 1 ? 1 : 2) void mla_decode_kernel(
   const int i_end =
       !trow_ok ? i_begin : (i_begin + keys_per_split < k ? i_begin + keys_per_split : k);
 
-  const int tid = threadIdx.x, lane = tid % 64;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // wave-uniform, kept in an SGPR
-  const int g = lane / 16, c16 = lane % 16;
-  const int head = wave * 16 + c16;  // head of this lane's column in the S/softmax phase
-  const bool head_ok = head < H;
-
-  // Q^T fragments: head `head`, dims 32*ks + 8*g .. +8 (loads overlap the index staging).
-  // Heads past H read head H-1 and are zeroed.
-  bf16x8 qf[18];
-  {
-    const uint16_t* qrow = q + (t * H + (head_ok ? head : H - 1)) * DQK + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < 18; ++ks) {
-      const i32x4 v = *reinterpret_cast<const i32x4*>(qrow + 32 * ks);
-      const i32x4 zero = {0, 0, 0, 0};
-      qf[ks] = as_bf16x8(head_ok ? v : zero);
-    }
-  }
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
+  const bool s_role = wave < NSW;
 
   // 1. compact the valid indices of the slice into sidx, in list order
   int mine[PER_T];
@@ -154,217 +164,242 @@ __global__ __launch_bounds__(NW * 64, NW == 1 ? 1 : 2) void mla_decode_kernel(
     cnt += p >= 0;
   }
   int nvalid;
-  int pos = block_excl_scan<NW>(cnt, scan_tmp, &nvalid);
+  int pos = block_excl_scan(cnt, scan_tmp, &nvalid);
 #pragma unroll
   for (int j = 0; j < PER_T; ++j)
     if (mine[j] >= 0) sidx[pos++] = mine[j];
-  const int nchunks = (nvalid + KC - 1) / KC;
-  for (int i = nvalid + tid; i < nchunks * KC; i += NT) sidx[i] = -1;
+  const int nch = (nvalid + KC - 1) / KC;
+  __syncthreads();
+  // padding rows of the last chunk load the slice's first row (masked)
+  for (int i = nvalid + tid; i < nch * KC; i += NT) sidx[i] = sidx[0];
   __syncthreads();
 
-  // 2. chunk c -> LDS slot c&1 in wave-wide 1 KB DMA blocks m = wave + j*NW. Lane l
-  // loads chunk row (l%32) ^ (4*(l/32)) for all of them: dims 8*(2m + l/32) .. +8.
-  // `ln` is an opaque copy of the lane index (recomputed per chunk rather than hoisted
-  // into registers held across the loop).
   const uint16_t* kvreq = kv + ri.kv_base * DQK;
-  auto dma_src = [&](int c, int ln) {  // this lane's source for DMA block 0 of chunk c
-    const int p = sidx[c * KC + ((ln & 31) ^ (4 * (ln >> 5)))];
-    // padding rows load position 0 and are masked below
-    return kvreq + static_cast<int64_t>(p < 0 ? 0 : p) * DQK + 8 * (ln >> 5);
-  };
-  auto dma_one = [&](int c, int j, const uint16_t* src) {
-    const int m = wave + j * NW;
-    if (m < BLOCKS)  // wave-uniform
-      lds_dma16(src + 16 * m, (const lds_void*)((const lds_u8*)kvbuf[c & 1] + m * 1024));
-  };
+  const int g = lane >> 4, c16 = lane & 15;  // 16x16 operand / accumulator coordinates
+  const int h = lane >> 5, r = lane & 31;    // 32x32 operand / accumulator coordinates
 
-  f32x4 o[DTW][NW];  // O^T tiles: dims 16*(wave*DTW + d) .., heads 16h .. of the block
+  if (s_role) {
+    // ================================ S waves ================================
+    const int hq = wave >> 1, kt = wave & 1;
+    const int head = min(HPB * hg + 16 * hq + c16, H - 1);  // heads past H repeat H-1
+    i32x4 qf[KS];  // Q^T operand: head `head`, dims 32ks + 8g .. +8
+    {
+      const uint16_t* qrow = q + (t * H + head) * DQK + 8 * g;
 #pragma unroll
-  for (int d = 0; d < DTW; ++d)
-#pragma unroll
-    for (int h = 0; h < NW; ++h) o[d][h] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  float m_ref = -INFINITY;  // reference max (base-2 logits) of head `head`
-  float lsum = 0.0f;        // running sum of this lane's share of the keys of `head`
-
-  if (nchunks > 0) {
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const uint16_t* src = dma_src(0, ln);
-#pragma unroll
-    for (int j = 0; j < DMA_PER; ++j) dma_one(0, j, src);
-  }
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const i32x4*>(qrow + 32 * ks);
+    }
+    float m_ref = M_INIT;  // reference max (base-2 logits) of head 16hq + c16
+    float lsum = 0.0f;     // this lane's share of the row sum of that head
+    // lane (g, c16) reads unit 4ks + g of chunk row 16kt + c16: block 4(ks/2) + 2kt + c16/8,
+    // row c16%8, unit position (4(ks%2) + g) ^ sw with sw = (c16%8) ^ 2(c16/8)
+    const int ksw = g ^ ((c16 & 7) ^ (2 * (c16 >> 3)));
+    const int kb0 = 1024 * (2 * kt + (c16 >> 3)) + 128 * (c16 & 7) + 16 * ksw;
+    const int kb1 = kb0 + 64 - 128 * (ksw >> 2);  // odd k-steps: position bit 2 flipped
 #pragma unroll 1
-  for (int c = 0; c < nchunks; ++c) {
-    DSA_WAIT_VMCNT(0);  // the only loads in flight: chunk c
-    __syncthreads();    // chunk c is in LDS for every wave; chunk c-1's slot and pbuf are free
-    const bool more = c + 1 < nchunks;
+    for (int i = 0; i <= nch; ++i) {
+      __syncthreads();  // B0: chunk i is in LDS; P^T and factors of chunk i-1 are visible
+      float cm = -INFINITY;
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+      const uint8_t* buf = kvbuf[i % NBUF];
+      if (i < nch) {
+        const uint8_t* ka0 = buf + kb0;
+        const uint8_t* ka1 = buf + kb1;
+        auto kread = [&](auto KSC) {
+          constexpr int ks = decltype(KSC)::value;
+          return *reinterpret_cast<const i32x4*>((ks & 1 ? ka1 : ka0) + 4096 * (ks >> 1));
+        };
+        i32x4 kr[KPF];
+        static_for<0, KPF>([&](auto I) { kr[decltype(I)::value] = kread(I); });
+        static_for<0, KS>([&](auto I) {
+          constexpr int ks = decltype(I)::value;
+          const i32x4 a = kr[ks % KPF];
+          if constexpr (ks + KPF < KS)
+            kr[ks % KPF] = kread(std::integral_constant<int, ks + KPF>{});
+          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(qf[ks]), s, 0, 0, 0);
+        });
+        // keys 32i + 16kt + 4g + j, j = 0..3
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool v = KC * i + 16 * kt + 4 * g + j < nvalid;
+          s[j] = v ? s[j] * c2 : -INFINITY;
+          cm = fmaxf(cm, s[j]);
+        }
+        cm = max_xor16_xor32(cm);
+        if (g == 0) sh_cm[kt][16 * hq + c16] = cm;
+      }
+      __syncthreads();  // B1: every S wave is done with chunk i's K (rope takes P^T)
+      if (i < nch) {
+        cm = fmaxf(cm, sh_cm[kt ^ 1][16 * hq + c16]);
+        const float mn = cm > m_ref + LAZY ? cm : m_ref;
+        const bool resc = __any(mn != m_ref);  // wave-uniform; same in both key halves
+        float alpha = 1.0f;
+        if (resc) {
+          alpha = exp2f(m_ref - mn);  // 0 at the first chunk, 1 if unchanged
+          lsum *= alpha;
+          m_ref = mn;
+        }
+        if (kt == 0) {
+          if (g == 0) sh_alpha[i & 1][16 * hq + c16] = alpha;
+          if (lane == 0) sh_resc[i & 1][hq] = resc;
+        }
+        // keys 4g .. 4g+3 of key step ko = kt are B operand slots 4g .. 4g+3 of lane
+        // 32(g/2) + 16(hq%2) + c16, head tile hq/2, bytes 8(g%2) .. +8
+        uint32_t pw[2];
+        float psum = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {  // masked keys: exp2(-inf) = 0; bf16 round to nearest even
+          const bf16x2 pp = __builtin_convertvector(
+              (f32x2){exp2f(s[2 * j] - m_ref), exp2f(s[2 * j + 1] - m_ref)}, bf16x2);
+          psum += static_cast<float>(pp[0]) + static_cast<float>(pp[1]);
+          pw[j] = __builtin_bit_cast(uint32_t, pp);
+        }
+        lsum += psum;
+        uint8_t* pdst = const_cast<uint8_t*>(buf) + 32768 + 1024 * (2 * (hq >> 1) + kt) +
+                        16 * (32 * (g >> 1) + 16 * (hq & 1) + c16) + 8 * (g & 1);
+        *reinterpret_cast<uint2*>(pdst) = make_uint2(pw[0], pw[1]);
+      }
+    }
+    // row sums and reference maxima for the O waves
+    const float lt = sum_xor16_xor32(lsum);
+    if (g == 0) {
+      sh_l[kt][16 * hq + c16] = lt;
+      if (kt == 0) sh_m[16 * hq + c16] = m_ref;
+    }
+    __syncthreads();
+  } else {
+    // ================================ O waves ================================
+    const int ow = wave - NSW;
+    const int ndma = ow < DMA_BLOCKS - 4 * NOW ? 5 : 4;  // blocks ow + 8j of a chunk
+    // DMA block ow + 8j is (ug, rg) = (ow/4 + 2j, ow%4): this lane copies row
+    // 8(ow%4) + l/8, unit 8ug + ((l%8) ^ (l/8) ^ 2(ow%2)).
     int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const uint16_t* src = more ? dma_src(c + 1, ln) : kvreq;
-    const uint8_t* buf = kvbuf[c & 1];
-
-    // 3. S^T for keys 0..15 (s0) and 16..31 (s1): lane holds keys 4g+i / 16+4g+i of head
-    // `head`. Chunk c+1's DMAs are spread over this loop, so the wave never stalls on a
-    // burst of them.
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    // k-step ks: lane (g, c16) reads unit 4ks + g of rows c16 (s0) and 16 + c16 (s1)
-    const uint8_t* kfrag = buf + g * UNIT_BYTES + 16 * cell(c16, g);
-#pragma unroll
-    for (int ks = 0; ks < 18; ++ks) {
-      if (more) {
-#pragma unroll
-        for (int j = ks * DMA_PER / 18; j < (ks + 1) * DMA_PER / 18; ++j) dma_one(c + 1, j, src);
-      }
-      const uint8_t* kp = kfrag + 4 * ks * UNIT_BYTES;
-      const bf16x8 a0 = as_bf16x8(*reinterpret_cast<const i32x4*>(kp));
-      const bf16x8 a1 = as_bf16x8(*reinterpret_cast<const i32x4*>(kp + 16 * 16));
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks], s1, 0, 0, 0);
-    }
-
-    // 4. softmax of this wave's 16 heads with a lazy reference max: it moves (and the
-    // accumulators are rescaled) only when the chunk max exceeds it by more than
-    // 2^LAZY; otherwise P <= 2^LAZY, and the reference cancels between numerator and
-    // denominator.
-    const int kb = c * KC;
-    float z[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      z[i] = kb + 4 * g + i < nvalid ? s0[i] * c2 : -INFINITY;
-      z[4 + i] = kb + 16 + 4 * g + i < nvalid ? s1[i] * c2 : -INFINITY;
-    }
-    float cm = z[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) cm = fmaxf(cm, z[i]);
-    cm = fmaxf(cm, __shfl_xor(cm, 16));
-    cm = fmaxf(cm, __shfl_xor(cm, 32));  // finite: every chunk holds at least one valid key
-    const bool resc = __any(cm > m_ref + LAZY);  // wave-uniform; always on the first chunk
-    if (resc) {
-      const float mn = cm > m_ref + LAZY ? cm : m_ref;
-      const float alpha = exp2f(m_ref - mn);  // 0 on the first chunk, 1 if unchanged
-      lsum *= alpha;
-      m_ref = mn;
-      if (g == 0) sh_alpha[head] = alpha;
-    }
-    if (lane == 0) sh_resc[wave] = resc;
-    uint32_t pw[4];
-    float psum = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint16_t ha = f32_to_bf16_bits(exp2f(z[2 * i] - m_ref));  // masked keys: 0
-      const uint16_t hb = f32_to_bf16_bits(exp2f(z[2 * i + 1] - m_ref));
-      psum += bf16_bits_to_f32(ha) + bf16_bits_to_f32(hb);
-      pw[i] = static_cast<uint32_t>(ha) | (static_cast<uint32_t>(hb) << 16);
-    }
-    lsum += psum;
-    // The P^T operand of the 16x16x32 MFMA: lane (head c16, group g) holds keys
-    // 4g..4g+3 and 16+4g..16+4g+3 (the K index order shared with the V^T operand).
-    __syncthreads();  // every wave is done reading K (the rope columns take P^T)
-    *pslot(buf, wave, lane) = (i32x4){(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3]};
-    __syncthreads();  // every wave's P^T and rescale factors are in LDS
-
-    // 5. O^T[dim, head] += V^T . P^T for this wave's dims and every head of the block. The
-    // V^T operand comes from transposing reads: source lane s of group g points at row
-    // key(g, s/4) and dims 16*dt + 4*(s%4) .. +4; the read hands lane i the value at dim
-    // 16*dt + i of rows key(g, 0..3) -- keys 4g..4g+3, then 16+4g..16+4g+3.
-    // Rescale the tiles of heads whose wave moved its reference this chunk.
-#pragma unroll
-    for (int h = 0; h < NW; ++h) {
-      if (sh_resc[h]) {  // block-uniform
-        const float a = sh_alpha[16 * h + c16];
-#pragma unroll
-        for (int d = 0; d < DTW; ++d) o[d][h] *= a;
-      }
-    }
-    // Dim tile dt: source lane (group g, s = lane%16) points at row 4g + s/4 (+16 for
-    // the second read), unit 2dt + (s%4)/2, byte 8*(s%2) of the unit cell. `ln` keeps the
-    // lane-dependent base from being hoisted across the loop.
-    const int g2 = ln >> 4, s2 = ln & 15;
-    const int vu = (s2 & 3) >> 1;  // unit parity
-    const lds_u8* vbase = (const lds_u8*)buf + vu * UNIT_BYTES +
-                          16 * cell(4 * g2 + (s2 >> 2), vu) + 8 * (s2 & 1);
-    auto v_operand = [&](int d) {
-      const int dt = wave * DTW + d;
-      const lds_u8* pa = vbase + 2 * dt * UNIT_BYTES;
-      const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)pa);
-      const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(pa + 16 * 16));
-      const s16x4 v8[2] = {va, vb};
-      return __builtin_bit_cast(bf16x8, v8);
+    const uint16_t* dsrc = kvreq;  // this lane's source for the chunk being issued
+    auto dma_src = [&](int c) {
+      asm volatile("" : "+v"(ln));
+      const int p = sidx[c * KC + 8 * (ow & 3) + (ln >> 3)];
+      const int uu = (ln & 7) ^ (ln >> 3) ^ (2 * (ow & 1));
+      dsrc = kvreq + static_cast<int64_t>(p) * DQK + 64 * (ow >> 2) + 8 * uu;
     };
-    if constexpr (NW <= 4) {  // all P^T operands in registers, one V^T operand at a time
-      bf16x8 pf[NW];
+    // DMA blocks j0 <= j < j1 of chunk c (source row from dma_src(c))
+    auto dma_part = [&](int c, auto J0, auto J1) {
+      const lds_u8* dst = (const lds_u8*)kvbuf[c % NBUF] + 1024 * ow;
+      static_for<decltype(J0)::value, decltype(J1)::value>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        if (j < 4 || ndma == 5)  // wave-uniform
+          lds_dma16(dsrc + 128 * j, (const lds_void*)(dst + 8192 * j));
+      });
+    };
+    auto dma_chunk = [&](int c) {
+      dma_src(c);
+      dma_part(c, std::integral_constant<int, 0>{}, std::integral_constant<int, 5>{});
+    };
+    f32x16 o[2][2];  // O^T tiles: dims 64ow + 32dt .., heads 32ht ..
 #pragma unroll
-      for (int h = 0; h < NW; ++h) pf[h] = as_bf16x8(*pslot(buf, h, lane));
+    for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-      for (int d = 0; d < DTW; ++d) {
-        const bf16x8 aop = v_operand(d);
+      for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
-        for (int h = 0; h < NW; ++h)
-          o[d][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, pf[h], o[d][h], 0, 0, 0);
+        for (int e = 0; e < 16; ++e) o[dt][ht][e] = 0.0f;
+    // V^T reads: 16-lane group g reads rows 16ko + 8(g/2) + 4rd + s/4 (read rd = 0/1) and
+    // dims 64ow + 32dt + 16(g%2) + 4(s%4) .. +4 (s = lane%16): block 4ow + 2ko + g/2, row
+    // 4rd + s/4, unit position (4dt + 2(g%2) + (s%4)/2) ^ (4rd + ((s/4) ^ 2(g/2))), which
+    // is 4(dt ^ rd) + (low two bits, fixed per lane).
+    const int vpos = (2 * (g & 1) + ((c16 & 3) >> 1)) ^ ((c16 >> 2) ^ (2 * (g >> 1)));
+    const int vlane = 4096 * ow + 1024 * (g >> 1) + 128 * (c16 >> 2) + 16 * vpos + 8 * (c16 & 1);
+    if (nch > 0) dma_chunk(0);
+    if (nch > 1) dma_chunk(1);
+#pragma unroll 1
+    for (int i = 0; i <= nch; ++i) {
+      // chunk i landed: only chunk i+1's DMAs may still be in flight
+      if (i + 1 < nch) {
+        if (ndma == 5) DSA_WAIT_VMCNT(5);
+        else DSA_WAIT_VMCNT(4);
+      } else {
+        DSA_WAIT_VMCNT(0);
       }
-    } else {  // 128 heads: all V^T operands in registers, one P^T operand at a time
-      bf16x8 aop[DTW];
-#pragma unroll
-      for (int d = 0; d < DTW; ++d) aop[d] = v_operand(d);
-#pragma unroll
-      for (int h = 0; h < NW; ++h) {
-        const bf16x8 pf = as_bf16x8(*pslot(buf, h, lane));
-#pragma unroll
-        for (int d = 0; d < DTW; ++d)
-          o[d][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[d], pf, o[d][h], 0, 0, 0);
+      __syncthreads();  // B0
+      if (i + 2 < nch) {
+        dma_src(i + 2);
+        dma_part(i + 2, std::integral_constant<int, 0>{}, std::integral_constant<int, DMA_A>{});
       }
+      const int c = i - 1;  // chunk accumulated in this iteration
+      const uint8_t* buf = kvbuf[(c + NBUF) % NBUF];
+      auto o_step = [&](int ko) {
+        const uint8_t* pb = buf + 32768 + 1024 * ko + 16 * lane;
+        const i32x4 p0 = *reinterpret_cast<const i32x4*>(pb);         // heads 0..31
+        const i32x4 p1 = *reinterpret_cast<const i32x4*>(pb + 2048);  // heads 32..63
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          const lds_u8* pa = (const lds_u8*)buf + vlane + 2048 * ko;
+          const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(pa + 64 * dt));
+          const s16x4 x1 =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(pa + 512 + 64 * (dt ^ 1)));
+          const s16x4 v8[2] = {x0, x1};
+          const bf16x8 aop = __builtin_bit_cast(bf16x8, v8);
+          o[dt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, as_bf16x8(p0), o[dt][0], 0, 0, 0);
+          o[dt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, as_bf16x8(p1), o[dt][1], 0, 0, 0);
+        }
+      };
+      if (c >= 0) {
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) {
+          if (sh_resc[c & 1][2 * ht] | sh_resc[c & 1][2 * ht + 1]) {  // block-uniform
+            const float a = sh_alpha[c & 1][32 * ht + r];
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt) o[dt][ht] *= a;
+          }
+        }
+        o_step(0);
+      }
+      __syncthreads();  // B1
+      if (i + 2 < nch)
+        dma_part(i + 2, std::integral_constant<int, DMA_A>{}, std::integral_constant<int, 5>{});
+      if (c >= 0) o_step(1);
     }
-  }
-
-  // Row sums of every head, for the waves that store its dims (slot 0 of the ring is
-  // free once every wave is past the loop).
-  float l = lsum + __shfl_xor(lsum, 16);
-  l += __shfl_xor(l, 32);
-  float* sh_l = reinterpret_cast<float*>(kvbuf[0]);
-  __syncthreads();
-  if (g == 0) sh_l[head] = l;
-  __syncthreads();
-  if (g == 0 && head_ok) {
-    if (nsplit == 1) {
-      if (lse) lse[t * H + head] = l > 0.0f ? (m_ref + __log2f(l)) * 0.69314718055994531f : -INFINITY;
-    } else {
-      const int64_t slot = (t * nsplit + split) * H + head;
-      ws_ml[2 * slot] = m_ref;
-      ws_ml[2 * slot + 1] = l;
-    }
-  }
-  // this lane holds dims 16*dt + 4g .. +4 of head 16h + c16 in o[d][h]
+    __syncthreads();  // row sums and maxima from the S waves
+    // this lane holds dims 64ow + 32dt + 8qd + 4h .. +4 of head 32ht + r in o[dt][ht]
 #pragma unroll
-  for (int h = 0; h < NW; ++h) {
-    const int hd = 16 * h + c16;
-    if (hd >= H) continue;
-    if (nsplit == 1) {
-      const float lh = sh_l[hd];
-      const float inv = lh > 0.0f ? 1.0f / lh : 0.0f;
-      uint16_t* orow = out + (t * H + hd) * DV + 4 * g;
+    for (int ht = 0; ht < 2; ++ht) {
+      const int hd = HPB * hg + 32 * ht + r;
+      if (hd >= H) continue;
+      const float mh = sh_m[32 * ht + r];
+      const float lh = sh_l[0][32 * ht + r] + sh_l[1][32 * ht + r];
+      if (nsplit == 1) {
+        const float inv = lh > 0.0f ? 1.0f / lh : 0.0f;
+        uint16_t* orow = out + (t * H + hd) * DV + 64 * ow + 4 * h;
 #pragma unroll
-      for (int d = 0; d < DTW; ++d) {
-        const int dt = wave * DTW + d;
-        const uint32_t lo = f32_to_bf16_bits(o[d][h][0] * inv) |
-                            (static_cast<uint32_t>(f32_to_bf16_bits(o[d][h][1] * inv)) << 16);
-        const uint32_t hi = f32_to_bf16_bits(o[d][h][2] * inv) |
-                            (static_cast<uint32_t>(f32_to_bf16_bits(o[d][h][3] * inv)) << 16);
-        *reinterpret_cast<uint2*>(orow + 16 * dt) = make_uint2(lo, hi);
-      }
-    } else {
-      const int64_t slot = (t * nsplit + split) * H + hd;
-      float* orow = ws_o + slot * DV + 4 * g;
+        for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-      for (int d = 0; d < DTW; ++d) {
-        const int dt = wave * DTW + d;
-        *reinterpret_cast<float4*>(orow + 16 * dt) =
-            make_float4(o[d][h][0], o[d][h][1], o[d][h][2], o[d][h][3]);
+          for (int qd = 0; qd < 4; ++qd) {
+            const f32x16& a = o[dt][ht];
+            const uint32_t lo = f32_to_bf16_bits(a[4 * qd] * inv) |
+                                (static_cast<uint32_t>(f32_to_bf16_bits(a[4 * qd + 1] * inv)) << 16);
+            const uint32_t hi = f32_to_bf16_bits(a[4 * qd + 2] * inv) |
+                                (static_cast<uint32_t>(f32_to_bf16_bits(a[4 * qd + 3] * inv)) << 16);
+            *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * qd) = make_uint2(lo, hi);
+          }
+        if (lse && ow == 0 && h == 0)
+          lse[t * H + hd] = lh > 0.0f ? (mh + __log2f(lh)) * 0.69314718055994531f : -INFINITY;
+      } else {
+        const int64_t slot = (t * nsplit + split) * H + hd;
+        float* orow = ws_o + slot * DV + 64 * ow + 4 * h;
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd)
+            *reinterpret_cast<float4*>(orow + 32 * dt + 8 * qd) =
+                make_float4(o[dt][ht][4 * qd], o[dt][ht][4 * qd + 1], o[dt][ht][4 * qd + 2],
+                            o[dt][ht][4 * qd + 3]);
+        if (ow == 0 && h == 0) {
+          ws_ml[2 * slot] = mh;
+          ws_ml[2 * slot + 1] = lh;
+        }
       }
     }
   }
 }
 
-// Merge split-K partials of one (row, head): 128 threads x 4 dims.
+// Merge split partials of one (row, head): 128 threads x 4 dims.
 __global__ __launch_bounds__(128) void mla_combine_kernel(const float* __restrict__ ws_o,
                                                           const float* __restrict__ ws_ml,
                                                           int H, int nsplit,
@@ -372,20 +407,16 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(const float* __restric
                                                           float* __restrict__ lse) {
   const int64_t t = blockIdx.x;
   const int head = blockIdx.y;
-  float M = -INFINITY;
+  float M = M_INIT;
   for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ws_ml[2 * ((t * nsplit + s) * H + head)]);
   float L = 0.0f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (M != -INFINITY) {
-    for (int s = 0; s < nsplit; ++s) {
-      const int64_t slot = (t * nsplit + s) * H + head;
-      const float ms = ws_ml[2 * slot];
-      if (ms == -INFINITY) continue;
-      const float f = exp2f(ms - M);
-      L += ws_ml[2 * slot + 1] * f;
-      const float4 v = reinterpret_cast<const float4*>(ws_o + slot * DV)[threadIdx.x];
-      acc.x += v.x * f; acc.y += v.y * f; acc.z += v.z * f; acc.w += v.w * f;
-    }
+  for (int s = 0; s < nsplit; ++s) {
+    const int64_t slot = (t * nsplit + s) * H + head;
+    const float f = exp2f(ws_ml[2 * slot] - M);  // 0 for a slice without valid keys
+    L += ws_ml[2 * slot + 1] * f;
+    const float4 v = reinterpret_cast<const float4*>(ws_o + slot * DV)[threadIdx.x];
+    acc.x += v.x * f; acc.y += v.y * f; acc.z += v.z * f; acc.w += v.w * f;
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   const uint32_t lo = f32_to_bf16_bits(acc.x * inv) | (static_cast<uint32_t>(f32_to_bf16_bits(acc.y * inv)) << 16);
@@ -396,14 +427,16 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(const float* __restric
 }
 
 #ifndef DSA_MLA_TARGET_BLOCKS
-#define DSA_MLA_TARGET_BLOCKS 256
+#define DSA_MLA_TARGET_BLOCKS 160
 #endif
 
-// Split count: at least ceil(k / 1024) (LDS index staging), then doubled while the grid
-// is below DSA_MLA_TARGET_BLOCKS blocks and each split keeps >= 256 entries.
-int choose_splits(int64_t rows, int k) {
+// Slices per row: at least ceil(k / 2048) (LDS index staging), then doubled while the
+// grid is below DSA_MLA_TARGET_BLOCKS blocks (one per CU) and each slice keeps >= 256
+// entries.
+int choose_splits(int64_t blocks_per_split, int k) {
   int s = static_cast<int>(ceil_div(k, MAX_KPS));
-  while (s < 16 && rows * s < DSA_MLA_TARGET_BLOCKS && ceil_div(k, 2 * s) >= 256) s *= 2;
+  while (s < 16 && blocks_per_split * s < DSA_MLA_TARGET_BLOCKS && ceil_div(k, 2 * s) >= 256)
+    s *= 2;
   return s;
 }
 
@@ -415,7 +448,7 @@ int64_t keys_per_split(int k, int s) { return ceil_div(ceil_div(k, s), KC) * KC;
 extern "C" size_t dsa_sparse_mla_workspace_size(int32_t T, int32_t H, int32_t k) {
   using namespace dsa;
   if (T <= 0 || H <= 0 || k <= 0) return 0;
-  const int s = choose_splits(T, k);
+  const int s = choose_splits(static_cast<int64_t>(T) * ceil_div(H, HPB), k);
   if (s == 1) return 0;
   return static_cast<size_t>(T) * s * H * (DV + 2) * sizeof(float);
 }
@@ -450,7 +483,8 @@ extern "C" dsa_status dsa_sparse_mla_decode(const uint16_t* q, const uint16_t* k
               "dsa_sparse_mla_decode: q, kv and out must be 16-byte aligned");
   DSA_REQUIRE(B <= 65535 && max_q_rows <= 65535,
               "dsa_sparse_mla_decode: B and max_q_rows must be <= 65535");
-  const int s = choose_splits(T, k);
+  const int nhg = static_cast<int>(ceil_div(H, HPB));
+  const int s = choose_splits(static_cast<int64_t>(T) * nhg, k);
   const size_t need = dsa_sparse_mla_workspace_size(T, H, k);
   if (ws_bytes < need || (need && !ws))
     return fail(DSA_ERR_WORKSPACE_TOO_SMALL,
@@ -463,19 +497,10 @@ extern "C" dsa_status dsa_sparse_mla_decode(const uint16_t* q, const uint16_t* k
   float* ws_ml = need ? ws_o + static_cast<size_t>(T) * nsplit * H * DV : nullptr;
   const float c2 = sm_scale * 1.4426950408889634f;  // natural -> base-2 logits
   hipStream_t st = as_stream(stream);
-  dim3 grid((unsigned)nsplit, (unsigned)max_q_rows, (unsigned)B);
-  const int nw = H <= 16 ? 1 : H <= 32 ? 2 : H <= 64 ? 4 : 8;  // waves of 16 heads, power of 2
-#define DSA_MLA_LAUNCH(NWV)                                                                    \
-  hipLaunchKernelGGL(mla_decode_kernel<NWV>, grid, dim3(NWV * 64), 0, st, q, kv, topk,         \
-                     share_base, num_accepted, q_row_offsets, kv_row_offsets, H, k, topk_rows, \
-                     c2, nsplit, kps, out, lse, ws_o, ws_ml)
-  switch (nw) {
-    case 1: DSA_MLA_LAUNCH(1); break;
-    case 2: DSA_MLA_LAUNCH(2); break;
-    case 4: DSA_MLA_LAUNCH(4); break;
-    default: DSA_MLA_LAUNCH(8); break;
-  }
-#undef DSA_MLA_LAUNCH
+  hipLaunchKernelGGL(mla_decode_kernel,
+                     dim3((unsigned)(nsplit * nhg), (unsigned)max_q_rows, (unsigned)B), dim3(NT),
+                     0, st, q, kv, topk, share_base, num_accepted, q_row_offsets, kv_row_offsets,
+                     H, nhg, k, topk_rows, c2, nsplit, kps, out, lse, ws_o, ws_ml);
   dsa_status stt = check_launch("dsa_sparse_mla_decode");
   if (stt != DSA_OK || nsplit == 1) return stt;
   hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)T, (unsigned)H), dim3(128), 0, st, ws_o,

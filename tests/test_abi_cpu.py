@@ -36,10 +36,11 @@ def test_version_and_workspace_queries():
     # split-K partials: T * splits * H * (512 + 2) floats, or none when one split suffices
     ws = lib.dsa_sparse_mla_workspace_size(192, 64, 2048)
     assert ws == 0 or ws % (192 * 64 * 514 * 4) == 0
-    # a split holds at most 1024 top-k entries: k = 1024 over many rows needs no partials,
-    # k = 2048 needs at least two splits
-    assert lib.dsa_sparse_mla_workspace_size(1024, 64, 1024) == 0
-    assert lib.dsa_sparse_mla_workspace_size(1024, 64, 2048) == 1024 * 2 * 64 * 514 * 4
+    # a split holds at most 2048 top-k entries: k = 2048 over many rows needs no partials,
+    # k = 4096 needs two splits; few rows are split further (>= 256 entries per split)
+    assert lib.dsa_sparse_mla_workspace_size(1024, 64, 2048) == 0
+    assert lib.dsa_sparse_mla_workspace_size(1024, 64, 4096) == 1024 * 2 * 64 * 514 * 4
+    assert lib.dsa_sparse_mla_workspace_size(16, 128, 2048) == 16 * 8 * 128 * 514 * 4
     # greedy accept: one (max, index) pair per 8192-entry vocabulary slice per row
     assert lib.greedy_accept_workspace_size(32, 5, 151552) == 32 * 6 * 19 * 8
     assert lib.greedy_accept_workspace_size(0, 5, 10) == 0

@@ -189,6 +189,32 @@ def test_sparse_mla_index_share_equals_compacted_copy():
     mla_check(o_sh, l_sh, ref_o, ref_l)
 
 
+@pytest.mark.parametrize("heads", [64, 128])
+def test_sparse_mla_many_rows_split_lists_and_workspace_reuse(heads):
+    # 200 rows with k = 448 (ragged contexts, 20% padding): lists split over blocks whose
+    # partial results are merged; a second call on the same workspace gives the same bits.
+    _say(f"sparse_mla many rows heads={heads}")
+    w = W.replace(W.scaled(W.MTP5_VERIFY, ctx=1200, batch=40, topk=448), rows=5, mla_heads=heads)
+    lens = synth.context_lengths(w)
+    qo, ko = synth.q_row_offsets(w), synth.kv_row_offsets(lens)
+    m = synth.mla_inputs(w, lens)
+    idx = synth.random_topk(w, lens, qo, w.topk, pad_frac=0.2)
+    idx[7, :] = -1
+    T = int(qo[-1])
+    need = api.sparse_mla_workspace_size(T, heads, w.topk)
+    ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=DEV)
+    u16 = lambda x: x.view(torch.uint16).numpy()
+    ref_o, ref_l = oracle.sparse_mla(u16(m["q"]), u16(m["kv"]), idx.numpy(), qo.numpy(),
+                                     ko.numpy(), w.sm_scale)
+    outs = []
+    for call in range(2):
+        out, lse = api.sparse_mla_decode(m["q"].to(DEV), m["kv"].to(DEV), idx.to(DEV), qo.to(DEV),
+                                         ko.to(DEV), w.rows, w.sm_scale, workspace=ws)
+        _say(f"  call {call}: worst err/bound = {mla_check(out, lse, ref_o, ref_l):.3f}")
+        outs.append((out.clone(), lse.clone()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
 def test_sparse_mla_dense_equals_full_visible_set():
     # k >= visible: sparse MLA over every visible position is dense causal attention
     _say("sparse_mla dense case")
