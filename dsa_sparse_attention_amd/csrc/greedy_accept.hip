@@ -15,8 +15,14 @@
 namespace dsa {
 namespace {
 
-constexpr int GA_THREADS = 256;
-constexpr int GA_SLICE = 8192;  // vocabulary entries per block
+#ifndef DSA_GA_THREADS
+#define DSA_GA_THREADS 256
+#endif
+#ifndef DSA_GA_SLICE
+#define DSA_GA_SLICE 8192
+#endif
+constexpr int GA_THREADS = DSA_GA_THREADS;
+constexpr int GA_SLICE = DSA_GA_SLICE;  // vocabulary entries per block
 
 struct ArgMax {
   float v;
@@ -43,14 +49,26 @@ __global__ __launch_bounds__(GA_THREADS) void argmax_slices_kernel(const void* _
     const bool vec = ((reinterpret_cast<uintptr_t>(lr + v0) & 15) == 0);
     int v = v0;
     if (vec) {
+      // every 16-byte load of the thread is issued before any is used (a whole slice is
+      // in flight per block)
+      constexpr int UNR = GA_SLICE / 8 / GA_THREADS;
       const int nvec = (v1 - v0) / 8;
-      for (int j = threadIdx.x; j < nvec; j += GA_THREADS) {
-        const i32x4 d = *reinterpret_cast<const i32x4*>(lr + v0 + 8 * j);
+      i32x4 d[UNR];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t w = static_cast<uint32_t>(d[e]);
-          take(best, __uint_as_float(w << 16), v0 + 8 * j + 2 * e);
-          take(best, __uint_as_float(w & 0xFFFF0000u), v0 + 8 * j + 2 * e + 1);
+      for (int u = 0; u < UNR; ++u) {
+        const int j = threadIdx.x + u * GA_THREADS;
+        if (j < nvec) d[u] = *reinterpret_cast<const i32x4*>(lr + v0 + 8 * j);
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int j = threadIdx.x + u * GA_THREADS;
+        if (j < nvec) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t w = static_cast<uint32_t>(d[u][e]);
+            take(best, __uint_as_float(w << 16), v0 + 8 * j + 2 * e);
+            take(best, __uint_as_float(w & 0xFFFF0000u), v0 + 8 * j + 2 * e + 1);
+          }
         }
       }
       v = v0 + 8 * nvec;
@@ -61,13 +79,23 @@ __global__ __launch_bounds__(GA_THREADS) void argmax_slices_kernel(const void* _
     const bool vec = ((reinterpret_cast<uintptr_t>(lr + v0) & 15) == 0);
     int v = v0;
     if (vec) {
+      constexpr int UNR = GA_SLICE / 4 / GA_THREADS;
       const int nvec = (v1 - v0) / 4;
-      for (int j = threadIdx.x; j < nvec; j += GA_THREADS) {
-        const float4 d = *reinterpret_cast<const float4*>(lr + v0 + 4 * j);
-        take(best, d.x, v0 + 4 * j);
-        take(best, d.y, v0 + 4 * j + 1);
-        take(best, d.z, v0 + 4 * j + 2);
-        take(best, d.w, v0 + 4 * j + 3);
+      float4 d[UNR];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int j = threadIdx.x + u * GA_THREADS;
+        if (j < nvec) d[u] = *reinterpret_cast<const float4*>(lr + v0 + 4 * j);
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int j = threadIdx.x + u * GA_THREADS;
+        if (j < nvec) {
+          take(best, d[u].x, v0 + 4 * j);
+          take(best, d[u].y, v0 + 4 * j + 1);
+          take(best, d[u].z, v0 + 4 * j + 2);
+          take(best, d[u].w, v0 + 4 * j + 3);
+        }
       }
       v = v0 + 4 * nvec;
     }
@@ -92,29 +120,44 @@ __global__ __launch_bounds__(GA_THREADS) void argmax_slices_kernel(const void* _
   }
 }
 
-__global__ __launch_bounds__(64) void accept_kernel(const float* __restrict__ ws_v,
-                                                    const int32_t* __restrict__ ws_i, int nslice,
-                                                    const int32_t* __restrict__ draft, int K,
-                                                    int32_t* __restrict__ num_accepted,
-                                                    int32_t* __restrict__ next_token,
-                                                    int32_t* __restrict__ argmax) {
-  const int b = blockIdx.x, i = threadIdx.x;
-  int32_t a = -1;
-  bool miss = false;
-  if (i <= K) {
+// One block per request: wave w merges the slices of rows w, w + nwaves, .. (lane j takes
+// slices j, j + 64, ..; the merge keeps the lower index on ties, so its order does not
+// matter); wave 0 then finds the first mismatching draft with a ballot.
+__global__ __launch_bounds__(1024) void accept_kernel(const float* __restrict__ ws_v,
+                                                      const int32_t* __restrict__ ws_i,
+                                                      int nslice, const int32_t* __restrict__ draft,
+                                                      int K, int32_t* __restrict__ num_accepted,
+                                                      int32_t* __restrict__ next_token,
+                                                      int32_t* __restrict__ argmax) {
+  __shared__ int32_t row_arg[64];
+  const int b = blockIdx.x, lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const int nwaves = blockDim.x / 64;
+  for (int i = wave; i <= K; i += nwaves) {
     const int64_t row = static_cast<int64_t>(b) * (K + 1) + i;
-    ArgMax best = {ws_v[row * nslice], ws_i[row * nslice]};
-    for (int s = 1; s < nslice; ++s) take(best, ws_v[row * nslice + s], ws_i[row * nslice + s]);
-    a = best.i;
-    if (argmax) argmax[row] = a;
-    if (i < K) miss = draft[static_cast<int64_t>(b) * K + i] != a;
+    ArgMax best = {-INFINITY, 0x7FFFFFFF};
+    for (int sl = lane; sl < nslice; sl += 64) take(best, ws_v[row * nslice + sl], ws_i[row * nslice + sl]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(best.v, o);
+      const int32_t oi = __shfl_xor(best.i, o);
+      take(best, ov, oi);
+    }
+    if (lane == 0) {
+      row_arg[i] = best.i;
+      if (argmax) argmax[row] = best.i;
+    }
   }
-  const uint64_t mask = __ballot(miss);
-  const int n = mask ? __builtin_ctzll(mask) : K;  // first mismatching draft
-  const int32_t an = __shfl(a, n);
-  if (i == 0) {
-    num_accepted[b] = n;
-    next_token[b] = an;
+  __syncthreads();
+  if (wave == 0) {
+    const int32_t a = lane <= K ? row_arg[lane] : -1;
+    const bool miss = lane < K && draft[static_cast<int64_t>(b) * K + lane] != a;
+    const uint64_t mask = __ballot(miss);
+    const int n = mask ? __builtin_ctzll(mask) : K;  // first mismatching draft
+    const int32_t an = __shfl(a, n);
+    if (lane == 0) {
+      num_accepted[b] = n;
+      next_token[b] = an;
+    }
   }
 }
 
@@ -158,7 +201,8 @@ extern "C" dsa_status greedy_accept(const void* logits, int32_t dtype, int64_t l
                        V, nslice, ws_v, ws_i);
   dsa_status s = check_launch("greedy_accept(argmax)");
   if (s != DSA_OK) return s;
-  hipLaunchKernelGGL(accept_kernel, dim3((unsigned)B), dim3(64), 0, st, ws_v, ws_i, nslice, draft, K,
+  const int acc_waves = K + 1 < 16 ? K + 1 : 16;  // one wave per verify row, at most 16
+  hipLaunchKernelGGL(accept_kernel, dim3((unsigned)B), dim3(64 * acc_waves), 0, st, ws_v, ws_i, nslice, draft, K,
                      num_accepted, next_token, argmax);
   return check_launch("greedy_accept(accept)");
 }
