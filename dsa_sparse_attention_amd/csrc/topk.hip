@@ -7,7 +7,16 @@
 // Selection order: (score desc, position asc). Scores map to order-preserving 32-bit
 // keys (-0.0 canonicalised to +0.0, so equal values tie on position). One 1024-thread
 // block per row.
-// Rows of up to 64K scores (fast path) are read once: the top 16 bits of every key go
+// Rows of up to 64K scores first try the register path: the row is loaded once into
+// registers (lane l of wave w holds positions 4096w + 64r + l, r < 64), every eighth
+// slot serves as a sample whose 16-bit key classes give a threshold admitting about
+// 1.25 k keys, and one ballot pass compacts the keys at or above it into per-wave LDS
+// regions, in position order. Three histogram rounds over these few thousand
+// candidates (16-bit class below the maximum, bits 15..5, bits 4..0) give theta and
+// the number of theta-ties to take, and a ballot pass emits ascending positions. A
+// sample that admits fewer than k keys, or more than a wave region holds, sends the
+// row to the exact LDS path below, which needs no sampling:
+// the top 16 bits of every key go
 // to LDS (128 KB) together with the row maximum; a histogram of each key's distance
 // below the maximum (keys spread over hundreds of bins, so LDS atomics rarely collide)
 // gives the 16-bit class of the k-th largest key; the positions at or above that class
@@ -26,6 +35,7 @@
 // The last 10 bits, the tie count at theta and the ascending emission then run on
 // the LDS candidates only. If the candidates overflow LDS (massive exact ties), a
 // slow path finishes the select and the emission with further reads of the row.
+// Block-wide prefix sums use DPP row shifts and row broadcasts within each wave.
 #include "common.hpp"
 
 namespace dsa {
@@ -37,35 +47,60 @@ constexpr int NSUB = 4;        // privatised level-1 histograms
 constexpr int CAND = 8192;     // slow-path LDS candidate capacity (key + position)
 constexpr int FAST_MAX = 65536;  // rows up to this length keep 16-bit keys in LDS
 constexpr int FCAND = 6016;     // fast-path candidate capacity
+constexpr int RS = 64;          // register path: slots per lane (64 x 1024 lanes = 65536 keys)
+constexpr int SSTEP = 8;        // register path: every eighth slot is a threshold sample
+constexpr int CW = 1024;        // register path: candidates per wave region (8 B each)
 
 __device__ __forceinline__ uint32_t order_key(float x) {
   uint32_t u = __float_as_uint(x == 0.0f ? 0.0f : x);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inclusive prefix sum across the 64 lanes of a wave: Hillis-Steele steps of 1, 2, 4 and
+// 8 lanes inside each 16-lane row (DPP row_shr; lanes with no source add 0), then row
+// broadcasts of lane 15 into rows 1 and 3 and of lane 31 into rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x111, 0xF, 0xF, false));
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x112, 0xF, 0xF, false));
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x114, 0xF, 0xF, false));
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x118, 0xF, 0xF, false));
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x142, 0xA, 0xF, false));
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x143, 0xC, 0xF, false));
+  return x;
+}
+
+// Wave-wide sum and maximum (unsigned), returned in every lane.
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(wave_incl_scan(x)), 63));
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x111, 0xF, 0xF, false)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x112, 0xF, 0xF, false)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x114, 0xF, 0xF, false)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x118, 0xF, 0xF, false)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x142, 0xA, 0xF, false)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x143, 0xC, 0xF, false)));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), 63));
+}
+
+// Number of set bits of a ballot in the lanes below this one.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t b) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(b >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b), 0u));
+}
+
 // Exclusive block-wide prefix sum over TK_THREADS threads; *total gets the sum.
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
-  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const int lane = threadIdx.x % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / 64));
+  const uint32_t x = wave_incl_scan(v);
   if (lane == 63) tmp[wave] = x;
   __syncthreads();
-  if (wave == 0) {
-    uint32_t s = lane < TK_WAVES ? tmp[lane] : 0u;
-#pragma unroll
-    for (int o = 1; o < TK_WAVES; o <<= 1) {
-      uint32_t y = __shfl_up(s, o);
-      if (lane >= o) s += y;
-    }
-    if (lane < TK_WAVES) tmp[TK_WAVES + lane] = s;  // inclusive wave totals
-  }
-  __syncthreads();
-  const uint32_t before = wave ? tmp[TK_WAVES + wave - 1] : 0u;
-  *total = tmp[2 * TK_WAVES - 1];
+  const uint32_t tw = wave_incl_scan(lane < TK_WAVES ? tmp[lane] : 0u);  // inclusive wave totals
+  const uint32_t before =
+      wave ? static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(tw), wave - 1)) : 0u;
+  *total = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(tw), TK_WAVES - 1));
   __syncthreads();
   return before + x - v;
 }
@@ -156,6 +191,257 @@ __device__ __forceinline__ void emit_ordered(int64_t n, uint32_t theta, uint32_t
   }
 }
 
+// Smallest float whose order key is at least c16 << 16 (the floor of a 16-bit key class).
+__device__ __forceinline__ float class_floor(uint32_t c16) {
+  const uint32_t key = c16 << 16;
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+// Bin holding the need-th largest key of an NB-bin histogram whose bin 0 holds the
+// largest keys, computed by every wave on its own (no block barrier): *bin gets the bin
+// and *above the count in bins before it. Returns false (uniformly) if the histogram holds
+// fewer than `need` keys.
+template <int NB>
+__device__ __forceinline__ bool wave_select(const uint32_t* hist, uint32_t need, uint32_t* bin,
+                                            uint32_t* above) {
+  constexpr int PER = NB / 64;
+  const int lane = threadIdx.x % 64;
+  uint32_t c[PER];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    c[j] = hist[PER * lane + j];
+    sum += c[j];
+  }
+  const uint32_t incl = wave_incl_scan(sum);
+  const uint32_t ex = incl - sum;
+  const uint64_t hit = __builtin_amdgcn_ballot_w64(ex < need && need <= incl);
+  if (!hit) return false;
+  const int src = __builtin_ctzll(hit);
+  uint32_t acc = ex, b = 0, ab = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    if (acc < need && need <= acc + c[j]) {
+      b = PER * lane + j;
+      ab = acc;
+    }
+    acc += c[j];
+  }
+  *bin = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(b), src));
+  *above = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ab), src));
+  return true;
+}
+
+// Register path for a row of k < n <= 65536 visible scores (see the top of the file);
+// wave w holds positions 4096 w + 64 r + lane in slot r. Returns false, uniformly over
+// the block, when the sampled threshold admits fewer than k keys or more than a wave
+// region holds, or theta's class falls outside the class histogram; nothing has been
+// written to `out` then. cand: 128 KB of LDS (16 wave regions of CW key bits followed by
+// CW positions); hist: 1280 words; rs: 80 words.
+__device__ __forceinline__ bool select_in_registers(const float* __restrict__ srow, int n, int k,
+                                                    int32_t* __restrict__ out, uint32_t* cand,
+                                                    uint32_t* hist, uint32_t* rs) {
+  const int tid = threadIdx.x, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int p0 = wave * (64 * RS) + lane;  // wave w holds positions [4096 w, 4096 w + 4096)
+  const float* __restrict__ vrow = srow + p0;
+  uint32_t* hs = hist;          // 256 bins: sample classes below the sample maximum
+  uint32_t* h1 = hist + 256;    // 512 bins: candidate classes below R = sample max + 128
+  uint32_t* h2 = hist + 768;    // 256 bins: bits 15..8 inside theta's class
+  uint32_t* h3 = hist + 1024;   // 256 bins: bits 7..0
+
+  // ---- load: sample slots first. A wave whose whole segment is visible loads with
+  // immediate offsets; the wave holding the end of the row loads from positions clamped
+  // to n - 1 and then sets the slots past the end to -inf (sample slots before the
+  // threshold, the rest before the compaction); waves past the end load nothing. ----
+  float v[RS];
+  const int lim = n - p0;  // slot r is visible iff 64 r < lim
+  const int seg0 = wave * (64 * RS);
+  const bool partial = seg0 < n && seg0 + 64 * RS > n;  // wave-uniform
+  if (seg0 + 64 * RS <= n) {
+#pragma unroll
+    for (int r = 0; r < RS; r += SSTEP) v[r] = vrow[64 * r];
+    __builtin_amdgcn_sched_barrier(0);  // keep the sample loads ahead of the rest
+#pragma unroll
+    for (int r = 0; r < RS; ++r)
+      if (r % SSTEP != 0) v[r] = vrow[64 * r];
+  } else if (partial) {
+#pragma unroll
+    for (int r = 0; r < RS; r += SSTEP) v[r] = srow[min(p0 + 64 * r, n - 1)];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < RS; ++r)
+      if (r % SSTEP != 0) v[r] = srow[min(p0 + 64 * r, n - 1)];
+#pragma unroll
+    for (int r = 0; r < RS; r += SSTEP) v[r] = 64 * r < lim ? v[r] : -__builtin_inff();
+  } else {
+#pragma unroll
+    for (int r = 0; r < RS; ++r) v[r] = -__builtin_inff();
+  }
+  for (int i = tid; i < 1280; i += TK_THREADS) hist[i] = 0;
+
+  // ---- threshold: 16-bit classes of the samples below their maximum ----
+  uint32_t smax = 0, scount = 0;
+#pragma unroll
+  for (int r = 0; r < RS; r += SSTEP)
+    if (64 * r < lim) {
+      smax = max(smax, order_key(v[r]) >> 16);
+      ++scount;
+    }
+  smax = wave_max(smax);
+  scount = wave_sum(scount);
+  if (lane == 0) {
+    rs[wave] = smax;
+    rs[16 + wave] = scount;
+  }
+  __syncthreads();
+  const uint32_t m16 = wave_max(lane < TK_WAVES ? rs[lane] : 0u);
+  const uint32_t ns = wave_sum(lane < TK_WAVES ? rs[16 + lane] : 0u);
+#pragma unroll
+  for (int r = 0; r < RS; r += SSTEP)
+    if (64 * r < lim) {
+      const uint32_t d = m16 - (order_key(v[r]) >> 16);
+      atomicAdd(&hs[d < 255 ? d : 255], 1u);
+    }
+  __syncthreads();
+  // aim at 1.25 times the samples' expected share of the top k, plus 16
+  const uint64_t want = (5ull * k * ns + 4ull * n - 1) / (4ull * n) + 16;
+  uint32_t dcut, dummy;
+  wave_select<256>(hs, want < ns ? static_cast<uint32_t>(want) : ns, &dcut, &dummy);
+  uint32_t c16 = m16 > dcut ? m16 - dcut : 0u;
+  if (c16 < 0x80u) c16 = 0x80u;  // keeps the threshold above -inf (the padding value)
+  const float t_lo = class_floor(c16);
+  if (partial) {
+#pragma unroll
+    for (int r = 0; r < RS; ++r)
+      if (r % SSTEP != 0) v[r] = 64 * r < lim ? v[r] : -__builtin_inff();
+  }
+
+  // ---- compaction: keys >= t_lo into this wave's region, in position order ----
+  uint32_t* region = cand + wave * (2 * CW);  // CW key bits, then CW positions
+  uint32_t cnt = 0;
+  if (seg0 < n) {
+#pragma unroll
+    for (int r = 0; r < RS; ++r) {
+      const bool c = v[r] >= t_lo;  // padding holds -inf, below any finite t_lo
+      const uint64_t b = __builtin_amdgcn_ballot_w64(c);
+      if (b) {
+        // an overflowing wave falls back below, so its extra keys may share the last slot
+        const uint32_t idx = min(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(b >> 32),
+                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b), cnt)),
+                                 static_cast<uint32_t>(CW - 1));
+        if (c) {
+          region[idx] = __float_as_uint(v[r]);
+          region[CW + idx] = static_cast<uint32_t>(p0 + 64 * r);
+        }
+        cnt += static_cast<uint32_t>(__popcll(b));
+      }
+    }
+  }
+  if (lane == 0) rs[32 + wave] = cnt;
+  __syncthreads();
+  const uint32_t wc = lane < TK_WAVES ? rs[32 + lane] : 0u;
+  const uint32_t total = wave_sum(wc);
+  if (wave_max(wc) > static_cast<uint32_t>(CW) || total < static_cast<uint32_t>(k)) return false;
+  const uint32_t cw = cnt;
+
+  // this lane's candidate keys (region entries lane + 64 j); 0 marks no candidate, since
+  // every candidate key is at least 0x80 << 16. The whole region is read (it is all in
+  // LDS) so the reads issue back to back, and entries past cw are masked afterwards.
+  constexpr int KJ = CW / 64;
+  uint32_t kreg[KJ];
+#pragma unroll
+  for (int j = 0; j < KJ; ++j) kreg[j] = region[lane + 64 * j];
+#pragma unroll
+  for (int j = 0; j < KJ; ++j)
+    if (64 * j < static_cast<int>(cw))
+      kreg[j] = lane + 64 * j < cw ? order_key(__uint_as_float(kreg[j])) : 0u;
+  // slots j with 64 j >= cw hold no candidate in any lane: the loops below skip them with
+  // a scalar test, so a wave pays only for the slots it fills
+
+  // ---- round 1: 16-bit class of theta, counted from R = sample maximum + 128 down;
+  // bins 0 and 511 also hold everything beyond them, so theta may not fall there ----
+  const uint32_t R = m16 + 128;
+#pragma unroll
+  for (int j = 0; j < KJ; ++j)
+    if (64 * j < static_cast<int>(cw) && kreg[j]) {
+      const int d = static_cast<int>(R) - static_cast<int>(kreg[j] >> 16);
+      atomicAdd(&h1[d < 0 ? 0 : (d > 511 ? 511 : d)], 1u);
+    }
+  __syncthreads();
+  uint32_t b1, above;
+  wave_select<512>(h1, k, &b1, &above);
+  if (b1 == 0 || b1 == 511) return false;
+  const uint32_t c16t = R - b1;
+  uint32_t need = k - above;
+  // ---- round 2: bits 15..8 of the keys in theta's class ----
+#pragma unroll
+  for (int j = 0; j < KJ; ++j)
+    if (64 * j < static_cast<int>(cw) && (kreg[j] >> 16) == c16t) atomicAdd(&h2[255 - ((kreg[j] >> 8) & 255)], 1u);
+  __syncthreads();
+  uint32_t b2;
+  wave_select<256>(h2, need, &b2, &above);
+  const uint32_t p24 = (c16t << 8) | (255 - b2);
+  need -= above;
+  // ---- round 3: bits 7..0 ----
+#pragma unroll
+  for (int j = 0; j < KJ; ++j)
+    if (64 * j < static_cast<int>(cw) && (kreg[j] >> 8) == p24) atomicAdd(&h3[255 - (kreg[j] & 255)], 1u);
+  __syncthreads();
+  uint32_t b3;
+  wave_select<256>(h3, need, &b3, &above);
+  const uint32_t theta = (p24 << 8) | (255 - b3);
+  need -= above;
+
+  // ---- emission: keys > theta and the first `need` theta-ties, ascending positions ----
+  uint32_t gt = 0, eq = 0;
+#pragma unroll
+  for (int j = 0; j < KJ; ++j)
+    if (64 * j < static_cast<int>(cw)) {
+      gt += kreg[j] > theta ? 1u : 0u;
+      eq += kreg[j] == theta ? 1u : 0u;
+    }
+  gt = wave_sum(gt);
+  eq = wave_sum(eq);
+  if (lane == 0) {
+    rs[48 + wave] = gt;
+    rs[64 + wave] = eq;
+  }
+  uint32_t preg[KJ];  // positions, read while the counts settle
+#pragma unroll
+  for (int j = 0; j < KJ; ++j) preg[j] = region[CW + lane + 64 * j];
+  __syncthreads();
+  // lane w < 16 holds wave w's counts: ties before wave w, the ties it takes, and the
+  // number of outputs before it
+  const uint32_t eq_w = lane < TK_WAVES ? rs[64 + lane] : 0u;
+  const uint32_t gt_w = lane < TK_WAVES ? rs[48 + lane] : 0u;
+  const uint32_t ties_ex = wave_incl_scan(eq_w) - eq_w;
+  const uint32_t left = ties_ex < need ? need - ties_ex : 0u;
+  const uint32_t own = gt_w + (eq_w < left ? eq_w : left);
+  const uint32_t out_ex = wave_incl_scan(own) - own;
+  const uint32_t ties_before =
+      static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ties_ex), wave));
+  const uint32_t out_before =
+      static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(out_ex), wave));
+  uint32_t run_eq = 0, run_sel = 0;
+#pragma unroll
+  for (int j = 0; j < KJ; ++j) {
+    if (64 * j < static_cast<int>(cw)) {
+      const uint32_t key = kreg[j];
+      const bool is_eq = key == theta;
+      const uint64_t be = __builtin_amdgcn_ballot_w64(is_eq);
+      const uint32_t rank = ties_before + run_eq + lanes_below(be);
+      const bool take = key > theta || (is_eq && rank < need);
+      const uint64_t bt = __builtin_amdgcn_ballot_w64(take);
+      const uint32_t o = out_before + run_sel + lanes_below(bt);
+      if (take && o < static_cast<uint32_t>(k)) out[o] = static_cast<int32_t>(preg[j]);
+      run_eq += static_cast<uint32_t>(__popcll(be));
+      run_sel += static_cast<uint32_t>(__popcll(bt));
+    }
+  }
+  return true;
+}
+
 __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const float* __restrict__ scores,
                                                           int64_t ld,
                                                           const int32_t* __restrict__ q_off,
@@ -168,6 +454,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const float* __restric
   __shared__ uint32_t tmp[2 * TK_WAVES];
   __shared__ uint32_t sel[2];
   __shared__ uint32_t smax;
+  __shared__ uint32_t rs[80];  // register path: per-wave maxima and counts
   uint32_t (*hist)[2048] = reinterpret_cast<uint32_t (*)[2048]>(regA);  // slow path: NSUB x 8 KB
   uint32_t* ckey = regA + NSUB * 2048;                                  // slow path: 32 KB
   int32_t* cpos = reinterpret_cast<int32_t*>(regA + NSUB * 2048 + CAND);  // slow path: 32 KB
@@ -187,6 +474,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const float* __restric
   const float* srow = scores + t * ld;
 
   if (n <= FAST_MAX) {
+    if (select_in_registers(srow, static_cast<int>(n), k, out, regA, fhist, rs)) return;
+    __syncthreads();  // fall back to the exact LDS path (region A and fhist are reused)
     // ---- fast path A: one read of the row; top 16 key bits to LDS, row maximum ----
     uint16_t* k16 = reinterpret_cast<uint16_t*>(regA);
     if (tid == 0) smax = 0;
