@@ -90,8 +90,13 @@ def index_score(q_fp8, q_scale, w, k_fp8, k_scale, q_row_offsets, kv_row_offsets
 
 
 def topk(scores, q_row_offsets, kv_row_offsets, max_q_rows: int, max_kv_len: int, k: int,
-         out: torch.Tensor | None = None):
-    """Per-row top-k positions [T, k] (ascending, -1 padded)."""
+         out: torch.Tensor | None = None, refine: dict | None = None):
+    """Per-row top-k positions [T, k] (ascending, -1 padded).
+
+    refine: the scored FP8 inputs, dict(q_fp8, q_scale, w, k_fp8, k_scale) plus optional
+    err_scale (float) and status (int32 [T]); the selection then follows the exact scores
+    (exact-boundary refine, see dsa_topk in include/dsa.h).
+    """
     _dev(scores, "scores", torch.float32)
     _dev(q_row_offsets, "q_row_offsets", torch.int32)
     _dev(kv_row_offsets, "kv_row_offsets", torch.int64)
@@ -101,10 +106,25 @@ def topk(scores, q_row_offsets, kv_row_offsets, max_q_rows: int, max_kv_len: int
         out = torch.empty((T, k), dtype=torch.int32, device=scores.device)
     _dev(out, "out", torch.int32)
     lib = _lib.load()
+    rf = None
+    if refine is not None:
+        _dev(refine["q_fp8"], "q_fp8", torch.uint8)
+        _dev(refine["q_scale"], "q_scale", torch.float32)
+        _dev(refine["w"], "w", torch.float32)
+        _dev(refine["k_fp8"], "k_fp8", torch.uint8)
+        _dev(refine["k_scale"], "k_scale", torch.float32)
+        st = refine.get("status")
+        if st is not None:
+            _dev(st, "status", torch.int32)
+        q = refine["q_fp8"]
+        rf = _lib.TopkRefine(_p(q), _p(refine["q_scale"]), _p(refine["w"]), _p(refine["k_fp8"]),
+                             _p(refine["k_scale"]), q.shape[1], q.shape[2],
+                             float(refine.get("err_scale", 0.0)), _p(st))
     wsb = lib.dsa_topk_workspace_size(T, max_kv_len, k)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=scores.device) if wsb else None
     _check(lib.dsa_topk(_p(scores), scores.shape[1], _p(q_row_offsets), _p(kv_row_offsets), B, T,
-                        max_q_rows, max_kv_len, k, _p(out), _p(ws), wsb, _stream()))
+                        max_q_rows, max_kv_len, k, ctypes.byref(rf) if rf is not None else None,
+                        _p(out), _p(ws), wsb, _stream()))
     return out
 
 

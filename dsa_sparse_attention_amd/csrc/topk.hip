@@ -732,6 +732,218 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const float* __restric
                [&](int64_t i) { return static_cast<int32_t>(i); });
 }
 
+// ---------------------------------------------------------------------------------------
+// Exact-boundary refine (see dsa_topk in dsa.h). One block per row, after topk_kernel:
+//  1. theta = the smallest float32 score in the row's selection; eps from the row's FP8
+//     queries, weights and the largest key scale among its visible keys;
+//  2. one pass over the row: keys above theta + 2 eps are kept (they are all in the
+//     selection already), keys in [theta - 2 eps, theta + 2 eps] form the band;
+//  3. every band key is rescored in float64 (the head dots are exact; the weighted sum
+//     over heads runs in ascending head order, one rounding per product and per sum);
+//  4. the best k - |kept| band keys by (exact score desc, position asc) join the kept
+//     keys, and the row is rewritten ascending.
+constexpr int RF_THREADS = 1024;
+constexpr int RF_WAVES = RF_THREADS / 64;
+constexpr int BAND_CAP = 4096;
+constexpr int RF_MAXK = 4096;
+
+// e4m3fn code -> value (exact): normal (8 + m) 2^(e-10), subnormal m 2^-9; 0x7F/0xFF
+// (NaN) are never produced by the quantiser and decode here as 0.
+__device__ __forceinline__ double e4m3_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  double v = (e == 15u && m == 7u) ? 0.0
+             : e ? __builtin_ldexp(static_cast<double>(8u + m), static_cast<int>(e) - 10)
+                 : __builtin_ldexp(static_cast<double>(m), -9);
+  return (c & 0x80u) ? -v : v;
+}
+
+__device__ __forceinline__ float block_min_f(float x, float* red) {
+  for (int o = 32; o >= 1; o >>= 1) x = fminf(x, __shfl_xor(x, o));
+  if (threadIdx.x % 64 == 0) red[threadIdx.x / 64] = x;
+  __syncthreads();
+  float y = red[0];
+  for (int w = 1; w < RF_WAVES; ++w) y = fminf(y, red[w]);
+  __syncthreads();
+  return y;
+}
+
+__device__ __forceinline__ float block_max_f(float x, float* red) {
+  return -block_min_f(-x, red);
+}
+
+__global__ __launch_bounds__(RF_THREADS) void topk_refine_kernel(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ q_off,
+    const int64_t* __restrict__ kv_off, int k, const uint8_t* __restrict__ q_fp8,
+    const float* __restrict__ q_scale, const float* __restrict__ wt,
+    const uint8_t* __restrict__ k_fp8, const float* __restrict__ k_scale, int H, int D,
+    double err_scale, int32_t* __restrict__ topk, int32_t* __restrict__ status) {
+  __shared__ double dtab[256];
+  __shared__ int32_t band_pos[BAND_CAP];
+  __shared__ double band_val[BAND_CAP];
+  __shared__ int32_t in_pos[RF_MAXK];
+  __shared__ int32_t sel_pos[RF_MAXK];
+  __shared__ double kdec[RF_WAVES][128];  // one band key's decoded codes per wave
+  __shared__ double term[RF_WAVES][128];  // u_j * max(d_j, 0) per head, per wave
+  __shared__ float redf[RF_WAVES];
+  __shared__ double redd[RF_WAVES];
+  __shared__ uint32_t tmp[2 * TK_WAVES];
+  __shared__ int counters[4];  // band size, selected band keys
+
+  const int b = blockIdx.y, r = blockIdx.x;
+  const RowInfo ri = load_row_info(q_off, kv_off, b);
+  if (r >= ri.R) return;
+  const int64_t t = ri.t0 + r;
+  int64_t n = visible_count(ri, r);
+  if (n > ld) n = ld;
+  const int tid = threadIdx.x, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  if (n <= k) {  // every visible key is selected whatever the scores
+    if (tid == 0 && status) status[t] = 0;
+    return;
+  }
+  const float* srow = scores + t * ld;
+  int32_t* out = topk + t * k;
+  const float* ksc = k_scale + ri.kv_base;
+  for (int c = tid; c < 256; c += RF_THREADS) dtab[c] = e4m3_value(static_cast<uint32_t>(c));
+  if (tid < 4) counters[tid] = 0;
+
+  // ---- 1. theta, the largest visible key scale, and sum_j |u_j| max_c |q_hat[j,c]| ----
+  float th = __builtin_inff();
+  for (int i = tid; i < k; i += RF_THREADS) th = fminf(th, srow[out[i]]);
+  th = block_min_f(th, redf);
+  float smax = 0.0f;
+  for (int64_t s = tid; s < n; s += RF_THREADS) smax = fmaxf(smax, ksc[s]);
+  smax = block_max_f(smax, redf);
+  double asum = 0.0;  // this wave's heads
+  for (int j = wave; j < H; j += RF_WAVES) {
+    const uint8_t* qj = q_fp8 + (t * H + j) * D;
+    uint32_t mc = 0;
+    for (int c = lane; c < D; c += 64) mc = max(mc, static_cast<uint32_t>(qj[c]) & 0x7Fu);
+    for (int o = 32; o >= 1; o >>= 1) mc = max(mc, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mc), o)));
+    const double u = static_cast<double>(wt[t * H + j]) * static_cast<double>(q_scale[t * H + j]);
+    asum += __builtin_fabs(u) * e4m3_value(mc);
+  }
+  if (lane == 0) redd[wave] = asum;
+  __syncthreads();
+  double A = 0.0;
+  for (int w = 0; w < RF_WAVES; ++w) A += redd[w];
+  const double C = err_scale > 0.0 ? err_scale : 4.0;
+  const double eps = C * 0x1p-16 * 448.0 * static_cast<double>(smax) * A;
+  const double hi = static_cast<double>(th) + 2.0 * eps, lo = static_cast<double>(th) - 2.0 * eps;
+
+  // ---- 2. kept keys (counted) and the band (collected) ----
+  uint32_t nin = 0;
+  for (int64_t s = tid; s < n; s += RF_THREADS) {
+    const double x = static_cast<double>(srow[s]);
+    if (x > hi) {
+      ++nin;
+    } else if (x >= lo) {
+      const int slot = atomicAdd(&counters[0], 1);
+      if (slot < BAND_CAP) band_pos[slot] = static_cast<int32_t>(s);
+    }
+  }
+  uint32_t nin_total;
+  block_excl_scan(nin, tmp, &nin_total);  // ends with a barrier: counters[0] is final
+  const int nb = counters[0];
+  const int need = k - static_cast<int>(nin_total);
+  if (nb > BAND_CAP || need < 1 || need > nb) {  // uniform: keep the float32 selection
+    if (tid == 0 && status) status[t] = nb > BAND_CAP ? -1 : -2;
+    return;
+  }
+
+  // ---- 3. exact rescore, one band key per wave at a time; lane j owns head j (and j+64) ----
+  for (int i = wave; i < nb; i += RF_WAVES) {
+    const int32_t p = band_pos[i];
+    const uint8_t* kr = k_fp8 + (ri.kv_base + p) * D;
+    for (int c = lane; c < D; c += 64) kdec[wave][c] = dtab[kr[c]];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int j = lane; j < H; j += 64) {
+      const uint8_t* qj = q_fp8 + (t * H + j) * D;
+      double d = 0.0;  // exact: every partial sum is a multiple of 2^-18 below 2^53 units
+      for (int c = 0; c < D; ++c) d = __builtin_fma(dtab[qj[c]], kdec[wave][c], d);
+      const double u = static_cast<double>(wt[t * H + j]) * static_cast<double>(q_scale[t * H + j]);
+      term[wave][j] = __dmul_rn(u, d > 0.0 ? d : 0.0);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (lane == 0) {
+      double acc = 0.0;
+      for (int j = 0; j < H; ++j) acc = __dadd_rn(acc, term[wave][j]);
+      band_val[i] = __dmul_rn(acc, static_cast<double>(ksc[p]));
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  __syncthreads();
+
+  // ---- 4. the best `need` band keys, then a merge with the kept keys, ascending ----
+  for (int i = tid; i < nb; i += RF_THREADS) {
+    const double v = band_val[i];
+    const int32_t p = band_pos[i];
+    int rank = 0;
+    for (int m = 0; m < nb; ++m) {
+      const double vm = band_val[m];
+      rank += (vm > v || (vm == v && band_pos[m] < p)) ? 1 : 0;
+    }
+    if (rank < need) {
+      const int slot = atomicAdd(&counters[1], 1);
+      if (slot < RF_MAXK) sel_pos[slot] = p;
+    }
+  }
+  // kept keys in the current (ascending) selection, order preserved; k <= RF_MAXK, so at
+  // most four entries per thread, taken as one contiguous run
+  constexpr int PER = RF_MAXK / RF_THREADS;
+  int32_t mine[PER];
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = tid * PER + j;
+    mine[j] = -1;
+    if (i < k) {
+      const int32_t p = out[i];
+      if (static_cast<double>(srow[p]) > hi) {
+        mine[j] = p;
+        ++cnt;
+      }
+    }
+  }
+  uint32_t kept;
+  uint32_t at = block_excl_scan(cnt, tmp, &kept);  // ends with a barrier: sel_pos is final
+  if (kept != nin_total) {  // uniform; cannot happen for a correct float32 selection
+    if (tid == 0 && status) status[t] = -3;
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    if (mine[j] >= 0) in_pos[at++] = mine[j];
+  __syncthreads();
+  // kept key i goes to i + (selected band keys below it); selected key p to (selected
+  // keys below p) + (kept keys below p)
+  for (int i = tid; i < static_cast<int>(kept); i += RF_THREADS) {
+    const int32_t p = in_pos[i];
+    int below = 0;
+    for (int m = 0; m < need; ++m) below += sel_pos[m] < p ? 1 : 0;
+    out[i + below] = p;
+  }
+  for (int i = tid; i < need; i += RF_THREADS) {
+    const int32_t p = sel_pos[i];
+    int below = 0;
+    for (int m = 0; m < need; ++m) below += sel_pos[m] < p ? 1 : 0;
+    int lo_i = 0, hi_i = static_cast<int>(kept);  // kept keys below p (in_pos ascending)
+    while (lo_i < hi_i) {
+      const int mid = (lo_i + hi_i) / 2;
+      if (in_pos[mid] < p) lo_i = mid + 1;
+      else hi_i = mid;
+    }
+    out[below + lo_i] = p;
+  }
+  if (tid == 0 && status) status[t] = nb;
+}
+
 }  // namespace
 }  // namespace dsa
 
@@ -740,8 +952,8 @@ extern "C" size_t dsa_topk_workspace_size(int32_t, int64_t, int32_t) { return 0;
 extern "C" dsa_status dsa_topk(const float* scores, int64_t score_ld,
                                const int32_t* q_row_offsets, const int64_t* kv_row_offsets,
                                int32_t B, int32_t T, int32_t max_q_rows, int64_t max_kv_len,
-                               int32_t k, int32_t* topk, void* ws, size_t ws_bytes,
-                               void* stream) {
+                               int32_t k, const dsa_topk_refine* refine, int32_t* topk, void* ws,
+                               size_t ws_bytes, void* stream) {
   using namespace dsa;
   (void)ws;
   (void)ws_bytes;
@@ -750,13 +962,27 @@ extern "C" dsa_status dsa_topk(const float* scores, int64_t score_ld,
   DSA_REQUIRE(score_ld >= max_kv_len && score_ld % 4 == 0,
               "dsa_topk: score_ld must be >= max_kv_len and a multiple of 4");
   DSA_REQUIRE(max_kv_len < (int64_t(1) << 31), "dsa_topk: max_kv_len must be < 2^31");
+  if (refine) {
+    DSA_REQUIRE(k <= RF_MAXK, "dsa_topk: the refine supports k <= %d (got %d)", RF_MAXK, k);
+    DSA_REQUIRE(refine->D_I == 64 || refine->D_I == 128, "dsa_topk: refine D_I must be 64 or 128");
+    DSA_REQUIRE(refine->H_I >= 1 && refine->H_I <= 128, "dsa_topk: refine H_I must be in [1, 128]");
+    DSA_REQUIRE(refine->err_scale >= 0.0, "dsa_topk: refine err_scale must be >= 0");
+  }
   if (B == 0 || T == 0 || max_q_rows == 0) return ok();
   DSA_REQUIRE(scores && q_row_offsets && kv_row_offsets && topk, "dsa_topk: null pointer");
+  DSA_REQUIRE(!refine || (refine->q_fp8 && refine->q_scale && refine->w && refine->k_fp8 &&
+                          refine->k_scale),
+              "dsa_topk: null refine pointer");
   DSA_REQUIRE((reinterpret_cast<uintptr_t>(scores) & 15) == 0,
               "dsa_topk: scores must be 16-byte aligned");
   DSA_REQUIRE(B <= 65535, "dsa_topk: B must be <= 65535");
   dim3 grid((unsigned)max_q_rows, (unsigned)B);
   hipLaunchKernelGGL(topk_kernel, grid, dim3(TK_THREADS), 0, as_stream(stream), scores, score_ld,
                      q_row_offsets, kv_row_offsets, k, topk);
+  if (refine)
+    hipLaunchKernelGGL(topk_refine_kernel, grid, dim3(RF_THREADS), 0, as_stream(stream), scores,
+                       score_ld, q_row_offsets, kv_row_offsets, k, refine->q_fp8, refine->q_scale,
+                       refine->w, refine->k_fp8, refine->k_scale, refine->H_I, refine->D_I,
+                       refine->err_scale, topk, refine->status);
   return check_launch("dsa_topk");
 }

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 1
+#define DSA_ABI_VERSION 2
 
 typedef enum {
   DSA_OK = 0,
@@ -115,6 +115,28 @@ dsa_status dsa_index_score(const uint8_t* q_fp8, const float* q_scale, const flo
                            int64_t max_kv_len, float* scores, int64_t score_ld, void* stream);
 
 /*
+ * dsa_topk_refine -- inputs of the exact-boundary refine of dsa_topk: the
+ * same FP8 queries, weights, keys and scales that dsa_index_score scored.
+ * All pointers are device pointers (layouts as in dsa_index_score).
+ *   err_scale  C of the error bound below; 0 selects 4
+ *   status     [T] int32, nullable: per row, the number of band keys that
+ *              were rescored (0 when the row needs no refine), or -1 when
+ *              the band held more than 4096 keys (that row keeps the
+ *              unrefined selection)
+ */
+typedef struct dsa_topk_refine {
+  const uint8_t* q_fp8;
+  const float* q_scale;
+  const float* w;
+  const uint8_t* k_fp8;
+  const float* k_scale;
+  int32_t H_I;
+  int32_t D_I;
+  double err_scale;
+  int32_t* status;
+} dsa_topk_refine;
+
+/*
  * dsa_topk -- per-row top-k selection over the visible scores.
  * ("MAX Pipeline 中的 DeepSeek-V3.2 架构实现解析", "Indexer 的结构与计算流程": top-k
  * output of shape (total_seq_len, index_topk); "GLM-5.3 推理全链路(十四)",
@@ -124,15 +146,29 @@ dsa_status dsa_index_score(const uint8_t* q_fp8, const float* q_scale, const flo
  * s asc) -- -0.0 equals +0.0, scores must not be NaN -- keeps the first
  * min(k, p_t+1), and writes them ASCENDING to topk[t, 0:k], padding with -1.
  * Positions are request-local.
+ *
+ * With refine != NULL the selection follows the exact scores instead of the
+ * float32 ones: the set becomes the one obtained by ordering on
+ *   I_exact[t,s] = s_k[s] * sum_{j ascending} u_j * max(d_j, 0),
+ *   d_j = q_hat[t,j] . k_hat[s] (exact), u_j = w[t,j] * q_scale[t,j],
+ * evaluated in float64 in exactly that order (one rounding per product and
+ * per sum), provided every float32 score lies within
+ *   eps_t = C * 2^-16 * 448 * max_{s <= p_t} k_scale[s] * sum_j |u_j| * max_c |q_hat[t,j,c]|
+ * of its exact value (a bound on the FP8 MFMA's reduced-width accumulation
+ * plus the float32 epilogue; C is checked by measurement, not derived).
+ * With theta the k-th largest float32 score, keys above theta + 2 eps_t are
+ * kept, keys below theta - 2 eps_t dropped, and the band in between is
+ * rescored exactly and ranked by (I_exact desc, s asc).
  *   scores [T, score_ld] float32 (as written by dsa_index_score)
  *   topk   [T, k] int32
  * Workspace: none (ws may be NULL; ws_bytes ignored).
- * Errors: DSA_ERR_INVALID_ARGUMENT (k < 1, k > 8192, ...).
+ * Errors: DSA_ERR_INVALID_ARGUMENT (k < 1, k > 8192, refine with k > 4096,
+ * D_I not 64/128, H_I not in [1, 128], ...).
  */
 dsa_status dsa_topk(const float* scores, int64_t score_ld, const int32_t* q_row_offsets,
                     const int64_t* kv_row_offsets, int32_t B, int32_t T, int32_t max_q_rows,
-                    int64_t max_kv_len, int32_t k, int32_t* topk, void* ws, size_t ws_bytes,
-                    void* stream);
+                    int64_t max_kv_len, int32_t k, const dsa_topk_refine* refine, int32_t* topk,
+                    void* ws, size_t ws_bytes, void* stream);
 
 size_t dsa_topk_workspace_size(int32_t T, int64_t max_kv_len, int32_t k);
 

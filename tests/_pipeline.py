@@ -149,3 +149,28 @@ def mla_check(out_gpu, lse_gpu, out_ref, lse_ref):
     assert np.array_equal(np.isfinite(lg), fin)
     assert np.all(np.abs(lg[fin] - lse_ref[fin]) <= 2.5e-3)
     return worst
+
+
+def refine_args(gi, case, status: bool = True):
+    """dsa_topk refine inputs: the HIP path's own quantised q/k (device), weights, status."""
+    d = dict(q_fp8=gi["qc"], q_scale=gi["qs"], w=case.w_f32, k_fp8=gi["kc"], k_scale=gi["ks"])
+    if status:
+        d["status"] = torch.zeros(case.T, dtype=torch.int32, device=DEV)
+    return d
+
+
+def refine_eps(qc, qs, w, ks, qo, ko, rows, C: float = 4.0):
+    """Per-row refine bound eps_t = C 2^-16 448 max_{s<=p_t} k_scale[s] sum_j |u_j| max|q_hat_j|.
+
+    Written from the statement of dsa_topk in include/dsa.h, on the host copies.
+    """
+    dec = oracle.fp8_decode(np.arange(256, dtype=np.uint8))
+    qmax = np.abs(dec[qc]).max(axis=-1)                                # [T, H]
+    u = np.abs(w.astype(np.float64) * qs.astype(np.float64))          # [T, H]
+    out = np.zeros(len(rows))
+    for i, t in enumerate(rows):
+        b = int(np.searchsorted(qo, t, side="right") - 1)
+        n = oracle.row_visible(qo, ko, int(t))
+        smax = float(ks[ko[b]:ko[b] + n].max()) if n else 0.0
+        out[i] = C * 2.0 ** -16 * 448.0 * smax * float((u[t] * qmax[t]).sum())
+    return out

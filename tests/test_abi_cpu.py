@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_workspace_queries():
     lib = _lib.load()
-    assert lib.dsa_abi_version() == 1
+    assert lib.dsa_abi_version() == 2
     assert lib.dsa_last_error() in (b"", None)
     assert lib.dsa_topk_workspace_size(192, 65536, 2048) == 0
     # split-K partials: T * splits * H * (512 + 2) floats, or none when one split suffices

@@ -17,8 +17,8 @@ The oracle cannot score every (row, key) pair at this size in seconds, so:
   (a score does not depend on the key's position, only its visibility does), within the
   FP8-MFMA error bound; every row's visible prefix is written and the rest untouched;
 * top-k on generated score rows (continuous and heavily tied): every row, bit-exact;
-* end-to-end top-k: a few rows scored in full by the oracle, sets equal up to the
-  error band around the k-th score;
+* end-to-end top-k: a few rows scored in full by the oracle; the float32 sets are equal
+  up to the error band around the k-th score, the refined sets exactly;
 * sparse MLA on generated index sets: a sample of rows, all heads, within the
   sparse-MLA tolerance;
 * planted spikes: the top-k of every row is the request's first 2048 spike positions;
@@ -31,7 +31,7 @@ import torch
 
 import oracle
 from dsa_sparse_attention_amd import api, synth, workloads
-from tests._pipeline import DEV, check_topk_valid, mla_check, score_tolerance
+from tests._pipeline import DEV, check_topk_valid, mla_check, refine_eps, score_tolerance
 
 pytestmark = pytest.mark.gpu
 
@@ -66,6 +66,11 @@ class Full:
                         self.max_kv, scores=self.scores)
         self.top = torch.empty((self.T, w.topk), dtype=torch.int32, device=DEV)
         api.topk(self.scores, self.qo_d, self.ko_d, w.rows, self.max_kv, w.topk, out=self.top)
+        # the same selection with the exact-boundary refine
+        self.rstatus = torch.zeros(self.T, dtype=torch.int32, device=DEV)
+        self.top_ref = api.topk(self.scores, self.qo_d, self.ko_d, w.rows, self.max_kv, w.topk,
+                                refine=dict(q_fp8=self.qc, q_scale=self.qs, w=self.w,
+                                            k_fp8=self.kc, k_scale=self.ks, status=self.rstatus))
         torch.cuda.synchronize()
 
     def visible(self, t: int) -> int:
@@ -155,9 +160,14 @@ def test_full_topk_bitexact_every_row(f, levels):
 
 
 def test_full_end_to_end_topk_sampled_rows(f):
+    # float32 selection: equal to the oracle's set up to the error band; refined selection:
+    # equal to it exactly, with the float32 scores within half the refine bound
     W = f.wl
     rows = [0, W.rows - 1, f.T - 1]
     _say(f"full end-to-end top-k: rows {rows} scored in full by the oracle")
+    st = f.rstatus.cpu().numpy()
+    assert st.min() >= 0, "refine band overflow"
+    _say(f"  refine band sizes over all rows: max {st.max()}, mean {st.mean():.1f}")
     for t in rows:
         b = f.request(t)
         n = f.visible(t)
@@ -174,7 +184,13 @@ def test_full_end_to_end_topk_sampled_rows(f):
         ref_k = oracle.topk(ref_s, [n], W.topk)
         tol = score_tolerance(qc, qs, wt, kc, ks, [r], qo1, ko1, f.max_kv)
         nd = check_topk_valid(f.top[t:t + 1].cpu().numpy(), ref_k, ref_s, [n], tol, W.topk)
-        _say(f"  row {t}: {'equal' if nd == 0 else 'differs only inside the error band'}")
+        eps = refine_eps(qc, qs, wt, ks, qo1, ko1, [r])[0]
+        got_s = f.scores[t, :n].cpu().numpy().astype(np.float64)
+        ratio = float(np.abs(got_s - ref_s[0, :n]).max() / eps)
+        assert ratio <= 0.5, f"row {t}: float32 error {ratio:.3f} of the refine bound"
+        assert np.array_equal(f.top_ref[t].cpu().numpy(), ref_k[0]), f"row {t}: refined set"
+        _say(f"  row {t}: float32 set {'equal' if nd == 0 else 'band-only differences'}, "
+             f"refined set equal (error/eps {ratio:.3f}, band {st[t]})")
 
 
 def test_full_sparse_mla_sampled_rows(f):
@@ -206,10 +222,12 @@ def test_full_planted_spikes_topk_closed_form(f):
         pytest.skip("no planted spikes in this workload")
     _say(f"full planted spikes: all {f.T} rows")
     top = f.top.cpu().numpy()
+    top_ref = f.top_ref.cpu().numpy()
     for t in range(f.T):
         exp = f.spike_pos[f.request(t)][:f.wl.topk].numpy()
         assert len(exp) == f.wl.topk
         assert np.array_equal(top[t], exp), f"row {t}"
+        assert np.array_equal(top_ref[t], exp), f"row {t} (refined)"
 
 
 def test_full_index_share_draft_rows(f):

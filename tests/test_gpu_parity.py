@@ -14,7 +14,7 @@ import torch
 import oracle
 from dsa_sparse_attention_amd import api, synth, workloads
 from tests._pipeline import (DEV, Case, check_topk_valid, gpu_indexer, mla_check,
-                             oracle_quant, score_tolerance)
+                             oracle_quant, refine_args, refine_eps, score_tolerance)
 
 pytestmark = pytest.mark.gpu
 
@@ -145,6 +145,52 @@ def test_end_to_end_topk_sets(name):
     if w.spike_frac:
         for t in rows:  # planted spikes: closed-form answer, decided purely by position
             assert list(gi["topk"][t].cpu().numpy()) == list(case.spike_pos[0][:w.topk].numpy())
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_end_to_end_topk_refined_equals_oracle(name):
+    # exact-boundary refine: the HIP set must equal the oracle's set on every row, and the
+    # float32 scores must sit within half of the refine's error bound (its constant is
+    # validated by this measurement, not derived)
+    w = SMALL[name]
+    _say(f"end-to-end refined top-k {name}")
+    case = Case(w, with_mla=False, with_accept=False)
+    gi = gpu_indexer(case)
+    qc, qs, kc, ks, ko = oracle_quant(case)
+    rows = np.arange(case.T)
+    ref_s = oracle.index_score(qc, qs, case.host("w_f32"), kc, ks, case.qo.numpy(), ko,
+                               rows=rows, width=case.max_kv)
+    nvis = np.array([case.visible(int(t)) for t in rows])
+    ref_k = oracle.topk(ref_s, nvis, w.topk)
+    eps = refine_eps(qc, qs, case.host("w_f32"), ks, case.qo.numpy(), ko, rows)
+    got_s = gi["scores"].cpu().numpy()[:, :case.max_kv].astype(np.float64)
+    ratio = max(float(np.abs(got_s[t, :nvis[t]] - ref_s[t, :nvis[t]]).max() / eps[t])
+                for t in rows if nvis[t])
+    _say(f"  max |I_f32 - I_exact| / eps = {ratio:.3f}")
+    assert ratio <= 0.5
+    ra = refine_args(gi, case)
+    got = api.topk(gi["scores"], case.qo_d, case.ko_d, w.rows, case.max_kv, w.topk, refine=ra)
+    st = ra["status"].cpu().numpy()
+    _say(f"  band sizes: max {st.max()}, mean {st.mean():.1f}")
+    assert st.min() >= 0
+    assert np.array_equal(got.cpu().numpy(), ref_k)
+
+
+def test_topk_refine_rejects_bad_arguments():
+    _say("topk refine error paths")
+    s = torch.zeros((2, 64), device=DEV)
+    qo = torch.tensor([0, 2], dtype=torch.int32, device=DEV)
+    ko = torch.tensor([0, 64], dtype=torch.int64, device=DEV)
+    ra = dict(q_fp8=torch.zeros((2, 8, 96), dtype=torch.uint8, device=DEV),
+              q_scale=torch.ones((2, 8), device=DEV), w=torch.ones((2, 8), device=DEV),
+              k_fp8=torch.zeros((64, 96), dtype=torch.uint8, device=DEV),
+              k_scale=torch.ones(64, device=DEV))
+    with pytest.raises(api.DsaError, match="INVALID_ARGUMENT"):
+        api.topk(s, qo, ko, 2, 64, 8, refine=ra)          # D_I = 96
+    ra["q_fp8"] = torch.zeros((2, 8, 64), dtype=torch.uint8, device=DEV)
+    ra["k_fp8"] = torch.zeros((64, 64), dtype=torch.uint8, device=DEV)
+    with pytest.raises(api.DsaError, match="INVALID_ARGUMENT"):
+        api.topk(s, qo, ko, 2, 64, 4097, refine=ra)       # k above the refine's limit
 
 
 # ---------------------------------------------------------------- sparse MLA
