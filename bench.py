@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--refine", action="store_true",
+                    help="top-k with the exact-boundary refine (float64 rescore of the band)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration) and exit")
     return ap.parse_args()
@@ -77,6 +79,11 @@ class Inputs:
         del ix
         m = synth.mla_inputs(w, lengths, device=dev, seed_offset=copy)
         self.q_mla, self.kv = m["q"], m["kv"]
+        self.q_draft = None
+        if w.share_steps:  # one draft row per request for each reuse step, same latent cache
+            self.q_draft = [synth.mla_inputs(w, lengths, device=dev, rows=1,
+                                             seed_offset=100 * (copy + 1) + j, kv=self.kv)["q"]
+                            for j in range(w.share_steps)]
         a = synth.accept_inputs(w, device=dev) if copy == 0 else None
         if a is None:
             a = Inputs.accept_cache
@@ -181,12 +188,22 @@ def main():
     ws_need = api.sparse_mla_workspace_size(T, w.mla_heads, w.topk)
     ws_mla = torch.empty(max(ws_need, 16), dtype=torch.uint8, device=dev)
     from dsa_sparse_attention_amd import _lib
+    tk_need = api.topk_workspace_size(T, max_kv, w.topk)
+    ws_tk = torch.empty(max(tk_need, 16), dtype=torch.uint8, device=dev)
     ga_need = _lib.load().greedy_accept_workspace_size(w.batch, w.drafts, w.vocab)
     ws_ga = torch.empty(max(ga_need, 16), dtype=torch.uint8, device=dev)
     print(f"[bench] inputs resident ({args.copies} copies); mla workspace {ws_need/1e6:.1f} MB",
           file=sys.stderr, flush=True)
 
     names = ["quantize_q", "index_score", "topk", "sparse_mla", "greedy_accept"]
+    if w.share_steps:
+        names.append("share_mla")
+        qo1 = torch.arange(w.batch + 1, dtype=torch.int32, device=dev)
+        n_acc = synth.accepted_lengths(w).to(dev)
+        out1 = torch.empty((w.batch, w.mla_heads, 512), dtype=torch.bfloat16, device=dev)
+        lse1 = torch.empty((w.batch, w.mla_heads), dtype=torch.float32, device=dev)
+        ws1_need = api.sparse_mla_workspace_size(w.batch, w.mla_heads, w.topk)
+        ws1 = torch.empty(max(ws1_need, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def step(inp, ev=None):
@@ -195,18 +212,25 @@ def main():
         if ev: ev[1].record(stream)
         api.index_score(qc, qs, inp.w, inp.k_fp8, inp.k_scale, qo, ko, w.rows, max_kv, scores=scores)
         if ev: ev[2].record(stream)
-        api.topk(scores, qo, ko, w.rows, max_kv, w.topk, out=topk)
+        rf = (dict(q_fp8=qc, q_scale=qs, w=inp.w, k_fp8=inp.k_fp8, k_scale=inp.k_scale)
+              if args.refine else None)
+        api.topk(scores, qo, ko, w.rows, max_kv, w.topk, out=topk, refine=rf, workspace=ws_tk)
         if ev: ev[3].record(stream)
         api.sparse_mla_decode(inp.q_mla, inp.kv, topk, qo, ko, w.rows, w.sm_scale, out=out, lse=lse,
                               workspace=ws_mla)
         if ev: ev[4].record(stream)
         api.greedy_accept(inp.logits, inp.draft, w.drafts, argmax=False, workspace=ws_ga)
         if ev: ev[5].record(stream)
+        for qd in inp.q_draft or []:  # draft steps: the step-0 top-k row at the accepted position
+            api.sparse_mla_decode(qd, inp.kv, topk, qo1, ko, 1, w.sm_scale, out=out1, lse=lse1,
+                                  workspace=ws1, share_base=qo, num_accepted=n_acc)
+        if ev and inp.q_draft: ev[6].record(stream)
 
     for i in range(args.warmup):
         step(copies[i % len(copies)])
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+           for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -237,6 +261,10 @@ def main():
         "sparse_mla": dict(bytes=wm["bytes"], flops=wm["flops"], bound="hbm", file="sparse_mla.hip"),
         "greedy_accept": dict(bytes=wg["bytes"], bound="hbm", file="greedy_accept.hip"),
     }
+    if w.share_steps:
+        ws_ = accounting.sparse_mla_work(w.batch, w.mla_heads, w.topk)
+        kern["share_mla"] = dict(bytes=w.share_steps * ws_["bytes"],
+                                 flops=w.share_steps * ws_["flops"], bound="hbm")
     kernels = {}
     for n, kd in kern.items():
         t_s = per[n] * 1e-3
@@ -262,7 +290,8 @@ def main():
     roof["kernel"] = dom
     roof["traffic"] = traffic_for(kd.get("file", ""), dom) if kd.get("file") else None
 
-    value = T / (ms_step * 1e-3)
+    rows_step = T + w.share_steps * w.batch  # verify rows, plus one draft row per reuse step
+    value = rows_step / (ms_step * 1e-3)
     rec = {
         "metric": "verify query rows/sec (indexer+top-k+sparse MLA) at 64K ctx; HBM GB/s, MFMA %",
         "value": round(value, 1), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
@@ -270,7 +299,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8+bf16", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "context": max_kv, "rows_per_request": w.rows,
                    "index_heads": w.index_heads, "index_dim": w.index_dim, "topk": w.topk,
-                   "mla_heads": w.mla_heads, "vocab": w.vocab, "global_batch": T, "seq_len": max_kv,
+                   "mla_heads": w.mla_heads, "vocab": w.vocab, "global_batch": rows_step,
+                   "seq_len": max_kv, "share_steps": w.share_steps, "topk_refine": args.refine,
                    "parallelism": "single-gpu"},
         "step_includes": names,
         "rows_per_s_indexer_topk_mla": round(T / ((per["index_score"] + per["topk"] +

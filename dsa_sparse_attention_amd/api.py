@@ -90,7 +90,8 @@ def index_score(q_fp8, q_scale, w, k_fp8, k_scale, q_row_offsets, kv_row_offsets
 
 
 def topk(scores, q_row_offsets, kv_row_offsets, max_q_rows: int, max_kv_len: int, k: int,
-         out: torch.Tensor | None = None, refine: dict | None = None):
+         out: torch.Tensor | None = None, refine: dict | None = None,
+         workspace: torch.Tensor | None = None):
     """Per-row top-k positions [T, k] (ascending, -1 padded).
 
     refine: the scored FP8 inputs, dict(q_fp8, q_scale, w, k_fp8, k_scale) plus optional
@@ -121,11 +122,20 @@ def topk(scores, q_row_offsets, kv_row_offsets, max_q_rows: int, max_kv_len: int
                              _p(refine["k_scale"]), q.shape[1], q.shape[2],
                              float(refine.get("err_scale", 0.0)), _p(st))
     wsb = lib.dsa_topk_workspace_size(T, max_kv_len, k)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=scores.device) if wsb else None
+    ws = workspace
+    if ws is None and wsb:
+        ws = torch.empty(wsb, dtype=torch.uint8, device=scores.device)
+    if ws is not None:
+        _dev(ws, "workspace", torch.uint8)
+        wsb = ws.numel()
     _check(lib.dsa_topk(_p(scores), scores.shape[1], _p(q_row_offsets), _p(kv_row_offsets), B, T,
                         max_q_rows, max_kv_len, k, ctypes.byref(rf) if rf is not None else None,
                         _p(out), _p(ws), wsb, _stream()))
     return out
+
+
+def topk_workspace_size(T: int, max_kv_len: int, k: int) -> int:
+    return int(_lib.load().dsa_topk_workspace_size(T, max_kv_len, k))
 
 
 def sparse_mla_workspace_size(T: int, H: int, k: int) -> int:

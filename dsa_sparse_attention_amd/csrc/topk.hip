@@ -46,7 +46,7 @@ constexpr int TK_WAVES = TK_THREADS / 64;
 constexpr int NSUB = 4;        // privatised level-1 histograms
 constexpr int CAND = 8192;     // slow-path LDS candidate capacity (key + position)
 constexpr int FAST_MAX = 65536;  // rows up to this length keep 16-bit keys in LDS
-constexpr int FCAND = 6016;     // fast-path candidate capacity
+constexpr int FCAND = 5984;     // fast-path candidate capacity
 constexpr int RS = 64;          // register path: slots per lane (64 x 1024 lanes = 65536 keys)
 constexpr int SSTEP = 8;        // register path: every eighth slot is a threshold sample
 constexpr int CW = 1024;        // register path: candidates per wave region (8 B each)
@@ -90,17 +90,18 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t b) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b), 0u));
 }
 
-// Exclusive block-wide prefix sum over TK_THREADS threads; *total gets the sum.
+// Exclusive block-wide prefix sum over NW waves (the whole block); *total gets the sum.
+template <int NW = TK_WAVES>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
   const int lane = threadIdx.x % 64;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / 64));
   const uint32_t x = wave_incl_scan(v);
   if (lane == 63) tmp[wave] = x;
   __syncthreads();
-  const uint32_t tw = wave_incl_scan(lane < TK_WAVES ? tmp[lane] : 0u);  // inclusive wave totals
+  const uint32_t tw = wave_incl_scan(lane < NW ? tmp[lane] : 0u);  // inclusive wave totals
   const uint32_t before =
       wave ? static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(tw), wave - 1)) : 0u;
-  *total = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(tw), TK_WAVES - 1));
+  *total = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(tw), NW - 1));
   __syncthreads();
   return before + x - v;
 }
@@ -442,11 +443,10 @@ __device__ __forceinline__ bool select_in_registers(const float* __restrict__ sr
   return true;
 }
 
-__global__ __launch_bounds__(TK_THREADS) void topk_kernel(const float* __restrict__ scores,
-                                                          int64_t ld,
-                                                          const int32_t* __restrict__ q_off,
-                                                          const int64_t* __restrict__ kv_off,
-                                                          int k, int32_t* __restrict__ topk) {
+// Top-k of one score row of n entries (entries 0..n-1 of srow) by (score desc, index asc),
+// written ascending to out[0..k), -1 padded. Called by a whole TK_THREADS block.
+__device__ __forceinline__ void select_row(const float* __restrict__ srow, int64_t n, int k,
+                                           int32_t* __restrict__ out) {
   // Region A (128 KB): 16-bit keys of the fast path; reused by both paths afterwards.
   __shared__ __attribute__((aligned(16))) uint32_t regA[32768];
   __shared__ uint32_t fhist[2048];
@@ -459,19 +459,11 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const float* __restric
   uint32_t* ckey = regA + NSUB * 2048;                                  // slow path: 32 KB
   int32_t* cpos = reinterpret_cast<int32_t*>(regA + NSUB * 2048 + CAND);  // slow path: 32 KB
 
-  const int b = blockIdx.y, r = blockIdx.x;
-  const RowInfo ri = load_row_info(q_off, kv_off, b);
-  if (r >= ri.R) return;
-  const int64_t t = ri.t0 + r;
-  int64_t n = visible_count(ri, r);
-  if (n > ld) n = ld;  // device lengths beyond the score stride are clipped
-  int32_t* out = topk + t * k;
   const int tid = threadIdx.x, wave = tid / 64;
   if (n <= k) {
     for (int i = tid; i < k; i += TK_THREADS) out[i] = i < n ? i : -1;
     return;
   }
-  const float* srow = scores + t * ld;
 
   if (n <= FAST_MAX) {
     if (select_in_registers(srow, static_cast<int>(n), k, out, regA, fhist, rs)) return;
@@ -732,6 +724,97 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const float* __restric
                [&](int64_t i) { return static_cast<int32_t>(i); });
 }
 
+// One block per row: rows of up to FAST_MAX visible scores, and every row when the grid
+// has no chunk stage.
+__global__ __launch_bounds__(TK_THREADS) void topk_kernel(const float* __restrict__ scores,
+                                                          int64_t ld,
+                                                          const int32_t* __restrict__ q_off,
+                                                          const int64_t* __restrict__ kv_off,
+                                                          int k, int32_t* __restrict__ topk) {
+  const int b = blockIdx.y, r = blockIdx.x;
+  const RowInfo ri = load_row_info(q_off, kv_off, b);
+  if (r >= ri.R) return;
+  const int64_t t = ri.t0 + r;
+  int64_t n = visible_count(ri, r);
+  if (n > ld) n = ld;  // device lengths beyond the score stride are clipped
+  select_row(scores + t * ld, n, k, topk + t * k);
+}
+
+// Grids with rows longer than FAST_MAX, stage 1: block (chunk c, row) selects the top-k of
+// visible positions [c FAST_MAX, (c+1) FAST_MAX) as chunk-local indices into ws
+// [T, nchunk, k] (every key of the row's top-k is in the top-k of its chunk); a row of at
+// most FAST_MAX positions is finished here by its chunk-0 block.
+__global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ q_off,
+    const int64_t* __restrict__ kv_off, int k, int nchunk, int32_t* __restrict__ ws,
+    int32_t* __restrict__ topk) {
+  const int b = blockIdx.y, r = blockIdx.x / nchunk, c = blockIdx.x % nchunk;
+  const RowInfo ri = load_row_info(q_off, kv_off, b);
+  if (r >= ri.R) return;
+  const int64_t t = ri.t0 + r;
+  int64_t n = visible_count(ri, r);
+  if (n > ld) n = ld;
+  const float* srow = scores + t * ld;
+  if (n <= FAST_MAX) {
+    if (c == 0) select_row(srow, n, k, topk + t * k);
+    return;
+  }
+  const int64_t c0 = static_cast<int64_t>(c) * FAST_MAX;
+  const int64_t nc = n - c0 < FAST_MAX ? n - c0 : FAST_MAX;
+  int32_t* o = ws + (t * nchunk + c) * k;
+  if (nc <= 0) {
+    for (int i = threadIdx.x; i < k; i += TK_THREADS) o[i] = -1;
+    return;
+  }
+  select_row(srow + c0, nc, k, o);
+}
+
+// Rows longer than FAST_MAX, stage 2: the candidates of all chunks, in ascending position
+// order, are gathered into a compact score row (cand_s) and position row (cand_p); the
+// top-k of that row, mapped back to positions, is the row's top-k (ties between equal
+// scores still go to the lower position, since the compact order is the position order).
+__global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ q_off,
+    const int64_t* __restrict__ kv_off, int k, int nchunk, int64_t cstride,
+    const int32_t* __restrict__ ws, float* __restrict__ cand_s, int32_t* __restrict__ cand_p,
+    int32_t* __restrict__ topk) {
+  __shared__ uint32_t mtmp[2 * TK_WAVES];
+  const int b = blockIdx.y, r = blockIdx.x;
+  const RowInfo ri = load_row_info(q_off, kv_off, b);
+  if (r >= ri.R) return;
+  const int64_t t = ri.t0 + r;
+  int64_t n = visible_count(ri, r);
+  if (n > ld) n = ld;
+  if (n <= FAST_MAX) return;
+  const float* srow = scores + t * ld;
+  const int32_t* wrow = ws + t * nchunk * k;
+  float* cs = cand_s + t * cstride;  // cstride: nchunk k rounded up to 4 (16-byte rows)
+  int32_t* cp = cand_p + t * cstride;
+  // compact the valid chunk entries in (chunk, index) order, i.e. ascending position
+  const int total = nchunk * k;
+  uint32_t base = 0;
+  for (int i0 = 0; i0 < total; i0 += TK_THREADS) {
+    const int i = i0 + threadIdx.x;
+    const int32_t idx = i < total ? wrow[i] : -1;
+    uint32_t cnt;
+    const uint32_t at = base + block_excl_scan(idx >= 0 ? 1u : 0u, mtmp, &cnt);
+    if (idx >= 0) {
+      const int64_t p = static_cast<int64_t>(i / k) * FAST_MAX + idx;
+      cs[at] = srow[p];
+      cp[at] = static_cast<int32_t>(p);
+    }
+    base += cnt;
+  }
+  __syncthreads();  // the block's stores to cs/cp are visible to its own loads after this
+  int32_t* out = topk + t * k;
+  select_row(cs, base, k, out);
+  __syncthreads();
+  for (int i = threadIdx.x; i < k; i += TK_THREADS) {
+    const int32_t j = out[i];
+    if (j >= 0) out[i] = cp[j];
+  }
+}
+
 // ---------------------------------------------------------------------------------------
 // Exact-boundary refine (see dsa_topk in dsa.h). One block per row, after topk_kernel:
 //  1. theta = the smallest float32 score in the row's selection; eps from the row's FP8
@@ -771,6 +854,28 @@ __device__ __forceinline__ float block_max_f(float x, float* red) {
   return -block_min_f(-x, red);
 }
 
+// Bitonic sort of np2 (a power of two) LDS entries by `before`, one compare-exchange per
+// pair and stage, the whole block taking part.
+template <class Before, class Swap>
+__device__ __forceinline__ void block_bitonic(int np2, Before before, Swap swap) {
+  for (int size = 2; size <= np2; size <<= 1) {
+    for (int stride = size / 2; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < np2 / 2; i += RF_THREADS) {
+        const int a = 2 * i - (i & (stride - 1)), c = a + stride;
+        const bool up = (a & size) == 0;
+        if (up ? before(c, a) : before(a, c)) swap(a, c);
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__device__ __forceinline__ int next_pow2(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
 __global__ __launch_bounds__(RF_THREADS) void topk_refine_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ q_off,
     const int64_t* __restrict__ kv_off, int k, const uint8_t* __restrict__ q_fp8,
@@ -787,7 +892,7 @@ __global__ __launch_bounds__(RF_THREADS) void topk_refine_kernel(
   __shared__ float redf[RF_WAVES];
   __shared__ double redd[RF_WAVES];
   __shared__ uint32_t tmp[2 * TK_WAVES];
-  __shared__ int counters[4];  // band size, selected band keys
+  __shared__ int counters[4];  // band size
 
   const int b = blockIdx.y, r = blockIdx.x;
   const RowInfo ri = load_row_info(q_off, kv_off, b);
@@ -807,21 +912,68 @@ __global__ __launch_bounds__(RF_THREADS) void topk_refine_kernel(
   for (int c = tid; c < 256; c += RF_THREADS) dtab[c] = e4m3_value(static_cast<uint32_t>(c));
   if (tid < 4) counters[tid] = 0;
 
-  // ---- 1. theta, the largest visible key scale, and sum_j |u_j| max_c |q_hat[j,c]| ----
+  // ---- 1. theta, the largest visible key scale, and sum_j |u_j| max_c |q_hat[j,c]|;
+  // loads are issued eight at a time per thread so the scans are not latency-bound ----
+  constexpr int U = 8;
   float th = __builtin_inff();
-  for (int i = tid; i < k; i += RF_THREADS) th = fminf(th, srow[out[i]]);
+  for (int i0 = tid; i0 < k; i0 += U * RF_THREADS) {
+    int32_t pp[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) pp[u] = i0 + u * RF_THREADS < k ? out[i0 + u * RF_THREADS] : -1;
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      v[u] = __builtin_inff();
+      if (pp[u] >= 0) v[u] = srow[pp[u]];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) th = fminf(th, v[u]);
+  }
   th = block_min_f(th, redf);
   float smax = 0.0f;
-  for (int64_t s = tid; s < n; s += RF_THREADS) smax = fmaxf(smax, ksc[s]);
+  {
+    // scalar head up to a 16-byte boundary, float4 body (four loads in flight), scalar tail
+    const int64_t head = static_cast<int64_t>((16 - (reinterpret_cast<uintptr_t>(ksc) & 15)) & 15) / 4;
+    const int64_t h0 = head < n ? head : n;
+    if (tid < h0) smax = ksc[tid];
+    const int64_t nb4 = (n - h0) / 4;
+    const float4* k4 = reinterpret_cast<const float4*>(ksc + h0);
+    for (int64_t i0 = tid; i0 < nb4; i0 += 4 * RF_THREADS) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (i0 + u * RF_THREADS < nb4) v[u] = k4[i0 + u * RF_THREADS];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        smax = fmaxf(smax, fmaxf(fmaxf(v[u].x, v[u].y), fmaxf(v[u].z, v[u].w)));
+    }
+    for (int64_t s = h0 + 4 * nb4 + tid; s < n; s += RF_THREADS) smax = fmaxf(smax, ksc[s]);
+  }
   smax = block_max_f(smax, redf);
-  double asum = 0.0;  // this wave's heads
-  for (int j = wave; j < H; j += RF_WAVES) {
-    const uint8_t* qj = q_fp8 + (t * H + j) * D;
-    uint32_t mc = 0;
-    for (int c = lane; c < D; c += 64) mc = max(mc, static_cast<uint32_t>(qj[c]) & 0x7Fu);
-    for (int o = 32; o >= 1; o >>= 1) mc = max(mc, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mc), o)));
-    const double u = static_cast<double>(wt[t * H + j]) * static_cast<double>(q_scale[t * H + j]);
-    asum += __builtin_fabs(u) * e4m3_value(mc);
+  double asum = 0.0;  // sum_j |u_j| max_c |q_hat[j,c]|: 8 codes per thread and load, the
+                      // D/8 threads of a head reduce with xor shuffles inside their group
+  {
+    const int per_head = D / 8;  // 16 or 8 threads
+    const uint2* q8 = reinterpret_cast<const uint2*>(q_fp8 + t * H * D);
+    for (int i0 = tid; i0 < H * per_head; i0 += RF_THREADS) {
+      const uint2 v = q8[i0];
+      uint32_t mc = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        mc = max(mc, (v.x >> (8 * e)) & 0x7Fu);
+        mc = max(mc, (v.y >> (8 * e)) & 0x7Fu);
+      }
+      for (int o = per_head / 2; o >= 1; o >>= 1)
+        mc = max(mc, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mc), o)));
+      if (i0 % per_head == 0) {
+        const int j = i0 / per_head;
+        const double u = static_cast<double>(wt[t * H + j]) * static_cast<double>(q_scale[t * H + j]);
+        asum += __builtin_fabs(u) * e4m3_value(mc);
+      }
+    }
+    for (int o = 32; o >= 1; o >>= 1) asum += __shfl_xor(asum, o);
   }
   if (lane == 0) redd[wave] = asum;
   __syncthreads();
@@ -831,19 +983,40 @@ __global__ __launch_bounds__(RF_THREADS) void topk_refine_kernel(
   const double eps = C * 0x1p-16 * 448.0 * static_cast<double>(smax) * A;
   const double hi = static_cast<double>(th) + 2.0 * eps, lo = static_cast<double>(th) - 2.0 * eps;
 
-  // ---- 2. kept keys (counted) and the band (collected) ----
+  // ---- 2. kept keys (counted) and the band (collected); float4 loads, four in flight ----
   uint32_t nin = 0;
-  for (int64_t s = tid; s < n; s += RF_THREADS) {
-    const double x = static_cast<double>(srow[s]);
+  auto classify = [&](float xf, int64_t s) {
+    const double x = static_cast<double>(xf);
     if (x > hi) {
       ++nin;
     } else if (x >= lo) {
       const int slot = atomicAdd(&counters[0], 1);
       if (slot < BAND_CAP) band_pos[slot] = static_cast<int32_t>(s);
     }
+  };
+  const int64_t n4 = n / 4;
+  const float4* s4 = reinterpret_cast<const float4*>(srow);  // rows are 16-byte aligned
+  for (int64_t i0 = tid; i0 < n4; i0 += 4 * RF_THREADS) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (i0 + u * RF_THREADS < n4) v[u] = s4[i0 + u * RF_THREADS];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = i0 + u * RF_THREADS;
+      if (i < n4) {
+        classify(v[u].x, 4 * i);
+        classify(v[u].y, 4 * i + 1);
+        classify(v[u].z, 4 * i + 2);
+        classify(v[u].w, 4 * i + 3);
+      }
+    }
   }
+  for (int64_t s = 4 * n4 + tid; s < n; s += RF_THREADS) classify(srow[s], s);
   uint32_t nin_total;
-  block_excl_scan(nin, tmp, &nin_total);  // ends with a barrier: counters[0] is final
+  block_excl_scan<RF_WAVES>(nin, tmp, &nin_total);  // ends with a barrier: counters[0] is final
   const int nb = counters[0];
   const int need = k - static_cast<int>(nin_total);
   if (nb > BAND_CAP || need < 1 || need > nb) {  // uniform: keep the float32 selection
@@ -851,48 +1024,132 @@ __global__ __launch_bounds__(RF_THREADS) void topk_refine_kernel(
     return;
   }
 
-  // ---- 3. exact rescore, one band key per wave at a time; lane j owns head j (and j+64) ----
+  // ---- 3. exact rescore, one band key per wave at a time; lane j owns heads j and j+64.
+  // A key's codes are prefetched one iteration ahead; the weighted head sum runs in
+  // ascending head order over readlane. ----
+  double uh[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int j = lane + 64 * hh;
+    uh[hh] = j < H ? static_cast<double>(wt[t * H + j]) * static_cast<double>(q_scale[t * H + j]) : 0.0;
+  }
+  auto key_codes = [&](int i) -> uint32_t {  // two codes of band key i per lane (D <= 128)
+    uint32_t c2 = 0;
+    if (i < nb && 2 * lane < D)
+      c2 = *reinterpret_cast<const uint16_t*>(k_fp8 + (ri.kv_base + band_pos[i]) * D + 2 * lane);
+    return c2;
+  };
+  uint32_t kc = key_codes(wave);
   for (int i = wave; i < nb; i += RF_WAVES) {
     const int32_t p = band_pos[i];
-    const uint8_t* kr = k_fp8 + (ri.kv_base + p) * D;
-    for (int c = lane; c < D; c += 64) kdec[wave][c] = dtab[kr[c]];
+    if (2 * lane < D) {
+      kdec[wave][2 * lane] = dtab[kc & 0xFFu];
+      kdec[wave][2 * lane + 1] = dtab[(kc >> 8) & 0xFFu];
+    }
+    kc = key_codes(i + RF_WAVES);  // next key of this wave, in flight during this one
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    for (int j = lane; j < H; j += 64) {
-      const uint8_t* qj = q_fp8 + (t * H + j) * D;
-      double d = 0.0;  // exact: every partial sum is a multiple of 2^-18 below 2^53 units
-      for (int c = 0; c < D; ++c) d = __builtin_fma(dtab[qj[c]], kdec[wave][c], d);
-      const double u = static_cast<double>(wt[t * H + j]) * static_cast<double>(q_scale[t * H + j]);
-      term[wave][j] = __dmul_rn(u, d > 0.0 ? d : 0.0);
+    double tj[2] = {0.0, 0.0};
+    for (int hh = 0; hh < (H > 64 ? 2 : 1); ++hh) {  // wave-uniform
+      uint4 qv[8];  // this lane's head codes (reloaded per key: cache hits)
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        qv[v] = make_uint4(0u, 0u, 0u, 0u);
+        if (lane + 64 * hh < H && v < D / 16)
+          qv[v] = reinterpret_cast<const uint4*>(q_fp8 + (t * H + lane + 64 * hh) * D)[v];
+      }
+      // exact: every partial sum is a multiple of 2^-18 below 2^53 units, so the four
+      // interleaved partial sums and their total are exact in any order
+      double d4[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        if (v < D / 16) {
+          const uint32_t wd[4] = {qv[v].x, qv[v].y, qv[v].z, qv[v].w};
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            d4[e % 4] = __builtin_fma(dtab[(wd[e / 4] >> (8 * (e % 4))) & 0xFFu],
+                                      kdec[wave][16 * v + e], d4[e % 4]);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep each group's table reads local
+      }
+      const double d = (d4[0] + d4[1]) + (d4[2] + d4[3]);
+      tj[hh] = __dmul_rn(uh[hh], d > 0.0 ? d : 0.0);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (lane == 0) {
-      double acc = 0.0;
-      for (int j = 0; j < H; ++j) acc = __dadd_rn(acc, term[wave][j]);
-      band_val[i] = __dmul_rn(acc, static_cast<double>(ksc[p]));
+    double acc = 0.0;  // heads 0..H-1 in order: lane j's tj[0], then lane j's tj[1] (j + 64)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int lo_w = __double2loint(tj[hh]), hi_w = __double2hiint(tj[hh]);
+#pragma unroll
+      for (int j = 0; j < 64; ++j)
+        if (64 * hh + j < H)
+          acc = __dadd_rn(acc, __hiloint2double(__builtin_amdgcn_readlane(hi_w, j),
+                                                __builtin_amdgcn_readlane(lo_w, j)));
     }
+    if (lane == 0) band_val[i] = __dmul_rn(acc, static_cast<double>(ksc[p]));
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
   __syncthreads();
 
-  // ---- 4. the best `need` band keys, then a merge with the kept keys, ascending ----
-  for (int i = tid; i < nb; i += RF_THREADS) {
-    const double v = band_val[i];
-    const int32_t p = band_pos[i];
-    int rank = 0;
-    for (int m = 0; m < nb; ++m) {
-      const double vm = band_val[m];
-      rank += (vm > v || (vm == v && band_pos[m] < p)) ? 1 : 0;
+  // ---- 4. the best `need` band keys by (exact score desc, position asc), as ascending
+  // positions in sel_pos; then a merge with the kept keys ----
+  if (nb <= 64) {  // one wave ranks the band with register broadcasts: no block barriers
+    if (wave == 0) {
+      const bool live = lane < nb;
+      const double v = live ? band_val[lane] : -__builtin_inf();
+      const int32_t p = live ? band_pos[lane] : 0x7FFFFFFF;
+      const int vlo = __double2loint(v), vhi = __double2hiint(v);
+      int rank = 0;
+      for (int m = 0; m < nb; ++m) {
+        const double vm = __hiloint2double(__builtin_amdgcn_readlane(vhi, m),
+                                           __builtin_amdgcn_readlane(vlo, m));
+        const int32_t pm = __builtin_amdgcn_readlane(p, m);
+        rank += (vm > v || (vm == v && pm < p)) ? 1 : 0;
+      }
+      const bool take = live && rank < need;
+      int at = 0;  // rank by position among the taken keys
+      for (int m = 0; m < nb; ++m) {
+        const int32_t pm = __builtin_amdgcn_readlane(p, m);
+        const bool tm = __builtin_amdgcn_readlane(take ? 1 : 0, m) != 0;
+        at += (tm && pm < p) ? 1 : 0;
+      }
+      if (take) sel_pos[at] = p;
     }
-    if (rank < need) {
-      const int slot = atomicAdd(&counters[1], 1);
-      if (slot < RF_MAXK) sel_pos[slot] = p;
+    __syncthreads();
+  } else {
+    // pad the band to a power of two with entries that sort last, then bitonic sorts
+    const int np2 = next_pow2(nb);
+    for (int i = nb + tid; i < np2; i += RF_THREADS) {
+      band_val[i] = -__builtin_inf();
+      band_pos[i] = 0x7FFFFFFF;
     }
+    __syncthreads();
+    block_bitonic(
+        np2,
+        [&](int x, int y) {
+          return band_val[x] > band_val[y] ||
+                 (band_val[x] == band_val[y] && band_pos[x] < band_pos[y]);
+        },
+        [&](int x, int y) {
+          const double v = band_val[x];
+          band_val[x] = band_val[y];
+          band_val[y] = v;
+          const int32_t q = band_pos[x];
+          band_pos[x] = band_pos[y];
+          band_pos[y] = q;
+        });
+    const int ns2 = next_pow2(need > 1 ? need : 2);
+    for (int i = tid; i < ns2; i += RF_THREADS) sel_pos[i] = i < need ? band_pos[i] : 0x7FFFFFFF;
+    __syncthreads();
+    block_bitonic(
+        ns2, [&](int x, int y) { return sel_pos[x] < sel_pos[y]; },
+        [&](int x, int y) {
+          const int32_t q = sel_pos[x];
+          sel_pos[x] = sel_pos[y];
+          sel_pos[y] = q;
+        });
   }
   // kept keys in the current (ascending) selection, order preserved; k <= RF_MAXK, so at
   // most four entries per thread, taken as one contiguous run
@@ -912,7 +1169,7 @@ __global__ __launch_bounds__(RF_THREADS) void topk_refine_kernel(
     }
   }
   uint32_t kept;
-  uint32_t at = block_excl_scan(cnt, tmp, &kept);  // ends with a barrier: sel_pos is final
+  uint32_t at = block_excl_scan<RF_WAVES>(cnt, tmp, &kept);  // ends with a barrier
   if (kept != nin_total) {  // uniform; cannot happen for a correct float32 selection
     if (tid == 0 && status) status[t] = -3;
     return;
@@ -921,33 +1178,43 @@ __global__ __launch_bounds__(RF_THREADS) void topk_refine_kernel(
   for (int j = 0; j < PER; ++j)
     if (mine[j] >= 0) in_pos[at++] = mine[j];
   __syncthreads();
-  // kept key i goes to i + (selected band keys below it); selected key p to (selected
-  // keys below p) + (kept keys below p)
-  for (int i = tid; i < static_cast<int>(kept); i += RF_THREADS) {
-    const int32_t p = in_pos[i];
-    int below = 0;
-    for (int m = 0; m < need; ++m) below += sel_pos[m] < p ? 1 : 0;
-    out[i + below] = p;
-  }
-  for (int i = tid; i < need; i += RF_THREADS) {
-    const int32_t p = sel_pos[i];
-    int below = 0;
-    for (int m = 0; m < need; ++m) below += sel_pos[m] < p ? 1 : 0;
-    int lo_i = 0, hi_i = static_cast<int>(kept);  // kept keys below p (in_pos ascending)
+  auto count_below = [](const int32_t* a, int len, int32_t p) {  // a ascending
+    int lo_i = 0, hi_i = len;
     while (lo_i < hi_i) {
       const int mid = (lo_i + hi_i) / 2;
-      if (in_pos[mid] < p) lo_i = mid + 1;
+      if (a[mid] < p) lo_i = mid + 1;
       else hi_i = mid;
     }
-    out[below + lo_i] = p;
-  }
+    return lo_i;
+  };
+  for (int i = tid; i < static_cast<int>(kept); i += RF_THREADS)
+    out[i + count_below(sel_pos, need, in_pos[i])] = in_pos[i];
+  for (int i = tid; i < need; i += RF_THREADS)
+    out[i + count_below(in_pos, static_cast<int>(kept), sel_pos[i])] = sel_pos[i];
   if (tid == 0 && status) status[t] = nb;
 }
 
 }  // namespace
 }  // namespace dsa
 
-extern "C" size_t dsa_topk_workspace_size(int32_t, int64_t, int32_t) { return 0; }
+namespace dsa {
+namespace {
+// Chunks of rows longer than FAST_MAX, and the stride of the compact candidate rows.
+int64_t topk_nchunk(int64_t max_kv_len) { return max_kv_len > FAST_MAX ? ceil_div(max_kv_len, FAST_MAX) : 1; }
+int64_t topk_cstride(int64_t nchunk, int k) { return (nchunk * k + 3) / 4 * 4; }
+}  // namespace
+}  // namespace dsa
+
+extern "C" size_t dsa_topk_workspace_size(int32_t T, int64_t max_kv_len, int32_t k) {
+  using namespace dsa;
+  if (T <= 0 || k <= 0) return 0;
+  const int64_t nc = topk_nchunk(max_kv_len);
+  if (nc <= 1) return 0;
+  // chunk indices [T, nc, k] (padded to 16 bytes), compact candidate scores and positions
+  // [T, cstride] each
+  return static_cast<size_t>((static_cast<int64_t>(T) * nc * k + 3) / 4 * 4 +
+                             2 * static_cast<int64_t>(T) * topk_cstride(nc, k)) * 4;
+}
 
 extern "C" dsa_status dsa_topk(const float* scores, int64_t score_ld,
                                const int32_t* q_row_offsets, const int64_t* kv_row_offsets,
@@ -955,14 +1222,14 @@ extern "C" dsa_status dsa_topk(const float* scores, int64_t score_ld,
                                int32_t k, const dsa_topk_refine* refine, int32_t* topk, void* ws,
                                size_t ws_bytes, void* stream) {
   using namespace dsa;
-  (void)ws;
-  (void)ws_bytes;
   DSA_REQUIRE(k >= 1 && k <= 8192, "dsa_topk: k must be in [1, 8192] (got %d)", k);
   DSA_REQUIRE(B >= 0 && T >= 0 && max_q_rows >= 0 && max_kv_len >= 0, "dsa_topk: negative size");
   DSA_REQUIRE(score_ld >= max_kv_len && score_ld % 4 == 0,
               "dsa_topk: score_ld must be >= max_kv_len and a multiple of 4");
   DSA_REQUIRE(max_kv_len < (int64_t(1) << 31), "dsa_topk: max_kv_len must be < 2^31");
   if (refine) {
+    DSA_REQUIRE((reinterpret_cast<uintptr_t>(refine->q_fp8) & 15) == 0,
+                "dsa_topk: refine q_fp8 must be 16-byte aligned");
     DSA_REQUIRE(k <= RF_MAXK, "dsa_topk: the refine supports k <= %d (got %d)", RF_MAXK, k);
     DSA_REQUIRE(refine->D_I == 64 || refine->D_I == 128, "dsa_topk: refine D_I must be 64 or 128");
     DSA_REQUIRE(refine->H_I >= 1 && refine->H_I <= 128, "dsa_topk: refine H_I must be in [1, 128]");
@@ -977,8 +1244,29 @@ extern "C" dsa_status dsa_topk(const float* scores, int64_t score_ld,
               "dsa_topk: scores must be 16-byte aligned");
   DSA_REQUIRE(B <= 65535, "dsa_topk: B must be <= 65535");
   dim3 grid((unsigned)max_q_rows, (unsigned)B);
-  hipLaunchKernelGGL(topk_kernel, grid, dim3(TK_THREADS), 0, as_stream(stream), scores, score_ld,
-                     q_row_offsets, kv_row_offsets, k, topk);
+  const int64_t nchunk = topk_nchunk(max_kv_len);
+  if (nchunk > 1) {
+    const size_t need = dsa_topk_workspace_size(T, max_kv_len, k);
+    if (ws_bytes < need || !ws)
+      return fail(DSA_ERR_WORKSPACE_TOO_SMALL,
+                  "dsa_topk: rows longer than %d need a %zu-byte workspace (got %zu)", FAST_MAX,
+                  need, ws_bytes);
+    DSA_REQUIRE((reinterpret_cast<uintptr_t>(ws) & 15) == 0, "dsa_topk: ws must be 16-byte aligned");
+    DSA_REQUIRE(max_q_rows * nchunk <= 0x7FFFFFFF, "dsa_topk: too many chunks");
+    int32_t* widx = static_cast<int32_t*>(ws);
+    const int64_t cstride = topk_cstride(nchunk, k);
+    float* cand_s = reinterpret_cast<float*>(widx + (static_cast<int64_t>(T) * nchunk * k + 3) / 4 * 4);
+    int32_t* cand_p = reinterpret_cast<int32_t*>(cand_s + static_cast<int64_t>(T) * cstride);
+    hipLaunchKernelGGL(topk_chunk_kernel, dim3((unsigned)(max_q_rows * nchunk), (unsigned)B),
+                       dim3(TK_THREADS), 0, as_stream(stream), scores, score_ld, q_row_offsets,
+                       kv_row_offsets, k, (int)nchunk, widx, topk);
+    hipLaunchKernelGGL(topk_merge_kernel, grid, dim3(TK_THREADS), 0, as_stream(stream), scores,
+                       score_ld, q_row_offsets, kv_row_offsets, k, (int)nchunk, cstride, widx,
+                       cand_s, cand_p, topk);
+  } else {
+    hipLaunchKernelGGL(topk_kernel, grid, dim3(TK_THREADS), 0, as_stream(stream), scores,
+                       score_ld, q_row_offsets, kv_row_offsets, k, topk);
+  }
   if (refine)
     hipLaunchKernelGGL(topk_refine_kernel, grid, dim3(RF_THREADS), 0, as_stream(stream), scores,
                        score_ld, q_row_offsets, kv_row_offsets, k, refine->q_fp8, refine->q_scale,

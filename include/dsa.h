@@ -161,9 +161,13 @@ typedef struct dsa_topk_refine {
  * rescored exactly and ranked by (I_exact desc, s asc).
  *   scores [T, score_ld] float32 (as written by dsa_index_score)
  *   topk   [T, k] int32
- * Workspace: none (ws may be NULL; ws_bytes ignored).
+ * Rows of up to 65536 visible scores take one block each. When max_kv_len
+ * exceeds 65536, every row is first cut into 65536-position chunks whose own
+ * top-k are selected in parallel (the row's top-k lies in their union), then
+ * merged; this needs dsa_topk_workspace_size(T, max_kv_len, k) bytes of
+ * 16-byte aligned workspace (0 bytes otherwise; ws may then be NULL).
  * Errors: DSA_ERR_INVALID_ARGUMENT (k < 1, k > 8192, refine with k > 4096,
- * D_I not 64/128, H_I not in [1, 128], ...).
+ * D_I not 64/128, H_I not in [1, 128], ...), DSA_ERR_WORKSPACE_TOO_SMALL.
  */
 dsa_status dsa_topk(const float* scores, int64_t score_ld, const int32_t* q_row_offsets,
                     const int64_t* kv_row_offsets, int32_t B, int32_t T, int32_t max_q_rows,

@@ -113,6 +113,28 @@ def test_topk_bitexact_on_shared_scores(levels):
         assert np.array_equal(got[t], ref), f"row {t} (visible {n})"
 
 
+@pytest.mark.parametrize("levels", [0, 3, 600])
+def test_topk_long_rows_chunked(levels):
+    # rows above 65536 positions are selected per 65536-position chunk and merged: boundary
+    # lengths (a one-key last chunk, exact multiples), a short row in the same grid, ties
+    _say(f"topk long rows levels={levels}")
+    lens = [65537, 131072, 200003, 3000]
+    R = 2
+    qo = torch.tensor([0, 2, 4, 6, 8], dtype=torch.int32)
+    ko = synth.kv_row_offsets(lens)
+    ld = 200004
+    s = synth.random_scores(8, ld, seed=50 + levels, tie_levels=levels)
+    for k in (7, 2048):
+        ws = torch.zeros(max(api.topk_workspace_size(8, max(lens), k), 16), dtype=torch.uint8,
+                         device=DEV)
+        got = api.topk(s.to(DEV), qo.to(DEV), ko.to(DEV), R, max(lens), k,
+                       workspace=ws).cpu().numpy()
+        for t in range(8):
+            n = oracle.row_visible(qo.numpy(), ko.numpy(), t)
+            ref = oracle.topk(s[t:t + 1].double().numpy(), [n], k)[0]
+            assert np.array_equal(got[t], ref), f"k={k} row {t} (visible {n})"
+
+
 def test_topk_small_k_and_padding():
     _say("topk k=1 and padding")
     lens = [10, 1, 300]
