@@ -11,7 +11,7 @@
 // registers (lane l of wave w holds positions 4096w + 64r + l, r < 64), every eighth
 // slot serves as a sample whose 16-bit key classes give a threshold admitting about
 // 1.25 k keys, and one ballot pass compacts the keys at or above it into per-wave LDS
-// regions, in position order. Three histogram rounds over these few thousand
+// regions, in position order. Three histogram selects over these few thousand
 // candidates (16-bit class below the maximum, bits 15..5, bits 4..0) give theta and
 // the number of theta-ties to take, and a ballot pass emits ascending positions. A
 // sample that admits fewer than k keys, or more than a wave region holds, sends the
@@ -360,7 +360,7 @@ __device__ __forceinline__ bool select_in_registers(const float* __restrict__ sr
   // slots j with 64 j >= cw hold no candidate in any lane: the loops below skip them with
   // a scalar test, so a wave pays only for the slots it fills
 
-  // ---- round 1: 16-bit class of theta, counted from R = sample maximum + 128 down;
+  // ---- select 1: 16-bit class of theta, counted from R = sample maximum + 128 down;
   // bins 0 and 511 also hold everything beyond them, so theta may not fall there ----
   const uint32_t R = m16 + 128;
 #pragma unroll
@@ -375,7 +375,7 @@ __device__ __forceinline__ bool select_in_registers(const float* __restrict__ sr
   if (b1 == 0 || b1 == 511) return false;
   const uint32_t c16t = R - b1;
   uint32_t need = k - above;
-  // ---- round 2: bits 15..8 of the keys in theta's class ----
+  // ---- select 2: bits 15..8 of the keys in theta's class ----
 #pragma unroll
   for (int j = 0; j < KJ; ++j)
     if (64 * j < static_cast<int>(cw) && (kreg[j] >> 16) == c16t) atomicAdd(&h2[255 - ((kreg[j] >> 8) & 255)], 1u);
@@ -384,7 +384,7 @@ __device__ __forceinline__ bool select_in_registers(const float* __restrict__ sr
   wave_select<256>(h2, need, &b2, &above);
   const uint32_t p24 = (c16t << 8) | (255 - b2);
   need -= above;
-  // ---- round 3: bits 7..0 ----
+  // ---- select 3: bits 7..0 ----
 #pragma unroll
   for (int j = 0; j < KJ; ++j)
     if (64 * j < static_cast<int>(cw) && (kreg[j] >> 8) == p24) atomicAdd(&h3[255 - (kreg[j] & 255)], 1u);
