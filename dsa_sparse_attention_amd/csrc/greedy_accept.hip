@@ -6,8 +6,10 @@
 // cat(bonus, drafts) ("验证输入是怎么拼出来的"), so logits row b*(K+1)+i follows row i.
 //
 // Pass 1 (HBM-bound): blocks of 256 threads scan a vocabulary slice of one logits row
-// with 16-byte loads and keep (max, first index); ties go to the lower index at every
-// merge, which reproduces "first maximum wins" exactly. Pass 2: one wave per request
+// with 16-byte loads and keep (max, first index): a thread sees its indices in
+// increasing order, so per 16-byte group it takes the group maximum only when strictly
+// larger and then locates its first index; the merges across threads keep the lower
+// index on ties. This reproduces "first maximum wins" exactly. Pass 2: one wave per request
 // merges the slices of its K+1 rows in slice order, and a ballot over the K draft
 // comparisons gives the first mismatch.
 #include "common.hpp"
@@ -31,6 +33,24 @@ struct ArgMax {
 
 __device__ __forceinline__ void take(ArgMax& a, float v, int32_t i) {
   if (v > a.v || (v == a.v && i < a.i)) { a.v = v; a.i = i; }
+}
+
+// A group of N values at indices i0..i0+N-1, later than every index `a` holds: its maximum
+// replaces `a` only if it is larger (so the earlier index wins a tie), and then the first
+// index holding it is located. The first group always replaces the empty state, so a
+// row of -inf still yields its first index.
+template <int N>
+__device__ __forceinline__ void take_group(ArgMax& a, const float (&x)[N], int32_t i0) {
+  float m = x[0];
+#pragma unroll
+  for (int e = 1; e < N; ++e) m = fmaxf(m, x[e]);
+  if (m > a.v || a.i == 0x7FFFFFFF) {
+    int k = N - 1;
+#pragma unroll
+    for (int e = N - 2; e >= 0; --e) k = x[e] == m ? e : k;
+    a.v = m;
+    a.i = i0 + k;
+  }
 }
 
 template <bool BF16>
@@ -63,12 +83,14 @@ __global__ __launch_bounds__(GA_THREADS) void argmax_slices_kernel(const void* _
       for (int u = 0; u < UNR; ++u) {
         const int j = threadIdx.x + u * GA_THREADS;
         if (j < nvec) {
+          float x[8];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const uint32_t w = static_cast<uint32_t>(d[u][e]);
-            take(best, __uint_as_float(w << 16), v0 + 8 * j + 2 * e);
-            take(best, __uint_as_float(w & 0xFFFF0000u), v0 + 8 * j + 2 * e + 1);
+            x[2 * e] = __uint_as_float(w << 16);
+            x[2 * e + 1] = __uint_as_float(w & 0xFFFF0000u);
           }
+          take_group(best, x, v0 + 8 * j);
         }
       }
       v = v0 + 8 * nvec;
@@ -91,10 +113,8 @@ __global__ __launch_bounds__(GA_THREADS) void argmax_slices_kernel(const void* _
       for (int u = 0; u < UNR; ++u) {
         const int j = threadIdx.x + u * GA_THREADS;
         if (j < nvec) {
-          take(best, d[u].x, v0 + 4 * j);
-          take(best, d[u].y, v0 + 4 * j + 1);
-          take(best, d[u].z, v0 + 4 * j + 2);
-          take(best, d[u].w, v0 + 4 * j + 3);
+          const float x[4] = {d[u].x, d[u].y, d[u].z, d[u].w};
+          take_group(best, x, v0 + 4 * j);
         }
       }
       v = v0 + 4 * nvec;
