@@ -21,7 +21,7 @@ namespace {
 #define DSA_GA_THREADS 256
 #endif
 #ifndef DSA_GA_SLICE
-#define DSA_GA_SLICE 8192
+#define DSA_GA_SLICE 4096
 #endif
 constexpr int GA_THREADS = DSA_GA_THREADS;
 constexpr int GA_SLICE = DSA_GA_SLICE;  // vocabulary entries per block

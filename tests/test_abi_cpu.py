@@ -43,6 +43,6 @@ def test_version_and_workspace_queries():
     assert lib.dsa_sparse_mla_workspace_size(1024, 64, 2048) == 0
     assert lib.dsa_sparse_mla_workspace_size(1024, 64, 4096) == 1024 * 2 * 64 * 514 * 4
     assert lib.dsa_sparse_mla_workspace_size(16, 128, 2048) == 16 * 8 * 128 * 514 * 4
-    # greedy accept: one (max, index) pair per 8192-entry vocabulary slice per row
-    assert lib.greedy_accept_workspace_size(32, 5, 151552) == 32 * 6 * 19 * 8
+    # greedy accept: one (max, index) pair per 4096-entry vocabulary slice per row
+    assert lib.greedy_accept_workspace_size(32, 5, 151552) == 32 * 6 * 37 * 8
     assert lib.greedy_accept_workspace_size(0, 5, 10) == 0
