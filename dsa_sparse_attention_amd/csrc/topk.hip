@@ -47,7 +47,6 @@ constexpr int NSUB = 4;        // privatised level-1 histograms
 constexpr int CAND = 8192;     // slow-path LDS candidate capacity (key + position)
 constexpr int FAST_MAX = 65536;  // rows up to this length keep 16-bit keys in LDS
 constexpr int FCAND = 5984;     // fast-path candidate capacity
-constexpr int RS = 64;          // register path: slots per lane (64 x 1024 lanes = 65536 keys)
 constexpr int SSTEP = 8;        // register path: every eighth slot is a threshold sample
 constexpr int CW = 1024;        // register path: candidates per wave region (8 B each)
 
@@ -233,18 +232,34 @@ __device__ __forceinline__ bool wave_select(const uint32_t* hist, uint32_t need,
   return true;
 }
 
-// Register path for a row of k < n <= 65536 visible scores (see the top of the file);
-// wave w holds positions 4096 w + 64 r + lane in slot r. Returns false, uniformly over
+// One histogram add per active lane of a wave. The lanes whose bin equals the first active
+// lane's add once through that lane, so a run of identical keys does not serialise on one
+// LDS address; every other active lane adds 1.
+__device__ __forceinline__ void hist_add(uint32_t* h, bool act, uint32_t bin) {
+  const uint64_t am = __builtin_amdgcn_ballot_w64(act);
+  if (am == 0) return;
+  const int first = __builtin_ctzll(am);
+  const uint32_t b0 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(bin), first));
+  const uint32_t same = static_cast<uint32_t>(__popcll(__builtin_amdgcn_ballot_w64(act && bin == b0)));
+  const bool lead = static_cast<int>(threadIdx.x % 64) == first;
+  if (act && (lead || bin != b0)) atomicAdd(&h[bin], lead ? same : 1u);
+}
+
+// Register path for a row of k < n <= 16 * 64 * RS visible scores (see the top of the
+// file); wave w holds positions 64 RS w + 64 r + lane in slot r < RS (RS = 64 for rows
+// up to 64K; shorter rows take fewer slots per lane, so their candidates still spread
+// over all sixteen waves). Returns false, uniformly over
 // the block, when the sampled threshold admits fewer than k keys or more than a wave
 // region holds, or theta's class falls outside the class histogram; nothing has been
 // written to `out` then. cand: 128 KB of LDS (16 wave regions of CW key bits followed by
 // CW positions); hist: 1280 words; rs: 80 words.
+template <int RS>
 __device__ __forceinline__ bool select_in_registers(const float* __restrict__ srow, int n, int k,
                                                     int32_t* __restrict__ out, uint32_t* cand,
                                                     uint32_t* hist, uint32_t* rs) {
   const int tid = threadIdx.x, lane = tid % 64;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
-  const int p0 = wave * (64 * RS) + lane;  // wave w holds positions [4096 w, 4096 w + 4096)
+  const int p0 = wave * (64 * RS) + lane;  // wave w holds positions [64 RS w, 64 RS (w + 1))
   const float* __restrict__ vrow = srow + p0;
   uint32_t* hs = hist;          // 256 bins: sample classes below the sample maximum
   uint32_t* h1 = hist + 256;    // 512 bins: candidate classes below R = sample max + 128
@@ -299,17 +314,43 @@ __device__ __forceinline__ bool select_in_registers(const float* __restrict__ sr
   const uint32_t m16 = wave_max(lane < TK_WAVES ? rs[lane] : 0u);
   const uint32_t ns = wave_sum(lane < TK_WAVES ? rs[16 + lane] : 0u);
 #pragma unroll
-  for (int r = 0; r < RS; r += SSTEP)
-    if (64 * r < lim) {
-      const uint32_t d = m16 - (order_key(v[r]) >> 16);
-      atomicAdd(&hs[d < 255 ? d : 255], 1u);
-    }
+  for (int r = 0; r < RS; r += SSTEP) {
+    const uint32_t d = m16 - (order_key(v[r]) >> 16);
+    hist_add(hs, 64 * r < lim, d < 255 ? d : 255);
+  }
   __syncthreads();
   // aim at 1.25 times the samples' expected share of the top k, plus 16
   const uint64_t want = (5ull * k * ns + 4ull * n - 1) / (4ull * n) + 16;
-  uint32_t dcut, dummy;
-  wave_select<256>(hs, want < ns ? static_cast<uint32_t>(want) : ns, &dcut, &dummy);
+  const uint32_t wsamp = want < ns ? static_cast<uint32_t>(want) : ns;
+  uint32_t dcut, above_s;
+  wave_select<256>(hs, wsamp, &dcut, &above_s);
   uint32_t c16 = m16 > dcut ? m16 - dcut : 0u;
+  if (dcut == 255) {  // uniform: the wanted sample lies past a gap of 255+ classes below the
+                      // maximum; classify the samples beyond the gap below their own maximum
+    uint32_t smax2 = 0;
+#pragma unroll
+    for (int r = 0; r < RS; r += SSTEP)
+      if (64 * r < lim) {
+        const uint32_t c = order_key(v[r]) >> 16;
+        if (m16 - c >= 255) smax2 = max(smax2, c);
+      }
+    smax2 = wave_max(smax2);
+    if (lane == 0) rs[wave] = smax2;  // the first maxima were read before the last barrier
+    __syncthreads();
+    const uint32_t m2 = wave_max(lane < TK_WAVES ? rs[lane] : 0u);
+#pragma unroll
+    for (int r = 0; r < RS; r += SSTEP) {
+      const uint32_t c = order_key(v[r]) >> 16;
+      const uint32_t d = m2 - c;
+      hist_add(h3, 64 * r < lim && m16 - c >= 255, d < 255 ? d : 255);
+    }
+    __syncthreads();
+    uint32_t d2, a2;
+    wave_select<256>(h3, wsamp - above_s, &d2, &a2);
+    c16 = m2 > d2 ? m2 - d2 : 0u;
+    __syncthreads();  // every wave has read h3 before it is cleared for select 3
+    for (int i = tid; i < 256; i += TK_THREADS) h3[i] = 0;
+  }
   if (c16 < 0x80u) c16 = 0x80u;  // keeps the threshold above -inf (the padding value)
   const float t_lo = class_floor(c16);
   if (partial) {
@@ -360,25 +401,33 @@ __device__ __forceinline__ bool select_in_registers(const float* __restrict__ sr
   // slots j with 64 j >= cw hold no candidate in any lane: the loops below skip them with
   // a scalar test, so a wave pays only for the slots it fills
 
-  // ---- select 1: 16-bit class of theta, counted from R = sample maximum + 128 down;
-  // bins 0 and 511 also hold everything beyond them, so theta may not fall there ----
-  const uint32_t R = m16 + 128;
+  // ---- select 1: 16-bit class of theta. Bin b holds class R - b for R = sample max + 128
+  // (bin 0 also every class above R) when R - c16 < 512; across a wider gap, bins 0..254
+  // hold classes R..R-254, bins 256..511 classes c16+255..c16 (the threshold class, below
+  // which no candidate lies) and bin 255 everything between. theta may not fall in bin 0
+  // nor in the gap bin ----
+  const int R = static_cast<int>(m16) + 128;
+  const int lo = static_cast<int>(c16);
+  const bool gap = R - lo > 511;  // uniform
 #pragma unroll
   for (int j = 0; j < KJ; ++j)
-    if (64 * j < static_cast<int>(cw) && kreg[j]) {
-      const int d = static_cast<int>(R) - static_cast<int>(kreg[j] >> 16);
-      atomicAdd(&h1[d < 0 ? 0 : (d > 511 ? 511 : d)], 1u);
+    if (64 * j < static_cast<int>(cw)) {
+      const int c = static_cast<int>(kreg[j] >> 16);
+      const int d = R - c;
+      int bin = d > 0 ? d : 0;
+      if (gap && d >= 255) bin = c - lo < 256 ? 511 - (c - lo) : 255;
+      hist_add(h1, kreg[j] != 0, static_cast<uint32_t>(bin < 511 ? bin : 511));
     }
   __syncthreads();
   uint32_t b1, above;
   wave_select<512>(h1, k, &b1, &above);
-  if (b1 == 0 || b1 == 511) return false;
-  const uint32_t c16t = R - b1;
+  if (b1 == 0 || (gap && b1 == 255)) return false;
+  const uint32_t c16t = gap && b1 > 255 ? c16 + (511 - b1) : static_cast<uint32_t>(R) - b1;
   uint32_t need = k - above;
   // ---- select 2: bits 15..8 of the keys in theta's class ----
 #pragma unroll
   for (int j = 0; j < KJ; ++j)
-    if (64 * j < static_cast<int>(cw) && (kreg[j] >> 16) == c16t) atomicAdd(&h2[255 - ((kreg[j] >> 8) & 255)], 1u);
+    if (64 * j < static_cast<int>(cw)) hist_add(h2, (kreg[j] >> 16) == c16t, 255 - ((kreg[j] >> 8) & 255));
   __syncthreads();
   uint32_t b2;
   wave_select<256>(h2, need, &b2, &above);
@@ -387,7 +436,7 @@ __device__ __forceinline__ bool select_in_registers(const float* __restrict__ sr
   // ---- select 3: bits 7..0 ----
 #pragma unroll
   for (int j = 0; j < KJ; ++j)
-    if (64 * j < static_cast<int>(cw) && (kreg[j] >> 8) == p24) atomicAdd(&h3[255 - (kreg[j] & 255)], 1u);
+    if (64 * j < static_cast<int>(cw)) hist_add(h3, (kreg[j] >> 8) == p24, 255 - (kreg[j] & 255));
   __syncthreads();
   uint32_t b3;
   wave_select<256>(h3, need, &b3, &above);
@@ -466,7 +515,11 @@ __device__ __forceinline__ void select_row(const float* __restrict__ srow, int64
   }
 
   if (n <= FAST_MAX) {
-    if (select_in_registers(srow, static_cast<int>(n), k, out, regA, fhist, rs)) return;
+    const int ni = static_cast<int>(n);
+    const bool done = n <= 16 * 64 * 8    ? select_in_registers<8>(srow, ni, k, out, regA, fhist, rs)
+                      : n <= 16 * 64 * 16 ? select_in_registers<16>(srow, ni, k, out, regA, fhist, rs)
+                                          : select_in_registers<64>(srow, ni, k, out, regA, fhist, rs);
+    if (done) return;
     __syncthreads();  // fall back to the exact LDS path (region A and fhist are reused)
     // ---- fast path A: one read of the row; top 16 key bits to LDS, row maximum ----
     uint16_t* k16 = reinterpret_cast<uint16_t*>(regA);
@@ -741,13 +794,14 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const float* __restric
 }
 
 // Grids with rows longer than FAST_MAX, stage 1: block (chunk c, row) selects the top-k of
-// visible positions [c FAST_MAX, (c+1) FAST_MAX) as chunk-local indices into ws
-// [T, nchunk, k] (every key of the row's top-k is in the top-k of its chunk); a row of at
-// most FAST_MAX positions is finished here by its chunk-0 block.
+// visible positions [c FAST_MAX, (c+1) FAST_MAX) as chunk-local indices into widx
+// [T, nchunk, k] and their scores into the row's candidate scores cand_s (chunk c at
+// offset c k; -inf where the index is -1). Every key of the row's top-k is in the top-k
+// of its chunk. A row of at most FAST_MAX positions is finished here by its chunk-0 block.
 __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ q_off,
-    const int64_t* __restrict__ kv_off, int k, int nchunk, int32_t* __restrict__ ws,
-    int32_t* __restrict__ topk) {
+    const int64_t* __restrict__ kv_off, int k, int nchunk, int64_t cstride,
+    int32_t* __restrict__ widx, float* __restrict__ cand_s, int32_t* __restrict__ topk) {
   const int b = blockIdx.y, r = blockIdx.x / nchunk, c = blockIdx.x % nchunk;
   const RowInfo ri = load_row_info(q_off, kv_off, b);
   if (r >= ri.R) return;
@@ -760,25 +814,27 @@ __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(
     return;
   }
   const int64_t c0 = static_cast<int64_t>(c) * FAST_MAX;
+  if (c0 >= n) return;  // the merge reads only the chunks holding visible positions
   const int64_t nc = n - c0 < FAST_MAX ? n - c0 : FAST_MAX;
-  int32_t* o = ws + (t * nchunk + c) * k;
-  if (nc <= 0) {
-    for (int i = threadIdx.x; i < k; i += TK_THREADS) o[i] = -1;
-    return;
-  }
+  int32_t* o = widx + (t * nchunk + c) * k;
   select_row(srow + c0, nc, k, o);
+  __syncthreads();  // the block's index stores are visible to its own loads after this
+  float* cs = cand_s + t * cstride + static_cast<int64_t>(c) * k;
+  for (int i = threadIdx.x; i < k; i += TK_THREADS) {
+    const int32_t j = o[i];
+    cs[i] = j >= 0 ? srow[c0 + j] : -__builtin_inff();
+  }
 }
 
-// Rows longer than FAST_MAX, stage 2: the candidates of all chunks, in ascending position
-// order, are gathered into a compact score row (cand_s) and position row (cand_p); the
-// top-k of that row, mapped back to positions, is the row's top-k (ties between equal
-// scores still go to the lower position, since the compact order is the position order).
+// Rows longer than FAST_MAX, stage 2: the candidate scores of the row's chunks, in chunk
+// order, are in ascending position order (each chunk's list is ascending and only the
+// last list ends in padding), so the top-k of that compact row, mapped back through the
+// chunk indices, is the row's top-k: ties between equal scores still go to the lower
+// position, and a -inf pad follows every visible -inf.
 __global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(
-    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ q_off,
-    const int64_t* __restrict__ kv_off, int k, int nchunk, int64_t cstride,
-    const int32_t* __restrict__ ws, float* __restrict__ cand_s, int32_t* __restrict__ cand_p,
-    int32_t* __restrict__ topk) {
-  __shared__ uint32_t mtmp[2 * TK_WAVES];
+    const int32_t* __restrict__ q_off, const int64_t* __restrict__ kv_off, int64_t ld, int k,
+    int nchunk, int64_t cstride, const int32_t* __restrict__ widx,
+    const float* __restrict__ cand_s, int32_t* __restrict__ topk) {
   const int b = blockIdx.y, r = blockIdx.x;
   const RowInfo ri = load_row_info(q_off, kv_off, b);
   if (r >= ri.R) return;
@@ -786,32 +842,14 @@ __global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(
   int64_t n = visible_count(ri, r);
   if (n > ld) n = ld;
   if (n <= FAST_MAX) return;
-  const float* srow = scores + t * ld;
-  const int32_t* wrow = ws + t * nchunk * k;
-  float* cs = cand_s + t * cstride;  // cstride: nchunk k rounded up to 4 (16-byte rows)
-  int32_t* cp = cand_p + t * cstride;
-  // compact the valid chunk entries in (chunk, index) order, i.e. ascending position
-  const int total = nchunk * k;
-  uint32_t base = 0;
-  for (int i0 = 0; i0 < total; i0 += TK_THREADS) {
-    const int i = i0 + threadIdx.x;
-    const int32_t idx = i < total ? wrow[i] : -1;
-    uint32_t cnt;
-    const uint32_t at = base + block_excl_scan(idx >= 0 ? 1u : 0u, mtmp, &cnt);
-    if (idx >= 0) {
-      const int64_t p = static_cast<int64_t>(i / k) * FAST_MAX + idx;
-      cs[at] = srow[p];
-      cp[at] = static_cast<int32_t>(p);
-    }
-    base += cnt;
-  }
-  __syncthreads();  // the block's stores to cs/cp are visible to its own loads after this
+  const int64_t m = (n + FAST_MAX - 1) / FAST_MAX * k;  // this row's chunks
   int32_t* out = topk + t * k;
-  select_row(cs, base, k, out);
+  select_row(cand_s + t * cstride, m, k, out);
   __syncthreads();
+  const int32_t* wrow = widx + t * nchunk * k;
   for (int i = threadIdx.x; i < k; i += TK_THREADS) {
     const int32_t j = out[i];
-    if (j >= 0) out[i] = cp[j];
+    if (j >= 0) out[i] = (j / k) * FAST_MAX + wrow[j];
   }
 }
 
@@ -1210,10 +1248,9 @@ extern "C" size_t dsa_topk_workspace_size(int32_t T, int64_t max_kv_len, int32_t
   if (T <= 0 || k <= 0) return 0;
   const int64_t nc = topk_nchunk(max_kv_len);
   if (nc <= 1) return 0;
-  // chunk indices [T, nc, k] (padded to 16 bytes), compact candidate scores and positions
-  // [T, cstride] each
+  // chunk indices [T, nc, k] (padded to 16 bytes), then candidate scores [T, cstride]
   return static_cast<size_t>((static_cast<int64_t>(T) * nc * k + 3) / 4 * 4 +
-                             2 * static_cast<int64_t>(T) * topk_cstride(nc, k)) * 4;
+                             static_cast<int64_t>(T) * topk_cstride(nc, k)) * 4;
 }
 
 extern "C" dsa_status dsa_topk(const float* scores, int64_t score_ld,
@@ -1256,13 +1293,12 @@ extern "C" dsa_status dsa_topk(const float* scores, int64_t score_ld,
     int32_t* widx = static_cast<int32_t*>(ws);
     const int64_t cstride = topk_cstride(nchunk, k);
     float* cand_s = reinterpret_cast<float*>(widx + (static_cast<int64_t>(T) * nchunk * k + 3) / 4 * 4);
-    int32_t* cand_p = reinterpret_cast<int32_t*>(cand_s + static_cast<int64_t>(T) * cstride);
     hipLaunchKernelGGL(topk_chunk_kernel, dim3((unsigned)(max_q_rows * nchunk), (unsigned)B),
                        dim3(TK_THREADS), 0, as_stream(stream), scores, score_ld, q_row_offsets,
-                       kv_row_offsets, k, (int)nchunk, widx, topk);
-    hipLaunchKernelGGL(topk_merge_kernel, grid, dim3(TK_THREADS), 0, as_stream(stream), scores,
-                       score_ld, q_row_offsets, kv_row_offsets, k, (int)nchunk, cstride, widx,
-                       cand_s, cand_p, topk);
+                       kv_row_offsets, k, (int)nchunk, cstride, widx, cand_s, topk);
+    hipLaunchKernelGGL(topk_merge_kernel, grid, dim3(TK_THREADS), 0, as_stream(stream),
+                       q_row_offsets, kv_row_offsets, score_ld, k, (int)nchunk, cstride, widx,
+                       cand_s, topk);
   } else {
     hipLaunchKernelGGL(topk_kernel, grid, dim3(TK_THREADS), 0, as_stream(stream), scores,
                        score_ld, q_row_offsets, kv_row_offsets, k, topk);

@@ -34,7 +34,7 @@ def test_version_and_workspace_queries():
     assert lib.dsa_last_error() in (b"", None)
     assert lib.dsa_topk_workspace_size(192, 65536, 2048) == 0
     # 262144-position rows: 4 chunks of 2048 indices, then compact scores and positions
-    assert lib.dsa_topk_workspace_size(24, 262144, 2048) == (24 * 4 * 2048 + 2 * 24 * 8192) * 4
+    assert lib.dsa_topk_workspace_size(24, 262144, 2048) == (24 * 4 * 2048 + 24 * 8192) * 4
     # split-K partials: T * splits * H * (512 + 2) floats, or none when one split suffices
     ws = lib.dsa_sparse_mla_workspace_size(192, 64, 2048)
     assert ws == 0 or ws % (192 * 64 * 514 * 4) == 0
