@@ -23,8 +23,9 @@
 //     16-head tile (K = 128 = index_head_dim in one instruction), each into its own
 //     accumulator: A = q codes [16 heads x 128], B = key codes [128 x 16 keys].
 //     The result layout (row = 4*(lane/16)+i, col = lane%16) puts 4 heads of one key
-//     in each lane: the ReLU * weight head sum is in-lane FMAs plus two lane-half
-//     swaps (v_permlane16_swap / v_permlane32_swap, plain VALU).
+//     in each lane: the ReLU * weight head sum is in-lane FMAs, then two lane-half
+//     swaps (v_permlane32_swap / v_permlane16_swap, plain VALU) finish both sub-tiles
+//     of a tile at once.
 //  3. Each compute wave stores its row's 32 scores of the tile (key scale applied)
 //     with one coalesced 128-byte store.
 // One barrier per tile hands a landed tile to the compute waves and the slot of the
@@ -68,17 +69,6 @@ __device__ __forceinline__ void wait_vm_at_most(int n) {
 // bank window (keys alternate 128-byte halves for D = 128).
 template <int NCH>
 __device__ __forceinline__ int kswz(int k) { return (k >> 1) & (NCH - 1); }
-
-// x + x from the lane 16 (xor) away, and from the lane 32 away: the lane-half swaps
-// of gfx950 hand each lane its partner's value without going through LDS.
-__device__ __forceinline__ float sum_xor16_xor32(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
 
 template <int D, int HT, int NR>
 __global__ __launch_bounds__((2 * NR + 1) * 64) void index_score_kernel(
@@ -207,7 +197,16 @@ __global__ __launch_bounds__((2 * NR + 1) * 64) void index_score_kernel(
     }
   }
   float* srow = scores + t * ld + key0;
-  const int kt = 32 * kh + 16 * g + c16;  // key of the tile this lane stores (lane groups 0, 1)
+  // Lane groups 1 and 2 store the wave's 32 keys of a tile: key 32kh + 16(g-1) + c16 (the
+  // other groups read a valid, unused scale).
+  const int kt = 32 * kh + 16 * ((g - 1) & 1) + c16;
+  // Byte offsets in a slot of this lane's two 16-byte B pieces of sub-tile 0: dims
+  // 32g..32g+31 = logical pieces 2g and 2g+1 of key 32kh + c16. Sub-tile 1 is 16 keys =
+  // 16 D bytes further on with the same permutation (kswz only sees key/2 mod NCH, and
+  // 16/2 is a multiple of NCH).
+  const int key_l = 32 * kh + c16;
+  const int off_lo = key_l * D + 16 * ((2 * g) ^ kswz<NCH>(key_l));
+  const int off_hi = key_l * D + 16 * ((2 * g + 1) ^ kswz<NCH>(key_l));
 
   // Software pipeline over 16-key sub-tiles (each wave owns sub-tiles 0 and 1 of its
   // 32-key half of every tile): the MFMAs of the next sub-tile are issued before the
@@ -216,15 +215,19 @@ __global__ __launch_bounds__((2 * NR + 1) * 64) void index_score_kernel(
   // refill it.
   const bool live = row_live;
   auto live_tile = [&](int it) { return live && it * KT + 32 * kh < nstore; };  // wave-uniform
-  auto mfma_sub = [&](int it, int sb, f32x4 (&acc)[HT]) {
-    const uint8_t* buf = ring[it % NBUF];
-    const int key = 32 * kh + sb * 16 + c16;
+  // this lane's piece addresses in the current tile's slot (carried from sub-tile 0 of a
+  // tile to its sub-tile 1)
+  const uint8_t* a_lo = ring[0] + off_lo;
+  const uint8_t* a_hi = ring[0] + off_hi;
+  auto set_tile = [&](int it) {
+    a_lo = ring[it % NBUF] + off_lo;
+    a_hi = ring[it % NBUF] + off_hi;
+  };
+  auto mfma_sub = [&](int sb, f32x4 (&acc)[HT]) {
     i32x8 bfrag = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (32 * g < D) {  // dims 32g..32g+31 = logical pieces 2g, 2g+1
-      const uint8_t* krow = buf + key * D;
-      const int sw = kswz<NCH>(key);
-      const i32x4 lo = *reinterpret_cast<const i32x4*>(krow + 16 * ((2 * g) ^ sw));
-      const i32x4 hi = *reinterpret_cast<const i32x4*>(krow + 16 * ((2 * g + 1) ^ sw));
+    if (32 * g < D) {
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(a_lo + sb * 16 * D);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(a_hi + sb * 16 * D);
       bfrag = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
 #pragma unroll
@@ -234,39 +237,51 @@ __global__ __launch_bounds__((2 * NR + 1) * 64) void index_score_kernel(
                                                                  0, 0);
     }
   };
-  // ReLU * weight sum over all heads of key (lane column) from one sub-tile's accumulators
-  auto reduce_sub = [&](const f32x4 (&acc)[HT]) {
+  // in-lane part of the ReLU * weight head sum of key c16 of a sub-tile (the lane's heads)
+  auto partial = [&](const f32x4 (&acc)[HT]) {
     float part = 0.0f;
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
       for (int i = 0; i < 4; ++i)  // ReLU as med3(x, 0, FLT_MAX): max(x, 0) in one op
         part = fmaf(u[ht][i], __builtin_amdgcn_fmed3f(acc[ht][i], 0.0f, 3.402823466e38f), part);
-    return sum_xor16_xor32(part);
+    return part;
+  };
+  // Both sub-tiles' sums over the four lane groups with two lane-half swaps: the 32-lane
+  // swap of (p0, p1) leaves p0's group pairs (0+2, 1+3) in lanes 0..31 and p1's in lanes
+  // 32..63; the 16-lane swap then adds neighbouring groups, so groups 0 and 1 hold
+  // sub-tile 0's sum and groups 2 and 3 sub-tile 1's.
+  auto combine = [&](float p0, float p1) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false,
+                                                    false);
+    const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false,
+                                                    false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
   };
 
   f32x4 acc0[HT], acc1[HT];  // sub-tile 0 / sub-tile 1 of the current tile
   if (ntiles > 0) {
     __syncthreads();  // tile 0 is in LDS (the producer waited for it)
-    if (live_tile(0)) mfma_sub(0, 0, acc0);
+    if (live_tile(0)) mfma_sub(0, acc0);
   }
 #pragma unroll 1
   for (int it = 0; it < ntiles; ++it) {
     const bool lv = live_tile(it);
-    float sc = 0.0f, res0 = 0.0f, res1 = 0.0f;
+    float sc = 0.0f, p0 = 0.0f;
     if (lv) {
-      mfma_sub(it, 1, acc1);
+      mfma_sub(1, acc1);
       sc = reinterpret_cast<const float*>(ring[it % NBUF] + TILE_K)[kt];
-      res0 = reduce_sub(acc0);
+      p0 = partial(acc0);
     }
     if (it + 1 < ntiles) {
       __syncthreads();  // tile it+1 is in LDS; every wave is done reading tile it
-      if (live_tile(it + 1)) mfma_sub(it + 1, 0, acc0);
+      set_tile(it + 1);
+      if (live_tile(it + 1)) mfma_sub(0, acc0);
     }
     if (lv) {
-      res1 = reduce_sub(acc1);
-      // lane groups 0 and 1 store the two sub-tiles: key 32kh + 16g + c16, scaled
-      if (g < 2 && it * KT + kt < nstore) srow[it * KT + kt] = (g == 0 ? res0 : res1) * sc;
+      const float sum = combine(p0, partial(acc1));
+      if ((g == 1 || g == 2) && it * KT + kt < nstore) srow[it * KT + kt] = sum * sc;
     }
   }
 }
