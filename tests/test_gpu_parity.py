@@ -135,6 +135,34 @@ def test_topk_long_rows_chunked(levels):
             assert np.array_equal(got[t], ref), f"k={k} row {t} (visible {n})"
 
 
+@pytest.mark.parametrize("cluster", [2500, 600, 0])
+def test_topk_identical_clusters_across_row_lengths(cluster):
+    # Rows at each register-path size class (up to 8192, 16384 and 65536 positions, with
+    # the boundaries) carry a cluster of identical keys far above the rest: more copies
+    # than k (theta is the cluster value), fewer (theta lies far below it), or none. A
+    # second, smaller cluster sits between the first and the bulk in every other row.
+    _say(f"topk clusters={cluster}")
+    lens = [3000, 8192, 8193, 16384, 16385, 40000, 65536]
+    B = len(lens)
+    qo = torch.arange(B + 1, dtype=torch.int32)
+    ko = synth.kv_row_offsets(lens)
+    ld = 65536
+    s = synth.random_scores(B, ld, seed=70 + cluster)
+    g = synth.generator(71 + cluster)
+    for t, n in enumerate(lens):
+        if cluster:
+            pos = torch.randperm(n, generator=g)[:min(cluster, n // 2)]
+            s[t, pos] = 3.0e7
+        if t % 2:
+            pos = torch.randperm(n, generator=g)[:300]
+            s[t, pos] = 2.5e4
+    for k in (64, 2048):
+        got = api.topk(s.to(DEV), qo.to(DEV), ko.to(DEV), 1, max(lens), k).cpu().numpy()
+        for t in range(B):
+            ref = oracle.topk(s[t:t + 1].double().numpy(), [lens[t]], k)[0]
+            assert np.array_equal(got[t], ref), f"k={k} row {t} (visible {lens[t]})"
+
+
 def test_topk_small_k_and_padding():
     _say("topk k=1 and padding")
     lens = [10, 1, 300]
