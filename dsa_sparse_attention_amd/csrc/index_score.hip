@@ -6,11 +6,13 @@
 // ("配置体系", 双 KV 缓存). Score of row t against key s:
 //     I[t,s] = k_scale[s] * sum_j (w[t,j] * q_scale[t,j]) * ReLU(q_hat[t,j] . k_hat[s])
 //
-// Work split: a block owns one request's 4096-key chunk and up to 7 of its query rows:
+// Work split: the keys of all requests, concatenated, are cut into equal ranges of whole
+// 64-key tiles (up to 512 ranges, at least 256 keys each), so ragged context lengths and
+// small batches still spread over all CUs. A block owns one range and up to 7 query rows
+// of each request the range touches, and walks the range one request segment at a time:
 // two compute waves per row (each takes 32 of every 64-key tile, so that 6 rows make
 // 12 waves, 3 per SIMD: the MFMA load is spread evenly over the CU) plus one producer
-// wave. Every key byte is fetched from HBM once per request and shared by all of its
-// rows.
+// wave. Every key byte is fetched from HBM once per row group and shared by its rows.
 //  1. The producer wave streams keys HBM -> LDS with LDS DMA (global_load_lds, no
 //     registers) in 64-key tiles through a ring of NBUF slots (NBUF-1 tiles in flight),
 //     together with the tile's 64 key scales. One 16-byte DMA instruction moves 1 KB of
@@ -30,19 +32,22 @@
 //     with one coalesced 128-byte store.
 // One barrier per tile hands a landed tile to the compute waves and the slot of the
 // previous tile back to the producer.
+#include <atomic>
+
 #include "common.hpp"
 
 namespace dsa {
 namespace {
 
-#ifndef DSA_IS_CHUNK
-#define DSA_IS_CHUNK 4096
+#ifndef DSA_IS_MIN_SHARE
+#define DSA_IS_MIN_SHARE 256
 #endif
+
 #ifndef DSA_IS_NBUF
 #define DSA_IS_NBUF 8
 #endif
 constexpr int KT = 64;                // keys per tile
-constexpr int CHUNK = DSA_IS_CHUNK;   // keys per block
+constexpr int MIN_SHARE = DSA_IS_MIN_SHARE;  // fewest keys per block (4 tiles)
 constexpr int NBUF = DSA_IS_NBUF;     // tile slots in LDS: NBUF - 1 tiles in flight
 constexpr int MAX_ROWS = 7;           // rows per block: 2 compute waves each, plus a producer
 constexpr int MAX_ROWS_H128 = 3;      // with 8 head tiles (registers: 256 per wave)
@@ -70,87 +75,103 @@ __device__ __forceinline__ void wait_vm_at_most(int n) {
 template <int NCH>
 __device__ __forceinline__ int kswz(int k) { return (k >> 1) & (NCH - 1); }
 
-template <int D, int HT, int NR>
-__global__ __launch_bounds__((2 * NR + 1) * 64) void index_score_kernel(
-    const uint8_t* __restrict__ q_fp8, const float* __restrict__ q_scale,
-    const float* __restrict__ w, const uint8_t* __restrict__ k_fp8,
-    const float* __restrict__ k_scale, const int32_t* __restrict__ q_off,
-    const int64_t* __restrict__ kv_off, int H, float* __restrict__ scores, int64_t ld) {
-  constexpr int NCH = D / 16;                  // 16-byte pieces per key = K DMAs per tile
-  constexpr int KPB = 1024 / D;                // keys per 1 KB DMA block
-  constexpr int TILE_K = KT * D;               // key bytes per tile
-  constexpr int SLOT = TILE_K + KT * 4;        // + the tile's key scales
-  constexpr int DMAS = NCH + 1;                // producer DMAs per tile
+template <int D>
+struct Ring {
+  static constexpr int NCH = D / 16;            // 16-byte pieces per key = K DMAs per tile
+  static constexpr int KPB = 1024 / D;          // keys per 1 KB DMA block
+  static constexpr int TILE_K = KT * D;         // key bytes per tile
+  static constexpr int SLOT = TILE_K + KT * 4;  // + the tile's key scales
+  static constexpr int DMAS = NCH + 1;          // producer DMAs per tile
   static_assert((NBUF - 2) * DMAS <= 63, "vmcnt holds at most 63");
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[NBUF][SLOT];
+};
 
-  const int b = blockIdx.y;
-  const RowInfo ri = load_row_info(q_off, kv_off, b);
-  const int64_t key0 = static_cast<int64_t>(blockIdx.x) * CHUNK;
-  const int row0 = blockIdx.z * NR;
-  if (key0 >= ri.L || row0 >= ri.R) return;  // block-uniform
-  int64_t key_end = key0 + CHUNK < ri.L ? key0 + CHUNK : ri.L;
-  if (key_end > ld) key_end = ld;  // device lengths beyond the score stride are clipped
+// Keys key0 .. key_end-1 (0 < key_end - key0 < 2^31) of request `ri` against its rows
+// row0 .. row0+NR-1, by the whole block: the producer wave streams the keys through the
+// ring, the compute waves score and store them. The block's barriers pair up one to one
+// between the two roles: one per tile.
+// Keys key0 .. key_end-1 (0 < key_end - key0 < 2^31) of request `ri` against its rows
+// row0 .. row0+NR-1, by the whole block: the producer wave (producer_segment) streams the
+// keys through the ring, the compute waves (compute_segment) score and store them. Each
+// side passes one barrier per tile, so the block's barriers pair up one to one.
+template <int D, int HT, int NR>
+__device__ __forceinline__ void producer_segment(
+    uint8_t (&ring)[NBUF][Ring<D>::SLOT], const uint8_t* __restrict__ q_fp8,
+    const float* __restrict__ q_scale, const float* __restrict__ w,
+    const uint8_t* __restrict__ k_fp8, const float* __restrict__ k_scale, const RowInfo& ri,
+    int64_t key0, int64_t key_end, int row0, int H, float* __restrict__ scores, int64_t ld,
+    int lane, int wave) {
+  constexpr int NCH = Ring<D>::NCH;
+  constexpr int KPB = Ring<D>::KPB;
+  constexpr int TILE_K = Ring<D>::TILE_K;
+  constexpr int DMAS = Ring<D>::DMAS;
   const int nkeys = static_cast<int>(key_end - key0);
-  const int ntiles = nkeys > 0 ? (nkeys + KT - 1) / KT : 0;
-
-  const int lane = threadIdx.x % 64;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);  // wave-uniform (SGPR)
-
-  if (wave == 2 * NR) {
-    // ---- producer wave: tile `it` -> slot it % NBUF. DMA m < NCH moves keys KPB*m ..
-    // KPB*m + KPB-1 of the tile: lane l writes physical piece l % NCH of key KPB*m + l/NCH,
-    // i.e. loads logical piece (l % NCH) ^ kswz(key); keys past the chunk load its last
-    // key again (their scores are never stored). DMA NCH moves the 64 key scales.
-    // In a full tile, key KPB*m + l/NCH has kswz = (KPB*m/2 + l/(2*NCH)) % NCH, which only
-    // depends on the parity of m (KPB*m/2 is a multiple of NCH for even m and NCH/2 more
-    // for odd m): two per-lane byte offsets serve every DMA of every full tile.
-    const uint8_t* kreq = k_fp8 + (ri.kv_base + key0) * D;
-    const float* sreq = k_scale + ri.kv_base + key0;
-    const int ful = nkeys / KT;  // full tiles
-    auto issue_tile = [&](int it) {
-      int ln = lane;
-      asm volatile("" : "+v"(ln));  // recomputed per tile, not held across the loop
-      const lds_u8* slot = (const lds_u8*)ring[it % NBUF];
-      if (it < ful) {
-        const uint8_t* base = kreq + static_cast<int64_t>(it) * TILE_K + (ln / NCH) * D;
-        const int off0 = 16 * ((ln % NCH) ^ kswz<NCH>(ln / NCH));
-        const int off1 = 16 * ((ln % NCH) ^ kswz<NCH>(KPB + ln / NCH));
+  const int ntiles = (nkeys + KT - 1) / KT;
+  // ---- producer wave: tile `it` -> slot it % NBUF. DMA m < NCH moves keys KPB*m ..
+  // KPB*m + KPB-1 of the tile: lane l writes physical piece l % NCH of key KPB*m + l/NCH,
+  // i.e. loads logical piece (l % NCH) ^ kswz(key); keys past the chunk load its last
+  // key again (their scores are never stored). DMA NCH moves the 64 key scales.
+  // In a full tile, key KPB*m + l/NCH has kswz = (KPB*m/2 + l/(2*NCH)) % NCH, which only
+  // depends on the parity of m (KPB*m/2 is a multiple of NCH for even m and NCH/2 more
+  // for odd m): two per-lane byte offsets serve every DMA of every full tile.
+  const uint8_t* kreq = k_fp8 + (ri.kv_base + key0) * D;
+  const float* sreq = k_scale + ri.kv_base + key0;
+  const int ful = nkeys / KT;  // full tiles
+  auto issue_tile = [&](int it) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));  // recomputed per tile, not held across the loop
+    const lds_u8* slot = (const lds_u8*)ring[it % NBUF];
+    if (it < ful) {
+      const uint8_t* base = kreq + static_cast<int64_t>(it) * TILE_K + (ln / NCH) * D;
+      const int off0 = 16 * ((ln % NCH) ^ kswz<NCH>(ln / NCH));
+      const int off1 = 16 * ((ln % NCH) ^ kswz<NCH>(KPB + ln / NCH));
 #pragma unroll
-        for (int m = 0; m < NCH; ++m)
-          lds_dma16(base + 1024 * m + ((m & 1) ? off1 : off0), (const lds_void*)(slot + 1024 * m));
-        lds_dma4(sreq + it * KT + ln, (const lds_void*)(slot + TILE_K));
-      } else {
+      for (int m = 0; m < NCH; ++m)
+        lds_dma16(base + 1024 * m + ((m & 1) ? off1 : off0), (const lds_void*)(slot + 1024 * m));
+      lds_dma4(sreq + it * KT + ln, (const lds_void*)(slot + TILE_K));
+    } else {
 #pragma unroll
-        for (int m = 0; m < NCH; ++m) {
-          const int kt = KPB * m + ln / NCH;  // key within the tile
-          const int key = it * KT + kt < nkeys ? it * KT + kt : nkeys - 1;
-          lds_dma16(kreq + static_cast<int64_t>(key) * D + 16 * ((ln % NCH) ^ kswz<NCH>(kt)),
-                    (const lds_void*)(slot + 1024 * m));
-        }
-        const int key = it * KT + ln < nkeys ? it * KT + ln : nkeys - 1;
-        lds_dma4(sreq + key, (const lds_void*)(slot + TILE_K));
+      for (int m = 0; m < NCH; ++m) {
+        const int kt = KPB * m + ln / NCH;  // key within the tile
+        const int key = it * KT + kt < nkeys ? it * KT + kt : nkeys - 1;
+        lds_dma16(kreq + static_cast<int64_t>(key) * D + 16 * ((ln % NCH) ^ kswz<NCH>(kt)),
+                  (const lds_void*)(slot + 1024 * m));
       }
-    };
-    // Tile it+NBUF-2 goes into the slot of tile it-2, which every compute wave finished
-    // reading before barrier it-1: the producer issues it before barrier it, overlapped
-    // with the compute of tile it-1, and reaches the barrier as soon as tile it is in.
-    // Retire every load the compiler issued so far: its own wait bookkeeping does not see
-    // the DMAs, and a wait it placed for one of its loads inside the loop would count them
-    // wrongly and drain the whole DMA pipeline.
-    DSA_WAIT_VMCNT(0);
-#pragma unroll 1
-    for (int j = 0; j < NBUF - 2 && j < ntiles; ++j) issue_tile(j);
-#pragma unroll 1
-    for (int it = 0; it < ntiles; ++it) {
-      if (it + NBUF - 2 < ntiles) issue_tile(it + NBUF - 2);
-      // tile `it` has landed when at most the DMAs of the tiles after it are in flight
-      const int after = ntiles - 1 - it < NBUF - 2 ? ntiles - 1 - it : NBUF - 2;
-      wait_vm_at_most<(NBUF - 2) * DMAS>(after * DMAS);
-      __syncthreads();  // hand tile `it` over; every compute wave is done with tile it-1
+      const int key = it * KT + ln < nkeys ? it * KT + ln : nkeys - 1;
+      lds_dma4(sreq + key, (const lds_void*)(slot + TILE_K));
     }
-    return;
+  };
+  // Tile it+NBUF-2 goes into the slot of tile it-2, which every compute wave finished
+  // reading before barrier it-1: the producer issues it before barrier it, overlapped
+  // with the compute of tile it-1, and reaches the barrier as soon as tile it is in.
+  // Retire every load the compiler issued so far: its own wait bookkeeping does not see
+  // the DMAs, and a wait it placed for one of its loads inside the loop would count them
+  // wrongly and drain the whole DMA pipeline.
+  DSA_WAIT_VMCNT(0);
+#pragma unroll 1
+  for (int j = 0; j < NBUF - 2 && j < ntiles; ++j) issue_tile(j);
+#pragma unroll 1
+  for (int it = 0; it < ntiles; ++it) {
+    if (it + NBUF - 2 < ntiles) issue_tile(it + NBUF - 2);
+    // tile `it` has landed when at most the DMAs of the tiles after it are in flight
+    const int after = ntiles - 1 - it < NBUF - 2 ? ntiles - 1 - it : NBUF - 2;
+    wait_vm_at_most<(NBUF - 2) * DMAS>(after * DMAS);
+    __syncthreads();  // hand tile `it` over; every compute wave is done with tile it-1
   }
+}
+
+template <int D, int HT, int NR>
+__device__ __forceinline__ void compute_segment(
+    uint8_t (&ring)[NBUF][Ring<D>::SLOT], const uint8_t* __restrict__ q_fp8,
+    const float* __restrict__ q_scale, const float* __restrict__ w,
+    const uint8_t* __restrict__ k_fp8, const float* __restrict__ k_scale, const RowInfo& ri,
+    int64_t key0, int64_t key_end, int row0, int H, float* __restrict__ scores, int64_t ld,
+    int lane, int wave) {
+  constexpr int NCH = Ring<D>::NCH;
+  constexpr int TILE_K = Ring<D>::TILE_K;
+  const int nkeys = static_cast<int>(key_end - key0);
+  const int ntiles = (nkeys + KT - 1) / KT;
+  // lane-derived addresses are recomputed per segment rather than held (spilled) across them
+  asm volatile("" : "+v"(lane));
 
   // ---- compute wave: row row0 + wave/2, keys 32*(wave%2) .. +32 of every tile
   const int g = lane / 16, c16 = lane % 16;
@@ -286,42 +307,140 @@ __global__ __launch_bounds__((2 * NR + 1) * 64) void index_score_kernel(
   }
 }
 
+// The request holding global key position g (kv_off[0] <= g < kv_off[B]): the largest b
+// with kv_off[b] <= g, which skips requests without keys. A 64-way search by the whole
+// wave, one round of loads per factor of 64 in B; the result is wave-uniform.
+__device__ __forceinline__ int request_of(const int64_t* __restrict__ kv_off, int B, int64_t g,
+                                          int lane) {
+  int lo = 0, hi = B;  // kv_off[lo] <= g; the answer lies in [lo, hi)
+  while (hi - lo > 1) {
+    const int step = (hi - lo + 63) / 64;
+    const int idx = lo + lane * step;
+    const bool ok = idx < hi && kv_off[idx < hi ? idx : lo] <= g;  // true for a lane prefix
+    const uint64_t m = __builtin_amdgcn_ballot_w64(ok);             // lane 0 always set
+    lo += (63 - __builtin_clzll(m)) * step;
+    hi = lo + step < hi ? lo + step : hi;
+  }
+  return lo;
+}
+
+// Work split: the requests' keys, concatenated in request order (global positions
+// kv_off[0] .. kv_off[B]), are cut into gridDim.x equal ranges, rounded up to whole
+// 64-key tiles; block (x, 0, z) scores range x against rows z NR .. z NR + NR - 1 of every
+// request the range touches, one segment per request. Ragged lengths thus spread evenly
+// over the blocks, and a small batch still occupies many CUs.
+template <int D, int HT, int NR>
+__global__ __launch_bounds__((2 * NR + 1) * 64) void index_score_kernel(
+    const uint8_t* __restrict__ q_fp8, const float* __restrict__ q_scale,
+    const float* __restrict__ w, const uint8_t* __restrict__ k_fp8,
+    const float* __restrict__ k_scale, const int32_t* __restrict__ q_off,
+    const int64_t* __restrict__ kv_off, int B, int H, float* __restrict__ scores, int64_t ld) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NBUF][Ring<D>::SLOT];
+  const int lane = threadIdx.x % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);  // wave-uniform (SGPR)
+  const int row0 = blockIdx.z * NR;
+  const int64_t base = kv_off[0], end = kv_off[B];
+  int64_t share = (end - base + gridDim.x - 1) / gridDim.x;
+  share = (share + KT - 1) / KT * KT;
+  const int64_t g0 = base + static_cast<int64_t>(blockIdx.x) * share;
+  const int64_t g1 = g0 + share < end ? g0 + share : end;
+  if (g0 >= g1) return;  // block-uniform
+  // Both roles walk the same segments and pass the same barriers.
+  auto for_segments = [&](auto&& body) {
+    bool first = true;
+    for (int b = request_of(kv_off, B, g0, lane); b < B; ++b) {
+      const RowInfo ri = load_row_info(q_off, kv_off, b);
+      if (ri.kv_base >= g1) break;  // block-uniform, as every test below
+      if (row0 >= ri.R) continue;
+      const int64_t key0 = (g0 > ri.kv_base ? g0 : ri.kv_base) - ri.kv_base;
+      int64_t key_end = (g1 < ri.kv_base + ri.L ? g1 : ri.kv_base + ri.L) - ri.kv_base;
+      if (key_end > ld) key_end = ld;  // device lengths beyond the score stride are clipped
+      if (key_end <= key0) continue;
+      // every wave is done with the previous segment's tiles before the producer refills
+      // their slots
+      if (!first) __syncthreads();
+      first = false;
+      body(ri, key0, key_end);
+    }
+  };
+  if (wave == 2 * NR) {
+    for_segments([&](const RowInfo& ri, int64_t key0, int64_t key_end) {
+      producer_segment<D, HT, NR>(ring, q_fp8, q_scale, w, k_fp8, k_scale, ri, key0, key_end,
+                                  row0, H, scores, ld, lane, wave);
+    });
+  } else {
+    for_segments([&](const RowInfo& ri, int64_t key0, int64_t key_end) {
+      compute_segment<D, HT, NR>(ring, q_fp8, q_scale, w, k_fp8, k_scale, ri, key0, key_end,
+                                 row0, H, scores, ld, lane, wave);
+    });
+  }
+}
+
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  const int slot = dev < 64 ? dev : 63;
+  int n = cache[slot].load(std::memory_order_relaxed);
+  if (n <= 0 || dev >= 64) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 1;
+    if (dev < 64) cache[slot].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// grid.x on entry: the key ranges the sizes call for; it is capped at one wave of resident
+// blocks (blocks per CU x CUs, shared by the grid.z row groups), so that every range starts
+// at once and equal ranges finish together.
 template <int D, int HT, int NRV>
 void launch_one(dim3 grid, hipStream_t st, const uint8_t* q, const float* qs, const float* w,
-                const uint8_t* k, const float* ks, const int32_t* qo, const int64_t* ko, int H,
+                const uint8_t* k, const float* ks, const int32_t* qo, const int64_t* ko, int B, int H,
                 float* sc, int64_t ld) {
   if constexpr (HT >= 8 && NRV > MAX_ROWS_H128) {
     return;  // never chosen: the host caps rows per block at MAX_ROWS_H128 for 8 head tiles
   } else {
-    hipLaunchKernelGGL((index_score_kernel<D, HT, NRV>), grid, dim3((2 * NRV + 1) * 64), 0, st, q,
-                       qs, w, k, ks, qo, ko, H, sc, ld);
+    constexpr int threads = (2 * NRV + 1) * 64;
+    static std::atomic<int> occ{0};  // resident blocks per CU of this instantiation
+    int o = occ.load(std::memory_order_relaxed);
+    if (o <= 0) {
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, index_score_kernel<D, HT, NRV>, threads,
+                                                       0) != hipSuccess || o < 1)
+        o = 1;
+      occ.store(o, std::memory_order_relaxed);
+    }
+    const int64_t cap = static_cast<int64_t>(o) * cu_count() / grid.z;
+    if (static_cast<int64_t>(grid.x) > cap) grid.x = static_cast<unsigned>(cap > 1 ? cap : 1);
+    hipLaunchKernelGGL((index_score_kernel<D, HT, NRV>), grid, dim3(threads), 0, st, q, qs, w, k,
+                       ks, qo, ko, B, H, sc, ld);
   }
 }
 
 template <int D, int HT>
 void launch_nr(int nr, dim3 grid, hipStream_t st, const uint8_t* q, const float* qs,
                const float* w, const uint8_t* k, const float* ks, const int32_t* qo,
-               const int64_t* ko, int H, float* sc, int64_t ld) {
+               const int64_t* ko, int B, int H, float* sc, int64_t ld) {
   switch (nr) {
-    case 1: launch_one<D, HT, 1>(grid, st, q, qs, w, k, ks, qo, ko, H, sc, ld); break;
-    case 2: launch_one<D, HT, 2>(grid, st, q, qs, w, k, ks, qo, ko, H, sc, ld); break;
-    case 3: launch_one<D, HT, 3>(grid, st, q, qs, w, k, ks, qo, ko, H, sc, ld); break;
-    case 4: launch_one<D, HT, 4>(grid, st, q, qs, w, k, ks, qo, ko, H, sc, ld); break;
-    case 5: launch_one<D, HT, 5>(grid, st, q, qs, w, k, ks, qo, ko, H, sc, ld); break;
-    case 6: launch_one<D, HT, 6>(grid, st, q, qs, w, k, ks, qo, ko, H, sc, ld); break;
-    default: launch_one<D, HT, 7>(grid, st, q, qs, w, k, ks, qo, ko, H, sc, ld); break;
+    case 1: launch_one<D, HT, 1>(grid, st, q, qs, w, k, ks, qo, ko, B, H, sc, ld); break;
+    case 2: launch_one<D, HT, 2>(grid, st, q, qs, w, k, ks, qo, ko, B, H, sc, ld); break;
+    case 3: launch_one<D, HT, 3>(grid, st, q, qs, w, k, ks, qo, ko, B, H, sc, ld); break;
+    case 4: launch_one<D, HT, 4>(grid, st, q, qs, w, k, ks, qo, ko, B, H, sc, ld); break;
+    case 5: launch_one<D, HT, 5>(grid, st, q, qs, w, k, ks, qo, ko, B, H, sc, ld); break;
+    case 6: launch_one<D, HT, 6>(grid, st, q, qs, w, k, ks, qo, ko, B, H, sc, ld); break;
+    default: launch_one<D, HT, 7>(grid, st, q, qs, w, k, ks, qo, ko, B, H, sc, ld); break;
   }
 }
 
 template <int D>
 void launch_ht(int ht, int nr, dim3 grid, hipStream_t st, const uint8_t* q, const float* qs,
                const float* w, const uint8_t* k, const float* ks, const int32_t* qo,
-               const int64_t* ko, int H, float* sc, int64_t ld) {
+               const int64_t* ko, int B, int H, float* sc, int64_t ld) {
   switch (ht) {
-    case 1: launch_nr<D, 1>(nr, grid, st, q, qs, w, k, ks, qo, ko, H, sc, ld); break;
-    case 2: launch_nr<D, 2>(nr, grid, st, q, qs, w, k, ks, qo, ko, H, sc, ld); break;
-    case 4: launch_nr<D, 4>(nr, grid, st, q, qs, w, k, ks, qo, ko, H, sc, ld); break;
-    default: launch_nr<D, 8>(nr, grid, st, q, qs, w, k, ks, qo, ko, H, sc, ld); break;
+    case 1: launch_nr<D, 1>(nr, grid, st, q, qs, w, k, ks, qo, ko, B, H, sc, ld); break;
+    case 2: launch_nr<D, 2>(nr, grid, st, q, qs, w, k, ks, qo, ko, B, H, sc, ld); break;
+    case 4: launch_nr<D, 4>(nr, grid, st, q, qs, w, k, ks, qo, ko, B, H, sc, ld); break;
+    default: launch_nr<D, 8>(nr, grid, st, q, qs, w, k, ks, qo, ko, B, H, sc, ld); break;
   }
 }
 
@@ -357,19 +476,23 @@ extern "C" dsa_status dsa_index_score(const uint8_t* q_fp8, const float* q_scale
                   (reinterpret_cast<uintptr_t>(k_fp8) & 15) == 0,
               "dsa_index_score: q_fp8 and k_fp8 must be 16-byte aligned");
   DSA_REQUIRE(B <= 65535, "dsa_index_score: B must be <= 65535");
+  DSA_REQUIRE(score_ld < (int64_t(1) << 31), "dsa_index_score: score_ld must be < 2^31");
   const int ht = pow2_at_least((H_I + 15) / 16);
   // row groups of at most max_rows_for(ht), balanced: e.g. 6 rows -> one group of 6, 8 -> 4 + 4
   const int64_t gz = ceil_div(max_q_rows, max_rows_for(ht));
   const int nr = static_cast<int>(ceil_div(max_q_rows, gz));  // rows per block
-  const int64_t gx = ceil_div(max_kv_len, CHUNK);
-  DSA_REQUIRE(gx <= 0x7FFFFFFF && gz <= 65535, "dsa_index_score: grid too large");
-  dim3 grid((unsigned)gx, (unsigned)B, (unsigned)gz);
+  // key ranges: one per MIN_SHARE keys of the largest batch the sizes allow (capped at one
+  // wave of resident blocks by launch_one)
+  int64_t gx = ceil_div(static_cast<int64_t>(B) * max_kv_len, MIN_SHARE);
+  gx = gx < 1 ? 1 : (gx > 0x7FFFFFFF ? 0x7FFFFFFF : gx);
+  DSA_REQUIRE(gz <= 65535, "dsa_index_score: grid too large");
+  dim3 grid((unsigned)gx, 1u, (unsigned)gz);
   hipStream_t st = as_stream(stream);
   if (D_I == 128)
     launch_ht<128>(ht, nr, grid, st, q_fp8, q_scale, w, k_fp8, k_scale, q_row_offsets,
-                   kv_row_offsets, H_I, scores, score_ld);
+                   kv_row_offsets, B, H_I, scores, score_ld);
   else
     launch_ht<64>(ht, nr, grid, st, q_fp8, q_scale, w, k_fp8, k_scale, q_row_offsets,
-                  kv_row_offsets, H_I, scores, score_ld);
+                  kv_row_offsets, B, H_I, scores, score_ld);
   return check_launch("dsa_index_score");
 }
