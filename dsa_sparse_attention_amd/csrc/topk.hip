@@ -926,7 +926,6 @@ __global__ __launch_bounds__(RF_THREADS) void topk_refine_kernel(
   __shared__ int32_t in_pos[RF_MAXK];
   __shared__ int32_t sel_pos[RF_MAXK];
   __shared__ double kdec[RF_WAVES][128];  // one band key's decoded codes per wave
-  __shared__ double term[RF_WAVES][128];  // u_j * max(d_j, 0) per head, per wave
   __shared__ float redf[RF_WAVES];
   __shared__ double redd[RF_WAVES];
   __shared__ uint32_t tmp[2 * TK_WAVES];
