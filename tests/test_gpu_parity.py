@@ -93,6 +93,41 @@ def test_index_score_exact_grid_bitexact():
         assert np.array_equal(got[t, :n], ref[t, :n])
 
 
+@pytest.mark.parametrize("H,D,seed", [(64, 128, 0), (128, 128, 1), (8, 64, 2)])
+def test_index_score_ragged_many_requests_exact_grid(H, D, seed):
+    # Many requests with ragged lengths (empty ones, a few keys, tile multiples) and a
+    # varying number of rows (up to 9, so rows split into row groups): the key ranges of
+    # the blocks cross request boundaries at arbitrary points. Integer codes keep every
+    # sum exact, so every visible score must equal the oracle's, and every entry past a
+    # row's visible prefix must keep its prefilled value.
+    _say(f"index_score ragged exact grid H={H} D={D}")
+    rng = np.random.default_rng(100 + seed)
+    B = 120
+    lens = rng.integers(0, 300, B)
+    lens[rng.choice(B, 12, replace=False)] = 0
+    lens[rng.choice(B, 8, replace=False)] = 64 * rng.integers(1, 5, 8)
+    R = rng.integers(1, 10, B)
+    qo = np.concatenate([[0], np.cumsum(R)]).astype(np.int32)
+    ko = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T, N, L = int(qo[-1]), int(ko[-1]), int(lens.max())
+    vals = np.array([-4, -3, -2, -1, 0, 1, 2, 3, 4], np.float32)
+    q = oracle.fp8_encode(rng.choice(vals, (T, H, D)))
+    k = oracle.fp8_encode(rng.choice(vals, (N, D)))
+    w = (rng.integers(0, 16, (T, H)) / 16).astype(np.float32)
+    qs = np.ones((T, H), np.float32)
+    ks = np.ones(N, np.float32)
+    ref = oracle.index_score(q, qs, w, k, ks, qo, ko, width=L)
+    d = lambda a: torch.from_numpy(a).to(DEV)
+    ld = (L + 3) // 4 * 4
+    scores = torch.full((T, ld), float("nan"), device=DEV)
+    api.index_score(d(q), d(qs), d(w), d(k), d(ks), d(qo), d(ko), int(R.max()), L, scores=scores)
+    got = scores.cpu().numpy().astype(np.float64)
+    for t in range(T):
+        n = oracle.row_visible(qo, ko, t)
+        assert np.array_equal(got[t, :n], ref[t, :n]), f"row {t} (visible {n})"
+        assert np.all(np.isnan(got[t, n:])), f"row {t}: written past its visible prefix"
+
+
 # ---------------------------------------------------------------- top-k
 @pytest.mark.parametrize("levels", [0, 5, 1000])
 def test_topk_bitexact_on_shared_scores(levels):
