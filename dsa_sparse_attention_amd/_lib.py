@@ -24,6 +24,7 @@ SIGNATURES = {
     "dsa_abi_version": ([], ctypes.c_int),
     "dsa_last_error": ([], ctypes.c_char_p),
     "dsa_quantize_fp8": ([P, I64, I32, P, P, P], ctypes.c_int),
+    "dsa_verify_cache_write": ([P, P, P, I32, I32, P, P, P, P, I32, P, P, P], ctypes.c_int),
     "dsa_index_score": ([P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I64, P, I64, P],
                         ctypes.c_int),
     "dsa_topk": ([P, I64, P, P, I32, I32, I32, I64, I32, P, P, P, SZ, P], ctypes.c_int),

@@ -67,6 +67,42 @@ def quantize_fp8(x: torch.Tensor, out: torch.Tensor | None = None,
     return out, scale
 
 
+def verify_cache_write(k_new, dst_rows, k_cache, k_scale, latent_new=None, kv_cache=None,
+                       q=None, q_fp8=None, q_scale=None):
+    """The verify rows' new index keys (quantised) and latent rows into the caches at
+    dst_rows, and optionally the queries quantised into q_fp8/q_scale, in one launch."""
+    _dev(k_new, "k_new", torch.float32)
+    _dev(dst_rows, "dst_rows", torch.int64)
+    _dev(k_cache, "k_cache", torch.uint8)
+    _dev(k_scale, "k_scale", torch.float32)
+    T, D = k_new.shape
+    if dst_rows.numel() != T or k_cache.shape[-1] != D:
+        raise ValueError("dst_rows must hold T rows and k_cache rows must match k_new's width")
+    if (latent_new is None) != (kv_cache is None):
+        raise ValueError("latent_new and kv_cache go together")
+    if latent_new is not None:
+        _dev(latent_new, "latent_new", torch.bfloat16)
+        _dev(kv_cache, "kv_cache", torch.bfloat16)
+        if latent_new.shape != (T, 576) or kv_cache.shape[-1] != 576:
+            raise ValueError("latent rows are 576 bf16 wide")
+    H = 0
+    if q is not None:
+        _dev(q, "q", torch.float32)
+        if q.dim() != 3 or q.shape[0] != T or q.shape[2] != D:
+            raise ValueError("q must be [T, H, D] with k_new's T and D")
+        H = q.shape[1]
+        if q_fp8 is None:
+            q_fp8 = torch.empty(q.shape, dtype=torch.uint8, device=q.device)
+        if q_scale is None:
+            q_scale = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+        _dev(q_fp8, "q_fp8", torch.uint8)
+        _dev(q_scale, "q_scale", torch.float32)
+    _check(_lib.load().dsa_verify_cache_write(
+        _p(k_new), _p(latent_new), _p(dst_rows), T, D, _p(k_cache), _p(k_scale), _p(kv_cache),
+        _p(q), H, _p(q_fp8), _p(q_scale), _stream()))
+    return q_fp8, q_scale
+
+
 def index_score(q_fp8, q_scale, w, k_fp8, k_scale, q_row_offsets, kv_row_offsets,
                 max_q_rows: int, max_kv_len: int, scores: torch.Tensor | None = None):
     """Indexer scores [T, score_ld]; entries past each row's visible prefix are untouched."""

@@ -39,16 +39,17 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float x) {
   return sign | (static_cast<uint32_t>(e + 7) << 3) | m3;
 }
 
+// One vector of D floats over D/4 consecutive lanes (lane_in_vec = 0 .. D/4-1, four
+// consecutive elements each); every lane of the group takes part in the shuffles, and only
+// live groups load and store. codes/scale: this vector's destination.
 template <int D>
-__global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__ x, int64_t n_vec,
-                                                       float rsqrt_d, uint8_t* __restrict__ out,
-                                                       float* __restrict__ scale) {
+__device__ __forceinline__ void quantize_vector(const float* __restrict__ src, bool live,
+                                                int lane_in_vec, float rsqrt_d,
+                                                uint8_t* __restrict__ codes,
+                                                float* __restrict__ scale) {
   constexpr int LPV = D / 4;  // lanes per vector
-  const int lane_in_vec = threadIdx.x % LPV;
-  const int64_t v = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / LPV;
-  const bool live = v < n_vec;
   float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (live) y = reinterpret_cast<const float4*>(x + v * D)[lane_in_vec];
+  if (live) y = reinterpret_cast<const float4*>(src)[lane_in_vec];
   // stride 1: pairs (0,1), (2,3)
   float a0 = y.x + y.y, a1 = y.x - y.y, a2 = y.z + y.w, a3 = y.z - y.w;
   // stride 2: pairs (0,2), (1,3)
@@ -72,8 +73,57 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
   if (!live) return;
   uint32_t packed = e4m3_rne_sat(e0 / s) | (e4m3_rne_sat(e1 / s) << 8) |
                     (e4m3_rne_sat(e2 / s) << 16) | (e4m3_rne_sat(e3 / s) << 24);
-  reinterpret_cast<uint32_t*>(out + v * D)[lane_in_vec] = packed;
-  if (lane_in_vec == 0) scale[v] = s;
+  reinterpret_cast<uint32_t*>(codes)[lane_in_vec] = packed;
+  if (lane_in_vec == 0) *scale = s;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__ x, int64_t n_vec,
+                                                       float rsqrt_d, uint8_t* __restrict__ out,
+                                                       float* __restrict__ scale) {
+  constexpr int LPV = D / 4;
+  const int64_t v = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / LPV;
+  const bool live = v < n_vec;
+  const int64_t vv = live ? v : 0;
+  quantize_vector<D>(x + vv * D, live, threadIdx.x % LPV, rsqrt_d, out + vv * D, scale + vv);
+}
+
+constexpr int LATENT = 576;               // bf16 per latent row (512 + 64)
+constexpr int LATENT_UNITS = LATENT / 8;  // 16-byte units per row
+
+// The verify step's writes in one launch. Blocks [0, nbq): query vectors (as
+// quantize_kernel); [nbq, nbq + nbk): the new index keys, quantised into cache row
+// dst_rows[t]; the rest: the new latent rows, one 16-byte unit per thread, copied to the
+// same cache rows. The block ranges are uniform per block.
+template <int D>
+__global__ __launch_bounds__(256) void verify_write_kernel(
+    const float* __restrict__ q, int64_t nq, uint8_t* __restrict__ q_fp8,
+    float* __restrict__ q_scale, const float* __restrict__ k_new,
+    const int64_t* __restrict__ dst_rows, int T, uint8_t* __restrict__ k_cache,
+    float* __restrict__ k_scale, const uint16_t* __restrict__ latent_new,
+    uint16_t* __restrict__ kv_cache, int nbq, int nbk, float rsqrt_d) {
+  constexpr int LPV = D / 4;
+  const int blk = blockIdx.x;
+  if (blk < nbq + nbk) {
+    const bool is_q = blk < nbq;
+    const int64_t v = (static_cast<int64_t>(is_q ? blk : blk - nbq) * blockDim.x + threadIdx.x) / LPV;
+    const bool live = v < (is_q ? nq : static_cast<int64_t>(T));
+    const int64_t vv = live ? v : 0;
+    if (is_q) {
+      quantize_vector<D>(q + vv * D, live, threadIdx.x % LPV, rsqrt_d, q_fp8 + vv * D, q_scale + vv);
+    } else {
+      const int64_t d = live ? dst_rows[vv] : 0;
+      quantize_vector<D>(k_new + vv * D, live, threadIdx.x % LPV, rsqrt_d, k_cache + d * D,
+                         k_scale + d);
+    }
+    return;
+  }
+  const int64_t u = static_cast<int64_t>(blk - nbq - nbk) * blockDim.x + threadIdx.x;
+  if (u >= static_cast<int64_t>(T) * LATENT_UNITS) return;
+  const int64_t t = u / LATENT_UNITS;
+  const int piece = static_cast<int>(u % LATENT_UNITS);
+  const i32x4 val = reinterpret_cast<const i32x4*>(latent_new + t * LATENT)[piece];
+  reinterpret_cast<i32x4*>(kv_cache + dst_rows[t] * LATENT)[piece] = val;
 }
 
 }  // namespace
@@ -102,4 +152,44 @@ extern "C" dsa_status dsa_quantize_fp8(const float* x, int64_t n_vec, int32_t di
     hipLaunchKernelGGL(quantize_kernel<64>, dim3((unsigned)blocks), dim3(256), 0,
                        as_stream(stream), x, n_vec, rsqrt_d, x_fp8, scale);
   return check_launch("dsa_quantize_fp8");
+}
+
+extern "C" dsa_status dsa_verify_cache_write(const float* k_new, const uint16_t* latent_new,
+                                             const int64_t* dst_rows, int32_t T, int32_t D_I,
+                                             uint8_t* k_cache, float* k_scale, uint16_t* kv_cache,
+                                             const float* q, int32_t H_I, uint8_t* q_fp8,
+                                             float* q_scale, void* stream) {
+  using namespace dsa;
+  DSA_REQUIRE(T >= 0, "dsa_verify_cache_write: T must be >= 0 (got %d)", T);
+  if (D_I != 64 && D_I != 128)
+    return fail(DSA_ERR_UNSUPPORTED, "dsa_verify_cache_write: D_I must be 64 or 128 (got %d)", D_I);
+  if (T == 0) return ok();
+  DSA_REQUIRE(k_new && dst_rows && k_cache && k_scale, "dsa_verify_cache_write: null pointer");
+  DSA_REQUIRE(!latent_new == !kv_cache, "dsa_verify_cache_write: latent_new and kv_cache go together");
+  DSA_REQUIRE(!q || (q_fp8 && q_scale && H_I >= 1),
+              "dsa_verify_cache_write: q needs q_fp8, q_scale and H_I >= 1");
+  DSA_REQUIRE((reinterpret_cast<uintptr_t>(k_new) & 15) == 0 &&
+                  (reinterpret_cast<uintptr_t>(k_cache) & 3) == 0 &&
+                  (!q || ((reinterpret_cast<uintptr_t>(q) & 15) == 0 &&
+                          (reinterpret_cast<uintptr_t>(q_fp8) & 3) == 0)) &&
+                  (!latent_new || ((reinterpret_cast<uintptr_t>(latent_new) & 15) == 0 &&
+                                   (reinterpret_cast<uintptr_t>(kv_cache) & 15) == 0)),
+              "dsa_verify_cache_write: k_new, q, latent rows 16-byte and code arrays 4-byte aligned");
+  const float rsqrt_d = static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(D_I)));
+  const int64_t vec_per_block = 256 / (D_I / 4);
+  const int64_t nq = q ? static_cast<int64_t>(T) * H_I : 0;
+  const int64_t nbq = ceil_div(nq, vec_per_block);
+  const int64_t nbk = ceil_div(T, vec_per_block);
+  const int64_t nbl = latent_new ? ceil_div(static_cast<int64_t>(T) * LATENT_UNITS, 256) : 0;
+  DSA_REQUIRE(nbq + nbk + nbl <= 0x7FFFFFFF, "dsa_verify_cache_write: too many rows");
+  const dim3 grid(static_cast<unsigned>(nbq + nbk + nbl));
+  if (D_I == 128)
+    hipLaunchKernelGGL(verify_write_kernel<128>, grid, dim3(256), 0, as_stream(stream), q, nq, q_fp8,
+                       q_scale, k_new, dst_rows, T, k_cache, k_scale, latent_new, kv_cache,
+                       static_cast<int>(nbq), static_cast<int>(nbk), rsqrt_d);
+  else
+    hipLaunchKernelGGL(verify_write_kernel<64>, grid, dim3(256), 0, as_stream(stream), q, nq, q_fp8,
+                       q_scale, k_new, dst_rows, T, k_cache, k_scale, latent_new, kv_cache,
+                       static_cast<int>(nbq), static_cast<int>(nbk), rsqrt_d);
+  return check_launch("dsa_verify_cache_write");
 }

@@ -33,6 +33,7 @@ COPY_BYTES = 1 << 30  # size of the calibration copy (bench.py --calibrate-copy)
 # kernel-name substring -> (entry key used by bench.py, source file)
 KERNELS = {
     "quantize_kernel": ("quantize_q", "quantize.hip"),
+    "verify_write_kernel": ("cache_write", "quantize.hip"),
     "index_score_kernel": ("index_score", "index_score.hip"),
     "topk_kernel": ("topk", "topk.hip"),
     "mla_decode_kernel": ("sparse_mla", "sparse_mla.hip"),

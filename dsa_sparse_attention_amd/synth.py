@@ -62,6 +62,17 @@ def kv_row_offsets(lengths) -> torch.Tensor:
     return prefix(lengths, torch.int64)
 
 
+def verify_cache_rows(lengths, rows) -> torch.Tensor:
+    """Cache row of each verify row (int64 [sum rows]): row r of request b holds position
+    L_b - R_b + r, i.e. the last R_b positions of the request's cached range."""
+    rs = [rows] * len(lengths) if isinstance(rows, int) else list(rows)
+    out, base = [], 0
+    for L, R in zip(lengths, rs):
+        out.extend(base + L - R + r for r in range(R))
+        base += L
+    return torch.tensor(out, dtype=torch.int64)
+
+
 def indexer_inputs(w: Workload, lengths, device="cpu", rows: int | None = None,
                    seed_offset: int = 0) -> dict:
     """Float32 indexer q [T,H_I,D_I], k [N,D_I] and head weights w [T,H_I]."""

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 2
+#define DSA_ABI_VERSION 3
 
 typedef enum {
   DSA_OK = 0,
@@ -90,6 +90,38 @@ const char* dsa_last_error(void);
  */
 dsa_status dsa_quantize_fp8(const float* x, int64_t n_vec, int32_t dim, uint8_t* x_fp8,
                             float* scale, void* stream);
+
+/*
+ * dsa_verify_cache_write -- the verify step's cache writes, with its query
+ * quantisation, in one launch.
+ * ("GLM-5.3 推理全链路(十四)", the accept/rollback discussion: the verify segment
+ * writes one indexer key per verify row into the indexer cache before the
+ * acceptance decision, and the verify window's latent rows into the MLA cache;
+ * "MAX Pipeline 中的 DeepSeek-V3.2 架构实现解析", "Indexer 的结构与计算流程" and
+ * "配置体系": keys are rotated and quantised like queries, into the indexer K
+ * cache and its fp32 per-token scale cache.)
+ *
+ * For each verify row t < T with cache row d = dst_rows[t]:
+ *   k_cache[d, :], k_scale[d] = dsa_quantize_fp8 of k_new[t, :]
+ *   kv_cache[d, :] = latent_new[t, :]  (576 bf16 copied bit for bit; skipped when
+ *                                      latent_new is NULL)
+ * and, when q is not NULL, q_fp8 / q_scale = dsa_quantize_fp8 of the T*H_I query
+ * vectors q[t, j, :].
+ *   k_new [T, D_I] float32 (16-byte aligned); latent_new [T, 576] bf16 (16-byte
+ *   aligned rows); dst_rows [T] int64 device array (distinct rows, trusted);
+ *   k_cache [N, D_I] u8; k_scale [N] f32; kv_cache [N, 576] bf16;
+ *   q [T, H_I, D_I] float32; q_fp8 [T, H_I, D_I] u8; q_scale [T, H_I] f32.
+ * The caller decides the rows: under the ragged layout of dsa_index_score, row
+ * t = q_off[b] + r is position L_b - R_b + r of request b, cache row
+ * kv_row_offsets[b] + L_b - R_b + r.
+ * Errors: DSA_ERR_INVALID_ARGUMENT (null or misaligned pointers, T < 0, q without
+ * q_fp8/q_scale or H_I < 1), DSA_ERR_UNSUPPORTED (D_I not 64/128).
+ */
+dsa_status dsa_verify_cache_write(const float* k_new, const uint16_t* latent_new,
+                                  const int64_t* dst_rows, int32_t T, int32_t D_I,
+                                  uint8_t* k_cache, float* k_scale, uint16_t* kv_cache,
+                                  const float* q, int32_t H_I, uint8_t* q_fp8, float* q_scale,
+                                  void* stream);
 
 /*
  * dsa_index_score -- lightning-indexer scores of every verify row against

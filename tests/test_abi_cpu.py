@@ -17,7 +17,8 @@ pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
 def test_header_declares_the_four_calls_and_helpers():
     names = set(_lib.header_symbols())
     for n in ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_decode", "greedy_accept",
-              "dsa_quantize_fp8", "dsa_abi_version", "dsa_last_error"):
+              "dsa_quantize_fp8", "dsa_verify_cache_write", "dsa_abi_version",
+              "dsa_last_error"):
         assert n in names
 
 
@@ -30,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_workspace_queries():
     lib = _lib.load()
-    assert lib.dsa_abi_version() == 2
+    assert lib.dsa_abi_version() == 3
     assert lib.dsa_last_error() in (b"", None)
     assert lib.dsa_topk_workspace_size(192, 65536, 2048) == 0
     # 262144-position rows: 4 chunks of 2048 indices, then compact scores and positions

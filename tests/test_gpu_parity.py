@@ -46,6 +46,48 @@ def test_quantize_bitexact(dim):
     assert np.array_equal(scale.cpu().numpy(), rs)
 
 
+@pytest.mark.parametrize("D,H,with_latent,with_q", [(128, 64, True, True), (64, 8, False, True),
+                                                    (128, 16, True, False)])
+def test_verify_cache_write_bitexact(D, H, with_latent, with_q):
+    # the verify rows' keys land quantised (oracle codes and scales) in their cache rows,
+    # their latent rows are copied, the queries are quantised, and no other row changes
+    _say(f"verify_cache_write D={D} H={H} latent={with_latent} q={with_q}")
+    rng = np.random.default_rng(D + H)
+    N, T = 3000, 37
+    dst = np.sort(rng.choice(N, T, replace=False)).astype(np.int64)
+    rng.shuffle(dst)
+    k_new = rng.standard_normal((T, D)).astype(np.float32)
+    k_cache = rng.integers(0, 256, (N, D), dtype=np.uint8)
+    k_scale = rng.random(N).astype(np.float32)
+    d = lambda a: torch.from_numpy(a).to(DEV)
+    kc_d, ks_d = d(k_cache), d(k_scale)
+    lat = kv_d = None
+    if with_latent:
+        lat = torch.randn((T, 576), generator=synth.generator(5)).to(torch.bfloat16)
+        kv = torch.randn((N, 576), generator=synth.generator(6)).to(torch.bfloat16)
+        kv_d = kv.to(DEV)
+    q = qc = qs = None
+    if with_q:
+        q = rng.standard_normal((T, H, D)).astype(np.float32)
+    got_qc, got_qs = api.verify_cache_write(d(k_new), d(dst), kc_d, ks_d,
+                                            latent_new=None if lat is None else lat.to(DEV),
+                                            kv_cache=kv_d, q=None if q is None else d(q))
+    codes, scales = oracle.quantize(k_new)
+    want_c, want_s = k_cache.copy(), k_scale.copy()
+    want_c[dst], want_s[dst] = codes, scales
+    assert np.array_equal(kc_d.cpu().numpy(), want_c)
+    assert np.array_equal(ks_d.cpu().numpy(), want_s)
+    if with_latent:
+        want_kv = kv.clone()
+        want_kv[torch.from_numpy(dst)] = lat
+        assert torch.equal(kv_d.cpu().view(torch.int16), want_kv.view(torch.int16))
+    if with_q:
+        qc, qs = oracle.quantize(q)
+        assert np.array_equal(got_qc.cpu().numpy(), qc) and np.array_equal(got_qs.cpu().numpy(), qs)
+    with pytest.raises(api.DsaError, match="UNSUPPORTED"):
+        api.verify_cache_write(d(k_new[:, :32].copy()), d(dst), kc_d[:, :32].contiguous(), ks_d)
+
+
 # ---------------------------------------------------------------- indexer score
 @pytest.mark.parametrize("name", list(SMALL))
 def test_index_score_within_bound(name):
