@@ -61,6 +61,9 @@ def _load():
         lib.dsa_oracle_sparse_mla_rows.restype = i32
         lib.dsa_oracle_greedy_accept.argtypes = [P, i32, i64, P, i32, i32, i32, P, P, P]
         lib.dsa_oracle_greedy_accept.restype = i32
+        lib.dsa_oracle_rejection_accept.argtypes = [P, i32, i64, P, P, P, P, i32, i32, i32, P, P,
+                                                    P, P]
+        lib.dsa_oracle_rejection_accept.restype = i32
         _lib = lib
     return _lib
 
@@ -222,3 +225,40 @@ def greedy_accept(logits, draft, K: int) -> tuple[np.ndarray, np.ndarray, np.nda
     if rc != 0:
         raise ValueError("oracle greedy_accept: bad arguments")
     return n, nxt, am.reshape(B, K + 1)
+
+
+def rejection_accept(logits, draft_probs, draft, u, us, K: int):
+    """Rejection-sampling acceptance ("GLM-5.3 推理全链路(十四)", "接受判定:greedy 与
+    rejection sampling": keep draft i with probability min(1, p/q); at the first refusal
+    draw the step's token from the corrected distribution max(0, p - q)).
+
+    logits float32 or bfloat16-as-uint16 [B*(K+1), V]; draft_probs float32 [B, K, V];
+    draft int32 [B, K]; u float32 [B, K] and us float32 [B] uniforms in [0, 1).
+    Returns (num_accepted [B], next_token [B], acc_margin [B, K], samp_margin [B]): the
+    margins are the relative distance of each accept decision and of the draw from their
+    boundaries (a float rounding there could flip them).
+    """
+    lib = _load()
+    logits = np.ascontiguousarray(logits)
+    if logits.dtype == np.float32:
+        dtype = 0
+    elif logits.dtype == np.uint16:
+        dtype = 1
+    else:
+        raise TypeError("logits must be float32 or bfloat16 bits (uint16)")
+    rows, V = logits.shape
+    B = rows // (K + 1)
+    dp = _c(draft_probs, np.float32).reshape(B, K, V) if K else np.zeros((B, 0, V), np.float32)
+    dr = _c(draft, np.int32).reshape(B, K) if K else np.zeros((B, 0), np.int32)
+    uu = _c(u, np.float32).reshape(B, K) if K else np.zeros((B, 0), np.float32)
+    us = _c(us, np.float32).reshape(B)
+    n = np.empty(B, np.int32)
+    nxt = np.empty(B, np.int32)
+    am = np.zeros((B, max(K, 1)), np.float64)
+    sm = np.empty(B, np.float64)
+    rc = lib.dsa_oracle_rejection_accept(_p(logits), dtype, V, _p(np.ascontiguousarray(dp)),
+                                         _p(np.ascontiguousarray(dr)), _p(np.ascontiguousarray(uu)),
+                                         _p(us), B, K, V, _p(n), _p(nxt), _p(am), _p(sm))
+    if rc != 0:
+        raise ValueError("oracle rejection_accept: bad arguments")
+    return n, nxt, am[:, :K], sm

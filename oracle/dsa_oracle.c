@@ -1,7 +1,7 @@
 /*
  * dsa_oracle.c -- plain, slow CPU oracle for the DSA sparse-attention
  * verify step (lightning-indexer score -> per-row top-k -> sparse MLA ->
- * greedy acceptance).
+ * greedy acceptance, or rejection-sampling acceptance).
  *
  * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the
  * benchmark's CPU-baseline leg may load this library. It shares no code,
@@ -39,7 +39,9 @@
  *    verify rows) sits at position p = L_b - R_b + r and sees keys 0..p;
  *  - top-k ties go to the lower position; output ascending, -1 padded;
  *  - sparse MLA logits use all 576 dims, values are the first 512;
- *  - greedy: first maximum wins the argmax.
+ *  - greedy: first maximum wins the argmax;
+ *  - rejection sampling: softmax targets, given draft probabilities and
+ *    uniforms, residual max(0, p - q), inverse-CDF draw (see that section).
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC (no fast-math:
  * every float operation below is meant exactly as written).
@@ -365,4 +367,106 @@ ORACLE_API int dsa_oracle_greedy_accept(const void* logits, int dtype, int64_t l
     next_token[b] = a[n];
   }
   return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Rejection-sampling acceptance ([P2] "接受判定:greedy 与 rejection       */
+/* sampling": draft token i is kept with probability min(1, p/q), q the */
+/* draft distribution and p the target's; at the first refused step a   */
+/* token is drawn from the corrected distribution and becomes that      */
+/* step's bonus). Readings (listed in the design notes):                */
+/*  - p_i = softmax of logits row b*(K+1)+i over the V entries, float64; */
+/*  - q_i = draft_probs[b, i, :] as given (float32 probabilities);        */
+/*  - the uniforms are inputs: draft i is kept iff u[b,i] * q_i(x_i) <   */
+/*    p_i(x_i), the event u < min(1, p/q) for u in [0, 1);               */
+/*  - corrected distribution at the first refusal n: w(v) = max(0,      */
+/*    p_n(v) - q_n(v)); when every draft is kept, w = p_K (bonus row);    */
+/*    if w sums to 0, w = p_n;                                           */
+/*  - the token is the smallest v with C(v) > us[b] * C(V-1), C the      */
+/*    running sum of w in index order (inverse CDF).                     */
+/* For the tests, acc_margin[b*K+i] = (p - u*q) / max(p, u*q) of every   */
+/* decision taken (0 where none was), and samp_margin[b] = the distance  */
+/* of us*W to the nearer of C(v-1), C(v) of the drawn v, divided by W.    */
+/* ------------------------------------------------------------------ */
+static double logit_at(const void* logits, int dtype, int64_t idx) {
+  return dtype == 0 ? (double)((const float*)logits)[idx]
+                    : bf16_to_f64(((const uint16_t*)logits)[idx]);
+}
+
+/* p[v] = softmax of one logits row, float64 */
+static void softmax_row(const void* logits, int dtype, int64_t row_start, int V, double* p) {
+  double m = -INFINITY;
+  for (int v = 0; v < V; ++v) {
+    double x = logit_at(logits, dtype, row_start + v);
+    if (x > m) m = x;
+  }
+  double s = 0.0;
+  for (int v = 0; v < V; ++v) {
+    p[v] = exp(logit_at(logits, dtype, row_start + v) - m);
+    s = s + p[v];
+  }
+  for (int v = 0; v < V; ++v) p[v] = p[v] / s;
+}
+
+ORACLE_API int dsa_oracle_rejection_accept(const void* logits, int dtype, int64_t ld,
+                                           const float* draft_probs, const int32_t* draft,
+                                           const float* u, const float* us, int B, int K, int V,
+                                           int32_t* num_accepted, int32_t* next_token,
+                                           double* acc_margin, double* samp_margin) {
+  if ((dtype != 0 && dtype != 1) || V < 1 || K < 0) return -1;
+  double* p = (double*)malloc(sizeof(double) * (size_t)V);
+  double* w = (double*)malloc(sizeof(double) * (size_t)V);
+  if (!p || !w) { free(p); free(w); return -1; }
+  int bad = 0;
+  for (int b = 0; b < B && !bad; ++b) {
+    int n = 0;
+    for (; n < K; ++n) {
+      const int64_t row = (int64_t)b * (K + 1) + n;
+      const int32_t x = draft[(int64_t)b * K + n];
+      if (x < 0 || x >= V) { bad = 1; break; }
+      softmax_row(logits, dtype, row * ld, V, p);
+      const double pq = p[x];
+      const double uq = (double)u[(int64_t)b * K + n] *
+                        (double)draft_probs[((int64_t)b * K + n) * V + x];
+      const double big = pq > uq ? pq : uq;
+      if (acc_margin) acc_margin[(int64_t)b * K + n] = big > 0.0 ? (pq - uq) / big : 0.0;
+      if (!(uq < pq)) break;  /* refused */
+    }
+    if (bad) break;
+    for (int i = n + 1; i < K && acc_margin; ++i) acc_margin[(int64_t)b * K + i] = 0.0;
+    const int64_t row = (int64_t)b * (K + 1) + n;
+    softmax_row(logits, dtype, row * ld, V, p);
+    double W = 0.0;
+    for (int v = 0; v < V; ++v) {
+      double d = n < K ? p[v] - (double)draft_probs[((int64_t)b * K + n) * V + v] : p[v];
+      w[v] = d > 0.0 ? d : 0.0;
+      W = W + w[v];
+    }
+    if (!(W > 0.0)) {
+      W = 0.0;
+      for (int v = 0; v < V; ++v) { w[v] = p[v]; W = W + w[v]; }
+    }
+    const double target = (double)us[b] * W;
+    double c = 0.0, prev = 0.0;
+    int tok = -1;
+    for (int v = 0; v < V; ++v) {
+      prev = c;
+      c = c + w[v];
+      if (c > target) { tok = v; break; }
+    }
+    if (tok < 0) { /* rounding left target at or above the total: the last positive entry */
+      for (int v = V - 1; v >= 0; --v)
+        if (w[v] > 0.0) { tok = v; break; }
+      prev = c - w[tok];
+    }
+    num_accepted[b] = n;
+    next_token[b] = tok;
+    if (samp_margin) {
+      double d0 = target - prev, d1 = c - target;
+      samp_margin[b] = (d0 < d1 ? d0 : d1) / W;
+    }
+  }
+  free(p);
+  free(w);
+  return bad ? -1 : 0;
 }
