@@ -239,3 +239,40 @@ def greedy_accept(logits, draft, K: int, argmax: bool = True, workspace=None):
     _check(lib.greedy_accept(_p(logits), dt, V, _p(draft) if K else None, B, K, V, _p(n), _p(nxt),
                              _p(am), _p(workspace), wsb, _stream()))
     return n, nxt, am
+
+
+def rejection_accept(logits, draft_probs, draft, u, us, K: int, workspace=None):
+    """Rejection-sampling acceptance: (num_accepted [B], next_token [B])."""
+    if not isinstance(logits, torch.Tensor) or not logits.is_cuda or not logits.is_contiguous():
+        raise TypeError("logits must be a contiguous CUDA tensor")
+    if logits.dtype == torch.float32:
+        dt = DSA_F32
+    elif logits.dtype == torch.bfloat16:
+        dt = DSA_BF16
+    else:
+        raise TypeError("logits must be float32 or bfloat16")
+    rows, V = logits.shape
+    B = rows // (K + 1)
+    if B * (K + 1) != rows:
+        raise ValueError("logits rows must be B*(K+1)")
+    _dev(us, "us", torch.float32)
+    if K:
+        _dev(draft_probs, "draft_probs", torch.float32)
+        _dev(draft, "draft", torch.int32)
+        _dev(u, "u", torch.float32)
+        if draft_probs.numel() != B * K * V or draft.numel() != B * K or u.numel() != B * K:
+            raise ValueError("draft_probs [B,K,V], draft [B,K] and u [B,K] must match the logits")
+    if us.numel() != B:
+        raise ValueError("us must hold B uniforms")
+    dev = logits.device
+    n = torch.empty(B, dtype=torch.int32, device=dev)
+    nxt = torch.empty(B, dtype=torch.int32, device=dev)
+    lib = _lib.load()
+    need = lib.rejection_accept_workspace_size(B, K, V)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=dev)
+    wsb = workspace.numel() * workspace.element_size()
+    _check(lib.rejection_accept(_p(logits), dt, V, _p(draft_probs) if K else None,
+                                _p(draft) if K else None, _p(u) if K else None, _p(us), B, K, V,
+                                _p(n), _p(nxt), _p(workspace), wsb, _stream()))
+    return n, nxt

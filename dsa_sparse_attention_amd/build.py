@@ -20,6 +20,7 @@ LIB = os.path.join(PKG, "libdsa.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["abi.cpp", "quantize.hip", "index_score.hip", "topk.hip", "sparse_mla.hip",
+           "rejection_accept.hip",
            "greedy_accept.hip"]
 
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -164,6 +164,30 @@ def accept_inputs(w: Workload, device="cpu") -> dict:
     return dict(logits=logits, draft=draft.to(device), planted_n=n)
 
 
+def rejection_inputs(w: Workload, device="cpu", draft_noise: float = 1.0,
+                     seed_offset: int = 0) -> dict:
+    """Inputs of rejection-sampling acceptance: target logits [B*(K+1), V] (f32 or bf16,
+    ~N(0, logits_std^2)); the draft model's probabilities [B, K, V] float32, taken as the
+    normalised exponential of the target row plus N(0, draft_noise^2) noise (a draft law
+    close to the target's, as a trained draft layer gives); the draft tokens drawn from
+    those probabilities; the uniforms u [B, K] and us [B]."""
+    K, B, V = w.drafts, w.batch, w.vocab
+    g = generator(w.seed * 1000 + 71 + seed_offset, device)
+    dt = torch.float32 if w.logits_dtype == "f32" else torch.bfloat16
+    logits = (w.logits_std * torch.randn((B * (K + 1), V), generator=g, device=device)).to(dt)
+    tgt = logits.float().view(B, K + 1, V)[:, :K]
+    z = tgt + draft_noise * torch.randn((B, K, V), generator=g, device=device)
+    z = torch.exp(z - z.amax(dim=-1, keepdim=True))
+    probs = (z / z.sum(dim=-1, keepdim=True)).float().contiguous()
+    # draft tokens: inverse CDF of the draft law (float64 running sums)
+    c = probs.double().cumsum(dim=-1)
+    pick = torch.rand((B, K, 1), generator=g, device=device, dtype=torch.float64) * c[..., -1:]
+    draft = torch.searchsorted(c, pick, right=True).clamp_(max=V - 1).view(B, K).to(torch.int32)
+    u = torch.rand((B, K), generator=g, device=device)
+    us = torch.rand(B, generator=g, device=device)
+    return dict(logits=logits, draft_probs=probs, draft=draft.contiguous(), u=u, us=us)
+
+
 def random_topk(w: Workload, lengths, q_off, k: int, device="cpu", pad_frac: float = 0.0,
                 seed_offset: int = 0) -> torch.Tensor:
     """Random ascending sets of distinct visible positions per row, -1 padded."""

@@ -264,6 +264,35 @@ dsa_status greedy_accept(const void* logits, int32_t dtype, int64_t logits_ld,
 
 size_t greedy_accept_workspace_size(int32_t B, int32_t K, int32_t V);
 
+/*
+ * rejection_accept -- acceptance of a chain of K drafts per request by rejection
+ * sampling.
+ * ("GLM-5.3 推理全链路(十四)", "接受判定:greedy 与 rejection sampling": draft i is kept
+ * with probability min(1, p/q), q the draft distribution and p the target's; at the
+ * first refused step a token is drawn from the corrected distribution as that step's
+ * bonus.)
+ *
+ * With p_i = softmax(logits row b*(K+1)+i) over V and the uniforms as inputs:
+ *   draft i is kept iff u[b,i] * draft_probs[b,i,x_i] < p_i(x_i), x_i = draft[b,i]
+ *   num_accepted[b] = n = the first refused i (K when none is refused)
+ *   w(v) = max(0, p_n(v) - draft_probs[b,n,v]) if n < K, else p_K(v); w = p_n if it
+ *          sums to 0
+ *   next_token[b] = the smallest v with C(v) > us[b] * C(V-1), C the running sum of w
+ *   logits [B*(K+1), logits_ld] float32 or bf16 (dtype); draft_probs [B, K, V] float32;
+ *   draft [B, K] int32; u [B, K] and us [B] float32 in [0, 1).
+ * Probabilities and sums are taken in float64 except the exponentials of the softmax
+ * denominators (float32, summed in float64). A draft outside [0, V) counts as refused.
+ * Workspace: rejection_accept_workspace_size() bytes, 8-byte aligned.
+ * Errors: DSA_ERR_INVALID_ARGUMENT, DSA_ERR_WORKSPACE_TOO_SMALL.
+ */
+dsa_status rejection_accept(const void* logits, int32_t dtype, int64_t logits_ld,
+                            const float* draft_probs, const int32_t* draft, const float* u,
+                            const float* us, int32_t B, int32_t K, int32_t V,
+                            int32_t* num_accepted, int32_t* next_token, void* ws, size_t ws_bytes,
+                            void* stream);
+
+size_t rejection_accept_workspace_size(int32_t B, int32_t K, int32_t V);
+
 #ifdef __cplusplus
 }
 #endif

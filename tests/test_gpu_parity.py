@@ -3,7 +3,9 @@
 Bars: quantised codes/scales, top-k sets on shared fp32 scores, accepted lengths and
 argmaxes are bit-exact; indexer scores lie within the bound derived from the FP8 MFMA
 and float32 epilogue arithmetic; end-to-end top-k sets are equal or differ only inside
-that bound around the k-th score; sparse MLA meets max|d| <= 2e-2*max|o| + 1e-2*|o|.
+that bound around the k-th score; sparse MLA meets max|d| <= 2e-2*max|o| + 1e-2*|o|;
+rejection-sampling acceptance equals the oracle wherever no decision or draw sits within
+float rounding of its boundary, and is one of the oracle's nudged outcomes where one does.
 """
 import math
 
@@ -443,3 +445,42 @@ def test_abi_rejects_bad_arguments_before_launch():
     with pytest.raises(api.DsaError, match="WORKSPACE"):
         api.greedy_accept(lg, torch.zeros((2, 1), dtype=torch.int32, device=DEV), 1,
                           workspace=torch.zeros(4, dtype=torch.uint8, device=DEV))
+
+
+# ---------------------------------------------------------------- rejection-sampling accept
+def _rejection_candidates(lg, dp, draft, u, us, K, eps_u=1e-5, eps_s=2e-6):
+    """Oracle results under relative nudges of the uniforms: a decision or a draw that a
+    nudge flips sits within float rounding of its boundary, where either side is right."""
+    outs = []
+    for su in (-1, 0, 1):
+        for ss in (-1, 0, 1):
+            uu = np.clip(u.astype(np.float64) * (1 + su * eps_u), 0, 1).astype(np.float32)
+            sv = np.clip(us.astype(np.float64) * (1 + ss * eps_s), 0, 0.99999994).astype(np.float32)
+            n, nxt, _, _ = oracle.rejection_accept(lg, dp, draft, uu, sv, K)
+            outs.append((n, nxt))
+    return outs
+
+
+@pytest.mark.parametrize("name,batch,vocab,K,noise", [("f32", 7, 5000, 4, 1.0), ("bf16", 32, 151552, 5, 1.0),
+                                                      ("bf16", 16, 151552, 5, 0.3)])
+def test_rejection_accept_matches_oracle(name, batch, vocab, K, noise):
+    _say(f"rejection_accept {name} B={batch} V={vocab} K={K}")
+    w = W.scaled(W.MTP5_VERIFY if name == "bf16" else W.TINY, ctx=4096, batch=batch, vocab=vocab,
+                 rows=K + 1, logits_dtype="f32" if name == "f32" else "bf16")
+    d = synth.rejection_inputs(w, draft_noise=noise)
+    g = {k: v.to(DEV) for k, v in d.items()}
+    n, nxt = api.rejection_accept(g["logits"], g["draft_probs"], g["draft"], g["u"], g["us"], K)
+    n, nxt = n.cpu().numpy(), nxt.cpu().numpy()
+    lg = d["logits"].numpy() if name == "f32" else d["logits"].view(torch.int16).numpy().view(np.uint16)
+    args = (d["draft_probs"].numpy(), d["draft"].numpy(), d["u"].numpy(), d["us"].numpy())
+    rn, rnx, _, _ = oracle.rejection_accept(lg, *args, K)
+    cands = _rejection_candidates(lg, *args, K)
+    strict = 0
+    for b in range(batch):
+        options = {(int(cn[b]), int(cx[b])) for cn, cx in cands}
+        assert (int(n[b]), int(nxt[b])) in options, f"request {b}: {n[b], nxt[b]} not in {options}"
+        if len(options) == 1:
+            strict += 1
+            assert n[b] == rn[b] and nxt[b] == rnx[b]
+    _say(f"  {strict}/{batch} requests away from every float boundary; mean accepted {n.mean():.2f}")
+    assert strict >= batch // 2
