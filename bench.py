@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--accept", choices=("greedy", "rejection"), default="greedy",
+                    help="acceptance rule of the step: greedy argmax prefix, or rejection "
+                         "sampling against a draft law (uniforms drawn per step copy)")
     ap.add_argument("--refine", action="store_true",
                     help="top-k with the exact-boundary refine (float64 rescore of the band)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -68,6 +71,8 @@ def calibrate_copy():
 class Inputs:
     """One resident copy of the step's inputs (device tensors)."""
 
+    rejection = False  # also draw rejection-sampling inputs (bench --accept rejection)
+
     def __init__(self, w, lengths, copy: int):
         import torch
 
@@ -92,6 +97,7 @@ class Inputs:
             self.q_draft = [synth.mla_inputs(w, lengths, device=dev, rows=1,
                                              seed_offset=100 * (copy + 1) + j, kv=self.kv)["q"]
                             for j in range(w.share_steps)]
+        self.rej = synth.rejection_inputs(w, device=dev, seed_offset=copy) if Inputs.rejection else None
         a = synth.accept_inputs(w, device=dev) if copy == 0 else None
         if a is None:
             a = Inputs.accept_cache
@@ -133,6 +139,12 @@ def cpu_baseline(w, lengths, inp0, target_s: float):
     L = lengths[0]
     kf = inp0.k_f32_sample.numpy()
     kv_host = inp0.kv[:L].view(__import__("torch").uint16).cpu().numpy()
+    rej_host = None
+    if inp0.rej is not None:
+        t = __import__("torch")
+        rl = inp0.rej["logits"]
+        rej_host = {k: v.cpu().numpy() for k, v in inp0.rej.items() if k != "logits"}
+        rej_host["logits"] = (rl.view(t.uint16) if rl.dtype == t.bfloat16 else rl).cpu().numpy()
     done_rows, t_total = 0, 0.0
     b = 0
     while b < w.batch and (t_total < target_s or b == 0):
@@ -151,14 +163,20 @@ def cpu_baseline(w, lengths, inp0, target_s: float):
         nvis = np.array([L - w.rows + r + 1 for r in range(w.rows)])
         tk = oracle.topk(sc, nvis, w.topk)
         oracle.sparse_mla(qm, kv_host, tk, qo1, ko1, w.sm_scale)
-        oracle.greedy_accept(lg, draft[b:b + 1], w.drafts)
+        if inp0.rej is None:
+            oracle.greedy_accept(lg, draft[b:b + 1], w.drafts)
+        else:
+            r = rej_host
+            oracle.rejection_accept(r["logits"][rows], r["draft_probs"][b:b + 1], r["draft"][b:b + 1],
+                                    r["u"][b:b + 1], r["us"][b:b + 1], w.drafts)
         t_total += time.perf_counter() - t0
         done_rows += w.rows
         b += 1
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": done_rows / t_total, "unit": "rows/s", "cores": threads, "kind": "oracle",
             "sample": f"{b} request(s) x {w.rows} rows at context {L}: quantise, index score, "
-                      f"top-k, sparse MLA, greedy accept ({t_total:.1f} s)"}
+                      f"top-k, sparse MLA, {'greedy' if inp0.rej is None else 'rejection-sampling'} "
+                      f"accept ({t_total:.1f} s)"}
 
 
 def main():
@@ -183,6 +201,7 @@ def main():
     dev = "cuda"
     print(f"[bench] workload {w.name}: B={w.batch} ctx={max_kv} rows={w.rows} T={T}", file=sys.stderr,
           flush=True)
+    Inputs.rejection = args.accept == "rejection"
     copies = [Inputs(w, lengths, c) for c in range(args.copies)]
     qo = synth.q_row_offsets(w).to(dev)
     ko = synth.kv_row_offsets(lengths).to(dev)
@@ -200,10 +219,13 @@ def main():
     ws_tk = torch.empty(max(tk_need, 16), dtype=torch.uint8, device=dev)
     ga_need = _lib.load().greedy_accept_workspace_size(w.batch, w.drafts, w.vocab)
     ws_ga = torch.empty(max(ga_need, 16), dtype=torch.uint8, device=dev)
+    ra_need = _lib.load().rejection_accept_workspace_size(w.batch, w.drafts, w.vocab)
+    ws_ra = torch.empty(max(ra_need, 16), dtype=torch.uint8, device=dev)
     print(f"[bench] inputs resident ({args.copies} copies); mla workspace {ws_need/1e6:.1f} MB",
           file=sys.stderr, flush=True)
 
-    names = ["cache_write", "index_score", "topk", "sparse_mla", "greedy_accept"]
+    acc_name = "greedy_accept" if args.accept == "greedy" else "rejection_accept"
+    names = ["cache_write", "index_score", "topk", "sparse_mla", acc_name]
     if w.share_steps:
         names.append("share_mla")
         qo1 = torch.arange(w.batch + 1, dtype=torch.int32, device=dev)
@@ -228,7 +250,12 @@ def main():
         api.sparse_mla_decode(inp.q_mla, inp.kv, topk, qo, ko, w.rows, w.sm_scale, out=out, lse=lse,
                               workspace=ws_mla)
         if ev: ev[4].record(stream)
-        api.greedy_accept(inp.logits, inp.draft, w.drafts, argmax=False, workspace=ws_ga)
+        if inp.rej is None:
+            api.greedy_accept(inp.logits, inp.draft, w.drafts, argmax=False, workspace=ws_ga)
+        else:
+            r = inp.rej
+            api.rejection_accept(r["logits"], r["draft_probs"], r["draft"], r["u"], r["us"],
+                                 w.drafts, workspace=ws_ra)
         if ev: ev[5].record(stream)
         for qd in inp.q_draft or []:  # draft steps: the step-0 top-k row at the accepted position
             api.sparse_mla_decode(qd, inp.kv, topk, qo1, ko, 1, w.sm_scale, out=out1, lse=lse1,
@@ -275,14 +302,16 @@ def main():
     wi = accounting.index_score_work(lengths, w.rows, w.index_heads, w.index_dim)
     wt = accounting.topk_work(lengths, w.rows, w.topk)
     wm = accounting.sparse_mla_work(T, w.mla_heads, w.topk)
-    wg = accounting.greedy_accept_work(w.batch, w.drafts, w.vocab, 2)
+    wg = (accounting.greedy_accept_work if args.accept == "greedy" else
+          accounting.rejection_accept_work)(w.batch, w.drafts, w.vocab, 2)
     wq = dict(bytes=T * (w.index_heads + 1) * (w.index_dim * 4 + w.index_dim + 4) + T * 2 * 1152)
     kern = {
         "cache_write": dict(bytes=wq["bytes"], bound="hbm", file="quantize.hip"),
         "index_score": dict(bytes=wi["bytes"], flops=wi["flops"], bound="mfma", file="index_score.hip"),
         "topk": dict(bytes=wt["bytes"], bound="hbm", file="topk.hip"),
         "sparse_mla": dict(bytes=wm["bytes"], flops=wm["flops"], bound="hbm", file="sparse_mla.hip"),
-        "greedy_accept": dict(bytes=wg["bytes"], bound="hbm", file="greedy_accept.hip"),
+        acc_name: dict(bytes=wg["bytes"], bound="hbm",
+                       file="greedy_accept.hip" if args.accept == "greedy" else "rejection_accept.hip"),
     }
     if w.share_steps:
         ws_ = accounting.sparse_mla_work(w.batch, w.mla_heads, w.topk)
@@ -324,6 +353,7 @@ def main():
                    "index_heads": w.index_heads, "index_dim": w.index_dim, "topk": w.topk,
                    "mla_heads": w.mla_heads, "vocab": w.vocab, "global_batch": rows_step,
                    "seq_len": max_kv, "share_steps": w.share_steps, "topk_refine": args.refine,
+                   "accept": args.accept,
                    "parallelism": "single-gpu"},
         "step_includes": names,
         "rows_per_s_indexer_topk_mla": round(T / ((per["index_score"] + per["topk"] +

@@ -71,3 +71,11 @@ def sparse_mla_work(n_rows: int, heads: int, k: int, selected_per_row=None) -> d
 def greedy_accept_work(batch: int, drafts: int, vocab: int, elem_bytes: int) -> dict:
     rows = batch * (drafts + 1)
     return dict(bytes=rows * vocab * elem_bytes + batch * drafts * 4 + batch * 8, flops=0)
+
+
+def rejection_accept_work(batch: int, drafts: int, vocab: int, elem_bytes: int) -> dict:
+    """Every logits row once (softmax statistics), and the draft law of each request's
+    drawing row once (the corrected weights); the drafts, uniforms and outputs."""
+    rows = batch * (drafts + 1)
+    return dict(bytes=rows * vocab * elem_bytes + batch * vocab * 4 + batch * drafts * 12 +
+                batch * 12, flops=0)

@@ -13,12 +13,14 @@
 //   next_token[b] = the smallest v with C(v) > us[b] * C(V-1), C the running sum of w.
 //
 // Four launches, HBM-bound (the logits are read once in full, the draw's row twice):
-//  1. stats: per (row, 4096-entry slice), the slice maximum m and sum_v exp(l_v - m)
-//     (float32 exponentials summed in float64);
-//  2. decide: one wave per request merges the slices of each row it needs (float64) and
-//     takes the accept decisions in float64, stopping at the first refusal;
+//  1. stats: per (row, 16384-entry slice, 16-byte loads), the slice maximum m and
+//     sum_v exp(l_v - m): per-thread pairs merged in one block reduction (float32
+//     exponentials, float64 sums);
+//  2. decide: one block per request, wave i merging the slices of row i (float64) and
+//     testing draft i; the first refusal ends the chain;
 //  3. weights: per (request, slice) of the drawing row, the sums of w (and of p, for the
-//     fallback) in float64, with p(v) = exp(l_v - M) / S in float64;
+//     fallback) in float64, with p(v) = exp(l_v - M) / S (float32 exponential of the
+//     exact float32 difference, float64 division);
 //  4. draw: one block per request finds the slice holding us * W, then the entry inside
 //     it by a block scan in float64.
 #include "common.hpp"
@@ -27,8 +29,8 @@ namespace dsa {
 namespace {
 
 constexpr int RA_THREADS = 256;
-constexpr int RA_SLICE = 4096;                  // vocabulary entries per block
-constexpr int RA_PER = RA_SLICE / RA_THREADS;   // entries per thread (16)
+constexpr int RA_SLICE = 16384;                 // vocabulary entries per block
+constexpr int RA_PER = RA_SLICE / RA_THREADS;   // entries per thread (64)
 
 template <bool BF16>
 __device__ __forceinline__ float logit(const void* lg, int64_t idx) {
@@ -49,46 +51,90 @@ __device__ __forceinline__ double block_sum_d(double x, double* red) {
   return s;
 }
 
-__device__ __forceinline__ float block_max_f(float x, float* red) {
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  const int wave = threadIdx.x / 64;
-  if (threadIdx.x % 64 == 0) red[wave] = x;
-  __syncthreads();
-  float m = red[0];
-  for (int w = 1; w < RA_THREADS / 64; ++w) m = fmaxf(m, red[w]);
-  __syncthreads();
-  return m;
+// This thread's RA_PER consecutive-in-groups entries of a slice: 16-byte loads of 8 bf16
+// (or 4 float32) at units threadIdx.x + j * RA_THREADS; entries past V read as -inf.
+template <bool BF16>
+__device__ __forceinline__ void load_slice(const void* lg, int64_t row_start, int v0, int V,
+                                           float (&x)[RA_PER]) {
+  constexpr int E = BF16 ? 8 : 4;  // entries per 16-byte unit
+  constexpr int EB = BF16 ? 2 : 4;  // bytes per entry
+  if (v0 + RA_SLICE <= V && (row_start * EB) % 16 == 0) {  // block-uniform: every load issued
+    const i32x4* src = reinterpret_cast<const i32x4*>(static_cast<const uint8_t*>(lg) +
+                                                      (row_start + v0) * EB);
+    i32x4 d[RA_PER / E];
+#pragma unroll
+    for (int j = 0; j < RA_PER / E; ++j) d[j] = src[j * RA_THREADS + threadIdx.x];
+#pragma unroll
+    for (int j = 0; j < RA_PER / E; ++j)
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const uint32_t wd = static_cast<uint32_t>(d[j][BF16 ? e / 2 : e]);
+        x[j * E + e] = BF16 ? __uint_as_float((e & 1) ? (wd & 0xFFFF0000u) : (wd << 16))
+                            : __uint_as_float(wd);
+      }
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < RA_PER / E; ++j) {
+    const int v = v0 + (j * RA_THREADS + static_cast<int>(threadIdx.x)) * E;
+    if (v + E <= V && ((row_start + v) * (BF16 ? 2 : 4)) % 16 == 0) {
+      const i32x4 d = reinterpret_cast<const i32x4*>(
+          static_cast<const uint8_t*>(lg) + (row_start + v) * (BF16 ? 2 : 4))[0];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const uint32_t wd = static_cast<uint32_t>(d[BF16 ? e / 2 : e]);
+        x[j * E + e] = BF16 ? __uint_as_float((e & 1) ? (wd & 0xFFFF0000u) : (wd << 16))
+                            : __uint_as_float(wd);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        x[j * E + e] = v + e < V ? logit<BF16>(lg, row_start + v + e) : -INFINITY;
+    }
+  }
 }
 
-// 1. slice statistics of every logits row
+// (m, s) pairs merged to the larger reference: s = s1 e^(m1-M) + s2 e^(m2-M)
+__device__ __forceinline__ void merge_ms(float& m, double& sum, float m2, double s2) {
+  const float M = fmaxf(m, m2);
+  if (M == -INFINITY) return;
+  sum = sum * static_cast<double>(expf(m - M)) + s2 * static_cast<double>(expf(m2 - M));
+  m = M;
+}
+
+// 1. slice statistics of every logits row: per thread (max, sum of exponentials below it),
+// merged over the block in one reduction
 template <bool BF16>
 __global__ __launch_bounds__(RA_THREADS) void ra_stats_kernel(const void* __restrict__ logits,
                                                               int64_t ld, int V, int nslice,
                                                               float* __restrict__ ws_m,
                                                               double* __restrict__ ws_s) {
-  __shared__ float redf[RA_THREADS / 64];
-  __shared__ double redd[RA_THREADS / 64];
+  __shared__ float redm[RA_THREADS / 64];
+  __shared__ double reds[RA_THREADS / 64];
   const int slice = blockIdx.x;
   const int64_t row = blockIdx.y;
-  const int v0 = slice * RA_SLICE;
   float x[RA_PER];
+  load_slice<BF16>(logits, row * ld, slice * RA_SLICE, V, x);
   float m = -INFINITY;
 #pragma unroll
-  for (int e = 0; e < RA_PER; ++e) {
-    const int v = v0 + e * RA_THREADS + threadIdx.x;
-    x[e] = v < V ? logit<BF16>(logits, row * ld + v) : -INFINITY;
-    m = fmaxf(m, x[e]);
-  }
-  m = block_max_f(m, redf);
-  double s = 0.0;
+  for (int e = 0; e < RA_PER; ++e) m = fmaxf(m, x[e]);
+  double sum = 0.0;
   if (m > -INFINITY) {
 #pragma unroll
-    for (int e = 0; e < RA_PER; ++e) s += static_cast<double>(expf(x[e] - m));
+    for (int e = 0; e < RA_PER; ++e) sum += static_cast<double>(expf(x[e] - m));
   }
-  s = block_sum_d(s, redd);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) merge_ms(m, sum, __shfl_xor(m, o), __shfl_xor(sum, o));
+  const int wave = threadIdx.x / 64;
+  if (threadIdx.x % 64 == 0) {
+    redm[wave] = m;
+    reds[wave] = sum;
+  }
+  __syncthreads();
   if (threadIdx.x == 0) {
+    for (int w = 1; w < RA_THREADS / 64; ++w) merge_ms(m, sum, redm[w], reds[w]);
     ws_m[row * nslice + slice] = m;
-    ws_s[row * nslice + slice] = s;
+    ws_s[row * nslice + slice] = sum;
   }
 }
 
@@ -109,49 +155,124 @@ __device__ __forceinline__ void row_stats(const float* ws_m, const double* ws_s,
   *S = s;
 }
 
-// 2. accept decisions, one wave per request; writes n and the drawing row's (M, S)
+// 2. accept decisions: wave i of the request's block takes row i (its (M, S) and, for
+// i < K, p_i(x_i)); wave 0 then walks the decisions up to the first refusal
 template <bool BF16>
-__global__ __launch_bounds__(64) void ra_decide_kernel(
+__global__ __launch_bounds__(1024) void ra_decide_kernel(
     const void* __restrict__ logits, int64_t ld, const float* __restrict__ draft_probs,
     const int32_t* __restrict__ draft, const float* __restrict__ u, int K, int V, int nslice,
     const float* __restrict__ ws_m, const double* __restrict__ ws_s, int32_t* __restrict__ ws_n,
     double* __restrict__ ws_ms, int32_t* __restrict__ num_accepted) {
+  __shared__ double rm[64], rs[64];
+  __shared__ int keep[64];
   const int b = blockIdx.x;
-  int n = 0;
-  double M = 0.0, S = 0.0;
-  for (; n < K; ++n) {
-    const int64_t row = static_cast<int64_t>(b) * (K + 1) + n;
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  for (int i = wave; i <= K; i += blockDim.x / 64) {
+    const int64_t row = static_cast<int64_t>(b) * (K + 1) + i;
+    double M, S;
     row_stats(ws_m, ws_s, row, nslice, &M, &S);
-    const int32_t x = draft[static_cast<int64_t>(b) * K + n];
-    if (x < 0 || x >= V) break;  // an out-of-range draft is refused
-    const double p = exp(static_cast<double>(logit<BF16>(logits, row * ld + x)) - M) / S;
-    const double uq = static_cast<double>(u[static_cast<int64_t>(b) * K + n]) *
-                      static_cast<double>(draft_probs[(static_cast<int64_t>(b) * K + n) * V + x]);
-    if (!(uq < p)) break;
+    int kept = 0;
+    if (i < K) {
+      const int32_t x = draft[static_cast<int64_t>(b) * K + i];
+      if (x >= 0 && x < V) {  // an out-of-range draft is refused
+        const double p = exp(static_cast<double>(logit<BF16>(logits, row * ld + x)) - M) / S;
+        const double uq = static_cast<double>(u[static_cast<int64_t>(b) * K + i]) *
+                          static_cast<double>(draft_probs[(static_cast<int64_t>(b) * K + i) * V + x]);
+        kept = uq < p;
+      }
+    }
+    if (lane == 0) {
+      rm[i] = M;
+      rs[i] = S;
+      keep[i] = kept;
+    }
   }
-  if (n == K) row_stats(ws_m, ws_s, static_cast<int64_t>(b) * (K + 1) + K, nslice, &M, &S);
+  __syncthreads();
   if (threadIdx.x == 0) {
+    int n = 0;
+    while (n < K && keep[n]) ++n;
     ws_n[b] = n;
-    ws_ms[2 * b] = M;
-    ws_ms[2 * b + 1] = S;
+    ws_ms[2 * b] = rm[n];
+    ws_ms[2 * b + 1] = rs[n];
     num_accepted[b] = n;
   }
 }
 
-// w(v) of the drawing row: corrected (rw) or target (pv) probability
-template <bool BF16>
-__device__ __forceinline__ void weights_at(const void* logits, int64_t ld, const float* draft_probs,
-                                           int b, int n, int K, int V, double M, double S, int v,
-                                           double* rw, double* pv) {
-  const int64_t row = static_cast<int64_t>(b) * (K + 1) + n;
-  const double p = v < V ? exp(static_cast<double>(logit<BF16>(logits, row * ld + v)) - M) / S : 0.0;
-  double r = p;
-  if (n < K && v < V) {
-    const double d = p - static_cast<double>(draft_probs[(static_cast<int64_t>(b) * K + n) * V + v]);
-    r = d > 0.0 ? d : 0.0;
+// N consecutive draft probabilities from v_begin (16-byte loads when aligned; 0 past V)
+template <int N>
+__device__ __forceinline__ void load_q_run(const float* qrow, int v_begin, int V, float (&q)[N]) {
+  if (v_begin + N <= V && (reinterpret_cast<uintptr_t>(qrow + v_begin) & 15) == 0) {
+    float4 d[N / 4];
+#pragma unroll
+    for (int j = 0; j < N / 4; ++j) d[j] = reinterpret_cast<const float4*>(qrow + v_begin)[j];
+#pragma unroll
+    for (int j = 0; j < N / 4; ++j) {
+      q[4 * j] = d[j].x; q[4 * j + 1] = d[j].y; q[4 * j + 2] = d[j].z; q[4 * j + 3] = d[j].w;
+    }
+    return;
   }
-  *rw = r;
+#pragma unroll
+  for (int j = 0; j < N / 4; ++j) {
+    const int v = v_begin + 4 * j;
+    if (v + 4 <= V && (reinterpret_cast<uintptr_t>(qrow + v) & 15) == 0) {
+      const float4 d = *reinterpret_cast<const float4*>(qrow + v);
+      q[4 * j] = d.x; q[4 * j + 1] = d.y; q[4 * j + 2] = d.z; q[4 * j + 3] = d.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) q[4 * j + e] = v + e < V ? qrow[v + e] : 0.0f;
+    }
+  }
+}
+
+// N consecutive logits from v_begin (16-byte loads when aligned; -inf past V)
+template <bool BF16, int N>
+__device__ __forceinline__ void load_run(const void* lg, int64_t row_start, int v_begin, int V,
+                                         float (&x)[N]) {
+  constexpr int E = BF16 ? 8 : 4;
+  constexpr int EB = BF16 ? 2 : 4;
+  if (v_begin + N <= V && ((row_start + v_begin) * EB) % 16 == 0) {  // every load issued first
+    const i32x4* src = reinterpret_cast<const i32x4*>(static_cast<const uint8_t*>(lg) +
+                                                      (row_start + v_begin) * EB);
+    i32x4 d[N / E];
+#pragma unroll
+    for (int j = 0; j < N / E; ++j) d[j] = src[j];
+#pragma unroll
+    for (int j = 0; j < N / E; ++j)
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const uint32_t wd = static_cast<uint32_t>(d[j][BF16 ? e / 2 : e]);
+        x[j * E + e] = BF16 ? __uint_as_float((e & 1) ? (wd & 0xFFFF0000u) : (wd << 16))
+                            : __uint_as_float(wd);
+      }
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < N / E; ++j) {
+    const int v = v_begin + E * j;
+    if (v + E <= V && ((row_start + v) * (BF16 ? 2 : 4)) % 16 == 0) {
+      const i32x4 d = reinterpret_cast<const i32x4*>(
+          static_cast<const uint8_t*>(lg) + (row_start + v) * (BF16 ? 2 : 4))[0];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const uint32_t wd = static_cast<uint32_t>(d[BF16 ? e / 2 : e]);
+        x[j * E + e] = BF16 ? __uint_as_float((e & 1) ? (wd & 0xFFFF0000u) : (wd << 16))
+                            : __uint_as_float(wd);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[j * E + e] = v + e < V ? logit<BF16>(lg, row_start + v + e) : -INFINITY;
+    }
+  }
+}
+
+// p(v) and the corrected weight of one entry: l - M is exact in float32 (M is a float32
+// logit); one float32 exponential, then float64 arithmetic
+__device__ __forceinline__ void weight_of(float l, float q, float Mf, double invS, bool corrected,
+                                          double* rw, double* pv) {
+  const double p = static_cast<double>(expf(l - Mf)) * invS;  // 0 for l = -inf (past V)
+  const double d = p - static_cast<double>(q);
   *pv = p;
+  *rw = corrected ? (d > 0.0 ? d : 0.0) : p;
 }
 
 // 3. per (request, slice): sums of the corrected weights and of p over the drawing row
@@ -161,15 +282,35 @@ __global__ __launch_bounds__(RA_THREADS) void ra_weights_kernel(
     int V, int nslice, const int32_t* __restrict__ ws_n, const double* __restrict__ ws_ms,
     double* __restrict__ ws_w, double* __restrict__ ws_p) {
   __shared__ double redd[RA_THREADS / 64];
+  constexpr int E = BF16 ? 8 : 4;
   const int slice = blockIdx.x, b = blockIdx.y;
   const int n = ws_n[b];
-  const double M = ws_ms[2 * b], S = ws_ms[2 * b + 1];
+  const float Mf = static_cast<float>(ws_ms[2 * b]);
+  const double invS = 1.0 / ws_ms[2 * b + 1];
+  const bool corrected = n < K;
+  const int64_t row = static_cast<int64_t>(b) * (K + 1) + n;
+  const float* qrow = draft_probs + (static_cast<int64_t>(b) * K + (corrected ? n : 0)) * V;
+  // this thread's entries, in load_slice's layout: unit j * RA_THREADS + t of the slice
+  float x[RA_PER], q[RA_PER];
+  load_slice<BF16>(logits, row * ld, slice * RA_SLICE, V, x);
+#pragma unroll
+  for (int j = 0; j < RA_PER / E; ++j) {
+    const int v = slice * RA_SLICE + (j * RA_THREADS + static_cast<int>(threadIdx.x)) * E;
+    float qq[E];
+    if (corrected) {
+      load_q_run<E>(qrow, v, V, qq);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) qq[e] = 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) q[j * E + e] = qq[e];
+  }
   double sw = 0.0, sp = 0.0;
-#pragma unroll 4
+#pragma unroll
   for (int e = 0; e < RA_PER; ++e) {
     double rw, pv;
-    weights_at<BF16>(logits, ld, draft_probs, b, n, K, V, M, S,
-                     slice * RA_SLICE + e * RA_THREADS + static_cast<int>(threadIdx.x), &rw, &pv);
+    weight_of(x[e], q[e], Mf, invS, corrected, &rw, &pv);
     sw += rw;
     sp += pv;
   }
@@ -188,66 +329,102 @@ __global__ __launch_bounds__(RA_THREADS) void ra_draw_kernel(
     int V, int nslice, const float* __restrict__ us, const int32_t* __restrict__ ws_n,
     const double* __restrict__ ws_ms, const double* __restrict__ ws_w,
     const double* __restrict__ ws_p, int32_t* __restrict__ next_token) {
-  __shared__ double wsum[RA_THREADS / 64];
-  __shared__ int pick[2];  // slice, then token
+  __shared__ double shd[2];  // target, weight before the chosen slice
+  __shared__ int shi[2];     // chosen slice, law (0 corrected, 1 target)
+  __shared__ double wtot[RA_THREADS / 64];
+  __shared__ int fnd[RA_THREADS / 64], lst[RA_THREADS / 64];
   const int b = blockIdx.x;
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
   const int n = ws_n[b];
-  const double M = ws_ms[2 * b], S = ws_ms[2 * b + 1];
-  const double* sl = ws_w + static_cast<int64_t>(b) * nslice;
-  // corrected law unless it is empty; slice sums in index order by one thread
-  if (threadIdx.x == 0) {
-    double W = 0.0;
-    for (int j = 0; j < nslice; ++j) W += sl[j];
-    bool use_p = !(W > 0.0);
-    if (use_p) {
-      sl = ws_p + static_cast<int64_t>(b) * nslice;
-      W = 0.0;
-      for (int j = 0; j < nslice; ++j) W += sl[j];
+  const bool corrected = n < K;
+  if (wave == 0) {
+    // slice sums by lane (slices lane, lane + 64, ...); the corrected law unless it is empty
+    const double* sw = ws_w + static_cast<int64_t>(b) * nslice;
+    const double* sp = ws_p + static_cast<int64_t>(b) * nslice;
+    double W = 0.0, P = 0.0;
+    for (int j = lane; j < nslice; j += 64) {
+      W += sw[j];
+      P += sp[j];
     }
-    const double target = static_cast<double>(us[b]) * W;
-    double c = 0.0;
+    for (int o = 32; o >= 1; o >>= 1) {
+      W += __shfl_xor(W, o);
+      P += __shfl_xor(P, o);
+    }
+    const bool use_p = !(W > 0.0);
+    const double* sl = use_p ? sp : sw;
+    const double target = static_cast<double>(us[b]) * (use_p ? P : W);
+    // first slice whose running sum passes the target (chunks of 64 slices, in order)
+    double base = 0.0;
     int js = -1, last = 0;
-    for (int j = 0; j < nslice; ++j) {
-      if (sl[j] > 0.0) last = j;
-      if (js < 0 && c + sl[j] > target) js = j;
-      c += sl[j];
+    for (int j0 = 0; j0 < nslice; j0 += 64) {
+      const int j = j0 + lane;
+      const double x = j < nslice ? sl[j] : 0.0;
+      double incl = x;
+      for (int o = 1; o < 64; o <<= 1) {
+        const double y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+      }
+      const uint64_t pass = __ballot(j < nslice && base + incl > target && js < 0);
+      const uint64_t pos = __ballot(j < nslice && x > 0.0);
+      if (pos) last = j0 + 63 - __builtin_clzll(pos);
+      if (js < 0 && pass) {
+        const int f = __builtin_ctzll(pass);
+        js = j0 + f;
+        const double incl_f = __shfl(incl, f), x_f = __shfl(x, f);
+        if (lane == 0) shd[1] = base + incl_f - x_f;
+      }
+      base += __shfl(incl, 63);
     }
-    // rounding left the target at or above the total: the last slice with weight
-    pick[0] = js >= 0 ? js : last;
-    pick[1] = use_p ? 1 : 0;
-    wsum[0] = target;
-    double before = 0.0;
-    for (int j = 0; j < pick[0]; ++j) before += sl[j];
-    wsum[1] = before;
+    if (js < 0) {  // rounding left the target at or above the total: the last slice with weight
+      js = last;
+      double before = 0.0;
+      for (int j = lane; j < js; j += 64) before += sl[j];
+      for (int o = 32; o >= 1; o >>= 1) before += __shfl_xor(before, o);
+      if (lane == 0) shd[1] = before;
+    }
+    if (lane == 0) {
+      shd[0] = target;
+      shi[0] = js;
+      shi[1] = use_p ? 1 : 0;
+    }
   }
   __syncthreads();
-  const int js = pick[0];
-  const bool use_p = pick[1] != 0;
-  const double target = wsum[0], before = wsum[1];
-  __syncthreads();
-  // entries of slice js in index order: thread t holds 16 consecutive ones
+  const int js = shi[0];
+  const bool use_p = shi[1] != 0;
+  const double target = shd[0], before = shd[1];
+  const float Mf = static_cast<float>(ws_ms[2 * b]);
+  const double invS = 1.0 / ws_ms[2 * b + 1];
+  const int64_t row = static_cast<int64_t>(b) * (K + 1) + n;
+  const float* qrow = draft_probs + (static_cast<int64_t>(b) * K + (corrected ? n : 0)) * V;
+  // entries of slice js in index order: thread t holds RA_PER consecutive ones
   const int v0 = js * RA_SLICE + static_cast<int>(threadIdx.x) * RA_PER;
+  float x[RA_PER], q[RA_PER];
+  load_run<BF16, RA_PER>(logits, row * ld, v0, V, x);
+  if (corrected && !use_p) {
+    load_q_run<RA_PER>(qrow, v0, V, q);
+  } else {
+#pragma unroll
+    for (int e = 0; e < RA_PER; ++e) q[e] = 0.0f;
+  }
   double w[RA_PER];
   double tsum = 0.0;
 #pragma unroll
   for (int e = 0; e < RA_PER; ++e) {
     double rw, pv;
-    weights_at<BF16>(logits, ld, draft_probs, b, n, K, V, M, S, v0 + e, &rw, &pv);
+    weight_of(x[e], q[e], Mf, invS, corrected, &rw, &pv);
     w[e] = use_p ? pv : rw;
     tsum += w[e];
   }
   // exclusive scan of the thread sums (block, float64)
-  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
   double incl = tsum;
   for (int o = 1; o < 64; o <<= 1) {
     const double y = __shfl_up(incl, o);
     if (lane >= o) incl += y;
   }
-  __shared__ double wtot[RA_THREADS / 64];
   if (lane == 63) wtot[wave] = incl;
   __syncthreads();
   double c = before + incl - tsum;
-  for (int x = 0; x < wave; ++x) c += wtot[x];
+  for (int xw = 0; xw < wave; ++xw) c += wtot[xw];
   int found = 0x7FFFFFFF, lastpos = -1;
 #pragma unroll
   for (int e = 0; e < RA_PER; ++e) {
@@ -261,7 +438,6 @@ __global__ __launch_bounds__(RA_THREADS) void ra_draw_kernel(
     found = min(found, __shfl_xor(found, o));
     lastpos = max(lastpos, __shfl_xor(lastpos, o));
   }
-  __shared__ int fnd[RA_THREADS / 64], lst[RA_THREADS / 64];
   if (lane == 0) {
     fnd[wave] = found;
     lst[wave] = lastpos;
@@ -269,9 +445,9 @@ __global__ __launch_bounds__(RA_THREADS) void ra_draw_kernel(
   __syncthreads();
   if (threadIdx.x == 0) {
     int f = 0x7FFFFFFF, l = -1;
-    for (int x = 0; x < RA_THREADS / 64; ++x) {
-      f = min(f, fnd[x]);
-      l = max(l, lst[x]);
+    for (int xw = 0; xw < RA_THREADS / 64; ++xw) {
+      f = min(f, fnd[xw]);
+      l = max(l, lst[xw]);
     }
     next_token[b] = f != 0x7FFFFFFF ? f : l;
   }
@@ -324,11 +500,12 @@ extern "C" dsa_status rejection_accept(const void* logits, int32_t dtype, int64_
                        st, logits, logits_ld, V, nslice, ws_m, ws_s);
   dsa_status s = check_launch("rejection_accept(stats)");
   if (s != DSA_OK) return s;
+  const dim3 dec_threads(64 * (K + 1 < 16 ? K + 1 : 16));  // one wave per row, at most 16
   if (bf)
-    hipLaunchKernelGGL(ra_decide_kernel<true>, dim3((unsigned)B), dim3(64), 0, st, logits, logits_ld,
+    hipLaunchKernelGGL(ra_decide_kernel<true>, dim3((unsigned)B), dec_threads, 0, st, logits, logits_ld,
                        draft_probs, draft, u, K, V, nslice, ws_m, ws_s, ws_n, ws_ms, num_accepted);
   else
-    hipLaunchKernelGGL(ra_decide_kernel<false>, dim3((unsigned)B), dim3(64), 0, st, logits, logits_ld,
+    hipLaunchKernelGGL(ra_decide_kernel<false>, dim3((unsigned)B), dec_threads, 0, st, logits, logits_ld,
                        draft_probs, draft, u, K, V, nslice, ws_m, ws_s, ws_n, ws_ms, num_accepted);
   s = check_launch("rejection_accept(decide)");
   if (s != DSA_OK) return s;

@@ -40,8 +40,14 @@ KERNELS = {
     "mla_combine_kernel": ("sparse_mla", "sparse_mla.hip"),
     "argmax_slices_kernel": ("greedy_accept", "greedy_accept.hip"),
     "accept_kernel": ("greedy_accept", "greedy_accept.hip"),
+    "ra_stats_kernel": ("rejection_accept", "rejection_accept.hip"),
+    "ra_decide_kernel": ("rejection_accept", "rejection_accept.hip"),
+    "ra_weights_kernel": ("rejection_accept", "rejection_accept.hip"),
+    "ra_draw_kernel": ("rejection_accept", "rejection_accept.hip"),
 }
-SECOND = ("mla_combine_kernel", "accept_kernel")  # second kernel of a two-kernel call
+# later kernels of a multi-kernel call (counted in its traffic, not as launches)
+SECOND = ("mla_combine_kernel", "accept_kernel", "ra_decide_kernel", "ra_weights_kernel",
+          "ra_draw_kernel")
 
 
 def source_sha(name: str) -> str:
