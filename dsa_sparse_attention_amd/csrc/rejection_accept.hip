@@ -32,6 +32,23 @@ constexpr int RA_THREADS = 256;
 constexpr int RA_SLICE = 16384;                 // vocabulary entries per block
 constexpr int RA_PER = RA_SLICE / RA_THREADS;   // entries per thread (64)
 
+// e^d for d <= 0 (a logit minus a maximum): 2^(d log2 e) with the product's rounding error
+// and the constant's own error carried to first order, d*log2e = y + t, 2^(y+t) = 2^y (1 +
+// t ln 2); about one ulp in a handful of instructions. Exactly 0 below -104 (where e^d is
+// under the float32 range) and for -inf.
+__device__ __forceinline__ float exp_nonpos(float d) {
+  constexpr float L2E = 1.44269502163f;          // log2(e) rounded to float32
+  constexpr float L2E_LO = 1.925963033e-8f;       // log2(e) - L2E
+  constexpr float LN2 = 0.693147180560f;
+  const bool live = d > -104.0f;
+  const float dc = live ? d : -104.0f;
+  const float y = dc * L2E;
+  float t = fmaf(dc, L2E, -y);  // exact error of the rounded product
+  t = fmaf(dc, L2E_LO, t);
+  const float r = __builtin_amdgcn_exp2f(y);
+  return live ? fmaf(r, t * LN2, r) : 0.0f;
+}
+
 template <bool BF16>
 __device__ __forceinline__ float logit(const void* lg, int64_t idx) {
   if constexpr (BF16)
@@ -98,7 +115,7 @@ __device__ __forceinline__ void load_slice(const void* lg, int64_t row_start, in
 __device__ __forceinline__ void merge_ms(float& m, double& sum, float m2, double s2) {
   const float M = fmaxf(m, m2);
   if (M == -INFINITY) return;
-  sum = sum * static_cast<double>(expf(m - M)) + s2 * static_cast<double>(expf(m2 - M));
+  sum = sum * static_cast<double>(exp_nonpos(m - M)) + s2 * static_cast<double>(exp_nonpos(m2 - M));
   m = M;
 }
 
@@ -121,7 +138,7 @@ __global__ __launch_bounds__(RA_THREADS) void ra_stats_kernel(const void* __rest
   double sum = 0.0;
   if (m > -INFINITY) {
 #pragma unroll
-    for (int e = 0; e < RA_PER; ++e) sum += static_cast<double>(expf(x[e] - m));
+    for (int e = 0; e < RA_PER; ++e) sum += static_cast<double>(exp_nonpos(x[e] - m));
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) merge_ms(m, sum, __shfl_xor(m, o), __shfl_xor(sum, o));
@@ -269,7 +286,7 @@ __device__ __forceinline__ void load_run(const void* lg, int64_t row_start, int 
 // logit); one float32 exponential, then float64 arithmetic
 __device__ __forceinline__ void weight_of(float l, float q, float Mf, double invS, bool corrected,
                                           double* rw, double* pv) {
-  const double p = static_cast<double>(expf(l - Mf)) * invS;  // 0 for l = -inf (past V)
+  const double p = static_cast<double>(exp_nonpos(l - Mf)) * invS;  // 0 for l = -inf (past V)
   const double d = p - static_cast<double>(q);
   *pv = p;
   *rw = corrected ? (d > 0.0 ? d : 0.0) : p;
