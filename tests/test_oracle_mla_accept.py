@@ -192,3 +192,19 @@ def test_verify_layout_facts():
         gold["batch_example"]["verify_tokens"]
     K = 5
     assert accounting.merged_offsets([0, 7, 9, 20], K) == [0, 7 + 5, 9 + 10, 20 + 15]
+
+
+def test_verify_cache_rows_are_each_rows_own_position():
+    # the cache row a verify row writes is its own position: one past it is exactly the
+    # number of keys the row sees under the causal rule
+    from dsa_sparse_attention_amd import synth
+    lengths = [7, 300, 65, 1024]
+    rows = [3, 1, 6, 2]
+    qo = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+    ko = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    dst = synth.verify_cache_rows(lengths, rows).numpy()
+    assert len(dst) == qo[-1] and len(set(dst.tolist())) == len(dst)
+    for t in range(int(qo[-1])):
+        b = int(np.searchsorted(qo, t, side="right") - 1)
+        assert ko[b] <= dst[t] < ko[b + 1]
+        assert dst[t] - ko[b] + 1 == oracle.row_visible(qo, ko, t)
