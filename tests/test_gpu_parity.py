@@ -462,7 +462,8 @@ def _rejection_candidates(lg, dp, draft, u, us, K, eps_u=1e-5, eps_s=2e-6):
 
 
 @pytest.mark.parametrize("name,batch,vocab,K,noise", [("f32", 7, 5000, 4, 1.0), ("bf16", 32, 151552, 5, 1.0),
-                                                      ("bf16", 16, 151552, 5, 0.3)])
+                                                      ("bf16", 16, 151552, 5, 0.3),
+                                                      ("f32", 5, 3001, 0, 1.0), ("bf16", 9, 40000, 1, 2.0)])
 def test_rejection_accept_matches_oracle(name, batch, vocab, K, noise):
     _say(f"rejection_accept {name} B={batch} V={vocab} K={K}")
     w = W.scaled(W.MTP5_VERIFY if name == "bf16" else W.TINY, ctx=4096, batch=batch, vocab=vocab,
