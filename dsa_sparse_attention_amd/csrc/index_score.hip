@@ -49,10 +49,7 @@ namespace {
 constexpr int KT = 64;                // keys per tile
 constexpr int MIN_SHARE = DSA_IS_MIN_SHARE;  // fewest keys per block (4 tiles)
 constexpr int NBUF = DSA_IS_NBUF;     // tile slots in LDS: NBUF - 1 tiles in flight
-#ifndef DSA_IS_MAX_ROWS
-#define DSA_IS_MAX_ROWS 7
-#endif
-constexpr int MAX_ROWS = DSA_IS_MAX_ROWS;  // rows per block: 2 compute waves each, plus a producer
+constexpr int MAX_ROWS = 7;           // rows per block: 2 compute waves each, plus a producer
 constexpr int MAX_ROWS_H128 = 3;      // with 8 head tiles (registers: 256 per wave)
 
 int max_rows_for(int ht) { return ht >= 8 ? MAX_ROWS_H128 : MAX_ROWS; }
