@@ -255,6 +255,33 @@ def test_topk_small_k_and_padding():
             assert np.array_equal(got[t], ref), (k, t)
 
 
+def test_requests_without_keys_or_rows():
+    # Requests with no keys, a request with no rows, and rows placed before their request's
+    # first key (more rows than keys), beside ordinary requests: a row that sees no key
+    # selects nothing (all -1) and attends to nothing (out 0, lse -inf); every row equals
+    # the oracle's.
+    _say("requests without keys or rows")
+    lens, rows = [0, 300, 0, 40, 3], [2, 3, 0, 1, 5]
+    qo, ko = synth.prefix(rows, torch.int32), synth.kv_row_offsets(lens)
+    T, k, heads, sm = sum(rows), 64, 16, 0.0417
+    nvis = np.array([max(0, min(L, L - R + r + 1)) for L, R in zip(lens, rows) for r in range(R)])
+    s = synth.random_scores(T, 300, seed=9, tie_levels=3)
+    top = api.topk(s.to(DEV), qo.to(DEV), ko.to(DEV), max(rows), max(lens), k).cpu().numpy()
+    ref = np.asarray(oracle.topk(s.double().numpy(), nvis, k), dtype=np.int32)
+    assert np.array_equal(top, ref)
+    assert np.all(top[nvis == 0] == -1) and np.any(nvis == 0)
+    g = synth.generator(10)
+    q = torch.randn((T, heads, 576), generator=g).to(torch.bfloat16)
+    kv = torch.randn((sum(lens), 576), generator=g).to(torch.bfloat16)
+    out, lse = api.sparse_mla_decode(q.to(DEV), kv.to(DEV), torch.from_numpy(ref).to(DEV),
+                                     qo.to(DEV), ko.to(DEV), max(rows), sm)
+    u16 = lambda x: x.view(torch.uint16).numpy()
+    ref_o, ref_l = oracle.sparse_mla(u16(q), u16(kv), ref, qo.numpy(), ko.numpy(), sm)
+    mla_check(out, lse, ref_o, ref_l)
+    empty = torch.from_numpy(nvis == 0).to(DEV)
+    assert torch.all(out[empty] == 0) and torch.all(torch.isneginf(lse[empty]))
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_end_to_end_topk_sets(name):
     w = SMALL[name]
