@@ -46,8 +46,11 @@ def parse():
     ap.add_argument("--accept", choices=("greedy", "rejection"), default="greedy",
                     help="acceptance rule of the step: greedy argmax prefix, or rejection "
                          "sampling against a draft law (uniforms drawn per step copy)")
-    ap.add_argument("--refine", action="store_true",
-                    help="top-k with the exact-boundary refine (float64 rescore of the band)")
+    ap.add_argument("--no-refine", action="store_true",
+                    help="top-k on the float32 scores alone (default: the exact-boundary refine, "
+                         "so the step's top-k sets are the oracle's)")
+    ap.add_argument("--err-scale", type=float, default=0.0,
+                    help="C of the refine's error bound (0: the library default, 4)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration) and exit")
     return ap.parse_args()
@@ -124,27 +127,46 @@ def traffic_for(kernel_file: str, launches_key: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, lengths, inp0, target_s: float):
-    """Time the oracle (as it stands) on a bounded sample: whole requests of this workload."""
+    """Time the oracle (as it stands) on a bounded sample: whole requests of this workload.
+
+    Per sampled request the timed stages are the ones the GPU step runs: quantising the
+    step's queries and its verify rows' new keys (the cache write), the index score over the
+    request's whole history, top-k, sparse MLA and the acceptance. The history's keys are
+    quantised once beforehand, as the index cache is filled before the step on the GPU too.
+    """
     import numpy as np
 
     import oracle
 
-    qo = np.arange(w.batch + 1, dtype=np.int32) * w.rows
+    t_ = __import__("torch")
     q_all = inp0.q_f32.cpu().numpy()
     w_all = inp0.w.cpu().numpy()
-    qm_all = inp0.q_mla.view(__import__("torch").uint16)
+    qm_all = inp0.q_mla.view(t_.uint16)
     logits = inp0.logits
     draft = inp0.draft.cpu().numpy()
     L = lengths[0]
     kf = inp0.k_f32_sample.numpy()
-    kv_host = inp0.kv[:L].view(__import__("torch").uint16).cpu().numpy()
+    kc, ks = oracle.quantize(kf)  # the index cache of the sampled history (not timed)
+    k_new = np.ascontiguousarray(kf[L - w.rows:])
+    kv_host = inp0.kv[:L].view(t_.uint16).cpu().numpy()
     rej_host = None
     if inp0.rej is not None:
-        t = __import__("torch")
         rl = inp0.rej["logits"]
         rej_host = {k: v.cpu().numpy() for k, v in inp0.rej.items() if k != "logits"}
-        rej_host["logits"] = (rl.view(t.uint16) if rl.dtype == t.bfloat16 else rl).cpu().numpy()
+        rej_host["logits"] = (rl.view(t_.uint16) if rl.dtype == t_.bfloat16 else rl).cpu().numpy()
+    stages = {"cache_write": 0.0, "index_score": 0.0, "topk": 0.0, "sparse_mla": 0.0,
+              "accept": 0.0}
     done_rows, t_total = 0, 0.0
     b = 0
     while b < w.batch and (t_total < target_s or b == 0):
@@ -153,30 +175,40 @@ def cpu_baseline(w, lengths, inp0, target_s: float):
         q = np.ascontiguousarray(q_all[rows])
         wt = np.ascontiguousarray(w_all[rows])
         qm = qm_all[rows].cpu().numpy()
-        lg = logits[rows].view(__import__("torch").uint16).cpu().numpy()
-        t0 = time.perf_counter()
-        qc, qs = oracle.quantize(q)
-        kc, ks = oracle.quantize(kf)
+        lg = logits[rows].view(t_.uint16).cpu().numpy()
         qo1 = np.array([0, w.rows], np.int32)
         ko1 = np.array([0, L], np.int64)
-        sc = oracle.index_score(qc, qs, wt, kc, ks, qo1, ko1)
         nvis = np.array([L - w.rows + r + 1 for r in range(w.rows)])
+        t0 = time.perf_counter()
+        qc, qs = oracle.quantize(q)
+        oracle.quantize(k_new)
+        t1 = time.perf_counter()
+        sc = oracle.index_score(qc, qs, wt, kc, ks, qo1, ko1)
+        t2 = time.perf_counter()
         tk = oracle.topk(sc, nvis, w.topk)
+        t3 = time.perf_counter()
         oracle.sparse_mla(qm, kv_host, tk, qo1, ko1, w.sm_scale)
+        t4 = time.perf_counter()
         if inp0.rej is None:
             oracle.greedy_accept(lg, draft[b:b + 1], w.drafts)
         else:
             r = rej_host
             oracle.rejection_accept(r["logits"][rows], r["draft_probs"][b:b + 1], r["draft"][b:b + 1],
                                     r["u"][b:b + 1], r["us"][b:b + 1], w.drafts)
-        t_total += time.perf_counter() - t0
+        t5 = time.perf_counter()
+        for name, dt in zip(stages, (t1 - t0, t2 - t1, t3 - t2, t4 - t3, t5 - t4)):
+            stages[name] += dt
+        t_total += t5 - t0
         done_rows += w.rows
         b += 1
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": done_rows / t_total, "unit": "rows/s", "cores": threads, "kind": "oracle",
-            "sample": f"{b} request(s) x {w.rows} rows at context {L}: quantise, index score, "
-                      f"top-k, sparse MLA, {'greedy' if inp0.rej is None else 'rejection-sampling'} "
-                      f"accept ({t_total:.1f} s)"}
+            "cpu_model": cpu_model(),
+            "stages_s": {k: round(v, 3) for k, v in stages.items()},
+            "sample": f"{b} request(s) x {w.rows} rows at context {L}: quantise the step's "
+                      f"queries and new keys, index score, top-k, sparse MLA, "
+                      f"{'greedy' if inp0.rej is None else 'rejection-sampling'} accept "
+                      f"({t_total:.1f} s; history keys quantised beforehand, untimed)"}
 
 
 def main():
@@ -215,7 +247,9 @@ def main():
     ws_need = api.sparse_mla_workspace_size(T, w.mla_heads, w.topk)
     ws_mla = torch.empty(max(ws_need, 16), dtype=torch.uint8, device=dev)
     from dsa_sparse_attention_amd import _lib
-    tk_need = api.topk_workspace_size(T, max_kv, w.topk)
+    refine = not args.no_refine
+    tk_need = api.topk_workspace_size(w.batch, T, max_kv, w.topk, refine)
+    status = torch.zeros(T, dtype=torch.int32, device=dev)
     ws_tk = torch.empty(max(tk_need, 16), dtype=torch.uint8, device=dev)
     ga_need = _lib.load().greedy_accept_workspace_size(w.batch, w.drafts, w.vocab)
     ws_ga = torch.empty(max(ga_need, 16), dtype=torch.uint8, device=dev)
@@ -243,8 +277,8 @@ def main():
         if ev: ev[1].record(stream)
         api.index_score(qc, qs, inp.w, inp.k_fp8, inp.k_scale, qo, ko, w.rows, max_kv, scores=scores)
         if ev: ev[2].record(stream)
-        rf = (dict(q_fp8=qc, q_scale=qs, w=inp.w, k_fp8=inp.k_fp8, k_scale=inp.k_scale)
-              if args.refine else None)
+        rf = (dict(q_fp8=qc, q_scale=qs, w=inp.w, k_fp8=inp.k_fp8, k_scale=inp.k_scale,
+                   status=status, err_scale=args.err_scale) if refine else None)
         api.topk(scores, qo, ko, w.rows, max_kv, w.topk, out=topk, refine=rf, workspace=ws_tk)
         if ev: ev[3].record(stream)
         api.sparse_mla_decode(inp.q_mla, inp.kv, topk, qo, ko, w.rows, w.sm_scale, out=out, lse=lse,
@@ -295,6 +329,15 @@ def main():
     torch.cuda.synchronize()
     per = {n: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)) / args.steps
            for j, n in enumerate(names)}
+    refine_rec = None
+    if refine:
+        # every row of the last step must be refined (status >= 0): its top-k set is then
+        # the oracle's, provided the float32 errors stay within the bound (see dsa.h)
+        st = status.cpu()
+        assert int(st.min()) >= 0, f"refine left rows unresolved: statuses {sorted(set(st.tolist()))}"
+        refine_rec = {"status_min": int(st.min()), "band_max": int(st.max()),
+                      "band_mean": round(float(st.float().mean()), 2),
+                      "err_scale": args.err_scale or 4.0}
     print(f"[bench] {args.steps} steps: {ms_step:.4f} ms/step (wall {wall / args.steps * 1e3:.4f} ms); "
           + ", ".join(f"{n} {v * 1e3:.1f} us" for n, v in per.items()), file=sys.stderr, flush=True)
 
@@ -352,7 +395,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "context": max_kv, "rows_per_request": w.rows,
                    "index_heads": w.index_heads, "index_dim": w.index_dim, "topk": w.topk,
                    "mla_heads": w.mla_heads, "vocab": w.vocab, "global_batch": rows_step,
-                   "seq_len": max_kv, "share_steps": w.share_steps, "topk_refine": args.refine,
+                   "seq_len": max_kv, "share_steps": w.share_steps, "topk_refine": refine,
                    "accept": args.accept,
                    "parallelism": "single-gpu"},
         "step_includes": names,
@@ -360,6 +403,7 @@ def main():
                                                   per["sparse_mla"]) * 1e-3), 1),
         "kernels": kernels,
         "roofline": roof,
+        "refine": refine_rec,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)

@@ -49,6 +49,13 @@ def _dev(t, name, dtype):
     return t
 
 
+def _shape(t, name, shape):
+    """Caller-supplied buffers must have exactly the shape the kernels write."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
 def abi_version() -> int:
     return _lib.load().dsa_abi_version()
 
@@ -114,10 +121,16 @@ def index_score(q_fp8, q_scale, w, k_fp8, k_scale, q_row_offsets, kv_row_offsets
     _dev(kv_row_offsets, "kv_row_offsets", torch.int64)
     T, H, D = q_fp8.shape
     B = q_row_offsets.numel() - 1
+    _shape(q_scale, "q_scale", (T, H))
+    _shape(w, "w", (T, H))
+    if k_fp8.dim() != 2 or k_fp8.shape[1] != D or k_scale.numel() != k_fp8.shape[0]:
+        raise ValueError("k_fp8 must be [N, D_I] with one k_scale per key")
     if scores is None:
         ld = (max_kv_len + 3) // 4 * 4
         scores = torch.empty((T, ld), dtype=torch.float32, device=q_fp8.device)
     _dev(scores, "scores", torch.float32)
+    if scores.dim() != 2 or scores.shape[0] != T or scores.shape[1] < max_kv_len:
+        raise ValueError(f"scores must be [T={T}, >= {max_kv_len}], got {tuple(scores.shape)}")
     _check(_lib.load().dsa_index_score(
         _p(q_fp8), _p(q_scale), _p(w), _p(k_fp8), _p(k_scale), _p(q_row_offsets),
         _p(kv_row_offsets), B, T, max_q_rows, H, D, max_kv_len, _p(scores), scores.shape[1],
@@ -139,9 +152,12 @@ def topk(scores, q_row_offsets, kv_row_offsets, max_q_rows: int, max_kv_len: int
     _dev(kv_row_offsets, "kv_row_offsets", torch.int64)
     T = scores.shape[0]
     B = q_row_offsets.numel() - 1
+    if scores.dim() != 2 or scores.shape[1] < max_kv_len:
+        raise ValueError(f"scores must be [T, >= {max_kv_len}], got {tuple(scores.shape)}")
     if out is None:
         out = torch.empty((T, k), dtype=torch.int32, device=scores.device)
     _dev(out, "out", torch.int32)
+    _shape(out, "out", (T, k))
     lib = _lib.load()
     rf = None
     if refine is not None:
@@ -150,14 +166,19 @@ def topk(scores, q_row_offsets, kv_row_offsets, max_q_rows: int, max_kv_len: int
         _dev(refine["w"], "w", torch.float32)
         _dev(refine["k_fp8"], "k_fp8", torch.uint8)
         _dev(refine["k_scale"], "k_scale", torch.float32)
+        q = refine["q_fp8"]
+        if q.dim() != 3 or q.shape[0] != T:
+            raise ValueError("refine q_fp8 must be [T, H_I, D_I]")
+        _shape(refine["q_scale"], "q_scale", q.shape[:2])
+        _shape(refine["w"], "w", q.shape[:2])
         st = refine.get("status")
         if st is not None:
             _dev(st, "status", torch.int32)
-        q = refine["q_fp8"]
+            _shape(st, "status", (T,))
         rf = _lib.TopkRefine(_p(q), _p(refine["q_scale"]), _p(refine["w"]), _p(refine["k_fp8"]),
                              _p(refine["k_scale"]), q.shape[1], q.shape[2],
                              float(refine.get("err_scale", 0.0)), _p(st))
-    wsb = lib.dsa_topk_workspace_size(T, max_kv_len, k)
+    wsb = lib.dsa_topk_workspace_size(B, T, max_kv_len, k, 1 if refine is not None else 0)
     ws = workspace
     if ws is None and wsb:
         ws = torch.empty(wsb, dtype=torch.uint8, device=scores.device)
@@ -170,8 +191,8 @@ def topk(scores, q_row_offsets, kv_row_offsets, max_q_rows: int, max_kv_len: int
     return out
 
 
-def topk_workspace_size(T: int, max_kv_len: int, k: int) -> int:
-    return int(_lib.load().dsa_topk_workspace_size(T, max_kv_len, k))
+def topk_workspace_size(B: int, T: int, max_kv_len: int, k: int, refine: bool = False) -> int:
+    return int(_lib.load().dsa_topk_workspace_size(B, T, max_kv_len, k, 1 if refine else 0))
 
 
 def sparse_mla_workspace_size(T: int, H: int, k: int) -> int:
@@ -197,8 +218,13 @@ def sparse_mla_decode(q, kv, topk_idx, q_row_offsets, kv_row_offsets, max_q_rows
     B = q_row_offsets.numel() - 1
     if out is None:
         out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=q.device)
+    _dev(out, "out", torch.bfloat16)
+    _shape(out, "out", (T, H, 512))
     if lse is None and want_lse:
         lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+        _shape(lse, "lse", (T, H))
     lib = _lib.load()
     need = lib.dsa_sparse_mla_workspace_size(T, H, k)
     if workspace is None and need:

@@ -17,14 +17,8 @@
 namespace dsa {
 namespace {
 
-#ifndef DSA_GA_THREADS
-#define DSA_GA_THREADS 256
-#endif
-#ifndef DSA_GA_SLICE
-#define DSA_GA_SLICE 4096
-#endif
-constexpr int GA_THREADS = DSA_GA_THREADS;
-constexpr int GA_SLICE = DSA_GA_SLICE;  // vocabulary entries per block
+constexpr int GA_THREADS = 256;
+constexpr int GA_SLICE = 4096;  // vocabulary entries per block
 
 struct ArgMax {
   float v;

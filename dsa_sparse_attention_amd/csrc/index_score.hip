@@ -14,7 +14,7 @@
 // 12 waves, 3 per SIMD: the MFMA load is spread evenly over the CU) plus one producer
 // wave. Every key byte is fetched from HBM once per row group and shared by its rows.
 //  1. The producer wave streams keys HBM -> LDS with LDS DMA (global_load_lds, no
-//     registers) in 64-key tiles through a ring of NBUF slots (NBUF-1 tiles in flight),
+//     registers) in 64-key tiles through a ring of NBUF slots (NBUF-2 tiles in flight),
 //     together with the tile's 64 key scales. One 16-byte DMA instruction moves 1 KB of
 //     consecutive keys (contiguous in HBM); in LDS a key keeps its row, with its
 //     16-byte pieces XOR-permuted by (key >> 1) so that the MFMA operand reads (16
@@ -39,16 +39,9 @@
 namespace dsa {
 namespace {
 
-#ifndef DSA_IS_MIN_SHARE
-#define DSA_IS_MIN_SHARE 256
-#endif
-
-#ifndef DSA_IS_NBUF
-#define DSA_IS_NBUF 8
-#endif
 constexpr int KT = 64;                // keys per tile
-constexpr int MIN_SHARE = DSA_IS_MIN_SHARE;  // fewest keys per block (4 tiles)
-constexpr int NBUF = DSA_IS_NBUF;     // tile slots in LDS: NBUF - 1 tiles in flight
+constexpr int MIN_SHARE = 256;        // fewest keys per block (4 tiles)
+constexpr int NBUF = 8;               // tile slots in LDS: NBUF - 2 tiles in flight
 constexpr int MAX_ROWS = 7;           // rows per block: 2 compute waves each, plus a producer
 constexpr int MAX_ROWS_H128 = 3;      // with 8 head tiles (registers: 256 per wave)
 
@@ -85,10 +78,6 @@ struct Ring {
   static_assert((NBUF - 2) * DMAS <= 63, "vmcnt holds at most 63");
 };
 
-// Keys key0 .. key_end-1 (0 < key_end - key0 < 2^31) of request `ri` against its rows
-// row0 .. row0+NR-1, by the whole block: the producer wave streams the keys through the
-// ring, the compute waves score and store them. The block's barriers pair up one to one
-// between the two roles: one per tile.
 // Keys key0 .. key_end-1 (0 < key_end - key0 < 2^31) of request `ri` against its rows
 // row0 .. row0+NR-1, by the whole block: the producer wave (producer_segment) streams the
 // keys through the ring, the compute waves (compute_segment) score and store them. Each

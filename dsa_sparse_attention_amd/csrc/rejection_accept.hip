@@ -282,8 +282,9 @@ __device__ __forceinline__ void load_run(const void* lg, int64_t row_start, int 
   }
 }
 
-// p(v) and the corrected weight of one entry: l - M is exact in float32 (M is a float32
-// logit); one float32 exponential, then float64 arithmetic
+// p(v) and the corrected weight of one entry: l - M is one float32 subtraction (exact for
+// bf16 logits within 2^16 of each other in magnitude, rounded once otherwise), then one
+// float32 exponential, then float64 arithmetic
 __device__ __forceinline__ void weight_of(float l, float q, float Mf, double invS, bool corrected,
                                           double* rw, double* pv) {
   const double p = static_cast<double>(exp_nonpos(l - Mf)) * invS;  // 0 for l = -inf (past V)

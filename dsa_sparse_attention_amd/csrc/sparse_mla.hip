@@ -42,10 +42,7 @@ constexpr int HPB = 64;                          // heads per block
 constexpr int NSW = 8, NOW = 8, NWAVE = NSW + NOW, NT = NWAVE * 64;
 constexpr int KS = DQK / 32;                     // 18 k-steps of the S product
 constexpr int KPF = 5;                           // K operand reads in flight ahead
-#ifndef DSA_MLA_DMA_A
-#define DSA_MLA_DMA_A 2
-#endif
-constexpr int DMA_A = DSA_MLA_DMA_A;  // O waves: DMA blocks issued before B1, the rest after
+constexpr int DMA_A = 2;  // O waves: DMA blocks issued before B1, the rest after
 constexpr float LAZY = 8.0f;                     // reference-max slack, log2 units
 constexpr float M_INIT = -1.0e30f;               // reference before any valid key (finite)
 
@@ -244,13 +241,16 @@ __global__ __launch_bounds__(NT, 1) void mla_decode_kernel(
         }
         // keys 4g .. 4g+3 of key step ko = kt are B operand slots 4g .. 4g+3 of lane
         // 32(g/2) + 16(hq%2) + c16, head tile hq/2, bytes 8(g%2) .. +8
+        // The row sum takes the float32 weights; only the PV operand is rounded to bf16, so
+        // lse carries float32 accuracy (a sum of bf16-rounded weights would move it by up to
+        // 2^-9 when one key dominates).
         uint32_t pw[2];
         float psum = 0.0f;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {  // masked keys: exp2(-inf) = 0; bf16 round to nearest even
-          const bf16x2 pp = __builtin_convertvector(
-              (f32x2){exp2f(s[2 * j] - m_ref), exp2f(s[2 * j + 1] - m_ref)}, bf16x2);
-          psum += static_cast<float>(pp[0]) + static_cast<float>(pp[1]);
+          const float e0 = exp2f(s[2 * j] - m_ref), e1 = exp2f(s[2 * j + 1] - m_ref);
+          const bf16x2 pp = __builtin_convertvector((f32x2){e0, e1}, bf16x2);
+          psum += e0 + e1;
           pw[j] = __builtin_bit_cast(uint32_t, pp);
         }
         lsum += psum;
@@ -426,16 +426,14 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(const float* __restric
     lse[t * H + head] = L > 0.0f ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 
-#ifndef DSA_MLA_TARGET_BLOCKS
-#define DSA_MLA_TARGET_BLOCKS 160
-#endif
+constexpr int64_t TARGET_BLOCKS = 160;  // grids below this many blocks take more slices
 
 // Slices per row: at least ceil(k / 2048) (LDS index staging), then doubled while the
-// grid is below DSA_MLA_TARGET_BLOCKS blocks (one per CU) and each slice keeps >= 256
+// grid is below TARGET_BLOCKS blocks (one per CU) and each slice keeps >= 256
 // entries.
 int choose_splits(int64_t blocks_per_split, int k) {
   int s = static_cast<int>(ceil_div(k, MAX_KPS));
-  while (s < 16 && blocks_per_split * s < DSA_MLA_TARGET_BLOCKS && ceil_div(k, 2 * s) >= 256)
+  while (s < 16 && blocks_per_split * s < TARGET_BLOCKS && ceil_div(k, 2 * s) >= 256)
     s *= 2;
   return s;
 }

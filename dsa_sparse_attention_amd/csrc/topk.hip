@@ -46,7 +46,7 @@ constexpr int TK_WAVES = TK_THREADS / 64;
 constexpr int NSUB = 4;        // privatised level-1 histograms
 constexpr int CAND = 8192;     // slow-path LDS candidate capacity (key + position)
 constexpr int FAST_MAX = 65536;  // rows up to this length keep 16-bit keys in LDS
-constexpr int FCAND = 5984;     // fast-path candidate capacity
+constexpr int FCAND = 5952;     // fast-path candidate capacity
 constexpr int SSTEP = 8;        // register path: every eighth slot is a threshold sample
 constexpr int CW = 1024;        // register path: candidates per wave region (8 B each)
 
@@ -245,6 +245,437 @@ __device__ __forceinline__ void hist_add(uint32_t* h, bool act, uint32_t bin) {
   if (act && (lead || bin != b0)) atomicAdd(&h[bin], lead ? same : 1u);
 }
 
+// ---------------------------------------------------------------------------------------
+// Exact-boundary refine (see dsa_topk in dsa.h). With theta the k-th largest float32
+// score of a row and eps a bound on |I_f32 - I_exact| for every visible key, keys above
+// theta + 2 eps are in the exact top-k, keys below theta - 2 eps are not, and the band in
+// between is rescored exactly and ranked by (exact score desc, position asc).
+//  - The register path refines in place: the row is still in registers, so one pass
+//    over them marks the kept keys in a position bitmap and lists the band.
+//  - Every other path (rows whose sample missed, rows longer than 64K) runs the generic
+//    refine after its float32 selection is written: one more read of the row.
+// eps needs the largest key scale among the row's visible keys; a pre-pass stores the
+// maximum of every SC_CHUNK consecutive scales of each request, so no row rescans them.
+constexpr int BAND_CAP = 4096;   // band keys rescored per row
+constexpr int RF_MAXK = 4096;    // k supported by the refine
+constexpr int SC_CHUNK = 2048;   // key scales per stored maximum
+
+struct Refine {  // kernel argument; q_fp8 == nullptr: no refine
+  const uint8_t* q_fp8;
+  const float* q_scale;
+  const float* w;
+  const uint8_t* k_fp8;
+  const float* k_scale;
+  const float* kmax;  // [B, nsc] maxima of SC_CHUNK key scales each
+  int32_t* status;    // [T] or nullptr
+  double C;
+  int H, D, nsc;
+};
+
+struct RowRef {  // one row of a refine
+  Refine rf;
+  int64_t t;        // query row
+  int b;            // request
+  int64_t kv_base;  // first cache row of the request
+};
+
+// LDS of the refine, overlaid on the 128 KB candidate region once a selection no longer
+// needs it.
+constexpr int RS_TERMS = 4096;   // u_j max(d_j, 0) of one rescoring round: [head][key]
+struct RefineLds {
+  double band_val[BAND_CAP];      // exact band scores
+  double terms[RS_TERMS];
+  uint32_t digits[256];           // e4m3fn code -> its three signed base-128 digits (bytes 0..2)
+  int32_t band_pos[BAND_CAP];
+  int32_t sel_pos[RF_MAXK];
+  int32_t in_pos[RF_MAXK];
+  uint32_t bitmap[FAST_MAX / 32];  // register path: selected positions
+  double redd[TK_WAVES];
+  float redf[TK_WAVES];
+  uint32_t cnt[TK_WAVES];
+  int counters[4];
+  double eps;  // register path -> finish_register_refine
+  int nb, need;
+};
+static_assert(RF_MAXK >= BAND_CAP, "band scales and scores are staged in sel_pos / in_pos");
+static_assert(sizeof(RefineLds) <= 32768 * 4, "refine LDS overlays the 128 KB region");
+
+// e4m3fn code -> value (exact): normal (8 + m) 2^(e-10), subnormal m 2^-9; 0x7F/0xFF
+// (NaN) are never produced by the quantiser and decode here as 0.
+__device__ __forceinline__ double e4m3_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  double v = (e == 15u && m == 7u) ? 0.0
+             : e ? __builtin_ldexp(static_cast<double>(8u + m), static_cast<int>(e) - 10)
+                 : __builtin_ldexp(static_cast<double>(m), -9);
+  return (c & 0x80u) ? -v : v;
+}
+
+__device__ __forceinline__ double block_max_d(double x, double* red) {
+  for (int o = 32; o >= 1; o >>= 1) x = fmax(x, __shfl_xor(x, o));
+  if (threadIdx.x % 64 == 0) red[threadIdx.x / 64] = x;
+  __syncthreads();
+  double y = red[0];
+  for (int w = 1; w < TK_WAVES; ++w) y = fmax(y, red[w]);
+  __syncthreads();
+  return y;
+}
+
+// eps of a row (every thread gets it):
+//   C 2^-16 448 smax A  +  (H + 3) 2^-23 |theta|
+// A = sum_j |u_j| max_c |q_hat[t,j,c]| (u = w q_scale), smax = the largest key scale of the
+// SC_CHUNK chunks that hold the row's n visible keys. The first term is the FP8 MFMA's
+// accumulation error per head dot (up to C 2^-16 of the largest possible product, 448
+// max|q_hat_j|) weighted by |u_j| and the key scale; the second the float32 epilogue (H
+// products, H sums, the scale multiply) for nonnegative weights.
+// refine_prefetch leaves per-wave partial sums of A and maxima of smax in pa / ps (no block
+// barrier; issued before the selection so that its loads overlap the row's), and
+// refine_eps combines them once a block barrier has passed.
+__device__ __forceinline__ void refine_prefetch(const RowRef& rr, int64_t n, double* pa, float* ps) {
+  const Refine& rf = rr.rf;
+  const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+  const int H = rf.H, D = rf.D;
+  const int per_head = D / 8;  // threads per head, 8 codes each (16 or 8, a divisor of 64)
+  const uint2* q8 = reinterpret_cast<const uint2*>(rf.q_fp8 + rr.t * H * D);
+  double asum = 0.0;
+  for (int i0 = tid; i0 < H * per_head; i0 += TK_THREADS) {  // whole head groups stay together
+    const uint2 v = q8[i0];
+    uint32_t mc = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      mc = max(mc, (v.x >> (8 * e)) & 0x7Fu);
+      mc = max(mc, (v.y >> (8 * e)) & 0x7Fu);
+    }
+    for (int o = per_head / 2; o >= 1; o >>= 1)
+      mc = max(mc, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mc), o)));
+    if (i0 % per_head == 0) {
+      const int j = i0 / per_head;
+      const double u = static_cast<double>(rf.w[rr.t * H + j]) *
+                       static_cast<double>(rf.q_scale[rr.t * H + j]);
+      asum += __builtin_fabs(u) * e4m3_value(mc);  // codes with the sign bit cleared
+    }
+  }
+  float sm = 0.0f;
+  int nc = static_cast<int>((n + SC_CHUNK - 1) / SC_CHUNK);
+  if (nc > rf.nsc) nc = rf.nsc;  // rows are clipped to the score stride; stay in the table
+  for (int c = tid; c < nc; c += TK_THREADS)
+    sm = fmaxf(sm, rf.kmax[static_cast<int64_t>(rr.b) * rf.nsc + c]);
+  for (int o = 32; o >= 1; o >>= 1) {
+    asum += __shfl_xor(asum, o);
+    sm = fmaxf(sm, __shfl_xor(sm, o));
+  }
+  if (lane == 0) {
+    pa[wave] = asum;
+    ps[wave] = sm;
+  }
+}
+
+__device__ __forceinline__ double refine_eps(const Refine& rf, float theta, const double* pa,
+                                             const float* ps) {
+  double A = 0.0, smax = 0.0;
+  for (int w = 0; w < TK_WAVES; ++w) {  // fixed order: the same value in every thread
+    A += pa[w];
+    smax = fmax(smax, static_cast<double>(ps[w]));
+  }
+  const double C = rf.C > 0.0 ? rf.C : 4.0;
+  return C * 0x1p-16 * 448.0 * smax * A +
+         (rf.H + 3) * 0x1p-23 * __builtin_fabs(static_cast<double>(theta));
+}
+
+// The next float above / below a finite x (one ulp; -0 and +0 step to the smallest
+// subnormals).
+__device__ __forceinline__ float float_up(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if (x == 0.0f) return __uint_as_float(1u);
+  return __uint_as_float((u & 0x80000000u) ? u - 1u : u + 1u);
+}
+
+__device__ __forceinline__ float float_down(float x) { return -float_up(-x); }
+
+// Float thresholds around theta: x > hi_f implies x > theta + 2 eps, and x >= lo_f holds for
+// every x >= theta - 2 eps (rounded outwards, so the band can only grow). Finite inputs.
+__device__ __forceinline__ void band_edges(float theta, double eps, float* lo_f, float* hi_f) {
+  const double hi = static_cast<double>(theta) + 2.0 * eps;
+  const double lo = static_cast<double>(theta) - 2.0 * eps;
+  float h = static_cast<float>(hi), l = static_cast<float>(lo);
+  if (static_cast<double>(h) < hi) h = float_up(h);
+  if (static_cast<double>(l) > lo) l = float_down(l);
+  *hi_f = h;
+  *lo_f = l;
+}
+
+// The exact value of e4m3fn code c times 2^9 is an integer of magnitude below 2^18: (8 + m)
+// 2^(e-1) for a normal code, m for a subnormal one. Written x = x0 + 2^7 x1 + 2^14 x2 in base
+// 128, each digit carrying the code's sign, it packs into one word as three signed bytes
+// (|x0|, |x1| <= 127, |x2| <= 15).
+__device__ __forceinline__ uint32_t e4m3_digit_word(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const uint32_t x = e ? (8u + m) << (e - 1u) : m;
+  const bool neg = (c & 0x80u) != 0u;
+  uint32_t word = 0;
+#pragma unroll
+  for (int p = 0; p < 3; ++p) {
+    const uint32_t dgt = (x >> (7 * p)) & 127u;
+    word |= ((neg ? 0u - dgt : dgt) & 0xFFu) << (8 * p);
+  }
+  return word;
+}
+
+// The digit words (e4m3_digit_word, from the LDS table) of sixteen codes (one 16-byte load).
+__device__ __forceinline__ void digit_words(i32x4 codes, const uint32_t* table, uint32_t (&wd)[16]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    wd[i] = table[(static_cast<uint32_t>(codes[i / 4]) >> (8 * (i % 4))) & 0xFFu];
+}
+
+// Digit plane p of sixteen codes as an int8 MFMA operand: byte i of the operand is digit p of
+// code i.
+__device__ __forceinline__ i32x4 digit_plane(const uint32_t (&wd)[16], int p) {
+  i32x4 out;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t packed = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) packed |= ((wd[4 * w + b] >> (8 * p)) & 0xFFu) << (8 * b);
+    out[w] = static_cast<int>(packed);
+  }
+  return out;
+}
+
+// Exact scores of the nb band keys (positions in L.band_pos, request-local) into
+// L.band_val; returns (to every thread) the largest |I_f32 - I_exact| over the band, I_f32
+// read from srow.
+//   I_exact = s_k * sum_{j ascending} u_j * max(d_j, 0), d_j = q_hat[t,j] . k_hat (exact),
+// evaluated in float64 with one rounding per product and per sum.
+// The head dots are exact integer arithmetic on the int8 MFMA: every e4m3fn value times 2^9
+// is an integer below 2^18, split into three base-128 digits; the nine digit-plane products
+// (v_mfma_i32_16x16x64_i8, int32 accumulation, |sum| < 2^21 per plane pair) recombine
+// exactly in float64 (|d| 2^18 < 2^43). A wave takes one tile of 16 heads x 16 band keys
+// per round; the u_j max(d_j, 0) terms of a round go to LDS, and one thread per key then
+// adds them in ascending head order.
+__device__ __forceinline__ double rescore_band(const RowRef& rr, const float* __restrict__ srow,
+                                               int nb, RefineLds& L, bool table_ready) {
+  const Refine& rf = rr.rf;
+  const int tid = threadIdx.x, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int H = rf.H, D = rf.D;
+  const int HT = H <= 16 ? 1 : H <= 32 ? 2 : H <= 64 ? 4 : 8;  // 16-head tiles (padded)
+  const int KPR = 256 / HT;            // keys per round: (16 / HT) tiles of 16
+  const int ht = wave % HT, kt = wave / HT;
+  const int c16 = lane % 16, g = lane / 16;
+  const int64_t t = rr.t;
+  const uint8_t* __restrict__ kreq = rf.k_fp8 + rr.kv_base * D;
+  const float* __restrict__ ksc = rf.k_scale + rr.kv_base;
+  const int halves = D / 64;           // K = 64 per MFMA
+  const int slot = 16 * kt + c16;      // this lane's key within a round
+  // B operand codes of band key base + slot: dims 64 h + 16 g .. + 16 (zeros past the band)
+  auto load_keys = [&](int base, i32x4 (&kc)[2]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      kc[h] = (i32x4){0, 0, 0, 0};
+      if (h < halves && base + slot < nb)
+        kc[h] = *reinterpret_cast<const i32x4*>(
+            kreq + static_cast<int64_t>(L.band_pos[base + slot]) * D + 64 * h + 16 * g);
+    }
+  };
+  // every global load of the first round is issued before any is used: the first round's
+  // key codes, this lane's query codes (head 16 ht + c16, dims 64 h + 16 g .. + 16; heads
+  // past H are 0) and the weights of its output heads 16 ht + 4 g + i
+  i32x4 kc[2];
+  load_keys(0, kc);
+  i32x4 qc[2];
+  {
+    const int head = 16 * ht + c16;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      qc[h] = (i32x4){0, 0, 0, 0};
+      if (h < halves && head < H)
+        qc[h] = *reinterpret_cast<const i32x4*>(rf.q_fp8 + (t * H + head) * D + 64 * h + 16 * g);
+    }
+  }
+  double u[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int head = 16 * ht + 4 * g + i;
+    u[i] = head < H ? static_cast<double>(rf.w[t * H + head]) * static_cast<double>(rf.q_scale[t * H + head])
+                    : 0.0;
+  }
+  // every band key's scale and float32 score, staged in LDS while the loads above are in
+  // flight (sel_pos and in_pos are free until the band is chosen)
+  float* band_sk = reinterpret_cast<float*>(L.sel_pos);
+  float* band_f32 = reinterpret_cast<float*>(L.in_pos);
+  for (int i = tid; i < nb; i += TK_THREADS) {
+    const int32_t p = L.band_pos[i];
+    band_sk[i] = ksc[p];
+    band_f32[i] = srow[p];
+  }
+  if (!table_ready) {  // block-uniform
+    for (int c = tid; c < 256; c += TK_THREADS) L.digits[c] = e4m3_digit_word(static_cast<uint32_t>(c));
+    __syncthreads();
+  }
+  i32x4 qa[2][3];  // A operands: the query digit planes
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t wd[16];
+    digit_words(qc[h], L.digits, wd);
+#pragma unroll
+    for (int p = 0; p < 3; ++p) qa[h][p] = digit_plane(wd, p);
+  }
+  double worst = 0.0;
+  for (int base = 0; base < nb; base += KPR) {  // block-uniform rounds
+    if (base > 0) load_keys(base, kc);
+    if (base + 16 * kt < nb) {  // wave-uniform: the tile holds at least one band key
+      i32x4 kb[2][3];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t wd[16];
+        digit_words(kc[h], L.digits, wd);
+#pragma unroll
+        for (int p = 0; p < 3; ++p) kb[h][p] = digit_plane(wd, p);
+      }
+      double d[4] = {0.0, 0.0, 0.0, 0.0};  // exact dots times 2^18, heads 4 g + i, key c16
+#pragma unroll
+      for (int a = 0; a < 3; ++a)
+#pragma unroll
+        for (int b = 0; b < 3; ++b) {
+          i32x4 acc = {0, 0, 0, 0};
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[0][a], kb[0][b], acc, 0, 0, 0);
+          if (halves > 1) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[1][a], kb[1][b], acc, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) d[i] += __builtin_ldexp(static_cast<double>(acc[i]), 7 * (a + b));
+        }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int head = 16 * ht + 4 * g + i;
+        if (head < H) {
+          const double dj = __builtin_ldexp(d[i], -18);
+          L.terms[head * KPR + slot] = __dmul_rn(u[i], dj > 0.0 ? dj : 0.0);
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < KPR && base + tid < nb) {  // one thread per key: heads in ascending order
+      const float sk = band_sk[base + tid], f32 = band_f32[base + tid];
+      double acc = 0.0;
+      for (int j0 = 0; j0 < H; j0 += 8) {  // eight terms read ahead, added in order
+        double tv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) tv[j] = j0 + j < H ? L.terms[(j0 + j) * KPR + tid] : 0.0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (j0 + j < H) acc = __dadd_rn(acc, tv[j]);
+      }
+      const double ex = __dmul_rn(acc, static_cast<double>(sk));
+      L.band_val[base + tid] = ex;
+      worst = fmax(worst, __builtin_fabs(static_cast<double>(f32) - ex));
+    }
+    __syncthreads();
+  }
+  return block_max_d(worst, L.redd);
+}
+
+// Bitonic sort of np2 (a power of two) LDS entries by `before`, one compare-exchange per
+// pair and stage, the whole block taking part.
+template <class Before, class Swap>
+__device__ __forceinline__ void block_bitonic(int np2, Before before, Swap swap) {
+  for (int size = 2; size <= np2; size <<= 1) {
+    for (int stride = size / 2; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < np2 / 2; i += TK_THREADS) {
+        const int a = 2 * i - (i & (stride - 1)), c = a + stride;
+        const bool up = (a & size) == 0;
+        if (up ? before(c, a) : before(a, c)) swap(a, c);
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__device__ __forceinline__ int next_pow2(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+// The best `need` of the nb band keys by (exact score desc, position asc). With SORTED,
+// their positions go to L.sel_pos in ascending order; otherwise each is set in L.bitmap.
+template <bool SORTED>
+__device__ __forceinline__ void choose_band(int nb, int need, RefineLds& L) {
+  const int tid = threadIdx.x, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  if (nb <= 64) {  // one wave ranks the band with register broadcasts: no block barriers
+    if (wave == 0) {
+      const bool live = lane < nb;
+      const double v = live ? L.band_val[lane] : -__builtin_inf();
+      const int32_t p = live ? L.band_pos[lane] : 0x7FFFFFFF;
+      const int vlo = __double2loint(v), vhi = __double2hiint(v);
+      int rank = 0;
+      for (int m = 0; m < nb; ++m) {
+        const double vm = __hiloint2double(__builtin_amdgcn_readlane(vhi, m),
+                                           __builtin_amdgcn_readlane(vlo, m));
+        const int32_t pm = __builtin_amdgcn_readlane(p, m);
+        rank += (vm > v || (vm == v && pm < p)) ? 1 : 0;
+      }
+      const bool take = live && rank < need;
+      if constexpr (SORTED) {
+        int at = 0;  // rank by position among the taken keys
+        for (int m = 0; m < nb; ++m) {
+          const int32_t pm = __builtin_amdgcn_readlane(p, m);
+          const bool tm = __builtin_amdgcn_readlane(take ? 1 : 0, m) != 0;
+          at += (tm && pm < p) ? 1 : 0;
+        }
+        if (take) L.sel_pos[at] = p;
+      } else {
+        if (take) atomicOr(&L.bitmap[p >> 5], 1u << (p & 31));
+      }
+    }
+    __syncthreads();
+    return;
+  }
+  // pad the band to a power of two with entries that sort last, then bitonic sorts
+  const int np2 = next_pow2(nb);
+  for (int i = nb + tid; i < np2; i += TK_THREADS) {
+    L.band_val[i] = -__builtin_inf();
+    L.band_pos[i] = 0x7FFFFFFF;
+  }
+  __syncthreads();
+  block_bitonic(
+      np2,
+      [&](int x, int y) {
+        return L.band_val[x] > L.band_val[y] ||
+               (L.band_val[x] == L.band_val[y] && L.band_pos[x] < L.band_pos[y]);
+      },
+      [&](int x, int y) {
+        const double v = L.band_val[x];
+        L.band_val[x] = L.band_val[y];
+        L.band_val[y] = v;
+        const int32_t q = L.band_pos[x];
+        L.band_pos[x] = L.band_pos[y];
+        L.band_pos[y] = q;
+      });
+  if constexpr (SORTED) {
+    const int ns2 = next_pow2(need > 1 ? need : 2);
+    for (int i = tid; i < ns2; i += TK_THREADS) L.sel_pos[i] = i < need ? L.band_pos[i] : 0x7FFFFFFF;
+    __syncthreads();
+    block_bitonic(
+        ns2, [&](int x, int y) { return L.sel_pos[x] < L.sel_pos[y]; },
+        [&](int x, int y) {
+          const int32_t q = L.sel_pos[x];
+          L.sel_pos[x] = L.sel_pos[y];
+          L.sel_pos[y] = q;
+        });
+  } else {
+    for (int i = tid; i < need; i += TK_THREADS)
+      atomicOr(&L.bitmap[L.band_pos[i] >> 5], 1u << (L.band_pos[i] & 31));
+    __syncthreads();
+  }
+}
+
+// Status of a refined row: the band size, or -4 when a band key's float32 score is off
+// its exact value by more than eps / 2 (the set is the refined one, but the margin the
+// bound assumes is not there).
+__device__ __forceinline__ int32_t refine_status(int nb, double worst, double eps) {
+  return worst > 0.5 * eps ? -4 : nb;
+}
+
 // Register path for a row of k < n <= 16 * 64 * RS visible scores (see the top of the
 // file); wave w holds positions 64 RS w + 64 r + lane in slot r < RS (RS = 64 for rows
 // up to 64K; shorter rows take fewer slots per lane, so their candidates still spread
@@ -252,11 +683,20 @@ __device__ __forceinline__ void hist_add(uint32_t* h, bool act, uint32_t bin) {
 // the block, when the sampled threshold admits fewer than k keys or more than a wave
 // region holds, or theta's class falls outside the class histogram; nothing has been
 // written to `out` then. cand: 128 KB of LDS (16 wave regions of CW key bits followed by
-// CW positions); hist: 1280 words; rs: 80 words.
+// CW positions); hist: 1280 words; rs: 80 words; tmp: 32 words.
+// Returns REG_DONE with the selection written, REG_FALLBACK as described, or, with
+// `refine`, REG_BAND: the kept keys are in the refine's position bitmap and the band in its
+// list (one pass over the registers), and finish_register_refine completes the row. A band
+// that cannot be resolved here (it overflows, or eps is not finite) gives REG_FALLBACK, and
+// the generic refine decides after the LDS path.
+constexpr int REG_FALLBACK = 0, REG_DONE = 1, REG_BAND = 2;
+
 template <int RS>
-__device__ __forceinline__ bool select_in_registers(const float* __restrict__ srow, int n, int k,
+__device__ __forceinline__ int select_in_registers(const float* __restrict__ srow, int n, int k,
                                                     int32_t* __restrict__ out, uint32_t* cand,
-                                                    uint32_t* hist, uint32_t* rs) {
+                                                    uint32_t* hist, uint32_t* rs, uint32_t* tmp,
+                                                    const RowRef& rr, bool refine, double* pa,
+                                                    float* ps) {
   const int tid = threadIdx.x, lane = tid % 64;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int p0 = wave * (64 * RS) + lane;  // wave w holds positions [64 RS w, 64 RS (w + 1))
@@ -295,6 +735,8 @@ __device__ __forceinline__ bool select_in_registers(const float* __restrict__ sr
     for (int r = 0; r < RS; ++r) v[r] = -__builtin_inff();
   }
   for (int i = tid; i < 1280; i += TK_THREADS) hist[i] = 0;
+  // the refine's query-side bound: its loads queue behind the row's, whose wait comes next
+  if (refine) refine_prefetch(rr, n, pa, ps);
 
   // ---- threshold: 16-bit classes of the samples below their maximum ----
   uint32_t smax = 0, scount = 0;
@@ -384,7 +826,7 @@ __device__ __forceinline__ bool select_in_registers(const float* __restrict__ sr
   __syncthreads();
   const uint32_t wc = lane < TK_WAVES ? rs[32 + lane] : 0u;
   const uint32_t total = wave_sum(wc);
-  if (wave_max(wc) > static_cast<uint32_t>(CW) || total < static_cast<uint32_t>(k)) return false;
+  if (wave_max(wc) > static_cast<uint32_t>(CW) || total < static_cast<uint32_t>(k)) return REG_FALLBACK;
   const uint32_t cw = cnt;
 
   // this lane's candidate keys (region entries lane + 64 j); 0 marks no candidate, since
@@ -421,7 +863,7 @@ __device__ __forceinline__ bool select_in_registers(const float* __restrict__ sr
   __syncthreads();
   uint32_t b1, above;
   wave_select<512>(h1, k, &b1, &above);
-  if (b1 == 0 || (gap && b1 == 255)) return false;
+  if (b1 == 0 || (gap && b1 == 255)) return REG_FALLBACK;
   const uint32_t c16t = gap && b1 > 255 ? c16 + (511 - b1) : static_cast<uint32_t>(R) - b1;
   uint32_t need = k - above;
   // ---- select 2: bits 15..8 of the keys in theta's class ----
@@ -442,6 +884,65 @@ __device__ __forceinline__ bool select_in_registers(const float* __restrict__ sr
   wave_select<256>(h3, need, &b3, &above);
   const uint32_t theta = (p24 << 8) | (255 - b3);
   need -= above;
+
+  if (refine) {
+    // ---- refine in registers: theta's band lies among the compacted candidates unless it
+    // reaches below their threshold class (then the generic refine decides). Kept keys go
+    // to a position bitmap, band keys to a list; finish_register_refine rescores the band,
+    // adds its best keys to the bitmap and emits it in ascending order ----
+    RefineLds& L = *reinterpret_cast<RefineLds*>(cand);
+    uint32_t preg[KJ];  // this lane's candidate positions, read before L overlays the regions
+#pragma unroll
+    for (int j = 0; j < KJ; ++j) preg[j] = region[CW + lane + 64 * j];
+    __syncthreads();  // every wave is done with its region
+    const float th = __uint_as_float((theta & 0x80000000u) ? (theta & 0x7FFFFFFFu) : ~theta);
+    if (tid < 4) L.counters[tid] = 0;
+    for (int i = tid; i < FAST_MAX / 32; i += TK_THREADS) L.bitmap[i] = 0u;
+    if (tid < 256) L.digits[tid] = e4m3_digit_word(static_cast<uint32_t>(tid));  // for the rescore
+    const double eps = refine_eps(rr.rf, th, pa, ps);
+    if (!__builtin_isfinite(th) || !__builtin_isfinite(eps)) return REG_FALLBACK;  // uniform
+    __syncthreads();  // the cleared counters and bitmap are visible
+    float lo_f, hi_f;
+    band_edges(th, eps, &lo_f, &hi_f);
+    const uint32_t lo_k = order_key(lo_f), hi_k = order_key(hi_f);
+    if (lo_k < (c16 << 16)) return REG_FALLBACK;  // uniform: the band reaches below the candidates
+    uint32_t kept_w = 0;
+#pragma unroll
+    for (int j = 0; j < KJ; ++j) {
+      if (64 * j < static_cast<int>(cw)) {  // wave-uniform
+        const uint32_t key = kreg[j];       // 0: no candidate
+        const bool kp = key != 0u && key > hi_k;
+        const bool bd = key != 0u && !kp && key >= lo_k;
+        const int p = static_cast<int>(preg[j]);
+        if (kp) atomicOr(&L.bitmap[p >> 5], 1u << (p & 31));
+        kept_w += static_cast<uint32_t>(__popcll(__builtin_amdgcn_ballot_w64(kp)));
+        const uint64_t bb = __builtin_amdgcn_ballot_w64(bd);
+        if (bb) {
+          int base = 0;
+          if (lane == 0) base = atomicAdd(&L.counters[0], static_cast<int>(__popcll(bb)));
+          base = __builtin_amdgcn_readfirstlane(base);
+          if (bd) {
+            const int slot = base + static_cast<int>(lanes_below(bb));
+            if (slot < BAND_CAP) L.band_pos[slot] = p;
+          }
+        }
+      }
+    }
+    if (lane == 0) L.cnt[wave] = kept_w;
+    __syncthreads();
+    const int nb = L.counters[0];
+    int kept = 0;
+    for (int w2 = 0; w2 < TK_WAVES; ++w2) kept += static_cast<int>(L.cnt[w2]);
+    const int need_b = k - kept;
+    if (nb > BAND_CAP || need_b < 1 || need_b > nb) return REG_FALLBACK;  // uniform
+    if (tid == 0) {
+      L.eps = eps;
+      L.nb = nb;
+      L.need = need_b;
+    }
+    __syncthreads();
+    return REG_BAND;
+  }
 
   // ---- emission: keys > theta and the first `need` theta-ties, ascending positions ----
   uint32_t gt = 0, eq = 0;
@@ -489,38 +990,39 @@ __device__ __forceinline__ bool select_in_registers(const float* __restrict__ sr
       run_sel += static_cast<uint32_t>(__popcll(bt));
     }
   }
-  return true;
+  return REG_DONE;
 }
 
-// Top-k of one score row of n entries (entries 0..n-1 of srow) by (score desc, index asc),
-// written ascending to out[0..k), -1 padded. Called by a whole TK_THREADS block.
-__device__ __forceinline__ void select_row(const float* __restrict__ srow, int64_t n, int k,
-                                           int32_t* __restrict__ out) {
-  // Region A (128 KB): 16-bit keys of the fast path; reused by both paths afterwards.
-  __shared__ __attribute__((aligned(16))) uint32_t regA[32768];
-  __shared__ uint32_t fhist[2048];
-  __shared__ int32_t fpos[FCAND];
-  __shared__ uint32_t tmp[2 * TK_WAVES];
-  __shared__ uint32_t sel[2];
-  __shared__ uint32_t smax;
-  __shared__ uint32_t rs[80];  // register path: per-wave maxima and counts
+// LDS of one top-k block (one row at a time).
+struct TopkLds {
+  uint32_t regA[32768];  // 128 KB: register-path regions, 16-bit keys, slow-path histograms
+                         // and candidates, or the refine (RefineLds)
+  uint32_t fhist[2048];
+  int32_t fpos[FCAND];
+  uint32_t tmp[2 * TK_WAVES];
+  uint32_t sel[2];
+  uint32_t smax;
+  uint32_t rs[80];  // register path: per-wave maxima and counts
+  double rf_a[TK_WAVES];  // refine: per-wave partials of eps (refine_prefetch)
+  float rf_s[TK_WAVES];
+};
+
+// Float32 top-k of one score row by the LDS paths (every row length): writes the
+// selection ascending to out[0..k), -1 padded. Requires n > k.
+__device__ __forceinline__ void select_row_lds(const float* __restrict__ srow, int64_t n, int k,
+                                               int32_t* __restrict__ out, TopkLds& S) {
+  uint32_t* regA = S.regA;
+  uint32_t* fhist = S.fhist;
+  int32_t* fpos = S.fpos;
+  uint32_t* tmp = S.tmp;
+  uint32_t* sel = S.sel;
+  uint32_t& smax = S.smax;
   uint32_t (*hist)[2048] = reinterpret_cast<uint32_t (*)[2048]>(regA);  // slow path: NSUB x 8 KB
   uint32_t* ckey = regA + NSUB * 2048;                                  // slow path: 32 KB
   int32_t* cpos = reinterpret_cast<int32_t*>(regA + NSUB * 2048 + CAND);  // slow path: 32 KB
 
   const int tid = threadIdx.x, wave = tid / 64;
-  if (n <= k) {
-    for (int i = tid; i < k; i += TK_THREADS) out[i] = i < n ? i : -1;
-    return;
-  }
-
   if (n <= FAST_MAX) {
-    const int ni = static_cast<int>(n);
-    const bool done = n <= 16 * 64 * 8    ? select_in_registers<8>(srow, ni, k, out, regA, fhist, rs)
-                      : n <= 16 * 64 * 16 ? select_in_registers<16>(srow, ni, k, out, regA, fhist, rs)
-                                          : select_in_registers<64>(srow, ni, k, out, regA, fhist, rs);
-    if (done) return;
-    __syncthreads();  // fall back to the exact LDS path (region A and fhist are reused)
     // ---- fast path A: one read of the row; top 16 key bits to LDS, row maximum ----
     uint16_t* k16 = reinterpret_cast<uint16_t*>(regA);
     if (tid == 0) smax = 0;
@@ -777,31 +1279,240 @@ __device__ __forceinline__ void select_row(const float* __restrict__ srow, int64
                [&](int64_t i) { return static_cast<int32_t>(i); });
 }
 
+__device__ __forceinline__ void refine_generic(const float* __restrict__ srow, int64_t n, int k,
+                                               int32_t* __restrict__ out, const RowRef& rr,
+                                               RefineLds& L, uint32_t* tmp, const double* pa,
+                                               const float* ps);
+
+// The rest of a register-path refine (REG_BAND): rescore the band, add its best keys to the
+// bitmap, and emit the bitmap's positions in ascending order (thread i takes words 2i and
+// 2i + 1, positions 64 i .. 64 i + 63).
+__device__ __forceinline__ void finish_register_refine(const float* __restrict__ srow, int n,
+                                                       int k, int32_t* __restrict__ out,
+                                                       const RowRef& rr, RefineLds& L,
+                                                       uint32_t* tmp) {
+  const int tid = threadIdx.x;
+  const int nb = L.nb, need = L.need;
+  const double eps = L.eps;
+  const double worst = rescore_band(rr, srow, nb, L, true);
+  choose_band<false>(nb, need, L);
+  const int nw = (n + 31) / 32;
+  const uint32_t wd0 = 2 * tid < nw ? L.bitmap[2 * tid] : 0u;
+  const uint32_t wd1 = 2 * tid + 1 < nw ? L.bitmap[2 * tid + 1] : 0u;
+  uint32_t total;
+  uint32_t o = block_excl_scan(static_cast<uint32_t>(__popc(wd0) + __popc(wd1)), tmp, &total);
+  auto emit = [&](uint32_t wd, int pos0) {
+    while (wd) {
+      const int j = __builtin_ctz(wd);
+      wd &= wd - 1;
+      if (o < static_cast<uint32_t>(k)) out[o] = pos0 + j;
+      ++o;
+    }
+  };
+  emit(wd0, 64 * tid);
+  emit(wd1, 64 * tid + 32);
+  if (tid == 0 && rr.rf.status)
+    rr.rf.status[rr.t] = total == static_cast<uint32_t>(k) ? refine_status(nb, worst, eps) : -3;
+}
+
+// Top-k of one score row of n entries (entries 0..n-1 of srow) by (score desc, index asc),
+// written ascending to out[0..k), -1 padded; with `refine`, by the exact scores (see the
+// refine section). Called by a whole TK_THREADS block.
+__device__ __forceinline__ void select_row(const float* __restrict__ srow, int64_t n, int k,
+                                           int32_t* __restrict__ out, TopkLds& S,
+                                           const RowRef& rr, bool refine) {
+  const int tid = threadIdx.x;
+  if (n <= k) {
+    for (int i = tid; i < k; i += TK_THREADS) out[i] = i < n ? i : -1;
+    if (refine && tid == 0 && rr.rf.status) rr.rf.status[rr.t] = 0;
+    return;
+  }
+  if (n <= FAST_MAX) {
+    const int ni = static_cast<int>(n);
+    const int rc =
+        n <= 16 * 64 * 8    ? select_in_registers<8>(srow, ni, k, out, S.regA, S.fhist, S.rs, S.tmp, rr, refine, S.rf_a, S.rf_s)
+        : n <= 16 * 64 * 16 ? select_in_registers<16>(srow, ni, k, out, S.regA, S.fhist, S.rs, S.tmp, rr, refine, S.rf_a, S.rf_s)
+                            : select_in_registers<64>(srow, ni, k, out, S.regA, S.fhist, S.rs, S.tmp, rr, refine, S.rf_a, S.rf_s);
+    if (rc == REG_DONE) return;
+    if (rc == REG_BAND) {
+      finish_register_refine(srow, ni, k, out, rr, *reinterpret_cast<RefineLds*>(S.regA), S.tmp);
+      return;
+    }
+    __syncthreads();  // fall back to the exact LDS path (region A and fhist are reused)
+  }
+  select_row_lds(srow, n, k, out, S);
+  if (refine) {
+    refine_prefetch(rr, n, S.rf_a, S.rf_s);
+    __syncthreads();  // the block's selection stores are visible to its own loads after this
+    refine_generic(srow, n, k, out, rr, *reinterpret_cast<RefineLds*>(S.regA), S.tmp, S.rf_a,
+                   S.rf_s);
+  }
+}
+
+// Generic refine of a row whose float32 selection is already in out[0..k) (written by this
+// block): theta is the smallest selected score; one pass over the row counts the kept keys
+// and collects the band; the band is rescored exactly and its best keys are merged with the
+// kept ones, ascending. On a band it cannot resolve (more than BAND_CAP keys, or counts
+// that disagree) the float32 selection stays and the status says why.
+__device__ __forceinline__ void refine_generic(const float* __restrict__ srow, int64_t n, int k,
+                                               int32_t* __restrict__ out, const RowRef& rr,
+                                               RefineLds& L, uint32_t* tmp, const double* pa,
+                                               const float* ps) {
+  const int tid = threadIdx.x;
+  int32_t* status = rr.rf.status;
+  // ---- 1. theta; loads are issued eight at a time per thread ----
+  constexpr int U = 8;
+  float th = __builtin_inff();
+  for (int i0 = tid; i0 < k; i0 += U * TK_THREADS) {
+    int32_t pp[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) pp[u] = i0 + u * TK_THREADS < k ? out[i0 + u * TK_THREADS] : -1;
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      v[u] = __builtin_inff();
+      if (pp[u] >= 0) v[u] = srow[pp[u]];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) th = fminf(th, v[u]);
+  }
+  if (tid < 4) L.counters[tid] = 0;
+  th = static_cast<float>(-block_max_d(-static_cast<double>(th), L.redd));  // publishes counters
+  const double eps = refine_eps(rr.rf, th, pa, ps);
+  if (!__builtin_isfinite(th) || !__builtin_isfinite(eps)) {
+    if (tid == 0 && status) status[rr.t] = -2;
+    return;
+  }
+  float lo_f, hi_f;
+  band_edges(th, eps, &lo_f, &hi_f);
+
+  // ---- 2. kept keys (counted) and the band (collected); float4 loads, four in flight ----
+  uint32_t nin = 0;
+  auto classify = [&](float x, int64_t s) {
+    if (x > hi_f) {
+      ++nin;
+    } else if (x >= lo_f) {
+      const int slot = atomicAdd(&L.counters[0], 1);
+      if (slot < BAND_CAP) L.band_pos[slot] = static_cast<int32_t>(s);
+    }
+  };
+  const int64_t n4 = n / 4;
+  const float4* s4 = reinterpret_cast<const float4*>(srow);  // rows are 16-byte aligned
+  for (int64_t i0 = tid; i0 < n4; i0 += 4 * TK_THREADS) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (i0 + u * TK_THREADS < n4) v[u] = s4[i0 + u * TK_THREADS];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = i0 + u * TK_THREADS;
+      if (i < n4) {
+        classify(v[u].x, 4 * i);
+        classify(v[u].y, 4 * i + 1);
+        classify(v[u].z, 4 * i + 2);
+        classify(v[u].w, 4 * i + 3);
+      }
+    }
+  }
+  for (int64_t s = 4 * n4 + tid; s < n; s += TK_THREADS) classify(srow[s], s);
+  uint32_t nin_total;
+  block_excl_scan(nin, tmp, &nin_total);  // ends with a barrier: the counter is final
+  const int nb = L.counters[0];
+  const int need = k - static_cast<int>(nin_total);
+  if (nb > BAND_CAP || need < 1 || need > nb) {  // uniform: keep the float32 selection
+    if (tid == 0 && status) status[rr.t] = nb > BAND_CAP ? -1 : -2;
+    return;
+  }
+
+  // ---- 3. exact rescore; 4. the best `need` band keys, ascending, in sel_pos ----
+  const double worst = rescore_band(rr, srow, nb, L, false);
+  choose_band<true>(nb, need, L);
+
+  // ---- 5. merge with the kept keys of the current (ascending) selection; k <= RF_MAXK, so
+  // at most four entries per thread, taken as one contiguous run ----
+  constexpr int PER = RF_MAXK / TK_THREADS;
+  int32_t mine[PER];
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = tid * PER + j;
+    mine[j] = -1;
+    if (i < k) {
+      const int32_t p = out[i];
+      if (srow[p] > hi_f) {
+        mine[j] = p;
+        ++cnt;
+      }
+    }
+  }
+  uint32_t kept;
+  uint32_t at = block_excl_scan(cnt, tmp, &kept);  // ends with a barrier
+  if (kept != nin_total) {  // uniform; cannot happen for a correct float32 selection
+    if (tid == 0 && status) status[rr.t] = -3;
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    if (mine[j] >= 0) L.in_pos[at++] = mine[j];
+  __syncthreads();
+  auto count_below = [](const int32_t* a, int len, int32_t p) {  // a ascending
+    int lo_i = 0, hi_i = len;
+    while (lo_i < hi_i) {
+      const int mid = (lo_i + hi_i) / 2;
+      if (a[mid] < p) lo_i = mid + 1;
+      else hi_i = mid;
+    }
+    return lo_i;
+  };
+  for (int i = tid; i < static_cast<int>(kept); i += TK_THREADS)
+    out[i + count_below(L.sel_pos, need, L.in_pos[i])] = L.in_pos[i];
+  for (int i = tid; i < need; i += TK_THREADS)
+    out[i + count_below(L.in_pos, static_cast<int>(kept), L.sel_pos[i])] = L.sel_pos[i];
+  if (tid == 0 && status) status[rr.t] = refine_status(nb, worst, eps);
+}
+
+__device__ __forceinline__ RowRef row_ref(const Refine& rf, int64_t t, int b, int64_t kv_base) {
+  RowRef rr;
+  rr.rf = rf;
+  rr.t = t;
+  rr.b = b;
+  rr.kv_base = kv_base;
+  return rr;
+}
+
 // One block per row: rows of up to FAST_MAX visible scores, and every row when the grid
 // has no chunk stage.
 __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const float* __restrict__ scores,
                                                           int64_t ld,
                                                           const int32_t* __restrict__ q_off,
                                                           const int64_t* __restrict__ kv_off,
-                                                          int k, int32_t* __restrict__ topk) {
+                                                          int k, int32_t* __restrict__ topk,
+                                                          Refine rf) {
+  __shared__ __attribute__((aligned(16))) TopkLds S;
   const int b = blockIdx.y, r = blockIdx.x;
   const RowInfo ri = load_row_info(q_off, kv_off, b);
   if (r >= ri.R) return;
   const int64_t t = ri.t0 + r;
   int64_t n = visible_count(ri, r);
   if (n > ld) n = ld;  // device lengths beyond the score stride are clipped
-  select_row(scores + t * ld, n, k, topk + t * k);
+  select_row(scores + t * ld, n, k, topk + t * k, S, row_ref(rf, t, b, ri.kv_base),
+             rf.q_fp8 != nullptr);
 }
 
 // Grids with rows longer than FAST_MAX, stage 1: block (chunk c, row) selects the top-k of
 // visible positions [c FAST_MAX, (c+1) FAST_MAX) as chunk-local indices into widx
 // [T, nchunk, k] and their scores into the row's candidate scores cand_s (chunk c at
-// offset c k; -inf where the index is -1). Every key of the row's top-k is in the top-k
-// of its chunk. A row of at most FAST_MAX positions is finished here by its chunk-0 block.
+// offset c k; -inf where the index is -1). Every key of the row's float32 top-k is in the
+// top-k of its chunk. A row of at most FAST_MAX positions is finished here by its chunk-0
+// block (refine included).
 __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ q_off,
     const int64_t* __restrict__ kv_off, int k, int nchunk, int64_t cstride,
-    int32_t* __restrict__ widx, float* __restrict__ cand_s, int32_t* __restrict__ topk) {
+    int32_t* __restrict__ widx, float* __restrict__ cand_s, int32_t* __restrict__ topk,
+    Refine rf) {
+  __shared__ __attribute__((aligned(16))) TopkLds S;
   const int b = blockIdx.y, r = blockIdx.x / nchunk, c = blockIdx.x % nchunk;
   const RowInfo ri = load_row_info(q_off, kv_off, b);
   if (r >= ri.R) return;
@@ -809,15 +1520,16 @@ __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(
   int64_t n = visible_count(ri, r);
   if (n > ld) n = ld;
   const float* srow = scores + t * ld;
+  const RowRef rr = row_ref(rf, t, b, ri.kv_base);
   if (n <= FAST_MAX) {
-    if (c == 0) select_row(srow, n, k, topk + t * k);
+    if (c == 0) select_row(srow, n, k, topk + t * k, S, rr, rf.q_fp8 != nullptr);
     return;
   }
   const int64_t c0 = static_cast<int64_t>(c) * FAST_MAX;
   if (c0 >= n) return;  // the merge reads only the chunks holding visible positions
   const int64_t nc = n - c0 < FAST_MAX ? n - c0 : FAST_MAX;
   int32_t* o = widx + (t * nchunk + c) * k;
-  select_row(srow + c0, nc, k, o);
+  select_row(srow + c0, nc, k, o, S, rr, false);
   __syncthreads();  // the block's index stores are visible to its own loads after this
   float* cs = cand_s + t * cstride + static_cast<int64_t>(c) * k;
   for (int i = threadIdx.x; i < k; i += TK_THREADS) {
@@ -830,11 +1542,13 @@ __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(
 // order, are in ascending position order (each chunk's list is ascending and only the
 // last list ends in padding), so the top-k of that compact row, mapped back through the
 // chunk indices, is the row's top-k: ties between equal scores still go to the lower
-// position, and a -inf pad follows every visible -inf.
+// position, and a -inf pad follows every visible -inf. The refine then reads the row itself.
 __global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(
-    const int32_t* __restrict__ q_off, const int64_t* __restrict__ kv_off, int64_t ld, int k,
-    int nchunk, int64_t cstride, const int32_t* __restrict__ widx,
-    const float* __restrict__ cand_s, int32_t* __restrict__ topk) {
+    const float* __restrict__ scores, const int32_t* __restrict__ q_off,
+    const int64_t* __restrict__ kv_off, int64_t ld, int k, int nchunk, int64_t cstride,
+    const int32_t* __restrict__ widx, const float* __restrict__ cand_s,
+    int32_t* __restrict__ topk, Refine rf) {
+  __shared__ __attribute__((aligned(16))) TopkLds S;
   const int b = blockIdx.y, r = blockIdx.x;
   const RowInfo ri = load_row_info(q_off, kv_off, b);
   if (r >= ri.R) return;
@@ -844,391 +1558,52 @@ __global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(
   if (n <= FAST_MAX) return;
   const int64_t m = (n + FAST_MAX - 1) / FAST_MAX * k;  // this row's chunks
   int32_t* out = topk + t * k;
-  select_row(cand_s + t * cstride, m, k, out);
+  const RowRef rr = row_ref(rf, t, b, ri.kv_base);
+  select_row(cand_s + t * cstride, m, k, out, S, rr, false);
   __syncthreads();
   const int32_t* wrow = widx + t * nchunk * k;
   for (int i = threadIdx.x; i < k; i += TK_THREADS) {
     const int32_t j = out[i];
     if (j >= 0) out[i] = (j / k) * FAST_MAX + wrow[j];
   }
-}
-
-// ---------------------------------------------------------------------------------------
-// Exact-boundary refine (see dsa_topk in dsa.h). One block per row, after topk_kernel:
-//  1. theta = the smallest float32 score in the row's selection; eps from the row's FP8
-//     queries, weights and the largest key scale among its visible keys;
-//  2. one pass over the row: keys above theta + 2 eps are kept (they are all in the
-//     selection already), keys in [theta - 2 eps, theta + 2 eps] form the band;
-//  3. every band key is rescored in float64 (the head dots are exact; the weighted sum
-//     over heads runs in ascending head order, one rounding per product and per sum);
-//  4. the best k - |kept| band keys by (exact score desc, position asc) join the kept
-//     keys, and the row is rewritten ascending.
-constexpr int RF_THREADS = 1024;
-constexpr int RF_WAVES = RF_THREADS / 64;
-constexpr int BAND_CAP = 4096;
-constexpr int RF_MAXK = 4096;
-
-// e4m3fn code -> value (exact): normal (8 + m) 2^(e-10), subnormal m 2^-9; 0x7F/0xFF
-// (NaN) are never produced by the quantiser and decode here as 0.
-__device__ __forceinline__ double e4m3_value(uint32_t c) {
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  double v = (e == 15u && m == 7u) ? 0.0
-             : e ? __builtin_ldexp(static_cast<double>(8u + m), static_cast<int>(e) - 10)
-                 : __builtin_ldexp(static_cast<double>(m), -9);
-  return (c & 0x80u) ? -v : v;
-}
-
-__device__ __forceinline__ float block_min_f(float x, float* red) {
-  for (int o = 32; o >= 1; o >>= 1) x = fminf(x, __shfl_xor(x, o));
-  if (threadIdx.x % 64 == 0) red[threadIdx.x / 64] = x;
-  __syncthreads();
-  float y = red[0];
-  for (int w = 1; w < RF_WAVES; ++w) y = fminf(y, red[w]);
-  __syncthreads();
-  return y;
-}
-
-__device__ __forceinline__ float block_max_f(float x, float* red) {
-  return -block_min_f(-x, red);
-}
-
-// Bitonic sort of np2 (a power of two) LDS entries by `before`, one compare-exchange per
-// pair and stage, the whole block taking part.
-template <class Before, class Swap>
-__device__ __forceinline__ void block_bitonic(int np2, Before before, Swap swap) {
-  for (int size = 2; size <= np2; size <<= 1) {
-    for (int stride = size / 2; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < np2 / 2; i += RF_THREADS) {
-        const int a = 2 * i - (i & (stride - 1)), c = a + stride;
-        const bool up = (a & size) == 0;
-        if (up ? before(c, a) : before(a, c)) swap(a, c);
-      }
-      __syncthreads();
-    }
+  if (rf.q_fp8 != nullptr) {
+    refine_prefetch(rr, n, S.rf_a, S.rf_s);
+    __syncthreads();
+    refine_generic(scores + t * ld, n, k, out, rr, *reinterpret_cast<RefineLds*>(S.regA), S.tmp,
+                   S.rf_a, S.rf_s);
   }
 }
 
-__device__ __forceinline__ int next_pow2(int x) {
-  int p = 1;
-  while (p < x) p <<= 1;
-  return p;
-}
-
-__global__ __launch_bounds__(RF_THREADS) void topk_refine_kernel(
-    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ q_off,
-    const int64_t* __restrict__ kv_off, int k, const uint8_t* __restrict__ q_fp8,
-    const float* __restrict__ q_scale, const float* __restrict__ wt,
-    const uint8_t* __restrict__ k_fp8, const float* __restrict__ k_scale, int H, int D,
-    double err_scale, int32_t* __restrict__ topk, int32_t* __restrict__ status) {
-  __shared__ double dtab[256];
-  __shared__ int32_t band_pos[BAND_CAP];
-  __shared__ double band_val[BAND_CAP];
-  __shared__ int32_t in_pos[RF_MAXK];
-  __shared__ int32_t sel_pos[RF_MAXK];
-  __shared__ double kdec[RF_WAVES][128];  // one band key's decoded codes per wave
-  __shared__ float redf[RF_WAVES];
-  __shared__ double redd[RF_WAVES];
-  __shared__ uint32_t tmp[2 * TK_WAVES];
-  __shared__ int counters[4];  // band size
-
-  const int b = blockIdx.y, r = blockIdx.x;
-  const RowInfo ri = load_row_info(q_off, kv_off, b);
-  if (r >= ri.R) return;
-  const int64_t t = ri.t0 + r;
-  int64_t n = visible_count(ri, r);
-  if (n > ld) n = ld;
-  const int tid = threadIdx.x, lane = tid % 64;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
-  if (n <= k) {  // every visible key is selected whatever the scores
-    if (tid == 0 && status) status[t] = 0;
+// Refine pre-pass: kmax[b, c] = the largest |k_scale| of positions [c SC_CHUNK, (c+1)
+// SC_CHUNK) of request b (0 past its keys).
+__global__ __launch_bounds__(256) void topk_scale_max_kernel(const float* __restrict__ k_scale,
+                                                             const int64_t* __restrict__ kv_off,
+                                                             int nsc, float* __restrict__ kmax) {
+  constexpr int PER = SC_CHUNK / 256;  // scales per thread, all loads issued before use
+  __shared__ float red[4];
+  const int c = blockIdx.x, b = blockIdx.y;
+  const int64_t base = kv_off[b], L = kv_off[b + 1] - base;
+  const int64_t s0 = static_cast<int64_t>(c) * SC_CHUNK + threadIdx.x;
+  if (static_cast<int64_t>(c) * SC_CHUNK >= L) {  // block-uniform: no key of the request here
+    if (threadIdx.x == 0) kmax[static_cast<int64_t>(b) * nsc + c] = 0.0f;
     return;
   }
-  const float* srow = scores + t * ld;
-  int32_t* out = topk + t * k;
-  const float* ksc = k_scale + ri.kv_base;
-  for (int c = tid; c < 256; c += RF_THREADS) dtab[c] = e4m3_value(static_cast<uint32_t>(c));
-  if (tid < 4) counters[tid] = 0;
-
-  // ---- 1. theta, the largest visible key scale, and sum_j |u_j| max_c |q_hat[j,c]|;
-  // loads are issued eight at a time per thread so the scans are not latency-bound ----
-  constexpr int U = 8;
-  float th = __builtin_inff();
-  for (int i0 = tid; i0 < k; i0 += U * RF_THREADS) {
-    int32_t pp[U];
+  // positions past the request's end load its last scale (in bounds, unconditionally, so
+  // the loads issue back to back) and are masked afterwards
+  float v[PER];
 #pragma unroll
-    for (int u = 0; u < U; ++u) pp[u] = i0 + u * RF_THREADS < k ? out[i0 + u * RF_THREADS] : -1;
-    float v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      v[u] = __builtin_inff();
-      if (pp[u] >= 0) v[u] = srow[pp[u]];
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) th = fminf(th, v[u]);
+  for (int u = 0; u < PER; ++u) {
+    const int64_t s = s0 + 256 * u;
+    v[u] = k_scale[base + (s < L ? s : L - 1)];
   }
-  th = block_min_f(th, redf);
-  float smax = 0.0f;
-  {
-    // scalar head up to a 16-byte boundary, float4 body (four loads in flight), scalar tail
-    const int64_t head = static_cast<int64_t>((16 - (reinterpret_cast<uintptr_t>(ksc) & 15)) & 15) / 4;
-    const int64_t h0 = head < n ? head : n;
-    if (tid < h0) smax = ksc[tid];
-    const int64_t nb4 = (n - h0) / 4;
-    const float4* k4 = reinterpret_cast<const float4*>(ksc + h0);
-    for (int64_t i0 = tid; i0 < nb4; i0 += 4 * RF_THREADS) {
-      float4 v[4];
+  float m = 0.0f;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (i0 + u * RF_THREADS < nb4) v[u] = k4[i0 + u * RF_THREADS];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        smax = fmaxf(smax, fmaxf(fmaxf(v[u].x, v[u].y), fmaxf(v[u].z, v[u].w)));
-    }
-    for (int64_t s = h0 + 4 * nb4 + tid; s < n; s += RF_THREADS) smax = fmaxf(smax, ksc[s]);
-  }
-  smax = block_max_f(smax, redf);
-  double asum = 0.0;  // sum_j |u_j| max_c |q_hat[j,c]|: 8 codes per thread and load, the
-                      // D/8 threads of a head reduce with xor shuffles inside their group
-  {
-    const int per_head = D / 8;  // 16 or 8 threads
-    const uint2* q8 = reinterpret_cast<const uint2*>(q_fp8 + t * H * D);
-    for (int i0 = tid; i0 < H * per_head; i0 += RF_THREADS) {
-      const uint2 v = q8[i0];
-      uint32_t mc = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        mc = max(mc, (v.x >> (8 * e)) & 0x7Fu);
-        mc = max(mc, (v.y >> (8 * e)) & 0x7Fu);
-      }
-      for (int o = per_head / 2; o >= 1; o >>= 1)
-        mc = max(mc, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mc), o)));
-      if (i0 % per_head == 0) {
-        const int j = i0 / per_head;
-        const double u = static_cast<double>(wt[t * H + j]) * static_cast<double>(q_scale[t * H + j]);
-        asum += __builtin_fabs(u) * e4m3_value(mc);
-      }
-    }
-    for (int o = 32; o >= 1; o >>= 1) asum += __shfl_xor(asum, o);
-  }
-  if (lane == 0) redd[wave] = asum;
+  for (int u = 0; u < PER; ++u) m = fmaxf(m, s0 + 256 * u < L ? fabsf(v[u]) : 0.0f);
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if (threadIdx.x % 64 == 0) red[threadIdx.x / 64] = m;
   __syncthreads();
-  double A = 0.0;
-  for (int w = 0; w < RF_WAVES; ++w) A += redd[w];
-  const double C = err_scale > 0.0 ? err_scale : 4.0;
-  const double eps = C * 0x1p-16 * 448.0 * static_cast<double>(smax) * A;
-  const double hi = static_cast<double>(th) + 2.0 * eps, lo = static_cast<double>(th) - 2.0 * eps;
-
-  // ---- 2. kept keys (counted) and the band (collected); float4 loads, four in flight ----
-  uint32_t nin = 0;
-  auto classify = [&](float xf, int64_t s) {
-    const double x = static_cast<double>(xf);
-    if (x > hi) {
-      ++nin;
-    } else if (x >= lo) {
-      const int slot = atomicAdd(&counters[0], 1);
-      if (slot < BAND_CAP) band_pos[slot] = static_cast<int32_t>(s);
-    }
-  };
-  const int64_t n4 = n / 4;
-  const float4* s4 = reinterpret_cast<const float4*>(srow);  // rows are 16-byte aligned
-  for (int64_t i0 = tid; i0 < n4; i0 += 4 * RF_THREADS) {
-    float4 v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (i0 + u * RF_THREADS < n4) v[u] = s4[i0 + u * RF_THREADS];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t i = i0 + u * RF_THREADS;
-      if (i < n4) {
-        classify(v[u].x, 4 * i);
-        classify(v[u].y, 4 * i + 1);
-        classify(v[u].z, 4 * i + 2);
-        classify(v[u].w, 4 * i + 3);
-      }
-    }
-  }
-  for (int64_t s = 4 * n4 + tid; s < n; s += RF_THREADS) classify(srow[s], s);
-  uint32_t nin_total;
-  block_excl_scan<RF_WAVES>(nin, tmp, &nin_total);  // ends with a barrier: counters[0] is final
-  const int nb = counters[0];
-  const int need = k - static_cast<int>(nin_total);
-  if (nb > BAND_CAP || need < 1 || need > nb) {  // uniform: keep the float32 selection
-    if (tid == 0 && status) status[t] = nb > BAND_CAP ? -1 : -2;
-    return;
-  }
-
-  // ---- 3. exact rescore, one band key per wave at a time; lane j owns heads j and j+64.
-  // A key's codes are prefetched one iteration ahead; the weighted head sum runs in
-  // ascending head order over readlane. ----
-  double uh[2];
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const int j = lane + 64 * hh;
-    uh[hh] = j < H ? static_cast<double>(wt[t * H + j]) * static_cast<double>(q_scale[t * H + j]) : 0.0;
-  }
-  auto key_codes = [&](int i) -> uint32_t {  // two codes of band key i per lane (D <= 128)
-    uint32_t c2 = 0;
-    if (i < nb && 2 * lane < D)
-      c2 = *reinterpret_cast<const uint16_t*>(k_fp8 + (ri.kv_base + band_pos[i]) * D + 2 * lane);
-    return c2;
-  };
-  uint32_t kc = key_codes(wave);
-  for (int i = wave; i < nb; i += RF_WAVES) {
-    const int32_t p = band_pos[i];
-    if (2 * lane < D) {
-      kdec[wave][2 * lane] = dtab[kc & 0xFFu];
-      kdec[wave][2 * lane + 1] = dtab[(kc >> 8) & 0xFFu];
-    }
-    kc = key_codes(i + RF_WAVES);  // next key of this wave, in flight during this one
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    double tj[2] = {0.0, 0.0};
-    for (int hh = 0; hh < (H > 64 ? 2 : 1); ++hh) {  // wave-uniform
-      uint4 qv[8];  // this lane's head codes (reloaded per key: cache hits)
-#pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        qv[v] = make_uint4(0u, 0u, 0u, 0u);
-        if (lane + 64 * hh < H && v < D / 16)
-          qv[v] = reinterpret_cast<const uint4*>(q_fp8 + (t * H + lane + 64 * hh) * D)[v];
-      }
-      // exact: every partial sum is a multiple of 2^-18 below 2^53 units, so the four
-      // interleaved partial sums and their total are exact in any order
-      double d4[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        if (v < D / 16) {
-          const uint32_t wd[4] = {qv[v].x, qv[v].y, qv[v].z, qv[v].w};
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            d4[e % 4] = __builtin_fma(dtab[(wd[e / 4] >> (8 * (e % 4))) & 0xFFu],
-                                      kdec[wave][16 * v + e], d4[e % 4]);
-        }
-        __builtin_amdgcn_sched_barrier(0);  // keep each group's table reads local
-      }
-      const double d = (d4[0] + d4[1]) + (d4[2] + d4[3]);
-      tj[hh] = __dmul_rn(uh[hh], d > 0.0 ? d : 0.0);
-    }
-    double acc = 0.0;  // heads 0..H-1 in order: lane j's tj[0], then lane j's tj[1] (j + 64)
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int lo_w = __double2loint(tj[hh]), hi_w = __double2hiint(tj[hh]);
-#pragma unroll
-      for (int j = 0; j < 64; ++j)
-        if (64 * hh + j < H)
-          acc = __dadd_rn(acc, __hiloint2double(__builtin_amdgcn_readlane(hi_w, j),
-                                                __builtin_amdgcn_readlane(lo_w, j)));
-    }
-    if (lane == 0) band_val[i] = __dmul_rn(acc, static_cast<double>(ksc[p]));
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  }
-  __syncthreads();
-
-  // ---- 4. the best `need` band keys by (exact score desc, position asc), as ascending
-  // positions in sel_pos; then a merge with the kept keys ----
-  if (nb <= 64) {  // one wave ranks the band with register broadcasts: no block barriers
-    if (wave == 0) {
-      const bool live = lane < nb;
-      const double v = live ? band_val[lane] : -__builtin_inf();
-      const int32_t p = live ? band_pos[lane] : 0x7FFFFFFF;
-      const int vlo = __double2loint(v), vhi = __double2hiint(v);
-      int rank = 0;
-      for (int m = 0; m < nb; ++m) {
-        const double vm = __hiloint2double(__builtin_amdgcn_readlane(vhi, m),
-                                           __builtin_amdgcn_readlane(vlo, m));
-        const int32_t pm = __builtin_amdgcn_readlane(p, m);
-        rank += (vm > v || (vm == v && pm < p)) ? 1 : 0;
-      }
-      const bool take = live && rank < need;
-      int at = 0;  // rank by position among the taken keys
-      for (int m = 0; m < nb; ++m) {
-        const int32_t pm = __builtin_amdgcn_readlane(p, m);
-        const bool tm = __builtin_amdgcn_readlane(take ? 1 : 0, m) != 0;
-        at += (tm && pm < p) ? 1 : 0;
-      }
-      if (take) sel_pos[at] = p;
-    }
-    __syncthreads();
-  } else {
-    // pad the band to a power of two with entries that sort last, then bitonic sorts
-    const int np2 = next_pow2(nb);
-    for (int i = nb + tid; i < np2; i += RF_THREADS) {
-      band_val[i] = -__builtin_inf();
-      band_pos[i] = 0x7FFFFFFF;
-    }
-    __syncthreads();
-    block_bitonic(
-        np2,
-        [&](int x, int y) {
-          return band_val[x] > band_val[y] ||
-                 (band_val[x] == band_val[y] && band_pos[x] < band_pos[y]);
-        },
-        [&](int x, int y) {
-          const double v = band_val[x];
-          band_val[x] = band_val[y];
-          band_val[y] = v;
-          const int32_t q = band_pos[x];
-          band_pos[x] = band_pos[y];
-          band_pos[y] = q;
-        });
-    const int ns2 = next_pow2(need > 1 ? need : 2);
-    for (int i = tid; i < ns2; i += RF_THREADS) sel_pos[i] = i < need ? band_pos[i] : 0x7FFFFFFF;
-    __syncthreads();
-    block_bitonic(
-        ns2, [&](int x, int y) { return sel_pos[x] < sel_pos[y]; },
-        [&](int x, int y) {
-          const int32_t q = sel_pos[x];
-          sel_pos[x] = sel_pos[y];
-          sel_pos[y] = q;
-        });
-  }
-  // kept keys in the current (ascending) selection, order preserved; k <= RF_MAXK, so at
-  // most four entries per thread, taken as one contiguous run
-  constexpr int PER = RF_MAXK / RF_THREADS;
-  int32_t mine[PER];
-  uint32_t cnt = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int i = tid * PER + j;
-    mine[j] = -1;
-    if (i < k) {
-      const int32_t p = out[i];
-      if (static_cast<double>(srow[p]) > hi) {
-        mine[j] = p;
-        ++cnt;
-      }
-    }
-  }
-  uint32_t kept;
-  uint32_t at = block_excl_scan<RF_WAVES>(cnt, tmp, &kept);  // ends with a barrier
-  if (kept != nin_total) {  // uniform; cannot happen for a correct float32 selection
-    if (tid == 0 && status) status[t] = -3;
-    return;
-  }
-#pragma unroll
-  for (int j = 0; j < PER; ++j)
-    if (mine[j] >= 0) in_pos[at++] = mine[j];
-  __syncthreads();
-  auto count_below = [](const int32_t* a, int len, int32_t p) {  // a ascending
-    int lo_i = 0, hi_i = len;
-    while (lo_i < hi_i) {
-      const int mid = (lo_i + hi_i) / 2;
-      if (a[mid] < p) lo_i = mid + 1;
-      else hi_i = mid;
-    }
-    return lo_i;
-  };
-  for (int i = tid; i < static_cast<int>(kept); i += RF_THREADS)
-    out[i + count_below(sel_pos, need, in_pos[i])] = in_pos[i];
-  for (int i = tid; i < need; i += RF_THREADS)
-    out[i + count_below(in_pos, static_cast<int>(kept), sel_pos[i])] = sel_pos[i];
-  if (tid == 0 && status) status[t] = nb;
+  if (threadIdx.x == 0)
+    kmax[static_cast<int64_t>(b) * nsc + c] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
 }  // namespace
@@ -1239,17 +1614,24 @@ namespace {
 // Chunks of rows longer than FAST_MAX, and the stride of the compact candidate rows.
 int64_t topk_nchunk(int64_t max_kv_len) { return max_kv_len > FAST_MAX ? ceil_div(max_kv_len, FAST_MAX) : 1; }
 int64_t topk_cstride(int64_t nchunk, int k) { return (nchunk * k + 3) / 4 * 4; }
-}  // namespace
-}  // namespace dsa
-
-extern "C" size_t dsa_topk_workspace_size(int32_t T, int64_t max_kv_len, int32_t k) {
-  using namespace dsa;
-  if (T <= 0 || k <= 0) return 0;
+// Bytes of the chunk stage (16-byte multiple); the refine's scale maxima follow.
+int64_t topk_chunk_bytes(int32_t T, int64_t max_kv_len, int32_t k) {
   const int64_t nc = topk_nchunk(max_kv_len);
   if (nc <= 1) return 0;
   // chunk indices [T, nc, k] (padded to 16 bytes), then candidate scores [T, cstride]
-  return static_cast<size_t>((static_cast<int64_t>(T) * nc * k + 3) / 4 * 4 +
-                             static_cast<int64_t>(T) * topk_cstride(nc, k)) * 4;
+  return ((static_cast<int64_t>(T) * nc * k + 3) / 4 * 4 + static_cast<int64_t>(T) * topk_cstride(nc, k)) * 4;
+}
+int64_t topk_nsc(int64_t max_kv_len) { return max_kv_len > 0 ? ceil_div(max_kv_len, SC_CHUNK) : 1; }
+}  // namespace
+}  // namespace dsa
+
+extern "C" size_t dsa_topk_workspace_size(int32_t B, int32_t T, int64_t max_kv_len, int32_t k,
+                                          int32_t refine) {
+  using namespace dsa;
+  if (B <= 0 || T <= 0 || k <= 0 || max_kv_len < 0) return 0;
+  int64_t bytes = topk_chunk_bytes(T, max_kv_len, k);
+  if (refine) bytes += (static_cast<int64_t>(B) * topk_nsc(max_kv_len) * 4 + 15) / 16 * 16;
+  return static_cast<size_t>(bytes);
 }
 
 extern "C" dsa_status dsa_topk(const float* scores, int64_t score_ld,
@@ -1264,12 +1646,14 @@ extern "C" dsa_status dsa_topk(const float* scores, int64_t score_ld,
               "dsa_topk: score_ld must be >= max_kv_len and a multiple of 4");
   DSA_REQUIRE(max_kv_len < (int64_t(1) << 31), "dsa_topk: max_kv_len must be < 2^31");
   if (refine) {
-    DSA_REQUIRE((reinterpret_cast<uintptr_t>(refine->q_fp8) & 15) == 0,
-                "dsa_topk: refine q_fp8 must be 16-byte aligned");
+    DSA_REQUIRE((reinterpret_cast<uintptr_t>(refine->q_fp8) & 15) == 0 &&
+                    (reinterpret_cast<uintptr_t>(refine->k_fp8) & 15) == 0,
+                "dsa_topk: refine q_fp8 and k_fp8 must be 16-byte aligned");
     DSA_REQUIRE(k <= RF_MAXK, "dsa_topk: the refine supports k <= %d (got %d)", RF_MAXK, k);
     DSA_REQUIRE(refine->D_I == 64 || refine->D_I == 128, "dsa_topk: refine D_I must be 64 or 128");
     DSA_REQUIRE(refine->H_I >= 1 && refine->H_I <= 128, "dsa_topk: refine H_I must be in [1, 128]");
-    DSA_REQUIRE(refine->err_scale >= 0.0, "dsa_topk: refine err_scale must be >= 0");
+    DSA_REQUIRE(refine->err_scale >= 0.0 && refine->err_scale < 1e30,
+                "dsa_topk: refine err_scale must be in [0, 1e30)");
   }
   if (B == 0 || T == 0 || max_q_rows == 0) return ok();
   DSA_REQUIRE(scores && q_row_offsets && kv_row_offsets && topk, "dsa_topk: null pointer");
@@ -1279,33 +1663,47 @@ extern "C" dsa_status dsa_topk(const float* scores, int64_t score_ld,
   DSA_REQUIRE((reinterpret_cast<uintptr_t>(scores) & 15) == 0,
               "dsa_topk: scores must be 16-byte aligned");
   DSA_REQUIRE(B <= 65535, "dsa_topk: B must be <= 65535");
-  dim3 grid((unsigned)max_q_rows, (unsigned)B);
+  const size_t need = dsa_topk_workspace_size(B, T, max_kv_len, k, refine ? 1 : 0);
+  if (need && (ws_bytes < need || !ws))
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "dsa_topk: the workspace needs %zu bytes (got %zu)",
+                need, ws_bytes);
+  DSA_REQUIRE(!need || (reinterpret_cast<uintptr_t>(ws) & 15) == 0,
+              "dsa_topk: ws must be 16-byte aligned");
   const int64_t nchunk = topk_nchunk(max_kv_len);
+  DSA_REQUIRE(max_q_rows * nchunk <= 0x7FFFFFFF, "dsa_topk: too many chunks");
+  const int64_t chunk_bytes = topk_chunk_bytes(T, max_kv_len, k);
+  hipStream_t st = as_stream(stream);
+  Refine rf{};
+  if (refine) {
+    const int64_t nsc = topk_nsc(max_kv_len);
+    DSA_REQUIRE(nsc <= 65535, "dsa_topk: max_kv_len too large for the refine");
+    rf.q_fp8 = refine->q_fp8;
+    rf.q_scale = refine->q_scale;
+    rf.w = refine->w;
+    rf.k_fp8 = refine->k_fp8;
+    rf.k_scale = refine->k_scale;
+    rf.kmax = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + chunk_bytes);
+    rf.status = refine->status;
+    rf.C = refine->err_scale;
+    rf.H = refine->H_I;
+    rf.D = refine->D_I;
+    rf.nsc = static_cast<int>(nsc);
+    hipLaunchKernelGGL(topk_scale_max_kernel, dim3((unsigned)nsc, (unsigned)B), dim3(256), 0, st,
+                       refine->k_scale, kv_row_offsets, (int)nsc, const_cast<float*>(rf.kmax));
+  }
+  dim3 grid((unsigned)max_q_rows, (unsigned)B);
   if (nchunk > 1) {
-    const size_t need = dsa_topk_workspace_size(T, max_kv_len, k);
-    if (ws_bytes < need || !ws)
-      return fail(DSA_ERR_WORKSPACE_TOO_SMALL,
-                  "dsa_topk: rows longer than %d need a %zu-byte workspace (got %zu)", FAST_MAX,
-                  need, ws_bytes);
-    DSA_REQUIRE((reinterpret_cast<uintptr_t>(ws) & 15) == 0, "dsa_topk: ws must be 16-byte aligned");
-    DSA_REQUIRE(max_q_rows * nchunk <= 0x7FFFFFFF, "dsa_topk: too many chunks");
     int32_t* widx = static_cast<int32_t*>(ws);
     const int64_t cstride = topk_cstride(nchunk, k);
     float* cand_s = reinterpret_cast<float*>(widx + (static_cast<int64_t>(T) * nchunk * k + 3) / 4 * 4);
     hipLaunchKernelGGL(topk_chunk_kernel, dim3((unsigned)(max_q_rows * nchunk), (unsigned)B),
-                       dim3(TK_THREADS), 0, as_stream(stream), scores, score_ld, q_row_offsets,
-                       kv_row_offsets, k, (int)nchunk, cstride, widx, cand_s, topk);
-    hipLaunchKernelGGL(topk_merge_kernel, grid, dim3(TK_THREADS), 0, as_stream(stream),
-                       q_row_offsets, kv_row_offsets, score_ld, k, (int)nchunk, cstride, widx,
-                       cand_s, topk);
+                       dim3(TK_THREADS), 0, st, scores, score_ld, q_row_offsets, kv_row_offsets, k,
+                       (int)nchunk, cstride, widx, cand_s, topk, rf);
+    hipLaunchKernelGGL(topk_merge_kernel, grid, dim3(TK_THREADS), 0, st, scores, q_row_offsets,
+                       kv_row_offsets, score_ld, k, (int)nchunk, cstride, widx, cand_s, topk, rf);
   } else {
-    hipLaunchKernelGGL(topk_kernel, grid, dim3(TK_THREADS), 0, as_stream(stream), scores,
-                       score_ld, q_row_offsets, kv_row_offsets, k, topk);
+    hipLaunchKernelGGL(topk_kernel, grid, dim3(TK_THREADS), 0, st, scores, score_ld, q_row_offsets,
+                       kv_row_offsets, k, topk, rf);
   }
-  if (refine)
-    hipLaunchKernelGGL(topk_refine_kernel, grid, dim3(RF_THREADS), 0, as_stream(stream), scores,
-                       score_ld, q_row_offsets, kv_row_offsets, k, refine->q_fp8, refine->q_scale,
-                       refine->w, refine->k_fp8, refine->k_scale, refine->H_I, refine->D_I,
-                       refine->err_scale, topk, refine->status);
   return check_launch("dsa_topk");
 }

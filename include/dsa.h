@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 3
+#define DSA_ABI_VERSION 4
 
 typedef enum {
   DSA_OK = 0,
@@ -131,13 +131,16 @@ dsa_status dsa_verify_cache_write(const float* k_new, const uint16_t* latent_new
  *
  *   scores[t, s] = k_scale[s] * sum_j (w[t,j] * q_scale[t,j]) * ReLU(q_hat[t,j] . k_hat[s])
  * i.e. sum_j w[t,j] ReLU(q[t,j] . k[s]) with the positive FP8 scales
- * factored out; FP8 products with float32 accumulation (MFMA), float32
- * epilogue. Written for s in [0, p_t] only; entries beyond are untouched.
+ * factored out. The FP8 products are exact, but the MFMA adds them at reduced
+ * width: a head dot can differ from its exact value by up to 2^-9 *
+ * max|q_hat_j| * max|k_hat| (128 products, each off by up to 2^-16 of the
+ * largest; typical errors are far smaller). The ReLU, weights and head sum run
+ * in float32. Written for s in [0, p_t] only; entries beyond are untouched.
  *
  *   q_fp8   [T, H_I, D_I] e4m3fn codes     q_scale, w [T, H_I] float32
  *   k_fp8   [N, D_I] e4m3fn codes          k_scale    [N] float32
  *   scores  [T, score_ld] float32, score_ld >= max_kv_len
- * Supported: D_I = 128 (or 64), H_I a multiple of 8 up to 128.
+ * Supported: D_I = 128 or 64, H_I in [1, 128].
  * Errors: DSA_ERR_INVALID_ARGUMENT, DSA_ERR_UNSUPPORTED.
  */
 dsa_status dsa_index_score(const uint8_t* q_fp8, const float* q_scale, const float* w,
@@ -150,11 +153,19 @@ dsa_status dsa_index_score(const uint8_t* q_fp8, const float* q_scale, const flo
  * dsa_topk_refine -- inputs of the exact-boundary refine of dsa_topk: the
  * same FP8 queries, weights, keys and scales that dsa_index_score scored.
  * All pointers are device pointers (layouts as in dsa_index_score).
- *   err_scale  C of the error bound below; 0 selects 4
- *   status     [T] int32, nullable: per row, the number of band keys that
- *              were rescored (0 when the row needs no refine), or -1 when
- *              the band held more than 4096 keys (that row keeps the
- *              unrefined selection)
+ *   err_scale  C of the error bound eps_t below; 0 selects 4
+ *   status     [T] int32, nullable. Per row:
+ *                >= 0  the row is refined; the value is the number of band keys
+ *                      rescored exactly (0 when every visible key is selected)
+ *                  -1  the band held more than 4096 keys: the float32 selection
+ *                      is kept
+ *                  -2  theta or eps is not finite, or the band cannot supply the
+ *                      missing keys: the float32 selection is kept
+ *                  -3  internal count mismatch: the float32 selection is kept
+ *                  -4  the row is refined, but some band key's float32 score lies
+ *                      farther than eps_t / 2 from its exact value, so the margin
+ *                      the bound relies on is thinner than measured (treat the
+ *                      set as possibly inexact)
  */
 typedef struct dsa_topk_refine {
   const uint8_t* q_fp8;
@@ -185,19 +196,30 @@ typedef struct dsa_topk_refine {
  *   d_j = q_hat[t,j] . k_hat[s] (exact), u_j = w[t,j] * q_scale[t,j],
  * evaluated in float64 in exactly that order (one rounding per product and
  * per sum), provided every float32 score lies within
- *   eps_t = C * 2^-16 * 448 * max_{s <= p_t} k_scale[s] * sum_j |u_j| * max_c |q_hat[t,j,c]|
- * of its exact value (a bound on the FP8 MFMA's reduced-width accumulation
- * plus the float32 epilogue; C is checked by measurement, not derived).
- * With theta the k-th largest float32 score, keys above theta + 2 eps_t are
- * kept, keys below theta - 2 eps_t dropped, and the band in between is
- * rescored exactly and ranked by (I_exact desc, s asc).
+ *   eps_t = C * 2^-16 * 448 * smax_t * sum_j |u_j| * max_c |q_hat[t,j,c]|
+ *           + (H_I + 3) * 2^-23 * |theta_t|
+ * of its exact value (smax_t: the largest key scale of the 2048-position
+ * chunks holding the row's visible keys; theta_t: the k-th largest float32
+ * score). The first term bounds the FP8 MFMA's accumulation error of each head
+ * dot by C times 2^-16 of the largest possible product; the second, the float32
+ * epilogue for nonnegative weights. EXACTNESS IS CONDITIONAL: with the default
+ * C = 4 the bound is not derived but checked by measurement (the largest
+ * observed |I_f32 - I_exact| / eps_t is 0.02-0.25 on the synthetic workloads),
+ * and each refined row re-checks it on its own band keys (status -4).
+ * C = 128 gives the worst case of the accumulation model (128 products each off
+ * by up to 2^-16 of the largest), at the price of a band about 32 times wider.
+ * Keys above theta_t + 2 eps_t are kept, keys below theta_t - 2 eps_t dropped,
+ * and the band in between is rescored exactly and ranked by (I_exact desc,
+ * s asc).
  *   scores [T, score_ld] float32 (as written by dsa_index_score)
  *   topk   [T, k] int32
  * Rows of up to 65536 visible scores take one block each. When max_kv_len
  * exceeds 65536, every row is first cut into 65536-position chunks whose own
  * top-k are selected in parallel (the row's top-k lies in their union), then
- * merged; this needs dsa_topk_workspace_size(T, max_kv_len, k) bytes of
- * 16-byte aligned workspace (0 bytes otherwise; ws may then be NULL).
+ * merged.
+ * Workspace: dsa_topk_workspace_size(B, T, max_kv_len, k, refine != NULL)
+ * bytes, 16-byte aligned (0 bytes for rows of at most 65536 positions without a
+ * refine; ws may then be NULL).
  * Errors: DSA_ERR_INVALID_ARGUMENT (k < 1, k > 8192, refine with k > 4096,
  * D_I not 64/128, H_I not in [1, 128], ...), DSA_ERR_WORKSPACE_TOO_SMALL.
  */
@@ -206,7 +228,8 @@ dsa_status dsa_topk(const float* scores, int64_t score_ld, const int32_t* q_row_
                     int64_t max_kv_len, int32_t k, const dsa_topk_refine* refine, int32_t* topk,
                     void* ws, size_t ws_bytes, void* stream);
 
-size_t dsa_topk_workspace_size(int32_t T, int64_t max_kv_len, int32_t k);
+size_t dsa_topk_workspace_size(int32_t B, int32_t T, int64_t max_kv_len, int32_t k,
+                               int32_t refine);
 
 /*
  * dsa_sparse_mla_decode -- attention of every query row over only its

@@ -136,18 +136,25 @@ def check_topk_valid(gpu_rows, ref_rows, ref_scores, nvis, tol, k):
     return ndiff
 
 
+LSE_TOL = 1e-3  # the sparse-MLA tolerance's lse term, |d lse| <= 1e-3 (natural log)
+
+
 def mla_check(out_gpu, lse_gpu, out_ref, lse_ref):
-    """Sparse-MLA tolerance: |d| <= 2e-2*max|o_ref| (per row/head) + 1e-2*|o_ref|; lse 2.5e-3."""
+    """Sparse-MLA tolerance: |d| <= 2e-2*max|o_ref| (per row/head) + 1e-2*|o_ref|, and
+    |d lse| <= 1e-3. Prints the worst ratio to the bound and the worst |d lse|."""
     og = out_gpu.float().cpu().numpy().astype(np.float64)
     scale = np.abs(out_ref).max(axis=-1, keepdims=True)
     bound = 2e-2 * scale + 1e-2 * np.abs(out_ref)
     err = np.abs(og - out_ref)
     worst = float((err / np.maximum(bound, 1e-30)).max()) if err.size else 0.0
-    assert np.all(err <= bound), f"sparse MLA out of tolerance (worst ratio {worst:.3f})"
     lg = lse_gpu.cpu().numpy().astype(np.float64)
     fin = np.isfinite(lse_ref)
+    dl = np.abs(lg[fin] - lse_ref[fin])
+    worst_lse = float(dl.max()) if dl.size else 0.0
+    print(f"  mla: worst |d|/bound {worst:.3f}, worst |d lse| {worst_lse:.2e}", flush=True)
+    assert np.all(err <= bound), f"sparse MLA out of tolerance (worst ratio {worst:.3f})"
     assert np.array_equal(np.isfinite(lg), fin)
-    assert np.all(np.abs(lg[fin] - lse_ref[fin]) <= 2.5e-3)
+    assert worst_lse <= LSE_TOL, f"lse off by {worst_lse:.2e}"
     return worst
 
 
@@ -159,18 +166,32 @@ def refine_args(gi, case, status: bool = True):
     return d
 
 
-def refine_eps(qc, qs, w, ks, qo, ko, rows, C: float = 4.0):
-    """Per-row refine bound eps_t = C 2^-16 448 max_{s<=p_t} k_scale[s] sum_j |u_j| max|q_hat_j|.
-
-    Written from the statement of dsa_topk in include/dsa.h, on the host copies.
-    """
+def refine_eps(qc, qs, w, ks, qo, ko, rows, theta, C: float = 4.0):
+    """Per-row refine bound, written from the statement of dsa_topk in include/dsa.h on the
+    host copies: eps_t = C 2^-16 448 smax_t sum_j |u_j| max|q_hat_j| + (H + 3) 2^-23 |theta_t|,
+    smax_t the largest key scale of the 2048-position chunks holding the row's visible keys,
+    theta_t the row's k-th largest float32 score (given)."""
     dec = oracle.fp8_decode(np.arange(256, dtype=np.uint8))
     qmax = np.abs(dec[qc]).max(axis=-1)                                # [T, H]
     u = np.abs(w.astype(np.float64) * qs.astype(np.float64))          # [T, H]
+    H = qc.shape[1]
     out = np.zeros(len(rows))
     for i, t in enumerate(rows):
         b = int(np.searchsorted(qo, t, side="right") - 1)
         n = oracle.row_visible(qo, ko, int(t))
-        smax = float(ks[ko[b]:ko[b] + n].max()) if n else 0.0
-        out[i] = C * 2.0 ** -16 * 448.0 * smax * float((u[t] * qmax[t]).sum())
+        L = int(ko[b + 1] - ko[b])
+        end = min(L, -(-n // 2048) * 2048)
+        smax = float(np.abs(ks[ko[b]:ko[b] + end]).max()) if n else 0.0
+        out[i] = (C * 2.0 ** -16 * 448.0 * smax * float((u[t] * qmax[t]).sum())
+                  + (H + 3) * 2.0 ** -23 * abs(float(theta[i])))
+    return out
+
+
+def kth_largest(scores, nvis, k):
+    """The k-th largest of each row's visible scores (the smallest score when k > visible)."""
+    out = np.zeros(len(nvis))
+    for i, n in enumerate(nvis):
+        if n:
+            row = np.sort(scores[i, :n])[::-1]
+            out[i] = row[min(k, n) - 1]
     return out

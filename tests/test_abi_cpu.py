@@ -31,11 +31,15 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_workspace_queries():
     lib = _lib.load()
-    assert lib.dsa_abi_version() == 3
+    assert lib.dsa_abi_version() == 4
     assert lib.dsa_last_error() in (b"", None)
-    assert lib.dsa_topk_workspace_size(192, 65536, 2048) == 0
+    assert lib.dsa_topk_workspace_size(32, 192, 65536, 2048, 0) == 0
+    # the refine keeps one key-scale maximum per 2048 positions of every request
+    assert lib.dsa_topk_workspace_size(32, 192, 65536, 2048, 1) == 32 * 32 * 4
     # 262144-position rows: 4 chunks of 2048 indices, then compact scores and positions
-    assert lib.dsa_topk_workspace_size(24, 262144, 2048) == (24 * 4 * 2048 + 24 * 8192) * 4
+    assert lib.dsa_topk_workspace_size(4, 24, 262144, 2048, 0) == (24 * 4 * 2048 + 24 * 8192) * 4
+    assert lib.dsa_topk_workspace_size(4, 24, 262144, 2048, 1) == (24 * 4 * 2048 + 24 * 8192) * 4 + 4 * 128 * 4
+    assert lib.dsa_topk_workspace_size(3, 5, 100, 8, 1) == 16  # padded to 16 bytes
     # split-K partials: T * splits * H * (512 + 2) floats, or none when one split suffices
     ws = lib.dsa_sparse_mla_workspace_size(192, 64, 2048)
     assert ws == 0 or ws % (192 * 64 * 514 * 4) == 0

@@ -15,7 +15,7 @@ import torch
 
 import oracle
 from dsa_sparse_attention_amd import api, synth, workloads
-from tests._pipeline import (DEV, Case, check_topk_valid, gpu_indexer, mla_check,
+from tests._pipeline import (DEV, Case, check_topk_valid, gpu_indexer, kth_largest, mla_check,
                              oracle_quant, refine_args, refine_eps, score_tolerance)
 
 pytestmark = pytest.mark.gpu
@@ -204,7 +204,7 @@ def test_topk_long_rows_chunked(levels):
     ld = 200004
     s = synth.random_scores(8, ld, seed=50 + levels, tie_levels=levels)
     for k in (7, 2048):
-        ws = torch.zeros(max(api.topk_workspace_size(8, max(lens), k), 16), dtype=torch.uint8,
+        ws = torch.zeros(max(api.topk_workspace_size(4, 8, max(lens), k), 16), dtype=torch.uint8,
                          device=DEV)
         got = api.topk(s.to(DEV), qo.to(DEV), ko.to(DEV), R, max(lens), k,
                        workspace=ws).cpu().numpy()
@@ -318,8 +318,9 @@ def test_end_to_end_topk_refined_equals_oracle(name):
                                rows=rows, width=case.max_kv)
     nvis = np.array([case.visible(int(t)) for t in rows])
     ref_k = oracle.topk(ref_s, nvis, w.topk)
-    eps = refine_eps(qc, qs, case.host("w_f32"), ks, case.qo.numpy(), ko, rows)
     got_s = gi["scores"].cpu().numpy()[:, :case.max_kv].astype(np.float64)
+    eps = refine_eps(qc, qs, case.host("w_f32"), ks, case.qo.numpy(), ko, rows,
+                     kth_largest(got_s, nvis, w.topk))
     ratio = max(float(np.abs(got_s[t, :nvis[t]] - ref_s[t, :nvis[t]]).max() / eps[t])
                 for t in rows if nvis[t])
     _say(f"  max |I_f32 - I_exact| / eps = {ratio:.3f}")
