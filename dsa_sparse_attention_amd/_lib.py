@@ -34,6 +34,7 @@ SIGNATURES = {
     "dsa_sparse_mla_workspace_size": ([I32, I32, I32], SZ),
     "greedy_accept": ([P, I32, I64, P, I32, I32, I32, P, P, P, P, SZ, P], ctypes.c_int),
     "greedy_accept_workspace_size": ([I32, I32, I32], SZ),
+    "greedy_accept_noalloc": ([P, I32, I64, P, I32, I32, I32, P, P, P, P], ctypes.c_int),
     "rejection_accept": ([P, I32, I64, P, P, P, P, I32, I32, I32, P, P, P, SZ, P], ctypes.c_int),
     "rejection_accept_workspace_size": ([I32, I32, I32], SZ),
 }

@@ -267,6 +267,44 @@ def greedy_accept(logits, draft, K: int, argmax: bool = True, workspace=None):
     return n, nxt, am
 
 
+NOALLOC_SCRATCH_BYTES = 1 << 20  # DSA_NOALLOC_SCRATCH_BYTES of include/dsa.h
+
+
+def greedy_accept_noalloc(logits, draft, K: int, num_accepted=None, next_token=None, argmax=None):
+    """greedy_accept through the entry point that allocates nothing (fixed device scratch).
+
+    The outputs may be passed in (num_accepted [B], next_token [B], argmax [B, K+1] int32);
+    any left out is allocated here by torch, outside the library call.
+    """
+    if not isinstance(logits, torch.Tensor) or not logits.is_cuda or not logits.is_contiguous():
+        raise TypeError("logits must be a contiguous CUDA tensor")
+    if logits.dtype == torch.float32:
+        dt = DSA_F32
+    elif logits.dtype == torch.bfloat16:
+        dt = DSA_BF16
+    else:
+        raise TypeError("logits must be float32 or bfloat16")
+    rows, V = logits.shape
+    B = rows // (K + 1)
+    if B * (K + 1) != rows:
+        raise ValueError("logits rows must be B*(K+1)")
+    if K:
+        _dev(draft, "draft", torch.int32)
+        _shape(draft, "draft", (B, K))
+    dev = logits.device
+    n = num_accepted if num_accepted is not None else torch.empty(B, dtype=torch.int32, device=dev)
+    nxt = next_token if next_token is not None else torch.empty(B, dtype=torch.int32, device=dev)
+    for name, t, shape in (("num_accepted", n, (B,)), ("next_token", nxt, (B,))):
+        _dev(t, name, torch.int32)
+        _shape(t, name, shape)
+    if argmax is not None:
+        _dev(argmax, "argmax", torch.int32)
+        _shape(argmax, "argmax", (B, K + 1))
+    _check(_lib.load().greedy_accept_noalloc(_p(logits), dt, V, _p(draft) if K else None, B, K, V,
+                                             _p(n), _p(nxt), _p(argmax), _stream()))
+    return n, nxt, argmax
+
+
 def rejection_accept(logits, draft_probs, draft, u, us, K: int, workspace=None):
     """Rejection-sampling acceptance: (num_accepted [B], next_token [B])."""
     if not isinstance(logits, torch.Tensor) or not logits.is_cuda or not logits.is_contiguous():

@@ -12,6 +12,8 @@
 // index on ties. This reproduces "first maximum wins" exactly. Pass 2: one wave per request
 // merges the slices of its K+1 rows in slice order, and a ballot over the K draft
 // comparisons gives the first mismatch.
+#include <atomic>
+
 #include "common.hpp"
 
 namespace dsa {
@@ -184,24 +186,15 @@ extern "C" size_t greedy_accept_workspace_size(int32_t B, int32_t K, int32_t V) 
   return static_cast<size_t>(B) * (K + 1) * nslice * (sizeof(float) + sizeof(int32_t));
 }
 
-extern "C" dsa_status greedy_accept(const void* logits, int32_t dtype, int64_t logits_ld,
-                                    const int32_t* draft, int32_t B, int32_t K, int32_t V,
-                                    int32_t* num_accepted, int32_t* next_token, int32_t* argmax,
-                                    void* ws, size_t ws_bytes, void* stream) {
-  using namespace dsa;
-  DSA_REQUIRE(dtype == DSA_F32 || dtype == DSA_BF16, "greedy_accept: dtype must be DSA_F32 or DSA_BF16");
-  DSA_REQUIRE(B >= 0 && K >= 0 && K <= 63, "greedy_accept: need B >= 0 and 0 <= K <= 63");
-  DSA_REQUIRE(V >= 1 && logits_ld >= V, "greedy_accept: need V >= 1 and logits_ld >= V");
-  if (B == 0) return ok();
-  DSA_REQUIRE(logits && num_accepted && next_token && (K == 0 || draft),
-              "greedy_accept: null pointer");
+namespace dsa {
+namespace {
+
+// Argument checks and the two launches, on a workspace already sized and aligned.
+dsa_status greedy_accept_launch(const void* logits, int32_t dtype, int64_t logits_ld,
+                                const int32_t* draft, int32_t B, int32_t K, int32_t V,
+                                int32_t* num_accepted, int32_t* next_token, int32_t* argmax,
+                                void* ws, void* stream) {
   const int64_t rows = static_cast<int64_t>(B) * (K + 1);
-  DSA_REQUIRE(rows <= 65535, "greedy_accept: B*(K+1) must be <= 65535");
-  const size_t need = greedy_accept_workspace_size(B, K, V);
-  if (!ws || ws_bytes < need)
-    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "greedy_accept: workspace needs %zu bytes (got %zu)", need,
-                ws_bytes);
-  DSA_REQUIRE((reinterpret_cast<uintptr_t>(ws) & 3) == 0, "greedy_accept: workspace must be 4-byte aligned");
   const int nslice = static_cast<int>(ceil_div(V, GA_SLICE));
   float* ws_v = static_cast<float*>(ws);
   int32_t* ws_i = reinterpret_cast<int32_t*>(ws_v + rows * nslice);
@@ -219,4 +212,86 @@ extern "C" dsa_status greedy_accept(const void* logits, int32_t dtype, int64_t l
   hipLaunchKernelGGL(accept_kernel, dim3((unsigned)B), dim3(64 * acc_waves), 0, st, ws_v, ws_i, nslice, draft, K,
                      num_accepted, next_token, argmax);
   return check_launch("greedy_accept(accept)");
+}
+
+// Host-side checks shared by both entry points (before any launch).
+dsa_status greedy_accept_check(const void* logits, int32_t dtype, int64_t logits_ld,
+                               const int32_t* draft, int32_t B, int32_t K, int32_t V,
+                               int32_t* num_accepted, int32_t* next_token) {
+  DSA_REQUIRE(dtype == DSA_F32 || dtype == DSA_BF16, "greedy_accept: dtype must be DSA_F32 or DSA_BF16");
+  DSA_REQUIRE(B >= 0 && K >= 0 && K <= 63, "greedy_accept: need B >= 0 and 0 <= K <= 63");
+  DSA_REQUIRE(V >= 1 && logits_ld >= V, "greedy_accept: need V >= 1 and logits_ld >= V");
+  if (B == 0) return ok();
+  DSA_REQUIRE(logits && num_accepted && next_token && (K == 0 || draft),
+              "greedy_accept: null pointer");
+  DSA_REQUIRE(static_cast<int64_t>(B) * (K + 1) <= 65535, "greedy_accept: B*(K+1) must be <= 65535");
+  return ok();
+}
+
+// Scratch of greedy_accept_noalloc: a fixed array in each device's memory for the whole life
+// of the process. Its name is a host-side stand-in; the device address comes from
+// hipGetSymbolAddress, resolved once per device with that device current.
+__device__ __align__(256) uint8_t scratch[DSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+dsa_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+    return fail(DSA_ERR_HIP, "greedy_accept_noalloc: no current device");
+  if (dev >= kMaxDevices)
+    return fail(DSA_ERR_UNSUPPORTED, "greedy_accept_noalloc: device index %d above %d", dev,
+                kMaxDevices - 1);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {  // two threads racing here resolve the same address
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(DSA_ERR_HIP, "greedy_accept_noalloc: hipGetSymbolAddress failed: %s",
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return DSA_OK;
+}
+
+}  // namespace
+}  // namespace dsa
+
+extern "C" dsa_status greedy_accept(const void* logits, int32_t dtype, int64_t logits_ld,
+                                    const int32_t* draft, int32_t B, int32_t K, int32_t V,
+                                    int32_t* num_accepted, int32_t* next_token, int32_t* argmax,
+                                    void* ws, size_t ws_bytes, void* stream) {
+  using namespace dsa;
+  dsa_status s = greedy_accept_check(logits, dtype, logits_ld, draft, B, K, V, num_accepted,
+                                     next_token);
+  if (s != DSA_OK || B == 0) return s;
+  const size_t need = greedy_accept_workspace_size(B, K, V);
+  if (!ws || ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "greedy_accept: workspace needs %zu bytes (got %zu)", need,
+                ws_bytes);
+  DSA_REQUIRE((reinterpret_cast<uintptr_t>(ws) & 3) == 0, "greedy_accept: workspace must be 4-byte aligned");
+  return greedy_accept_launch(logits, dtype, logits_ld, draft, B, K, V, num_accepted, next_token,
+                              argmax, ws, stream);
+}
+
+extern "C" dsa_status greedy_accept_noalloc(const void* logits, int32_t dtype, int64_t logits_ld,
+                                            const int32_t* draft, int32_t B, int32_t K, int32_t V,
+                                            int32_t* num_accepted, int32_t* next_token,
+                                            int32_t* argmax, void* stream) {
+  using namespace dsa;
+  dsa_status s = greedy_accept_check(logits, dtype, logits_ld, draft, B, K, V, num_accepted,
+                                     next_token);
+  if (s != DSA_OK || B == 0) return s;
+  const size_t need = greedy_accept_workspace_size(B, K, V);
+  if (need > DSA_NOALLOC_SCRATCH_BYTES)
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL,
+                "greedy_accept_noalloc: B*(K+1) rows of %d logits need %zu bytes of scratch, above "
+                "its fixed %zu bytes; call greedy_accept with a workspace instead",
+                V, need, static_cast<size_t>(DSA_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  s = scratch_of_current_device(&ws);
+  if (s != DSA_OK) return s;
+  return greedy_accept_launch(logits, dtype, logits_ld, draft, B, K, V, num_accepted, next_token,
+                              argmax, ws, stream);
 }

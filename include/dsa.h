@@ -288,6 +288,26 @@ dsa_status greedy_accept(const void* logits, int32_t dtype, int64_t logits_ld,
 size_t greedy_accept_workspace_size(int32_t B, int32_t K, int32_t V);
 
 /*
+ * greedy_accept_noalloc -- greedy_accept for callers that cannot allocate: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. Same inputs, outputs,
+ * results and errors as greedy_accept, without the workspace arguments: the per-slice maxima
+ * go to a fixed scratch array of DSA_NOALLOC_SCRATCH_BYTES in each device's memory, held
+ * until the process ends (its address is looked up once per device, on the first call made
+ * with that device current). The call allocates and frees nothing.
+ * Limit: greedy_accept_workspace_size(B, K, V) <= DSA_NOALLOC_SCRATCH_BYTES (for V = 151552,
+ * up to 3542 logits rows); larger batches return DSA_ERR_WORKSPACE_TOO_SMALL before any
+ * launch. Every call on a device shares that device's array: calls that overlap on one
+ * device (concurrent streams, or threads) race; calls on one stream are ordered.
+ * Nothing in the array needs clearing between calls (each call writes every entry it reads).
+ */
+#define DSA_NOALLOC_SCRATCH_BYTES (1u << 20)
+
+dsa_status greedy_accept_noalloc(const void* logits, int32_t dtype, int64_t logits_ld,
+                                 const int32_t* draft, int32_t B, int32_t K, int32_t V,
+                                 int32_t* num_accepted, int32_t* next_token, int32_t* argmax,
+                                 void* stream);
+
+/*
  * rejection_accept -- acceptance of a chain of K drafts per request by rejection
  * sampling.
  * ("GLM-5.3 推理全链路(十四)", "接受判定:greedy 与 rejection sampling": draft i is kept
