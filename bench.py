@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--no-refine", action="store_true",
                     help="top-k on the float32 scores alone (default: the exact-boundary refine, "
                          "so the step's top-k sets are the oracle's)")
+    ap.add_argument("--topk-path", choices=("fused", "separate"), default="separate",
+                    help="fused: dsa_index_topk (scores and refined top-k in one call, no score "
+                         "rows); separate: dsa_index_score, then dsa_topk with the refine")
     ap.add_argument("--err-scale", type=float, default=0.0,
                     help="C of the refine's error bound (0: the library default, 4)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -247,9 +250,17 @@ def main():
     ws_need = api.sparse_mla_workspace_size(T, w.mla_heads, w.topk)
     ws_mla = torch.empty(max(ws_need, 16), dtype=torch.uint8, device=dev)
     from dsa_sparse_attention_amd import _lib
+    fused = args.topk_path == "fused"
+    if fused and args.no_refine:
+        sys.exit("bench.py: the fused path always refines (--no-refine needs --topk-path separate)")
     refine = not args.no_refine
     tk_need = api.topk_workspace_size(w.batch, T, max_kv, w.topk, refine)
     status = torch.zeros(T, dtype=torch.int32, device=dev)
+    path = torch.zeros(T, dtype=torch.int32, device=dev)
+    ws_fused = None
+    if fused:
+        ws_fused = torch.empty(api.index_topk_workspace_size(w.batch, T, w.rows, w.index_heads, max_kv),
+                               dtype=torch.uint8, device=dev)
     ws_tk = torch.empty(max(tk_need, 16), dtype=torch.uint8, device=dev)
     ga_need = _lib.load().greedy_accept_workspace_size(w.batch, w.drafts, w.vocab)
     ws_ga = torch.empty(max(ga_need, 16), dtype=torch.uint8, device=dev)
@@ -259,7 +270,8 @@ def main():
           file=sys.stderr, flush=True)
 
     acc_name = "greedy_accept" if args.accept == "greedy" else "rejection_accept"
-    names = ["cache_write", "index_score", "topk", "sparse_mla", acc_name]
+    names = (["cache_write", "index_topk", "sparse_mla", acc_name] if args.topk_path == "fused" else
+             ["cache_write", "index_score", "topk", "sparse_mla", acc_name])
     if w.share_steps:
         names.append("share_mla")
         qo1 = torch.arange(w.batch + 1, dtype=torch.int32, device=dev)
@@ -271,30 +283,39 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step(inp, ev=None):
-        if ev: ev[0].record(stream)
+        e = iter(ev) if ev else None
+        mark = (lambda: next(e).record(stream)) if ev else (lambda: None)
+        mark()
         api.verify_cache_write(inp.k_new, inp.dst, inp.k_fp8, inp.k_scale, inp.latent_new, inp.kv,
                                q=inp.q_f32, q_fp8=qc, q_scale=qs)
-        if ev: ev[1].record(stream)
-        api.index_score(qc, qs, inp.w, inp.k_fp8, inp.k_scale, qo, ko, w.rows, max_kv, scores=scores)
-        if ev: ev[2].record(stream)
-        rf = (dict(q_fp8=qc, q_scale=qs, w=inp.w, k_fp8=inp.k_fp8, k_scale=inp.k_scale,
-                   status=status, err_scale=args.err_scale) if refine else None)
-        api.topk(scores, qo, ko, w.rows, max_kv, w.topk, out=topk, refine=rf, workspace=ws_tk)
-        if ev: ev[3].record(stream)
+        mark()
+        if fused:
+            api.index_topk(qc, qs, inp.w, inp.k_fp8, inp.k_scale, qo, ko, w.rows, max_kv, w.topk,
+                           out=topk, status=status, path=path, err_scale=args.err_scale,
+                           workspace=ws_fused)
+            mark()
+        else:
+            api.index_score(qc, qs, inp.w, inp.k_fp8, inp.k_scale, qo, ko, w.rows, max_kv, scores=scores)
+            mark()
+            rf = (dict(q_fp8=qc, q_scale=qs, w=inp.w, k_fp8=inp.k_fp8, k_scale=inp.k_scale,
+                       status=status, err_scale=args.err_scale) if refine else None)
+            api.topk(scores, qo, ko, w.rows, max_kv, w.topk, out=topk, refine=rf, workspace=ws_tk)
+            mark()
         api.sparse_mla_decode(inp.q_mla, inp.kv, topk, qo, ko, w.rows, w.sm_scale, out=out, lse=lse,
                               workspace=ws_mla)
-        if ev: ev[4].record(stream)
+        mark()
         if inp.rej is None:
             api.greedy_accept(inp.logits, inp.draft, w.drafts, argmax=False, workspace=ws_ga)
         else:
             r = inp.rej
             api.rejection_accept(r["logits"], r["draft_probs"], r["draft"], r["u"], r["us"],
                                  w.drafts, workspace=ws_ra)
-        if ev: ev[5].record(stream)
+        mark()
         for qd in inp.q_draft or []:  # draft steps: the step-0 top-k row at the accepted position
             api.sparse_mla_decode(qd, inp.kv, topk, qo1, ko, 1, w.sm_scale, out=out1, lse=lse1,
                                   workspace=ws1, share_base=qo, num_accepted=n_acc)
-        if ev and inp.q_draft: ev[6].record(stream)
+        if inp.q_draft:
+            mark()
 
     # Warm-up: at least --warmup steps, and steps in groups of 50 until --min-warmup-s of
     # wall time has passed. Under sustained load the GPU raises its clock within tens of
@@ -338,6 +359,8 @@ def main():
         refine_rec = {"status_min": int(st.min()), "band_max": int(st.max()),
                       "band_mean": round(float(st.float().mean()), 2),
                       "err_scale": args.err_scale or 4.0}
+        if fused:
+            refine_rec["rows_rescored"] = int(path.sum().item())
     print(f"[bench] {args.steps} steps: {ms_step:.4f} ms/step (wall {wall / args.steps * 1e3:.4f} ms); "
           + ", ".join(f"{n} {v * 1e3:.1f} us" for n, v in per.items()), file=sys.stderr, flush=True)
 
@@ -350,12 +373,18 @@ def main():
     wq = dict(bytes=T * (w.index_heads + 1) * (w.index_dim * 4 + w.index_dim + 4) + T * 2 * 1152)
     kern = {
         "cache_write": dict(bytes=wq["bytes"], bound="hbm", file="quantize.hip"),
-        "index_score": dict(bytes=wi["bytes"], flops=wi["flops"], bound="mfma", file="index_score.hip"),
-        "topk": dict(bytes=wt["bytes"], bound="hbm", file="topk.hip"),
         "sparse_mla": dict(bytes=wm["bytes"], flops=wm["flops"], bound="hbm", file="sparse_mla.hip"),
         acc_name: dict(bytes=wg["bytes"], bound="hbm",
                        file="greedy_accept.hip" if args.accept == "greedy" else "rejection_accept.hip"),
     }
+    if fused:
+        wf = accounting.index_topk_work(lengths, w.rows, w.index_heads, w.index_dim, w.topk)
+        kern["index_topk"] = dict(bytes=wf["bytes"], flops=wf["flops"], bound="mfma",
+                                  file="index_score.hip")
+    else:
+        kern["index_score"] = dict(bytes=wi["bytes"], flops=wi["flops"], bound="mfma",
+                                   file="index_score.hip")
+        kern["topk"] = dict(bytes=wt["bytes"], bound="hbm", file="topk.hip")
     if w.share_steps:
         ws_ = accounting.sparse_mla_work(w.batch, w.mla_heads, w.topk)
         kern["share_mla"] = dict(bytes=w.share_steps * ws_["bytes"],
@@ -366,7 +395,7 @@ def main():
         e = {"us": round(per[n] * 1e3, 2), "GB/s": round(kd["bytes"] / t_s / 1e9, 1),
              "hbm_frac": round(kd["bytes"] / t_s / 1e9 / HBM_PEAK_GBS, 4)}
         if "flops" in kd:
-            peak = FP8_PEAK_TFLOPS if n == "index_score" else BF16_PEAK_TFLOPS
+            peak = FP8_PEAK_TFLOPS if n in ("index_score", "index_topk") else BF16_PEAK_TFLOPS
             e["TFLOP/s"] = round(kd["flops"] / t_s / 1e12, 1)
             e["mfma_frac"] = round(kd["flops"] / t_s / 1e12 / peak, 4)
         kernels[n] = e
@@ -396,11 +425,12 @@ def main():
                    "index_heads": w.index_heads, "index_dim": w.index_dim, "topk": w.topk,
                    "mla_heads": w.mla_heads, "vocab": w.vocab, "global_batch": rows_step,
                    "seq_len": max_kv, "share_steps": w.share_steps, "topk_refine": refine,
+                   "topk_path": args.topk_path,
                    "accept": args.accept,
                    "parallelism": "single-gpu"},
         "step_includes": names,
-        "rows_per_s_indexer_topk_mla": round(T / ((per["index_score"] + per["topk"] +
-                                                  per["sparse_mla"]) * 1e-3), 1),
+        "rows_per_s_indexer_topk_mla": round(T / ((per.get("index_topk", 0.0) + per.get("index_score", 0.0) +
+                                                  per.get("topk", 0.0) + per["sparse_mla"]) * 1e-3), 1),
         "kernels": kernels,
         "roofline": roof,
         "refine": refine_rec,

@@ -29,6 +29,9 @@ SIGNATURES = {
                         ctypes.c_int),
     "dsa_topk": ([P, I64, P, P, I32, I32, I32, I64, I32, P, P, P, SZ, P], ctypes.c_int),
     "dsa_topk_workspace_size": ([I32, I32, I64, I32, I32], SZ),
+    "dsa_index_topk": ([P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I64, I32, ctypes.c_double,
+                        P, P, P, P, SZ, P], ctypes.c_int),
+    "dsa_index_topk_workspace_size": ([I32, I32, I32, I32, I64], SZ),
     "dsa_sparse_mla_decode": ([P, P, P, I32, P, P, P, P, I32, I32, I32, I32, I32, F32, P, P, P, SZ, P],
                               ctypes.c_int),
     "dsa_sparse_mla_workspace_size": ([I32, I32, I32], SZ),

@@ -56,6 +56,15 @@ def topk_work(lengths, rows: int, k: int) -> dict:
     return dict(bytes=4 * pairs + 4 * k * rows * len(lengths), flops=0)
 
 
+def index_topk_work(lengths, rows: int, heads: int, dim: int, k: int) -> dict:
+    """Bytes/flops of dsa_index_topk for one batch: the index scoring's key, scale and query
+    reads and its contraction, and the k indices written per row (no score rows)."""
+    wi = index_score_work(lengths, rows, heads, dim)
+    nrows = len(lengths) * rows
+    return dict(bytes=wi["bytes"] - 4 * wi["pairs"] + 4 * k * nrows, flops=wi["flops"],
+                pairs=wi["pairs"])
+
+
 def sparse_mla_work(n_rows: int, heads: int, k: int, selected_per_row=None) -> dict:
     """Bytes/flops of dsa_sparse_mla_decode.
 

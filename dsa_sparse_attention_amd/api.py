@@ -191,6 +191,50 @@ def topk(scores, q_row_offsets, kv_row_offsets, max_q_rows: int, max_kv_len: int
     return out
 
 
+def index_topk_workspace_size(B: int, T: int, max_q_rows: int, H_I: int, max_kv_len: int) -> int:
+    return int(_lib.load().dsa_index_topk_workspace_size(B, T, max_q_rows, H_I, max_kv_len))
+
+
+def index_topk(q_fp8, q_scale, w, k_fp8, k_scale, q_row_offsets, kv_row_offsets,
+               max_q_rows: int, max_kv_len: int, k: int, out=None, status=None, path=None,
+               err_scale: float = 0.0, workspace=None):
+    """Fused indexer score + refined top-k (dsa_index_topk): top-k positions [T, k], ascending,
+    -1 padded; status / path (int32 [T]) are filled when given."""
+    _dev(q_fp8, "q_fp8", torch.uint8)
+    _dev(k_fp8, "k_fp8", torch.uint8)
+    for n, t in (("q_scale", q_scale), ("w", w), ("k_scale", k_scale)):
+        _dev(t, n, torch.float32)
+    _dev(q_row_offsets, "q_row_offsets", torch.int32)
+    _dev(kv_row_offsets, "kv_row_offsets", torch.int64)
+    T, H, D = q_fp8.shape
+    B = q_row_offsets.numel() - 1
+    _shape(q_scale, "q_scale", (T, H))
+    _shape(w, "w", (T, H))
+    if k_fp8.dim() != 2 or k_fp8.shape[1] != D or k_scale.numel() != k_fp8.shape[0]:
+        raise ValueError("k_fp8 must be [N, D_I] with one k_scale per key")
+    if out is None:
+        out = torch.empty((T, k), dtype=torch.int32, device=q_fp8.device)
+    _dev(out, "out", torch.int32)
+    _shape(out, "out", (T, k))
+    for n, t in (("status", status), ("path", path)):
+        if t is not None:
+            _dev(t, n, torch.int32)
+            _shape(t, n, (T,))
+    lib = _lib.load()
+    need = lib.dsa_index_topk_workspace_size(B, T, max_q_rows, H, max_kv_len)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_fp8.device)
+    wsb = 0
+    if workspace is not None:
+        _dev(workspace, "workspace", torch.uint8)
+        wsb = workspace.numel()
+    _check(lib.dsa_index_topk(_p(q_fp8), _p(q_scale), _p(w), _p(k_fp8), _p(k_scale),
+                              _p(q_row_offsets), _p(kv_row_offsets), B, T, max_q_rows, H, D,
+                              max_kv_len, k, float(err_scale), _p(status), _p(path), _p(out),
+                              _p(workspace), wsb, _stream()))
+    return out
+
+
 def topk_workspace_size(B: int, T: int, max_kv_len: int, k: int, refine: bool = False) -> int:
     return int(_lib.load().dsa_topk_workspace_size(B, T, max_kv_len, k, 1 if refine else 0))
 

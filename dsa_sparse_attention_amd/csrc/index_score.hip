@@ -35,6 +35,7 @@
 #include <atomic>
 
 #include "common.hpp"
+#include "fused.hpp"
 
 namespace dsa {
 namespace {
@@ -78,17 +79,44 @@ struct Ring {
   static_assert((NBUF - 2) * DMAS <= 63, "vmcnt holds at most 63");
 };
 
+// What a launch produces (kernel template argument):
+//  SCORE   every visible score into scores[T, ld];
+//  SAMPLE  scores of S evenly spaced keys per request, sample j at position
+//          floor(j n0 / S) (n0 = the request's first row's visible count), into
+//          samples[T, S] (the key segments are sample indices);
+//  COMPACT only the scores >= tau[t] of each row, as (score bits, position) pairs in the
+//          row's slice of cand for the block's key segment (no score row is written), with
+//          the count and the largest key scale of every (row, range, wave half).
+enum { SCORE = 0, SAMPLE = 1, COMPACT = 2 };
+
+struct ModeArgs {
+  int S;               // SAMPLE: samples per request (scores: the sample buffer, ld = S)
+  const float* tau;    // COMPACT: [T] candidate threshold per row
+  uint2* cand;         // COMPACT: [T, ldc] (float bits, request-local position)
+  int64_t ldc;
+  int32_t* cnt;        // COMPACT: [T, gx, 2] candidates of each (row, range, half)
+  float* msc;          // COMPACT: [T, gx, 2] largest visible key scale of each
+  int gx;              // COMPACT: number of key ranges (the grid's x)
+};
+
+// First row's visible count of a request (at least 1 when it has keys): sample positions
+// are spread over the keys every row of the request sees.
+__device__ __forceinline__ int64_t sample_span(const RowInfo& ri) {
+  const int64_t n0 = ri.L - ri.R + 1;
+  return n0 < 1 ? 1 : (n0 > ri.L ? ri.L : n0);
+}
+
 // Keys key0 .. key_end-1 (0 < key_end - key0 < 2^31) of request `ri` against its rows
 // row0 .. row0+NR-1, by the whole block: the producer wave (producer_segment) streams the
 // keys through the ring, the compute waves (compute_segment) score and store them. Each
 // side passes one barrier per tile, so the block's barriers pair up one to one.
-template <int D, int HT, int NR>
+template <int D, int HT, int NR, int MODE>
 __device__ __forceinline__ void producer_segment(
     uint8_t (&ring)[NBUF][Ring<D>::SLOT], const uint8_t* __restrict__ q_fp8,
     const float* __restrict__ q_scale, const float* __restrict__ w,
     const uint8_t* __restrict__ k_fp8, const float* __restrict__ k_scale, const RowInfo& ri,
     int64_t key0, int64_t key_end, int row0, int H, float* __restrict__ scores, int64_t ld,
-    int lane, int wave) {
+    int lane, int wave, const ModeArgs& ma) {
   constexpr int NCH = Ring<D>::NCH;
   constexpr int KPB = Ring<D>::KPB;
   constexpr int TILE_K = Ring<D>::TILE_K;
@@ -104,7 +132,15 @@ __device__ __forceinline__ void producer_segment(
   // for odd m): two per-lane byte offsets serve every DMA of every full tile.
   const uint8_t* kreq = k_fp8 + (ri.kv_base + key0) * D;
   const float* sreq = k_scale + ri.kv_base + key0;
-  const int ful = nkeys / KT;  // full tiles
+  // SAMPLE: tile key i is sample key0 + i, at request position floor((key0 + i) n0 / S)
+  const int64_t n0 = MODE == SAMPLE ? sample_span(ri) : 0;
+  auto pos_of = [&](int i) -> int64_t {
+    if constexpr (MODE == SAMPLE)
+      return (key0 + i) * n0 / ma.S - key0;  // relative to kreq / sreq
+    else
+      return i;
+  };
+  const int ful = MODE == SAMPLE ? 0 : nkeys / KT;  // full (contiguous) tiles
   auto issue_tile = [&](int it) {
     int ln = lane;
     asm volatile("" : "+v"(ln));  // recomputed per tile, not held across the loop
@@ -122,11 +158,11 @@ __device__ __forceinline__ void producer_segment(
       for (int m = 0; m < NCH; ++m) {
         const int kt = KPB * m + ln / NCH;  // key within the tile
         const int key = it * KT + kt < nkeys ? it * KT + kt : nkeys - 1;
-        lds_dma16(kreq + static_cast<int64_t>(key) * D + 16 * ((ln % NCH) ^ kswz<NCH>(kt)),
+        lds_dma16(kreq + pos_of(key) * D + 16 * ((ln % NCH) ^ kswz<NCH>(kt)),
                   (const lds_void*)(slot + 1024 * m));
       }
       const int key = it * KT + ln < nkeys ? it * KT + ln : nkeys - 1;
-      lds_dma4(sreq + key, (const lds_void*)(slot + TILE_K));
+      lds_dma4(sreq + pos_of(key), (const lds_void*)(slot + TILE_K));
     }
   };
   // Tile it+NBUF-2 goes into the slot of tile it-2, which every compute wave finished
@@ -148,13 +184,13 @@ __device__ __forceinline__ void producer_segment(
   }
 }
 
-template <int D, int HT, int NR>
+template <int D, int HT, int NR, int MODE>
 __device__ __forceinline__ void compute_segment(
     uint8_t (&ring)[NBUF][Ring<D>::SLOT], const uint8_t* __restrict__ q_fp8,
     const float* __restrict__ q_scale, const float* __restrict__ w,
     const uint8_t* __restrict__ k_fp8, const float* __restrict__ k_scale, const RowInfo& ri,
     int64_t key0, int64_t key_end, int row0, int H, float* __restrict__ scores, int64_t ld,
-    int lane, int wave) {
+    int lane, int wave, const ModeArgs& ma) {
   constexpr int NCH = Ring<D>::NCH;
   constexpr int TILE_K = Ring<D>::TILE_K;
   const int nkeys = static_cast<int>(key_end - key0);
@@ -169,8 +205,11 @@ __device__ __forceinline__ void compute_segment(
   const bool row_live = r < ri.R;  // wave-uniform
   const int64_t nvis = row_live ? visible_count(ri, r) : 0;
   const int64_t t = ri.t0 + (row_live ? r : 0);  // a valid row for the (discarded) loads
-  // scores stored for keys key0 .. key0 + nstore - 1 of this row (visible and in chunk)
-  const int nstore = static_cast<int>(nvis - key0 < nkeys ? (nvis - key0 > 0 ? nvis - key0 : 0) : nkeys);
+  // scores stored for keys key0 .. key0 + nstore - 1 of this row (visible and in chunk;
+  // every sample is visible to every row of its request)
+  const int nstore =
+      MODE == SAMPLE ? (row_live ? nkeys : 0)
+                     : static_cast<int>(nvis - key0 < nkeys ? (nvis - key0 > 0 ? nvis - key0 : 0) : nkeys);
 
   // A operands (q codes) and per-output-row weights u = w * q_scale; all loads are issued
   // before any is used. Heads past H read head H-1 and are zeroed.
@@ -270,6 +309,21 @@ __device__ __forceinline__ void compute_segment(
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
   };
 
+  // COMPACT: the row's candidates of this segment go to cand[t, key0 .. key_end): the
+  // first wave half fills it upwards from key0, the second downwards from key_end - 1 (each
+  // keeps at most one entry per key it scores, so the two never meet); its running count,
+  // and the largest key scale it saw
+  uint2* creg = nullptr;
+  int cdir = 1;
+  float tau = 0.0f;
+  int ccount = 0;
+  float cmax = 0.0f;
+  if constexpr (MODE == COMPACT) {
+    creg = ma.cand + t * ma.ldc + (kh ? key_end - 1 : key0);
+    cdir = kh ? -1 : 1;
+    tau = ma.tau[t];
+  }
+
   f32x4 acc0[HT], acc1[HT];  // sub-tile 0 / sub-tile 1 of the current tile
   if (ntiles > 0) {
     __syncthreads();  // tile 0 is in LDS (the producer waited for it)
@@ -291,7 +345,33 @@ __device__ __forceinline__ void compute_segment(
     }
     if (lv) {
       const float sum = combine(p0, partial(acc1));
-      if ((g == 1 || g == 2) && it * KT + kt < nstore) srow[it * KT + kt] = sum * sc;
+      const bool mine = (g == 1 || g == 2) && it * KT + kt < nstore;
+      if constexpr (MODE == COMPACT) {
+        const float v = sum * sc;
+        const bool keep = mine && v >= tau;
+        const uint64_t bk = __builtin_amdgcn_ballot_w64(keep);
+        if (keep) {
+          const int at = ccount + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                                      static_cast<uint32_t>(bk >> 32),
+                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bk), 0u)));
+          creg[cdir * at] = make_uint2(__float_as_uint(v), static_cast<uint32_t>(key0 + it * KT + kt));
+        }
+        ccount += static_cast<int>(__popcll(bk));
+        if (mine) cmax = fmaxf(cmax, sc);
+      } else {
+        if (mine) srow[it * KT + kt] = sum * sc;
+      }
+    }
+  }
+  if constexpr (MODE == COMPACT) {
+    if (live) {
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) cmax = fmaxf(cmax, __shfl_xor(cmax, o));
+      if (lane == 0) {
+        const int64_t m = (t * ma.gx + blockIdx.x) * 2 + kh;
+        ma.cnt[m] = ccount;
+        ma.msc[m] = cmax;
+      }
     }
   }
 }
@@ -318,17 +398,21 @@ __device__ __forceinline__ int request_of(const int64_t* __restrict__ kv_off, in
 // 64-key tiles; block (x, 0, z) scores range x against rows z NR .. z NR + NR - 1 of every
 // request the range touches, one segment per request. Ragged lengths thus spread evenly
 // over the blocks, and a small batch still occupies many CUs.
-template <int D, int HT, int NR>
+template <int D, int HT, int NR, int MODE>
 __global__ __launch_bounds__((2 * NR + 1) * 64) void index_score_kernel(
     const uint8_t* __restrict__ q_fp8, const float* __restrict__ q_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ k_fp8,
     const float* __restrict__ k_scale, const int32_t* __restrict__ q_off,
-    const int64_t* __restrict__ kv_off, int B, int H, float* __restrict__ scores, int64_t ld) {
+    const int64_t* __restrict__ kv_off, int B, int H, float* __restrict__ scores, int64_t ld,
+    ModeArgs ma) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NBUF][Ring<D>::SLOT];
   const int lane = threadIdx.x % 64;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);  // wave-uniform (SGPR)
   const int row0 = blockIdx.z * NR;
-  const int64_t base = kv_off[0], end = kv_off[B];
+  // key space cut into ranges: the requests' keys laid end to end, or (SAMPLE) S sample
+  // slots per request
+  const int64_t base = MODE == SAMPLE ? 0 : kv_off[0];
+  const int64_t end = MODE == SAMPLE ? static_cast<int64_t>(B) * ma.S : kv_off[B];
   int64_t share = (end - base + gridDim.x - 1) / gridDim.x;
   share = (share + KT - 1) / KT * KT;
   const int64_t g0 = base + static_cast<int64_t>(blockIdx.x) * share;
@@ -337,12 +421,15 @@ __global__ __launch_bounds__((2 * NR + 1) * 64) void index_score_kernel(
   // Both roles walk the same segments and pass the same barriers.
   auto for_segments = [&](auto&& body) {
     bool first = true;
-    for (int b = request_of(kv_off, B, g0, lane); b < B; ++b) {
+    const int b_first = MODE == SAMPLE ? static_cast<int>(g0 / ma.S) : request_of(kv_off, B, g0, lane);
+    for (int b = b_first; b < B; ++b) {
       const RowInfo ri = load_row_info(q_off, kv_off, b);
-      if (ri.kv_base >= g1) break;  // block-uniform, as every test below
+      const int64_t sbase = MODE == SAMPLE ? static_cast<int64_t>(b) * ma.S : ri.kv_base;
+      const int64_t slen = MODE == SAMPLE ? (ri.L > 0 ? ma.S : 0) : ri.L;
+      if (sbase >= g1) break;  // block-uniform, as every test below
       if (row0 >= ri.R) continue;
-      const int64_t key0 = (g0 > ri.kv_base ? g0 : ri.kv_base) - ri.kv_base;
-      int64_t key_end = (g1 < ri.kv_base + ri.L ? g1 : ri.kv_base + ri.L) - ri.kv_base;
+      const int64_t key0 = (g0 > sbase ? g0 : sbase) - sbase;
+      int64_t key_end = (g1 < sbase + slen ? g1 : sbase + slen) - sbase;
       if (key_end > ld) key_end = ld;  // device lengths beyond the score stride are clipped
       if (key_end <= key0) continue;
       // every wave is done with the previous segment's tiles before the producer refills
@@ -354,13 +441,13 @@ __global__ __launch_bounds__((2 * NR + 1) * 64) void index_score_kernel(
   };
   if (wave == 2 * NR) {
     for_segments([&](const RowInfo& ri, int64_t key0, int64_t key_end) {
-      producer_segment<D, HT, NR>(ring, q_fp8, q_scale, w, k_fp8, k_scale, ri, key0, key_end,
-                                  row0, H, scores, ld, lane, wave);
+      producer_segment<D, HT, NR, MODE>(ring, q_fp8, q_scale, w, k_fp8, k_scale, ri, key0,
+                                        key_end, row0, H, scores, ld, lane, wave, ma);
     });
   } else {
     for_segments([&](const RowInfo& ri, int64_t key0, int64_t key_end) {
-      compute_segment<D, HT, NR>(ring, q_fp8, q_scale, w, k_fp8, k_scale, ri, key0, key_end,
-                                 row0, H, scores, ld, lane, wave);
+      compute_segment<D, HT, NR, MODE>(ring, q_fp8, q_scale, w, k_fp8, k_scale, ri, key0,
+                                       key_end, row0, H, scores, ld, lane, wave, ma);
     });
   }
 }
@@ -380,56 +467,80 @@ int cu_count() {
   return n;
 }
 
+// One launch of the scoring kernel: its arguments, and the grid before the cap below.
+struct ScoreLaunch {
+  dim3 grid;
+  hipStream_t st;
+  const uint8_t* q;
+  const float* qs;
+  const float* w;
+  const uint8_t* k;
+  const float* ks;
+  const int32_t* qo;
+  const int64_t* ko;
+  int B, H;
+  float* sc;
+  int64_t ld;
+  ModeArgs ma;
+};
+
 // grid.x on entry: the key ranges the sizes call for; it is capped at one wave of resident
 // blocks (blocks per CU x CUs, shared by the grid.z row groups), so that every range starts
-// at once and equal ranges finish together.
-template <int D, int HT, int NRV>
-void launch_one(dim3 grid, hipStream_t st, const uint8_t* q, const float* qs, const float* w,
-                const uint8_t* k, const float* ks, const int32_t* qo, const int64_t* ko, int B, int H,
-                float* sc, int64_t ld) {
+// at once and equal ranges finish together. Returns the capped grid.x; launches only when
+// `launch` (COMPACT needs the count before its launch, to size and index its tables).
+template <int D, int HT, int NRV, int MODE>
+int64_t run_one(ScoreLaunch a, bool launch) {
   if constexpr (HT >= 8 && NRV > MAX_ROWS_H128) {
-    return;  // never chosen: the host caps rows per block at MAX_ROWS_H128 for 8 head tiles
+    return 0;  // never chosen: the host caps rows per block at MAX_ROWS_H128 for 8 head tiles
   } else {
     constexpr int threads = (2 * NRV + 1) * 64;
     static std::atomic<int> occ{0};  // resident blocks per CU of this instantiation
     int o = occ.load(std::memory_order_relaxed);
     if (o <= 0) {
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, index_score_kernel<D, HT, NRV>, threads,
-                                                       0) != hipSuccess || o < 1)
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, index_score_kernel<D, HT, NRV, MODE>,
+                                                       threads, 0) != hipSuccess || o < 1)
         o = 1;
       occ.store(o, std::memory_order_relaxed);
     }
-    const int64_t cap = static_cast<int64_t>(o) * cu_count() / grid.z;
-    if (static_cast<int64_t>(grid.x) > cap) grid.x = static_cast<unsigned>(cap > 1 ? cap : 1);
-    hipLaunchKernelGGL((index_score_kernel<D, HT, NRV>), grid, dim3(threads), 0, st, q, qs, w, k,
-                       ks, qo, ko, B, H, sc, ld);
+    const int64_t cap = static_cast<int64_t>(o) * cu_count() / a.grid.z;
+    if (static_cast<int64_t>(a.grid.x) > cap) a.grid.x = static_cast<unsigned>(cap > 1 ? cap : 1);
+    if (launch) {
+      if constexpr (MODE == COMPACT) a.ma.gx = static_cast<int>(a.grid.x);
+      hipLaunchKernelGGL((index_score_kernel<D, HT, NRV, MODE>), a.grid, dim3(threads), 0, a.st, a.q,
+                         a.qs, a.w, a.k, a.ks, a.qo, a.ko, a.B, a.H, a.sc, a.ld, a.ma);
+    }
+    return a.grid.x;
   }
 }
 
-template <int D, int HT>
-void launch_nr(int nr, dim3 grid, hipStream_t st, const uint8_t* q, const float* qs,
-               const float* w, const uint8_t* k, const float* ks, const int32_t* qo,
-               const int64_t* ko, int B, int H, float* sc, int64_t ld) {
+template <int D, int HT, int MODE>
+int64_t run_nr(int nr, const ScoreLaunch& a, bool launch) {
   switch (nr) {
-    case 1: launch_one<D, HT, 1>(grid, st, q, qs, w, k, ks, qo, ko, B, H, sc, ld); break;
-    case 2: launch_one<D, HT, 2>(grid, st, q, qs, w, k, ks, qo, ko, B, H, sc, ld); break;
-    case 3: launch_one<D, HT, 3>(grid, st, q, qs, w, k, ks, qo, ko, B, H, sc, ld); break;
-    case 4: launch_one<D, HT, 4>(grid, st, q, qs, w, k, ks, qo, ko, B, H, sc, ld); break;
-    case 5: launch_one<D, HT, 5>(grid, st, q, qs, w, k, ks, qo, ko, B, H, sc, ld); break;
-    case 6: launch_one<D, HT, 6>(grid, st, q, qs, w, k, ks, qo, ko, B, H, sc, ld); break;
-    default: launch_one<D, HT, 7>(grid, st, q, qs, w, k, ks, qo, ko, B, H, sc, ld); break;
+    case 1: return run_one<D, HT, 1, MODE>(a, launch);
+    case 2: return run_one<D, HT, 2, MODE>(a, launch);
+    case 3: return run_one<D, HT, 3, MODE>(a, launch);
+    case 4: return run_one<D, HT, 4, MODE>(a, launch);
+    case 5: return run_one<D, HT, 5, MODE>(a, launch);
+    case 6: return run_one<D, HT, 6, MODE>(a, launch);
+    default: return run_one<D, HT, 7, MODE>(a, launch);
   }
 }
 
-template <int D>
-void launch_ht(int ht, int nr, dim3 grid, hipStream_t st, const uint8_t* q, const float* qs,
-               const float* w, const uint8_t* k, const float* ks, const int32_t* qo,
-               const int64_t* ko, int B, int H, float* sc, int64_t ld) {
+template <int MODE>
+int64_t run_scoring(int D, int ht, int nr, const ScoreLaunch& a, bool launch) {
+  if (D == 128) {
+    switch (ht) {
+      case 1: return run_nr<128, 1, MODE>(nr, a, launch);
+      case 2: return run_nr<128, 2, MODE>(nr, a, launch);
+      case 4: return run_nr<128, 4, MODE>(nr, a, launch);
+      default: return run_nr<128, 8, MODE>(nr, a, launch);
+    }
+  }
   switch (ht) {
-    case 1: launch_nr<D, 1>(nr, grid, st, q, qs, w, k, ks, qo, ko, B, H, sc, ld); break;
-    case 2: launch_nr<D, 2>(nr, grid, st, q, qs, w, k, ks, qo, ko, B, H, sc, ld); break;
-    case 4: launch_nr<D, 4>(nr, grid, st, q, qs, w, k, ks, qo, ko, B, H, sc, ld); break;
-    default: launch_nr<D, 8>(nr, grid, st, q, qs, w, k, ks, qo, ko, B, H, sc, ld); break;
+    case 1: return run_nr<64, 1, MODE>(nr, a, launch);
+    case 2: return run_nr<64, 2, MODE>(nr, a, launch);
+    case 4: return run_nr<64, 4, MODE>(nr, a, launch);
+    default: return run_nr<64, 8, MODE>(nr, a, launch);
   }
 }
 
@@ -437,6 +548,18 @@ int pow2_at_least(int x) {
   int p = 1;
   while (p < x) p <<= 1;
   return p;
+}
+
+// Grid of a scoring launch over `keys_per_request` key slots per request (before the cap):
+// row groups of at most max_rows_for(ht) rows, balanced (6 rows -> one group of 6, 8 -> 4 +
+// 4), and one key range per MIN_SHARE keys of the largest batch the sizes allow.
+void plan_scoring(int B, int max_q_rows, int H, int64_t keys_per_request, dim3* grid, int* nr) {
+  const int ht = pow2_at_least((H + 15) / 16);
+  const int64_t gz = ceil_div(max_q_rows, max_rows_for(ht));
+  *nr = static_cast<int>(ceil_div(max_q_rows, gz));
+  int64_t gx = ceil_div(static_cast<int64_t>(B) * keys_per_request, MIN_SHARE);
+  gx = gx < 1 ? 1 : (gx > 0x7FFFFFFF ? 0x7FFFFFFF : gx);
+  *grid = dim3((unsigned)gx, 1u, (unsigned)(gz > 65535 ? 65536 : gz));
 }
 
 }  // namespace
@@ -466,22 +589,171 @@ extern "C" dsa_status dsa_index_score(const uint8_t* q_fp8, const float* q_scale
               "dsa_index_score: q_fp8 and k_fp8 must be 16-byte aligned");
   DSA_REQUIRE(B <= 65535, "dsa_index_score: B must be <= 65535");
   DSA_REQUIRE(score_ld < (int64_t(1) << 31), "dsa_index_score: score_ld must be < 2^31");
-  const int ht = pow2_at_least((H_I + 15) / 16);
-  // row groups of at most max_rows_for(ht), balanced: e.g. 6 rows -> one group of 6, 8 -> 4 + 4
-  const int64_t gz = ceil_div(max_q_rows, max_rows_for(ht));
-  const int nr = static_cast<int>(ceil_div(max_q_rows, gz));  // rows per block
-  // key ranges: one per MIN_SHARE keys of the largest batch the sizes allow (capped at one
-  // wave of resident blocks by launch_one)
-  int64_t gx = ceil_div(static_cast<int64_t>(B) * max_kv_len, MIN_SHARE);
-  gx = gx < 1 ? 1 : (gx > 0x7FFFFFFF ? 0x7FFFFFFF : gx);
-  DSA_REQUIRE(gz <= 65535, "dsa_index_score: grid too large");
-  dim3 grid((unsigned)gx, 1u, (unsigned)gz);
-  hipStream_t st = as_stream(stream);
-  if (D_I == 128)
-    launch_ht<128>(ht, nr, grid, st, q_fp8, q_scale, w, k_fp8, k_scale, q_row_offsets,
-                   kv_row_offsets, B, H_I, scores, score_ld);
-  else
-    launch_ht<64>(ht, nr, grid, st, q_fp8, q_scale, w, k_fp8, k_scale, q_row_offsets,
-                  kv_row_offsets, B, H_I, scores, score_ld);
+  ScoreLaunch a{};
+  int nr = 0;
+  plan_scoring(B, max_q_rows, H_I, max_kv_len, &a.grid, &nr);
+  DSA_REQUIRE(a.grid.z <= 65535, "dsa_index_score: grid too large");
+  a.st = as_stream(stream);
+  a.q = q_fp8;
+  a.qs = q_scale;
+  a.w = w;
+  a.k = k_fp8;
+  a.ks = k_scale;
+  a.qo = q_row_offsets;
+  a.ko = kv_row_offsets;
+  a.B = B;
+  a.H = H_I;
+  a.sc = scores;
+  a.ld = score_ld;
+  run_scoring<SCORE>(D_I, pow2_at_least((H_I + 15) / 16), nr, a, true);
   return check_launch("dsa_index_score");
+}
+
+namespace dsa {
+namespace {
+
+constexpr int64_t kFusedMaxRanges = 4096;  // key ranges the compaction tables are sized for
+
+struct FusedLayout {
+  int S;           // samples per request
+  int64_t ldc;     // candidate row stride (entries)
+  int64_t gxb;     // key ranges the count tables hold
+  size_t samples, tau, cand, cnt, msc, total;  // byte offsets, then the size
+};
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+FusedLayout fused_layout(int32_t B, int32_t T, int32_t max_q_rows, int32_t H, int64_t max_kv_len) {
+  FusedLayout f{};
+  f.S = fused_sample_count(max_kv_len);
+  f.ldc = (max_kv_len + 3) / 4 * 4;
+  if (f.ldc < 4) f.ldc = 4;
+  dim3 grid;
+  int nr = 0;
+  plan_scoring(B, max_q_rows, H, max_kv_len, &grid, &nr);
+  f.gxb = grid.x < kFusedMaxRanges ? grid.x : kFusedMaxRanges;
+  size_t off = 0;
+  f.samples = off;
+  off = align256(off + static_cast<size_t>(T) * f.S * 4);
+  f.tau = off;
+  off = align256(off + static_cast<size_t>(T) * 4);
+  f.cand = off;
+  off = align256(off + static_cast<size_t>(T) * f.ldc * 8);
+  f.cnt = off;
+  off = align256(off + static_cast<size_t>(T) * f.gxb * 2 * 4);
+  f.msc = off;
+  off = align256(off + static_cast<size_t>(T) * f.gxb * 2 * 4);
+  f.total = off;
+  return f;
+}
+
+}  // namespace
+}  // namespace dsa
+
+extern "C" size_t dsa_index_topk_workspace_size(int32_t B, int32_t T, int32_t max_q_rows,
+                                                int32_t H_I, int64_t max_kv_len) {
+  using namespace dsa;
+  if (B <= 0 || T <= 0 || max_q_rows <= 0 || H_I < 1 || max_kv_len < 0) return 0;
+  return fused_layout(B, T, max_q_rows, H_I, max_kv_len).total;
+}
+
+extern "C" dsa_status dsa_index_topk(const uint8_t* q_fp8, const float* q_scale, const float* w,
+                                     const uint8_t* k_fp8, const float* k_scale,
+                                     const int32_t* q_row_offsets, const int64_t* kv_row_offsets,
+                                     int32_t B, int32_t T, int32_t max_q_rows, int32_t H_I,
+                                     int32_t D_I, int64_t max_kv_len, int32_t k, double err_scale,
+                                     int32_t* status, int32_t* path, int32_t* topk, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  using namespace dsa;
+  if (D_I != 64 && D_I != 128)
+    return fail(DSA_ERR_UNSUPPORTED, "dsa_index_topk: D_I must be 64 or 128 (got %d)", D_I);
+  if (H_I < 1 || H_I > 128)
+    return fail(DSA_ERR_UNSUPPORTED, "dsa_index_topk: H_I must be in [1, 128] (got %d)", H_I);
+  DSA_REQUIRE(k >= 1 && k <= 4096, "dsa_index_topk: k must be in [1, 4096] (got %d)", k);
+  DSA_REQUIRE(B >= 0 && T >= 0 && max_q_rows >= 0 && max_kv_len >= 0, "dsa_index_topk: negative size");
+  DSA_REQUIRE(max_kv_len < (int64_t(1) << 31), "dsa_index_topk: max_kv_len must be < 2^31");
+  DSA_REQUIRE(err_scale >= 0.0 && err_scale < 1e30, "dsa_index_topk: err_scale must be in [0, 1e30)");
+  if (B == 0 || T == 0 || max_q_rows == 0) return ok();
+  DSA_REQUIRE(q_fp8 && q_scale && w && k_fp8 && k_scale && q_row_offsets && kv_row_offsets && topk,
+              "dsa_index_topk: null pointer");
+  DSA_REQUIRE((reinterpret_cast<uintptr_t>(q_fp8) & 15) == 0 &&
+                  (reinterpret_cast<uintptr_t>(k_fp8) & 15) == 0,
+              "dsa_index_topk: q_fp8 and k_fp8 must be 16-byte aligned");
+  DSA_REQUIRE(B <= 65535 && max_q_rows <= 65535, "dsa_index_topk: B and max_q_rows must be <= 65535");
+  const FusedLayout f = fused_layout(B, T, max_q_rows, H_I, max_kv_len);
+  if (!ws || ws_bytes < f.total)
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "dsa_index_topk: workspace needs %zu bytes (got %zu)",
+                f.total, ws_bytes);
+  DSA_REQUIRE((reinterpret_cast<uintptr_t>(ws) & 255) == 0, "dsa_index_topk: ws must be 256-byte aligned");
+  uint8_t* wb = static_cast<uint8_t*>(ws);
+  float* samples = reinterpret_cast<float*>(wb + f.samples);
+  float* tau = reinterpret_cast<float*>(wb + f.tau);
+  uint2* cand = reinterpret_cast<uint2*>(wb + f.cand);
+  int32_t* cnt = reinterpret_cast<int32_t*>(wb + f.cnt);
+  float* msc = reinterpret_cast<float*>(wb + f.msc);
+  const int ht = pow2_at_least((H_I + 15) / 16);
+  hipStream_t st = as_stream(stream);
+
+  // 1. sample scores: S slots per request, scored like every other key
+  ScoreLaunch a{};
+  int nr = 0;
+  plan_scoring(B, max_q_rows, H_I, f.S, &a.grid, &nr);
+  DSA_REQUIRE(a.grid.z <= 65535, "dsa_index_topk: grid too large");
+  a.st = st;
+  a.q = q_fp8;
+  a.qs = q_scale;
+  a.w = w;
+  a.k = k_fp8;
+  a.ks = k_scale;
+  a.qo = q_row_offsets;
+  a.ko = kv_row_offsets;
+  a.B = B;
+  a.H = H_I;
+  a.sc = samples;
+  a.ld = f.S;
+  a.ma.S = f.S;
+  run_scoring<SAMPLE>(D_I, ht, nr, a, true);
+  dsa_status s = check_launch("dsa_index_topk(sample)");
+  if (s != DSA_OK) return s;
+  // 2. each row's candidate threshold
+  launch_sample_tau(samples, f.S, q_row_offsets, kv_row_offsets, B, max_q_rows, k, tau, st);
+  s = check_launch("dsa_index_topk(threshold)");
+  if (s != DSA_OK) return s;
+  // 3. scores >= tau of every row, kept per key range
+  plan_scoring(B, max_q_rows, H_I, max_kv_len, &a.grid, &nr);
+  a.sc = nullptr;
+  a.ld = f.ldc;
+  a.ma = ModeArgs{};
+  a.ma.tau = tau;
+  a.ma.cand = cand;
+  a.ma.ldc = f.ldc;
+  a.ma.cnt = cnt;
+  a.ma.msc = msc;
+  const int64_t gx = run_scoring<COMPACT>(D_I, ht, nr, a, false);
+  if (gx > f.gxb)
+    return fail(DSA_ERR_UNSUPPORTED, "dsa_index_topk: %lld key ranges exceed the tables' %lld",
+                (long long)gx, (long long)f.gxb);
+  run_scoring<COMPACT>(D_I, ht, nr, a, true);
+  s = check_launch("dsa_index_topk(score)");
+  if (s != DSA_OK) return s;
+  // 4. exact selection from the candidates (or from a rescored row)
+  FusedSelectLaunch fsl{};
+  fsl.cand = cand;
+  fsl.ldc = f.ldc;
+  fsl.cnt = cnt;
+  fsl.msc = msc;
+  fsl.tau = tau;
+  fsl.path = path;
+  fsl.gx = static_cast<int>(gx);
+  fsl.q_fp8 = q_fp8;
+  fsl.q_scale = q_scale;
+  fsl.w = w;
+  fsl.k_fp8 = k_fp8;
+  fsl.k_scale = k_scale;
+  fsl.status = status;
+  fsl.err_scale = err_scale;
+  fsl.H = H_I;
+  fsl.D = D_I;
+  launch_fused_select(fsl, q_row_offsets, kv_row_offsets, B, max_q_rows, k, topk, st);
+  return check_launch("dsa_index_topk(select)");
 }

@@ -37,6 +37,7 @@
 // slow path finishes the select and the emission with further reads of the row.
 // Block-wide prefix sums use DPP row shifts and row broadcasts within each wave.
 #include "common.hpp"
+#include "fused.hpp"
 
 namespace dsa {
 namespace {
@@ -266,10 +267,11 @@ struct Refine {  // kernel argument; q_fp8 == nullptr: no refine
   const float* w;
   const uint8_t* k_fp8;
   const float* k_scale;
-  const float* kmax;  // [B, nsc] maxima of SC_CHUNK key scales each
+  const float* kmax;  // [B, nsc] maxima of SC_CHUNK key scales each, or nullptr: smax_given
   int32_t* status;    // [T] or nullptr
   double C;
   int H, D, nsc;
+  float smax_given;   // the row's largest visible key scale when kmax is nullptr
 };
 
 struct RowRef {  // one row of a refine
@@ -355,10 +357,14 @@ __device__ __forceinline__ void refine_prefetch(const RowRef& rr, int64_t n, dou
     }
   }
   float sm = 0.0f;
-  int nc = static_cast<int>((n + SC_CHUNK - 1) / SC_CHUNK);
-  if (nc > rf.nsc) nc = rf.nsc;  // rows are clipped to the score stride; stay in the table
-  for (int c = tid; c < nc; c += TK_THREADS)
-    sm = fmaxf(sm, rf.kmax[static_cast<int64_t>(rr.b) * rf.nsc + c]);
+  if (rf.kmax) {
+    int nc = static_cast<int>((n + SC_CHUNK - 1) / SC_CHUNK);
+    if (nc > rf.nsc) nc = rf.nsc;  // rows are clipped to the score stride; stay in the table
+    for (int c = tid; c < nc; c += TK_THREADS)
+      sm = fmaxf(sm, rf.kmax[static_cast<int64_t>(rr.b) * rf.nsc + c]);
+  } else {
+    sm = rf.smax_given;
+  }
   for (int o = 32; o >= 1; o >>= 1) {
     asum += __shfl_xor(asum, o);
     sm = fmaxf(sm, __shfl_xor(sm, o));
@@ -443,7 +449,8 @@ __device__ __forceinline__ i32x4 digit_plane(const uint32_t (&wd)[16], int p) {
 
 // Exact scores of the nb band keys (positions in L.band_pos, request-local) into
 // L.band_val; returns (to every thread) the largest |I_f32 - I_exact| over the band, I_f32
-// read from srow.
+// read from srow (or given in band_f32 when srow is null). band_sk and band_f32 are LDS
+// staging arrays of at least nb entries, free until the band is chosen.
 //   I_exact = s_k * sum_{j ascending} u_j * max(d_j, 0), d_j = q_hat[t,j] . k_hat (exact),
 // evaluated in float64 with one rounding per product and per sum.
 // The head dots are exact integer arithmetic on the int8 MFMA: every e4m3fn value times 2^9
@@ -453,7 +460,8 @@ __device__ __forceinline__ i32x4 digit_plane(const uint32_t (&wd)[16], int p) {
 // per round; the u_j max(d_j, 0) terms of a round go to LDS, and one thread per key then
 // adds them in ascending head order.
 __device__ __forceinline__ double rescore_band(const RowRef& rr, const float* __restrict__ srow,
-                                               int nb, RefineLds& L, bool table_ready) {
+                                               int nb, RefineLds& L, bool table_ready,
+                                               float* band_sk, float* band_f32) {
   const Refine& rf = rr.rf;
   const int tid = threadIdx.x, lane = tid % 64;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -499,14 +507,12 @@ __device__ __forceinline__ double rescore_band(const RowRef& rr, const float* __
     u[i] = head < H ? static_cast<double>(rf.w[t * H + head]) * static_cast<double>(rf.q_scale[t * H + head])
                     : 0.0;
   }
-  // every band key's scale and float32 score, staged in LDS while the loads above are in
-  // flight (sel_pos and in_pos are free until the band is chosen)
-  float* band_sk = reinterpret_cast<float*>(L.sel_pos);
-  float* band_f32 = reinterpret_cast<float*>(L.in_pos);
+  // every band key's scale (and float32 score, unless band_f32 already holds them: srow
+  // null) staged in LDS while the loads above are in flight
   for (int i = tid; i < nb; i += TK_THREADS) {
     const int32_t p = L.band_pos[i];
     band_sk[i] = ksc[p];
-    band_f32[i] = srow[p];
+    if (srow) band_f32[i] = srow[p];
   }
   if (!table_ready) {  // block-uniform
     for (int c = tid; c < 256; c += TK_THREADS) L.digits[c] = e4m3_digit_word(static_cast<uint32_t>(c));
@@ -1294,7 +1300,8 @@ __device__ __forceinline__ void finish_register_refine(const float* __restrict__
   const int tid = threadIdx.x;
   const int nb = L.nb, need = L.need;
   const double eps = L.eps;
-  const double worst = rescore_band(rr, srow, nb, L, true);
+  const double worst = rescore_band(rr, srow, nb, L, true, reinterpret_cast<float*>(L.sel_pos),
+                                    reinterpret_cast<float*>(L.in_pos));
   choose_band<false>(nb, need, L);
   const int nw = (n + 31) / 32;
   const uint32_t wd0 = 2 * tid < nw ? L.bitmap[2 * tid] : 0u;
@@ -1427,7 +1434,8 @@ __device__ __forceinline__ void refine_generic(const float* __restrict__ srow, i
   }
 
   // ---- 3. exact rescore; 4. the best `need` band keys, ascending, in sel_pos ----
-  const double worst = rescore_band(rr, srow, nb, L, false);
+  const double worst = rescore_band(rr, srow, nb, L, false, reinterpret_cast<float*>(L.sel_pos),
+                                    reinterpret_cast<float*>(L.in_pos));
   choose_band<true>(nb, need, L);
 
   // ---- 5. merge with the kept keys of the current (ascending) selection; k <= RF_MAXK, so
@@ -1606,6 +1614,424 @@ __global__ __launch_bounds__(256) void topk_scale_max_kernel(const float* __rest
     kmax[static_cast<int64_t>(b) * nsc + c] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
+
+
+// The need-th largest of the order keys key[0..PER) of every thread (entries with live false
+// excluded), by the whole block: the 16-bit class (key >> 16) counted below the largest class
+// (2048 bins, the last one gathering every class 2047 or more below; keys drawn from the top of
+// a distribution span few classes, and bins relative to the maximum keep them apart), then
+// bits 15..8 and 7..0 inside the chosen class. Adds of lanes sharing a bin are merged
+// (hist_add). hist: 2048 words; tmp: 2 * TK_WAVES words; sel: 2 words; mx: 1 word. The count
+// of live keys must be at least need.
+template <int PER>
+__device__ __forceinline__ uint32_t block_kth_largest(const uint32_t (&key)[PER], const bool (&live)[PER],
+                                                      uint32_t need, uint32_t* hist, uint32_t* tmp,
+                                                      uint32_t* sel, uint32_t* mx) {
+  const int tid = threadIdx.x;
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    if (live[j]) m = max(m, key[j] >> 16);
+  m = wave_max(m);
+  if (tid == 0) *mx = 0;
+  for (int i = tid; i < 2048; i += TK_THREADS) hist[i] = 0;
+  __syncthreads();
+  if (tid % 64 == 0) atomicMax(mx, m);
+  __syncthreads();
+  const uint32_t top = *mx;
+  // round 1: classes below the top, bin 2047 - d (the histogram ascends in key order)
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const uint32_t d = top - (key[j] >> 16);
+    hist_add(hist, live[j], 2047u - (d < 2047u ? d : 2047u));
+  }
+  __syncthreads();
+  select_bin(hist, 2048, need, tmp, sel);
+  const uint32_t d1 = 2047u - sel[0];
+  need -= sel[1];
+  __syncthreads();
+  // a class 2047 or more below the top gathers several classes in its bin: fall back to
+  // the plain 16-bit class digit there (rare: a row spanning that many classes)
+  const bool gathered = d1 == 2047u;
+  uint32_t c16 = top - d1;
+  if (gathered) {
+    for (int i = tid; i < 2048; i += TK_THREADS) hist[i] = 0;
+    __syncthreads();
+    // the classes at or below top - 2047, by their top 11 bits relative to class 0
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const uint32_t c = key[j] >> 16;
+      hist_add(hist, live[j] && top - c >= 2047u, c >> 5);
+    }
+    __syncthreads();
+    select_bin(hist, 2048, need, tmp, sel);
+    const uint32_t hi11 = sel[0];
+    need -= sel[1];
+    __syncthreads();
+    for (int i = tid; i < 32; i += TK_THREADS) hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const uint32_t c = key[j] >> 16;
+      hist_add(hist, live[j] && top - c >= 2047u && (c >> 5) == hi11, c & 31u);
+    }
+    __syncthreads();
+    select_bin(hist, 32, need, tmp, sel);
+    c16 = (hi11 << 5) | sel[0];
+    need -= sel[1];
+    __syncthreads();
+  }
+  // rounds 2 and 3: bits 15..8, then 7..0, of the keys in class c16
+  uint32_t prefix = c16;
+#pragma unroll
+  for (int round = 0; round < 2; ++round) {
+    const int sh = round == 0 ? 8 : 0;
+    for (int i = tid; i < 256; i += TK_THREADS) hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      hist_add(hist, live[j] && (key[j] >> (sh + 8)) == prefix, (key[j] >> sh) & 255u);
+    __syncthreads();
+    select_bin(hist, 256, need, tmp, sel);
+    prefix = (prefix << 8) | sel[0];
+    need -= sel[1];
+    __syncthreads();
+  }
+  return prefix;
+}
+
+// ---------------------------------------------------------------------------------------
+// Fused scoring and selection (dsa_index_topk). dsa_index_score's kernel first scores S
+// evenly spaced keys per request; sample_tau_kernel turns each row's sample into a threshold
+// tau expected to leave about 2.5 k keys above it; the scoring kernel then keeps only
+// the scores >= tau, and fused_select_kernel selects from those candidates with the
+// exact-boundary refine. A row whose candidates cannot be trusted to hold its top-k and
+// band (fewer than k, more than CCAP, or theta - 2 eps below tau) is scored again by its own
+// block and selected by the standard path, so every row's set is exact.
+constexpr int CCAP = 8192;      // candidates a row's block selects from in LDS
+constexpr int MAX_SEGS = 1024;  // key ranges one row's candidates may come from
+
+// 1 block per row: tau[t] = the sample's m-th largest score, m = ceil(2.5 k S / n0) (n0 the
+// sampled span), or -inf when that leaves no sample out (the row keeps every key).
+__global__ __launch_bounds__(TK_THREADS) void sample_tau_kernel(
+    const float* __restrict__ samples, int S, const int32_t* __restrict__ q_off,
+    const int64_t* __restrict__ kv_off, int k, float* __restrict__ tau) {
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t tmp[2 * TK_WAVES];
+  __shared__ uint32_t sel[2];
+  const int b = blockIdx.y, r = blockIdx.x;
+  const RowInfo ri = load_row_info(q_off, kv_off, b);
+  if (r >= ri.R) return;
+  const int64_t t = ri.t0 + r;
+  const int tid = threadIdx.x;
+  int64_t n0 = ri.L - ri.R + 1;
+  n0 = n0 < 1 ? 1 : (n0 > ri.L ? ri.L : n0);
+  const int64_t m = (5 * static_cast<int64_t>(k) * S + 2 * n0 - 1) / (2 * n0);
+  if (ri.L <= 0 || m >= S) {
+    if (tid == 0) tau[t] = -__builtin_inff();
+    return;
+  }
+  constexpr int PER = 8;  // S <= 8192
+  uint32_t key[PER];
+  bool live[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = tid + TK_THREADS * j;
+    live[j] = i < S;
+    key[j] = live[j] ? order_key(samples[t * S + i]) : 0u;
+  }
+  __shared__ uint32_t mx;
+  const uint32_t prefix = block_kth_largest<PER>(key, live, static_cast<uint32_t>(m), hist, tmp, sel, &mx);
+  if (tid == 0) tau[t] = __uint_as_float((prefix & 0x80000000u) ? (prefix & 0x7FFFFFFFu) : ~prefix);
+}
+
+// Scores of the row of rr (its n visible keys) into frow by the whole block, with the FP8
+// MFMA and float32 epilogue of dsa_index_score (one 16-key sub-tile per wave at a time, the
+// query operand reloaded per head tile); the largest visible key scale goes to *smax.
+__device__ __forceinline__ void score_row_block(const RowRef& rr, int64_t n, float* __restrict__ frow,
+                                                float* smax, double* red) {
+  const Refine& rf = rr.rf;
+  const int tid = threadIdx.x, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int g = lane / 16, c16 = lane % 16;
+  const int H = rf.H, D = rf.D;
+  const int nht = (H + 15) / 16;
+  const int64_t t = rr.t;
+  const uint8_t* __restrict__ kreq = rf.k_fp8 + rr.kv_base * D;
+  const float* __restrict__ ksc = rf.k_scale + rr.kv_base;
+  float sm = 0.0f;
+  for (int64_t s0 = 16 * wave; s0 < n; s0 += 16 * TK_WAVES) {
+    const int64_t key = s0 + c16;
+    const bool valid = key < n;
+    i32x8 bfrag = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (valid && 32 * g < D) {
+      const i32x4* p = reinterpret_cast<const i32x4*>(kreq + key * D + 32 * g);
+      const i32x4 lo = p[0], hi = p[1];
+      bfrag = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    float part = 0.0f;
+    for (int ht = 0; ht < nht; ++ht) {  // wave-uniform
+      const int head = 16 * ht + c16;
+      i32x8 qa = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (head < H && 32 * g < D) {
+        const i32x4* p = reinterpret_cast<const i32x4*>(rf.q_fp8 + (t * H + head) * D + 32 * g);
+        const i32x4 lo = p[0], hi = p[1];
+        qa = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      const f32x4 acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa, bfrag, zero, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h2 = 16 * ht + 4 * g + i;
+        const float u = h2 < H ? rf.w[t * H + h2] * rf.q_scale[t * H + h2] : 0.0f;
+        part = fmaf(u, __builtin_amdgcn_fmed3f(acc[i], 0.0f, 3.402823466e38f), part);
+      }
+    }
+    part += __shfl_xor(part, 16);
+    part += __shfl_xor(part, 32);
+    if (g == 0 && valid) {
+      const float sc = ksc[key];
+      frow[key] = part * sc;
+      sm = fmaxf(sm, sc);
+    }
+  }
+  const double mx = block_max_d(static_cast<double>(sm), red);
+  *smax = static_cast<float>(mx);
+}
+
+struct FusedSel {  // kernel argument of fused_select_kernel
+  uint2* cand;          // [T, ldc] candidates from the scoring kernel (then a fallback row)
+  int64_t ldc;
+  const int32_t* cnt;   // [T, gx, 2]
+  const float* msc;     // [T, gx, 2]
+  const float* tau;     // [T]
+  int32_t* path;        // [T] or nullptr: 0 selected from the candidates, 1 row rescored
+  int gx;
+};
+
+// Ascending emission of the kept positions (kept_pos, any order) and the chosen band
+// positions (sel_pos, ascending) of a row of n positions, in windows of FAST_MAX positions
+// through the position bitmap.
+__device__ __forceinline__ void emit_selected(int64_t n, int k, int32_t* __restrict__ out,
+                                              const int32_t* kept_pos, int nkept,
+                                              const int32_t* sel_pos, int nsel, RefineLds& L,
+                                              uint32_t* tmp) {
+  const int tid = threadIdx.x;
+  uint32_t done = 0;
+  for (int64_t w0 = 0; w0 < n; w0 += FAST_MAX) {  // block-uniform
+    for (int i = tid; i < FAST_MAX / 32; i += TK_THREADS) L.bitmap[i] = 0u;
+    __syncthreads();
+    auto mark = [&](int32_t p) {
+      if (p >= w0 && p < w0 + FAST_MAX) {
+        const int q = static_cast<int>(p - w0);
+        atomicOr(&L.bitmap[q >> 5], 1u << (q & 31));
+      }
+    };
+    for (int i = tid; i < nkept; i += TK_THREADS) mark(kept_pos[i]);
+    for (int i = tid; i < nsel; i += TK_THREADS) mark(sel_pos[i]);
+    __syncthreads();
+    const uint32_t wd0 = L.bitmap[2 * tid], wd1 = L.bitmap[2 * tid + 1];
+    uint32_t total;
+    uint32_t o = done + block_excl_scan(static_cast<uint32_t>(__popc(wd0) + __popc(wd1)), tmp, &total);
+    auto emit = [&](uint32_t wd, int64_t pos0) {
+      while (wd) {
+        const int j = __builtin_ctz(wd);
+        wd &= wd - 1;
+        if (o < static_cast<uint32_t>(k)) out[o] = static_cast<int32_t>(pos0 + j);
+        ++o;
+      }
+    };
+    emit(wd0, w0 + 64 * tid);
+    emit(wd1, w0 + 64 * tid + 32);
+    done += total;
+  }
+  for (uint32_t i = done + tid; i < static_cast<uint32_t>(k); i += TK_THREADS) out[i] = -1;
+}
+
+__global__ __launch_bounds__(TK_THREADS) void fused_select_kernel(
+    FusedSel fs, Refine rf, const int32_t* __restrict__ q_off, const int64_t* __restrict__ kv_off,
+    int B, int k, int32_t* __restrict__ topk) {
+  __shared__ __attribute__((aligned(16))) TopkLds S;
+  const int b = blockIdx.y, r = blockIdx.x;
+  const RowInfo ri = load_row_info(q_off, kv_off, b);
+  if (r >= ri.R) return;
+  const int64_t t = ri.t0 + r;
+  int64_t n = visible_count(ri, r);
+  if (n > fs.ldc) n = fs.ldc;  // device lengths beyond the host bound are clipped
+  const int tid = threadIdx.x, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  int32_t* out = topk + t * k;
+  RowRef rr = row_ref(rf, t, b, ri.kv_base);
+  if (n <= k) {  // every visible key is selected
+    for (int i = tid; i < k; i += TK_THREADS) out[i] = i < n ? i : -1;
+    if (tid == 0) {
+      if (rf.status) rf.status[t] = 0;
+      if (fs.path) fs.path[t] = 0;
+    }
+    return;
+  }
+  RefineLds& L = *reinterpret_cast<RefineLds*>(S.regA);
+  // candidate keys and positions overlay band_val / terms, which the rescoring uses only
+  // after the candidates have been classified
+  uint32_t* ckey = reinterpret_cast<uint32_t*>(L.band_val);
+  int32_t* cpos = reinterpret_cast<int32_t*>(L.terms);
+  static_assert(sizeof(L.band_val) >= CCAP * 4 && sizeof(L.terms) >= CCAP * 4, "candidate arrays");
+  int* seg_k0 = S.fpos;  // per key range of the row: first key, end, the two counts, offset
+  int* seg_ke = S.fpos + MAX_SEGS;
+  int* seg_c0 = S.fpos + 2 * MAX_SEGS;
+  int* seg_c1 = S.fpos + 3 * MAX_SEGS;
+  int* seg_of = S.fpos + 4 * MAX_SEGS;
+  static_assert(5 * MAX_SEGS <= FCAND, "segment table");
+  bool fallback = false;
+  float eps_f = 0.0f;
+  // ---- 1. the row's key ranges in the scoring grid, their counts and key-scale maxima ----
+  const int64_t base = kv_off[0], end = kv_off[B];
+  int64_t share = (end - base + fs.gx - 1) / fs.gx;
+  share = (share + 63) / 64 * 64;
+  const int64_t x0 = (ri.kv_base - base) / share;
+  const int64_t x1 = (ri.kv_base + ri.L - 1 - base) / share;
+  const int nseg = static_cast<int>(x1 - x0 + 1);
+  if (nseg > MAX_SEGS || nseg < 1) fallback = true;  // uniform
+  uint32_t C = 0;
+  float sm = 0.0f;
+  if (!fallback) {
+    uint32_t c = 0;
+    int sk0 = 0, ske = 0, sc0 = 0, sc1 = 0;
+    if (tid < nseg) {
+      const int64_t x = x0 + tid;
+      const int64_t g0 = base + x * share, g1 = g0 + share < end ? g0 + share : end;
+      const int64_t k0 = (g0 > ri.kv_base ? g0 : ri.kv_base) - ri.kv_base;
+      int64_t ke = (g1 < ri.kv_base + ri.L ? g1 : ri.kv_base + ri.L) - ri.kv_base;
+      if (ke > fs.ldc) ke = fs.ldc;
+      if (ke > k0) {
+        const int64_t m = (t * fs.gx + x) * 2;
+        sk0 = static_cast<int>(k0);
+        ske = static_cast<int>(ke);
+        sc0 = fs.cnt[m];
+        sc1 = fs.cnt[m + 1];
+        sm = fmaxf(fs.msc[m], fs.msc[m + 1]);
+        c = static_cast<uint32_t>(sc0 + sc1);
+      }
+    }
+    const uint32_t off = block_excl_scan(c, S.tmp, &C);
+    if (tid < nseg) {
+      seg_k0[tid] = sk0;
+      seg_ke[tid] = ske;
+      seg_c0[tid] = sc0;
+      seg_c1[tid] = sc1;
+      seg_of[tid] = static_cast<int>(off);
+    }
+    if (C > static_cast<uint32_t>(CCAP) || C < static_cast<uint32_t>(k)) fallback = true;
+  }
+  const float smax = static_cast<float>(block_max_d(static_cast<double>(sm), L.redd));
+  uint32_t theta = 0;
+  if (!fallback) {
+    // ---- 2. candidates into LDS: wave w copies the ranges w, w + 16, .. ----
+    for (int sgi = wave; sgi < nseg; sgi += TK_WAVES) {
+      const uint2* crow = fs.cand + t * fs.ldc;
+      const int c0 = seg_c0[sgi], c1 = seg_c1[sgi], o = seg_of[sgi];
+      const int k0 = seg_k0[sgi], ke = seg_ke[sgi];
+      for (int i = lane; i < c0 + c1; i += 64) {
+        const uint2 e = i < c0 ? crow[k0 + i] : crow[ke - 1 - (i - c0)];
+        ckey[o + i] = order_key(__uint_as_float(e.x));
+        cpos[o + i] = static_cast<int32_t>(e.y);
+      }
+    }
+    // ---- 3. theta: the k-th largest candidate key ----
+    __syncthreads();  // the candidates are in LDS
+    constexpr int PERC = CCAP / TK_THREADS;
+    uint32_t key[PERC];
+    bool live[PERC];
+#pragma unroll
+    for (int j = 0; j < PERC; ++j) {
+      const uint32_t i = tid + TK_THREADS * j;
+      live[j] = i < C;
+      key[j] = live[j] ? ckey[i] : 0u;
+    }
+    theta = block_kth_largest<PERC>(key, live, static_cast<uint32_t>(k), S.fhist, S.tmp, S.sel,
+                                    &S.smax);
+  }
+  // ---- 4. eps, and whether every key of the band is among the candidates ----
+  double eps = 0.0;
+  float lo_f = 0.0f, hi_f = 0.0f;
+  if (!fallback) {
+    const float th = __uint_as_float((theta & 0x80000000u) ? (theta & 0x7FFFFFFFu) : ~theta);
+    rr.rf.kmax = nullptr;
+    rr.rf.smax_given = smax;
+    refine_prefetch(rr, n, S.rf_a, S.rf_s);
+    if (tid < 4) L.counters[tid] = 0;
+    __syncthreads();
+    eps = refine_eps(rr.rf, th, S.rf_a, S.rf_s);
+    if (!__builtin_isfinite(th) || !__builtin_isfinite(eps)) {
+      fallback = true;
+    } else {
+      band_edges(th, eps, &lo_f, &hi_f);
+      if (lo_f < fs.tau[t]) fallback = true;  // keys in the band may have been left out
+    }
+    eps_f = static_cast<float>(eps);
+  }
+  int nb = 0, nkept = 0;
+  if (!fallback) {
+    // ---- 5. kept keys (above the band) and the band ----
+    const uint32_t lo_k = order_key(lo_f), hi_k = order_key(hi_f);
+    for (uint32_t i0 = 0; i0 < C; i0 += TK_THREADS) {  // block-uniform trips
+      const uint32_t i = i0 + tid;
+      const bool live = i < C;
+      const uint32_t key = live ? ckey[i] : 0u;
+      const bool kp = live && key > hi_k;
+      const bool bd = live && !kp && key >= lo_k;
+      const uint64_t bkp = __builtin_amdgcn_ballot_w64(kp), bbd = __builtin_amdgcn_ballot_w64(bd);
+      int basek = 0, baseb = 0;
+      if (lane == 0) {
+        if (bkp) basek = atomicAdd(&L.counters[1], static_cast<int>(__popcll(bkp)));
+        if (bbd) baseb = atomicAdd(&L.counters[0], static_cast<int>(__popcll(bbd)));
+      }
+      basek = __builtin_amdgcn_readfirstlane(basek);
+      baseb = __builtin_amdgcn_readfirstlane(baseb);
+      if (kp) {
+        const int slot = basek + static_cast<int>(lanes_below(bkp));
+        if (slot < RF_MAXK) L.in_pos[slot] = cpos[i];
+      }
+      if (bd) {
+        const int slot = baseb + static_cast<int>(lanes_below(bbd));
+        if (slot < BAND_CAP) {
+          L.band_pos[slot] = cpos[i];
+          reinterpret_cast<float*>(S.fpos)[slot] = __uint_as_float(
+              (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);  // its float32 score
+        }
+      }
+    }
+    __syncthreads();
+    nb = L.counters[0];
+    nkept = L.counters[1];
+    const int need = k - nkept;
+    if (nb > BAND_CAP || need < 1 || need > nb) fallback = true;  // uniform
+  }
+  if (!fallback) {
+    // ---- 6. exact rescore of the band, its best keys, and the ascending emission ----
+    const int need = k - nkept;
+    const double worst = rescore_band(rr, nullptr, nb, L, false, reinterpret_cast<float*>(L.sel_pos),
+                                      reinterpret_cast<float*>(S.fpos));
+    choose_band<true>(nb, need, L);
+    emit_selected(n, k, out, L.in_pos, nkept, L.sel_pos, need, L, S.tmp);
+    if (tid == 0) {
+      if (rf.status) rf.status[t] = refine_status(nb, worst, eps);
+      if (fs.path) fs.path[t] = 0;
+    }
+    return;
+  }
+  // ---- fallback: score the whole row here, then the standard selection and refine ----
+  __syncthreads();
+  float* frow = reinterpret_cast<float*>(fs.cand + t * fs.ldc);  // this row's own slice
+  float fsmax;
+  score_row_block(rr, n, frow, &fsmax, L.redd);
+  __syncthreads();  // the block's score stores are visible to its own loads after this
+  rr.rf.kmax = nullptr;
+  rr.rf.smax_given = fsmax;
+  select_row(frow, n, k, out, S, rr, true);
+  if (tid == 0 && fs.path) fs.path[t] = 1;
+  (void)eps_f;
+}
 }  // namespace
 }  // namespace dsa
 
@@ -1707,3 +2133,46 @@ extern "C" dsa_status dsa_topk(const float* scores, int64_t score_ld,
   }
   return check_launch("dsa_topk");
 }
+
+namespace dsa {
+
+int fused_sample_count(int64_t max_kv_len) {
+  int64_t S = 1024;
+  while (S < 8192 && S * 32 < max_kv_len) S *= 2;
+  return static_cast<int>(S);
+}
+
+void launch_sample_tau(const float* samples, int S, const int32_t* q_off, const int64_t* kv_off,
+                       int B, int max_q_rows, int k, float* tau, hipStream_t st) {
+  hipLaunchKernelGGL(sample_tau_kernel, dim3((unsigned)max_q_rows, (unsigned)B), dim3(TK_THREADS), 0,
+                     st, samples, S, q_off, kv_off, k, tau);
+}
+
+void launch_fused_select(const FusedSelectLaunch& a, const int32_t* q_off, const int64_t* kv_off,
+                         int B, int max_q_rows, int k, int32_t* topk, hipStream_t st) {
+  FusedSel fs;
+  fs.cand = static_cast<uint2*>(a.cand);
+  fs.ldc = a.ldc;
+  fs.cnt = a.cnt;
+  fs.msc = a.msc;
+  fs.tau = a.tau;
+  fs.path = a.path;
+  fs.gx = a.gx;
+  Refine rf{};
+  rf.q_fp8 = a.q_fp8;
+  rf.q_scale = a.q_scale;
+  rf.w = a.w;
+  rf.k_fp8 = a.k_fp8;
+  rf.k_scale = a.k_scale;
+  rf.kmax = nullptr;
+  rf.status = a.status;
+  rf.C = a.err_scale;
+  rf.H = a.H;
+  rf.D = a.D;
+  rf.nsc = 0;
+  rf.smax_given = 0.0f;
+  hipLaunchKernelGGL(fused_select_kernel, dim3((unsigned)max_q_rows, (unsigned)B), dim3(TK_THREADS), 0,
+                     st, fs, rf, q_off, kv_off, B, k, topk);
+}
+
+}  // namespace dsa

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 4
+#define DSA_ABI_VERSION 5
 
 typedef enum {
   DSA_OK = 0,
@@ -230,6 +230,43 @@ dsa_status dsa_topk(const float* scores, int64_t score_ld, const int32_t* q_row_
 
 size_t dsa_topk_workspace_size(int32_t B, int32_t T, int64_t max_kv_len, int32_t k,
                                int32_t refine);
+
+/*
+ * dsa_index_topk -- the indexer scores and the refined top-k of every row in one call, with
+ * no score row written to memory.
+ * ("MAX Pipeline 中的 DeepSeek-V3.2 架构实现解析", "Indexer 的结构与计算流程": the indexer's
+ * output is the top-k of shape (total_seq_len, index_topk), produced there by one fused
+ * index-and-top-k operator.)
+ *
+ * Result: what dsa_index_score followed by dsa_topk with a refine gives (err_scale, status
+ * as in dsa_topk_refine): each row's set by the exact scores, ascending, -1 padded; the
+ * float32 scores are those of dsa_index_score's arithmetic. Steps:
+ *   1. S evenly spaced keys of each request (S = 1024..8192, about one key in 32 of the
+ *      longest request; positions floor(j n0 / S), n0 the first row's visible count) are
+ *      scored;
+ *   2. each row's threshold tau is the sample's m-th largest score, m = ceil(2.5 k S / n0)
+ *      (-inf when m >= S: the row keeps every key);
+ *   3. the scoring pass keeps only scores >= tau, with the largest key scale it saw;
+ *   4. one block per row selects the k-th largest candidate theta and refines the band
+ *      [theta - 2 eps, theta + 2 eps] exactly. A row with fewer than k or more than 8192
+ *      candidates, or with theta - 2 eps < tau (band keys may lie below tau), is scored
+ *      again in full by its own block and selected by the path of dsa_topk.
+ *   path  [T] int32, nullable: 0 when the row was selected from its candidates, 1 when it
+ *         was scored again (the result is the same either way).
+ * Inputs as in dsa_index_score; k in [1, 4096].
+ * Workspace: dsa_index_topk_workspace_size(B, T, max_q_rows, H_I, max_kv_len) bytes,
+ * 256-byte aligned (at 32 x 65536 with 6 rows: about 105 MB).
+ * Errors: DSA_ERR_INVALID_ARGUMENT, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE_TOO_SMALL.
+ */
+dsa_status dsa_index_topk(const uint8_t* q_fp8, const float* q_scale, const float* w,
+                          const uint8_t* k_fp8, const float* k_scale,
+                          const int32_t* q_row_offsets, const int64_t* kv_row_offsets, int32_t B,
+                          int32_t T, int32_t max_q_rows, int32_t H_I, int32_t D_I,
+                          int64_t max_kv_len, int32_t k, double err_scale, int32_t* status,
+                          int32_t* path, int32_t* topk, void* ws, size_t ws_bytes, void* stream);
+
+size_t dsa_index_topk_workspace_size(int32_t B, int32_t T, int32_t max_q_rows, int32_t H_I,
+                                     int64_t max_kv_len);
 
 /*
  * dsa_sparse_mla_decode -- attention of every query row over only its

@@ -72,6 +72,12 @@ class Full:
         self.top_ref = api.topk(self.scores, self.qo_d, self.ko_d, w.rows, self.max_kv, w.topk,
                                 refine=dict(q_fp8=self.qc, q_scale=self.qs, w=self.w,
                                             k_fp8=self.kc, k_scale=self.ks, status=self.rstatus))
+        # the fused path (no score rows), on the same inputs
+        self.fstatus = torch.zeros(self.T, dtype=torch.int32, device=DEV)
+        self.fpath = torch.zeros(self.T, dtype=torch.int32, device=DEV)
+        self.top_fused = api.index_topk(self.qc, self.qs, self.w, self.kc, self.ks, self.qo_d,
+                                        self.ko_d, w.rows, self.max_kv, w.topk,
+                                        status=self.fstatus, path=self.fpath)
         torch.cuda.synchronize()
 
     def visible(self, t: int) -> int:
@@ -192,6 +198,21 @@ def test_full_end_to_end_topk_sampled_rows(f):
         assert np.array_equal(f.top_ref[t].cpu().numpy(), ref_k[0]), f"row {t}: refined set"
         _say(f"  row {t}: float32 set {'equal' if nd == 0 else 'band-only differences'}, "
              f"refined set equal (error/eps {ratio:.3f}, band {st[t]})")
+
+
+def test_full_fused_topk_every_row(f):
+    # the fused score + top-k and the refined top-k of the written scores both give the exact
+    # sets: they must agree on every row (three rows are checked against the oracle above)
+    W = f.wl
+    st, path = f.fstatus.cpu().numpy(), f.fpath.cpu().numpy()
+    _say(f"full fused top-k: all {f.T} rows; status min {st.min()}, band max {st.max()}, "
+         f"rows rescored {int((path == 1).sum())}")
+    assert st.min() >= 0
+    assert np.array_equal(f.top_fused.cpu().numpy(), f.top_ref.cpu().numpy())
+    if f.spike_pos is not None:
+        top = f.top_fused.cpu().numpy()
+        for t in range(f.T):
+            assert np.array_equal(top[t], f.spike_pos[f.request(t)][:W.topk].numpy()), f"row {t}"
 
 
 def test_full_sparse_mla_sampled_rows(f):
