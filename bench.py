@@ -54,6 +54,10 @@ def parse():
                          "rows); separate: dsa_index_score, then dsa_topk with the refine")
     ap.add_argument("--err-scale", type=float, default=0.0,
                     help="C of the refine's error bound (0: the library default, 4)")
+    ap.add_argument("--no-share", action="store_true",
+                    help="draft steps select their own top-k (quantise q, index score over the "
+                         "whole context, refined top-k) instead of reusing the step-0 top-k; "
+                         "only for workloads with draft steps")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration) and exit")
     return ap.parse_args()
@@ -78,6 +82,7 @@ class Inputs:
     """One resident copy of the step's inputs (device tensors)."""
 
     rejection = False  # also draw rejection-sampling inputs (bench --accept rejection)
+    no_share = False   # also draw the draft rows' indexer queries (bench --no-share)
 
     def __init__(self, w, lengths, copy: int):
         import torch
@@ -103,6 +108,10 @@ class Inputs:
             self.q_draft = [synth.mla_inputs(w, lengths, device=dev, rows=1,
                                              seed_offset=100 * (copy + 1) + j, kv=self.kv)["q"]
                             for j in range(w.share_steps)]
+        self.ix_draft = None
+        if w.share_steps and Inputs.no_share:  # each draft row's own indexer query and weights
+            self.ix_draft = [synth.indexer_queries(w, 1, seed_offset=100 * (copy + 1) + j, device=dev)
+                             for j in range(w.share_steps)]
         self.rej = synth.rejection_inputs(w, device=dev, seed_offset=copy) if Inputs.rejection else None
         a = synth.accept_inputs(w, device=dev) if copy == 0 else None
         if a is None:
@@ -115,8 +124,11 @@ class Inputs:
 
 
 def source_sha(name: str) -> str:
-    p = os.path.join(ROOT, "dsa_sparse_attention_amd", "csrc", name)
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    """Hash of a call's source file(s): one name, or several joined by '+'."""
+    h = hashlib.sha256()
+    for n in name.split("+"):
+        h.update(open(os.path.join(ROOT, "dsa_sparse_attention_amd", "csrc", n), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_for(kernel_file: str, launches_key: str):
@@ -237,6 +249,11 @@ def main():
     print(f"[bench] workload {w.name}: B={w.batch} ctx={max_kv} rows={w.rows} T={T}", file=sys.stderr,
           flush=True)
     Inputs.rejection = args.accept == "rejection"
+    if args.no_share and not w.share_steps:
+        sys.exit(f"bench.py: --no-share needs a workload with draft steps ({w.name} has none)")
+    if args.no_share and (args.no_refine or args.topk_path == "fused"):
+        sys.exit("bench.py: --no-share runs the separate path with the refine")
+    Inputs.no_share = args.no_share
     copies = [Inputs(w, lengths, c) for c in range(args.copies)]
     qo = synth.q_row_offsets(w).to(dev)
     ko = synth.kv_row_offsets(lengths).to(dev)
@@ -273,13 +290,21 @@ def main():
     names = (["cache_write", "index_topk", "sparse_mla", acc_name] if args.topk_path == "fused" else
              ["cache_write", "index_score", "topk", "sparse_mla", acc_name])
     if w.share_steps:
-        names.append("share_mla")
+        names.append("draft_steps" if args.no_share else "share_mla")
         qo1 = torch.arange(w.batch + 1, dtype=torch.int32, device=dev)
         n_acc = synth.accepted_lengths(w).to(dev)
         out1 = torch.empty((w.batch, w.mla_heads, 512), dtype=torch.bfloat16, device=dev)
         lse1 = torch.empty((w.batch, w.mla_heads), dtype=torch.float32, device=dev)
         ws1_need = api.sparse_mla_workspace_size(w.batch, w.mla_heads, w.topk)
         ws1 = torch.empty(max(ws1_need, 16), dtype=torch.uint8, device=dev)
+        if args.no_share:  # one draft row per request, visible to the whole cached context
+            qc1 = torch.empty((w.batch, w.index_heads, w.index_dim), dtype=torch.uint8, device=dev)
+            qs1 = torch.empty((w.batch, w.index_heads), dtype=torch.float32, device=dev)
+            scores1 = torch.empty((w.batch, ld), dtype=torch.float32, device=dev)
+            top1 = torch.empty((w.batch, w.topk), dtype=torch.int32, device=dev)
+            status1 = torch.zeros(w.batch, dtype=torch.int32, device=dev)
+            tk1 = api.topk_workspace_size(w.batch, w.batch, max_kv, w.topk, True)
+            ws_tk1 = torch.empty(max(tk1, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def step(inp, ev=None):
@@ -311,9 +336,20 @@ def main():
             api.rejection_accept(r["logits"], r["draft_probs"], r["draft"], r["u"], r["us"],
                                  w.drafts, workspace=ws_ra)
         mark()
-        for qd in inp.q_draft or []:  # draft steps: the step-0 top-k row at the accepted position
-            api.sparse_mla_decode(qd, inp.kv, topk, qo1, ko, 1, w.sm_scale, out=out1, lse=lse1,
-                                  workspace=ws1, share_base=qo, num_accepted=n_acc)
+        for j, qd in enumerate(inp.q_draft or []):
+            if inp.ix_draft is None:  # index share: the step-0 top-k row at the accepted position
+                api.sparse_mla_decode(qd, inp.kv, topk, qo1, ko, 1, w.sm_scale, out=out1, lse=lse1,
+                                      workspace=ws1, share_base=qo, num_accepted=n_acc)
+                continue
+            ixd = inp.ix_draft[j]  # no share: the draft row runs the indexer over the whole cache
+            api.quantize_fp8(ixd["q"], out=qc1, scale=qs1)
+            api.index_score(qc1, qs1, ixd["w"], inp.k_fp8, inp.k_scale, qo1, ko, 1, max_kv,
+                            scores=scores1)
+            api.topk(scores1, qo1, ko, 1, max_kv, w.topk, out=top1, workspace=ws_tk1,
+                     refine=dict(q_fp8=qc1, q_scale=qs1, w=ixd["w"], k_fp8=inp.k_fp8,
+                                 k_scale=inp.k_scale, status=status1, err_scale=args.err_scale))
+            api.sparse_mla_decode(qd, inp.kv, top1, qo1, ko, 1, w.sm_scale, out=out1, lse=lse1,
+                                  workspace=ws1)
         if inp.q_draft:
             mark()
 
@@ -354,7 +390,7 @@ def main():
     if refine:
         # every row of the last step must be refined (status >= 0): its top-k set is then
         # the oracle's, provided the float32 errors stay within the bound (see dsa.h)
-        st = status.cpu()
+        st = status.cpu() if not args.no_share else torch.cat([status.cpu(), status1.cpu()])
         assert int(st.min()) >= 0, f"refine left rows unresolved: statuses {sorted(set(st.tolist()))}"
         refine_rec = {"status_min": int(st.min()), "band_max": int(st.max()),
                       "band_mean": round(float(st.float().mean()), 2),
@@ -380,15 +416,21 @@ def main():
     if fused:
         wf = accounting.index_topk_work(lengths, w.rows, w.index_heads, w.index_dim, w.topk)
         kern["index_topk"] = dict(bytes=wf["bytes"], flops=wf["flops"], bound="mfma",
-                                  file="index_score.hip")
+                                  file="index_score.hip+topk.hip")
     else:
         kern["index_score"] = dict(bytes=wi["bytes"], flops=wi["flops"], bound="mfma",
                                    file="index_score.hip")
         kern["topk"] = dict(bytes=wt["bytes"], bound="hbm", file="topk.hip")
-    if w.share_steps:
+    if w.share_steps and not args.no_share:
         ws_ = accounting.sparse_mla_work(w.batch, w.mla_heads, w.topk)
         kern["share_mla"] = dict(bytes=w.share_steps * ws_["bytes"],
                                  flops=w.share_steps * ws_["flops"], bound="hbm")
+    elif w.share_steps:  # several kernels per draft step: reported, never the roofline kernel
+        ws_ = accounting.sparse_mla_work(w.batch, w.mla_heads, w.topk)
+        wi1 = accounting.index_score_work(lengths, 1, w.index_heads, w.index_dim)
+        wt1 = accounting.topk_work(lengths, 1, w.topk)
+        kern["draft_steps"] = dict(bytes=w.share_steps * (ws_["bytes"] + wi1["bytes"] + wt1["bytes"]),
+                                   bound="hbm", composite=True)
     kernels = {}
     for n, kd in kern.items():
         t_s = per[n] * 1e-3
@@ -399,7 +441,7 @@ def main():
             e["TFLOP/s"] = round(kd["flops"] / t_s / 1e12, 1)
             e["mfma_frac"] = round(kd["flops"] / t_s / 1e12 / peak, 4)
         kernels[n] = e
-    dom = max(per, key=per.get)
+    dom = max((n for n in per if not kern[n].get("composite")), key=per.get)
     kd = kern[dom]
     t_dom = per[dom] * 1e-3
     if kd["bound"] == "mfma":
@@ -425,7 +467,7 @@ def main():
                    "index_heads": w.index_heads, "index_dim": w.index_dim, "topk": w.topk,
                    "mla_heads": w.mla_heads, "vocab": w.vocab, "global_batch": rows_step,
                    "seq_len": max_kv, "share_steps": w.share_steps, "topk_refine": refine,
-                   "topk_path": args.topk_path,
+                   "topk_path": args.topk_path, "index_share": (not args.no_share) if w.share_steps else None,
                    "accept": args.accept,
                    "parallelism": "single-gpu"},
         "step_includes": names,

@@ -273,8 +273,10 @@ __device__ __forceinline__ void compute_segment(
     a_hi = ring[it % NBUF] + off_hi;
   };
   auto mfma_sub = [&](int sb, f32x4 (&acc)[HT]) {
+    // (for D = 128 every lane group holds 32 of the key's dims: the load is unconditional,
+    // with no zero fill on the VALU)
     i32x8 bfrag = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (32 * g < D) {
+    if (D >= 128 || 32 * g < D) {
       const i32x4 lo = *reinterpret_cast<const i32x4*>(a_lo + sb * 16 * D);
       const i32x4 hi = *reinterpret_cast<const i32x4*>(a_hi + sb * 16 * D);
       bfrag = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -343,7 +345,7 @@ __device__ __forceinline__ void compute_segment(
       set_tile(it + 1);
       if (live_tile(it + 1)) mfma_sub(0, acc0);
     }
-    if (lv) {
+    if (live_tile(it)) {  // recomputed (scalar) rather than carried across the barrier
       const float sum = combine(p0, partial(acc1));
       const bool mine = (g == 1 || g == 2) && it * KT + kt < nstore;
       if constexpr (MODE == COMPACT) {
@@ -359,7 +361,9 @@ __device__ __forceinline__ void compute_segment(
         ccount += static_cast<int>(__popcll(bk));
         if (mine) cmax = fmaxf(cmax, sc);
       } else {
-        if (mine) srow[it * KT + kt] = sum * sc;
+        // the tile's row base is wave-uniform (scalar arithmetic); the lane adds its key kt
+        float* tile_row = srow + static_cast<int64_t>(__builtin_amdgcn_readfirstlane(it)) * KT;
+        if (mine) tile_row[kt] = sum * sc;
       }
     }
   }

@@ -89,6 +89,17 @@ def indexer_inputs(w: Workload, lengths, device="cpu", rows: int | None = None,
     return out
 
 
+def indexer_queries(w: Workload, rows: int, seed_offset: int = 0, device="cpu") -> dict:
+    """Float32 indexer queries q [B*rows,H_I,D_I] and head weights w [B*rows,H_I] alone, for
+    rows scored against an existing key cache (the draft rows of a step without index
+    sharing)."""
+    T = w.batch * rows
+    g = generator(w.seed * 1000 + 13 + seed_offset, device)
+    q = torch.randn((T, w.index_heads, w.index_dim), generator=g, device=device)
+    wt = torch.rand((T, w.index_heads), generator=g, device=device)
+    return dict(q=q, w=wt)
+
+
 def plant_spikes(w: Workload, lengths, q, k, wt, rows) -> list[torch.Tensor]:
     """Overwrite a fraction of each request's keys with one identical spike vector."""
     gcpu = generator(w.seed * 1000 + 23)
