@@ -59,6 +59,11 @@ def _load():
         lib.dsa_oracle_topk.restype = i32
         lib.dsa_oracle_sparse_mla_rows.argtypes = [P, P, P, i32, P, P, P, P, i32, i32, f32, P, i64, P, P]
         lib.dsa_oracle_sparse_mla_rows.restype = i32
+        lib.dsa_oracle_mla_fp8_pack.argtypes = [P, i64, P]
+        lib.dsa_oracle_mla_fp8_pack.restype = None
+        lib.dsa_oracle_sparse_mla_fp8_rows.argtypes = [P, P, P, i32, P, P, P, P, i32, i32, f32, P, i64,
+                                                      P, P]
+        lib.dsa_oracle_sparse_mla_fp8_rows.restype = i32
         lib.dsa_oracle_greedy_accept.argtypes = [P, i32, i64, P, i32, i32, i32, P, P, P]
         lib.dsa_oracle_greedy_accept.restype = i32
         lib.dsa_oracle_rejection_accept.argtypes = [P, i32, i64, P, P, P, P, i32, i32, i32, P, P,
@@ -201,6 +206,54 @@ def sparse_mla(q_bf16, kv_bf16, topk_idx, q_row_offsets, kv_row_offsets, sm_scal
                                         _p(rows), len(rows), _p(out), _p(lse))
     if rc != 0:
         raise ValueError("oracle sparse_mla: a row is outside every request")
+    return out, lse
+
+
+def mla_fp8_pack(latent_bf16) -> np.ndarray:
+    """Pack bf16 latent rows [n, 576] into FP8 cache rows [n, 656] ("GLM-5.3 推理全链路(十四)",
+    the draft layer's KV pool: 656 bytes per token per layer, fp8_ds_mla): 512 e4m3fn codes
+    in 4 blocks of 128 with a float32 scale each, then the 64 rope values in bf16."""
+    lib = _load()
+    x = _c(latent_bf16, np.uint16)
+    assert x.shape[-1] == 576
+    n = x.size // 576
+    out = np.empty(x.shape[:-1] + (656,), dtype=np.uint8)
+    lib.dsa_oracle_mla_fp8_pack(_p(x), n, _p(out))
+    return out
+
+
+def mla_fp8_values(kv8) -> np.ndarray:
+    """The float64 values [n, 576] that packed FP8 rows [n, 656] stand for."""
+    kv8 = _c(kv8, np.uint8)
+    lat = fp8_decode(kv8[..., :512]) * np.repeat(
+        kv8[..., 512:528].copy().view(np.float32).astype(np.float64), 128, axis=-1)
+    rope = kv8[..., 528:656].copy().view(np.uint16).astype(np.uint32) << 16
+    return np.concatenate([lat, rope.view(np.float32).astype(np.float64)], axis=-1)
+
+
+def sparse_mla_fp8(q_bf16, kv8, topk_idx, q_row_offsets, kv_row_offsets, sm_scale: float,
+                   rows=None, share_base=None, num_accepted=None) -> tuple[np.ndarray, np.ndarray]:
+    """Float64 sparse MLA over packed FP8 latent rows kv8 [N, 656] (see mla_fp8_pack)."""
+    lib = _load()
+    q = _c(q_bf16, np.uint16)
+    kv8 = _c(kv8, np.uint8)
+    tk = _c(topk_idx, np.int32)
+    T, H, dq = q.shape
+    assert dq == 576 and kv8.shape[-1] == 656
+    qo = _c(q_row_offsets, np.int32)
+    ko = _c(kv_row_offsets, np.int64)
+    if rows is None:
+        rows = np.arange(T, dtype=np.int64)
+    rows = _c(rows, np.int64)
+    sb = None if share_base is None else _c(share_base, np.int32)
+    na = None if num_accepted is None else _c(num_accepted, np.int32)
+    out = np.empty((len(rows), H, 512), dtype=np.float64)
+    lse = np.empty((len(rows), H), dtype=np.float64)
+    rc = lib.dsa_oracle_sparse_mla_fp8_rows(_p(q), _p(kv8), _p(tk), tk.shape[1], _p(sb), _p(na),
+                                            _p(qo), _p(ko), len(qo) - 1, H, float(sm_scale),
+                                            _p(rows), len(rows), _p(out), _p(lse))
+    if rc != 0:
+        raise ValueError("oracle sparse_mla_fp8: a row is outside every request")
     return out, lse
 
 

@@ -39,6 +39,9 @@
  *    verify rows) sits at position p = L_b - R_b + r and sees keys 0..p;
  *  - top-k ties go to the lower position; output ascending, -1 padded;
  *  - sparse MLA logits use all 576 dims, values are the first 512;
+ *  - FP8 latent cache row (656 bytes, see its section): 512 e4m3fn latent
+ *    codes in 4 blocks of 128 with one float32 scale each (amax/448, 1 when
+ *    amax == 0), then the 64 rope values as bf16;
  *  - greedy: first maximum wins the argmax;
  *  - rejection sampling: softmax targets, given draft probabilities and
  *    uniforms, residual max(0, p - q), inverse-CDF draw (see that section).
@@ -324,6 +327,116 @@ ORACLE_API int dsa_oracle_sparse_mla_rows(
       l = l + pj;
       const uint16_t* row = kv + (kv_off[b] + idx[j]) * (int64_t)DQK;
       for (int c = 0; c < DV; ++c) o[c] = o[c] + pj * bf16_to_f64(row[c]);
+    }
+    for (int c = 0; c < DV; ++c) o[c] = o[c] / l;
+    lse[i * H + h] = m + log(l);
+    free(z);
+  }
+  return bad ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* FP8 latent cache rows ([P2] the draft layer's KV pool: 656 bytes per   */
+/* token per layer in the fp8_ds_mla layout; [P3] "配置体系": the caches  */
+/* hold float8_e4m3fn with float32 scales).                              */
+/*                                                                      */
+/* Reading of the 656 bytes: 512 + 4*4 + 64*2, i.e.                      */
+/*   bytes [0, 512)   e4m3fn codes of latent values 0..511               */
+/*   bytes [512, 528) float32 scale of latent block b = 0..3 (128 values) */
+/*   bytes [528, 656) the 64 rope values, bf16, copied bit for bit       */
+/* Block b: amax = max |x| over its 128 values, scale = amax / 448 in    */
+/* float32 (1 when amax == 0), code = e4m3fn(x / scale) with the division */
+/* in float32 and the encoding of the indexer quantiser. The value a code */
+/* stands for is decode(code) * scale, formed exactly in float64.        */
+/* ------------------------------------------------------------------ */
+static float bf16_to_f32(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+/* latent: [n, 576] bf16 rows -> out: [n, 656] bytes. */
+ORACLE_API void dsa_oracle_mla_fp8_pack(const uint16_t* latent, int64_t n, uint8_t* out) {
+  fp8_table_init();
+  for (int64_t r = 0; r < n; ++r) {
+    const uint16_t* x = latent + r * 576;
+    uint8_t* o = out + r * 656;
+    for (int b = 0; b < 4; ++b) {
+      float amax = 0.0f;
+      for (int i = 0; i < 128; ++i) {
+        float a = fabsf(bf16_to_f32(x[128 * b + i]));
+        if (a > amax) amax = a;
+      }
+      float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+      memcpy(o + 512 + 4 * b, &sc, sizeof sc);
+      for (int i = 0; i < 128; ++i)
+        o[128 * b + i] = dsa_oracle_fp8_encode(bf16_to_f32(x[128 * b + i]) / sc);
+    }
+    memcpy(o + 528, x + 512, 64 * sizeof(uint16_t));
+  }
+}
+
+/* The 576 values a packed row stands for (float64, exact). */
+static void fp8_row_values(const uint8_t* row, double* v) {
+  float sc[4];
+  memcpy(sc, row + 512, sizeof sc);
+  for (int c = 0; c < 512; ++c) v[c] = dsa_oracle_fp8_decode(row[c]) * (double)sc[c / 128];
+  for (int c = 0; c < 64; ++c) {
+    uint16_t h;
+    memcpy(&h, row + 528 + 2 * c, sizeof h);
+    v[512 + c] = (double)bf16_to_f32(h);
+  }
+}
+
+/* Sparse MLA as dsa_oracle_sparse_mla_rows, over packed FP8 rows kv8 [N, 656]. */
+ORACLE_API int dsa_oracle_sparse_mla_fp8_rows(
+    const uint16_t* q, const uint8_t* kv8, const int32_t* topk, int k,
+    const int32_t* share_base, const int32_t* num_accepted,
+    const int32_t* q_off, const int64_t* kv_off, int B, int H, float sm_scale,
+    const int64_t* rows, int64_t n_rows, double* out, double* lse) {
+  const int DQK = 576, DV = 512, RB = 656;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t ii = 0; ii < n_rows * H; ++ii) {
+    int64_t i = ii / H;
+    int h = (int)(ii % H);
+    int64_t t = rows[i];
+    int b = row_request(q_off, B, t);
+    double* o = out + (i * H + h) * (int64_t)DV;
+    if (b < 0) { bad = 1; continue; }
+    int64_t L = kv_off[b + 1] - kv_off[b];
+    int64_t trow = share_base ? (int64_t)share_base[b] + num_accepted[b] : t;
+    const int32_t* idx = topk + trow * (int64_t)k;
+    const uint16_t* qh = q + (t * (int64_t)H + h) * DQK;
+    double* z = (double*)malloc(sizeof(double) * (size_t)k);
+    double v[576];
+    if (!z) { bad = 1; continue; }
+    double m = -INFINITY;
+    int nvalid = 0;
+    for (int j = 0; j < k; ++j) {
+      int64_t p = idx[j];
+      if (p < 0 || p >= L) { z[j] = NAN; continue; }
+      fp8_row_values(kv8 + (kv_off[b] + p) * (int64_t)RB, v);
+      double dot = 0.0;
+      for (int c = 0; c < DQK; ++c) dot = dot + (double)bf16_to_f32(qh[c]) * v[c];
+      z[j] = (double)sm_scale * dot;
+      if (z[j] > m) m = z[j];
+      ++nvalid;
+    }
+    for (int c = 0; c < DV; ++c) o[c] = 0.0;
+    if (nvalid == 0) {
+      lse[i * H + h] = -INFINITY;
+      free(z);
+      continue;
+    }
+    double l = 0.0;
+    for (int j = 0; j < k; ++j) {
+      if (isnan(z[j])) continue;
+      double pj = exp(z[j] - m);
+      l = l + pj;
+      fp8_row_values(kv8 + (kv_off[b] + idx[j]) * (int64_t)RB, v);
+      for (int c = 0; c < DV; ++c) o[c] = o[c] + pj * v[c];
     }
     for (int c = 0; c < DV; ++c) o[c] = o[c] / l;
     lse[i * H + h] = m + log(l);
