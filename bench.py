@@ -54,6 +54,10 @@ def parse():
                          "rows); separate: dsa_index_score, then dsa_topk with the refine")
     ap.add_argument("--err-scale", type=float, default=0.0,
                     help="C of the refine's error bound (0: the library default, 4)")
+    ap.add_argument("--mla-cache", choices=("bf16", "fp8"), default="bf16",
+                    help="latent cache of the sparse MLA: bf16 rows (1152 B) or FP8 rows (656 B: "
+                         "512 e4m3fn codes, 4 float32 block scales, 64 bf16 rope), written by "
+                         "the step's cache write and read by dsa_sparse_mla_decode_fp8")
     ap.add_argument("--no-share", action="store_true",
                     help="draft steps select their own top-k (quantise q, index score over the "
                          "whole context, refined top-k) instead of reusing the step-0 top-k; "
@@ -83,6 +87,7 @@ class Inputs:
 
     rejection = False  # also draw rejection-sampling inputs (bench --accept rejection)
     no_share = False   # also draw the draft rows' indexer queries (bench --no-share)
+    fp8_cache = False  # also hold the latent cache as FP8 rows (bench --mla-cache fp8)
 
     def __init__(self, w, lengths, copy: int):
         import torch
@@ -103,6 +108,7 @@ class Inputs:
         m = synth.mla_inputs(w, lengths, device=dev, seed_offset=copy)
         self.q_mla, self.kv = m["q"], m["kv"]
         self.latent_new = self.kv[self.dst].contiguous()
+        self.kv8 = api.mla_fp8_pack(self.kv) if Inputs.fp8_cache else None
         self.q_draft = None
         if w.share_steps:  # one draft row per request for each reuse step, same latent cache
             self.q_draft = [synth.mla_inputs(w, lengths, device=dev, rows=1,
@@ -254,6 +260,7 @@ def main():
     if args.no_share and (args.no_refine or args.topk_path == "fused"):
         sys.exit("bench.py: --no-share runs the separate path with the refine")
     Inputs.no_share = args.no_share
+    Inputs.fp8_cache = fp8 = args.mla_cache == "fp8"
     copies = [Inputs(w, lengths, c) for c in range(args.copies)]
     qo = synth.q_row_offsets(w).to(dev)
     ko = synth.kv_row_offsets(lengths).to(dev)
@@ -307,12 +314,25 @@ def main():
             ws_tk1 = torch.empty(max(tk1, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
+    def mla(qm, inp, tk, q_off, rows, o, l, ws, **share):
+        if fp8:
+            api.sparse_mla_decode_fp8(qm, inp.kv8, tk, q_off, ko, rows, w.sm_scale, out=o, lse=l,
+                                      workspace=ws, **share)
+        else:
+            api.sparse_mla_decode(qm, inp.kv, tk, q_off, ko, rows, w.sm_scale, out=o, lse=l,
+                                  workspace=ws, **share)
+
     def step(inp, ev=None):
         e = iter(ev) if ev else None
         mark = (lambda: next(e).record(stream)) if ev else (lambda: None)
         mark()
-        api.verify_cache_write(inp.k_new, inp.dst, inp.k_fp8, inp.k_scale, inp.latent_new, inp.kv,
-                               q=inp.q_f32, q_fp8=qc, q_scale=qs)
+        if not fp8:
+            api.verify_cache_write(inp.k_new, inp.dst, inp.k_fp8, inp.k_scale, inp.latent_new, inp.kv,
+                                   q=inp.q_f32, q_fp8=qc, q_scale=qs)
+        else:  # index keys and queries, then the verify rows' latent rows packed to FP8
+            api.verify_cache_write(inp.k_new, inp.dst, inp.k_fp8, inp.k_scale, q=inp.q_f32, q_fp8=qc,
+                                   q_scale=qs)
+            api.mla_fp8_pack(inp.latent_new, inp.kv8, dst_rows=inp.dst)
         mark()
         if fused:
             api.index_topk(qc, qs, inp.w, inp.k_fp8, inp.k_scale, qo, ko, w.rows, max_kv, w.topk,
@@ -326,8 +346,7 @@ def main():
                        status=status, err_scale=args.err_scale) if refine else None)
             api.topk(scores, qo, ko, w.rows, max_kv, w.topk, out=topk, refine=rf, workspace=ws_tk)
             mark()
-        api.sparse_mla_decode(inp.q_mla, inp.kv, topk, qo, ko, w.rows, w.sm_scale, out=out, lse=lse,
-                              workspace=ws_mla)
+        mla(inp.q_mla, inp, topk, qo, w.rows, out, lse, ws_mla)
         mark()
         if inp.rej is None:
             api.greedy_accept(inp.logits, inp.draft, w.drafts, argmax=False, workspace=ws_ga)
@@ -338,8 +357,7 @@ def main():
         mark()
         for j, qd in enumerate(inp.q_draft or []):
             if inp.ix_draft is None:  # index share: the step-0 top-k row at the accepted position
-                api.sparse_mla_decode(qd, inp.kv, topk, qo1, ko, 1, w.sm_scale, out=out1, lse=lse1,
-                                      workspace=ws1, share_base=qo, num_accepted=n_acc)
+                mla(qd, inp, topk, qo1, 1, out1, lse1, ws1, share_base=qo, num_accepted=n_acc)
                 continue
             ixd = inp.ix_draft[j]  # no share: the draft row runs the indexer over the whole cache
             api.quantize_fp8(ixd["q"], out=qc1, scale=qs1)
@@ -348,8 +366,7 @@ def main():
             api.topk(scores1, qo1, ko, 1, max_kv, w.topk, out=top1, workspace=ws_tk1,
                      refine=dict(q_fp8=qc1, q_scale=qs1, w=ixd["w"], k_fp8=inp.k_fp8,
                                  k_scale=inp.k_scale, status=status1, err_scale=args.err_scale))
-            api.sparse_mla_decode(qd, inp.kv, top1, qo1, ko, 1, w.sm_scale, out=out1, lse=lse1,
-                                  workspace=ws1)
+            mla(qd, inp, top1, qo1, 1, out1, lse1, ws1)
         if inp.q_draft:
             mark()
 
@@ -403,13 +420,15 @@ def main():
     # algorithmic work (bytes / flops the method must move or do)
     wi = accounting.index_score_work(lengths, w.rows, w.index_heads, w.index_dim)
     wt = accounting.topk_work(lengths, w.rows, w.topk)
-    wm = accounting.sparse_mla_work(T, w.mla_heads, w.topk)
+    row_bytes = accounting.FP8_ROW_BYTES if fp8 else 2 * 576
+    wm = accounting.sparse_mla_work(T, w.mla_heads, w.topk, row_bytes=row_bytes)
     wg = (accounting.greedy_accept_work if args.accept == "greedy" else
           accounting.rejection_accept_work)(w.batch, w.drafts, w.vocab, 2)
-    wq = dict(bytes=T * (w.index_heads + 1) * (w.index_dim * 4 + w.index_dim + 4) + T * 2 * 1152)
+    wq = dict(bytes=T * (w.index_heads + 1) * (w.index_dim * 4 + w.index_dim + 4) + T * (1152 + row_bytes))
     kern = {
         "cache_write": dict(bytes=wq["bytes"], bound="hbm", file="quantize.hip"),
-        "sparse_mla": dict(bytes=wm["bytes"], flops=wm["flops"], bound="hbm", file="sparse_mla.hip"),
+        "sparse_mla": dict(bytes=wm["bytes"], flops=wm["flops"], bound="hbm", file="sparse_mla.hip",
+                           traffic_key="sparse_mla_fp8" if fp8 else "sparse_mla"),
         acc_name: dict(bytes=wg["bytes"], bound="hbm",
                        file="greedy_accept.hip" if args.accept == "greedy" else "rejection_accept.hip"),
     }
@@ -422,11 +441,11 @@ def main():
                                    file="index_score.hip")
         kern["topk"] = dict(bytes=wt["bytes"], bound="hbm", file="topk.hip")
     if w.share_steps and not args.no_share:
-        ws_ = accounting.sparse_mla_work(w.batch, w.mla_heads, w.topk)
+        ws_ = accounting.sparse_mla_work(w.batch, w.mla_heads, w.topk, row_bytes=row_bytes)
         kern["share_mla"] = dict(bytes=w.share_steps * ws_["bytes"],
                                  flops=w.share_steps * ws_["flops"], bound="hbm")
     elif w.share_steps:  # several kernels per draft step: reported, never the roofline kernel
-        ws_ = accounting.sparse_mla_work(w.batch, w.mla_heads, w.topk)
+        ws_ = accounting.sparse_mla_work(w.batch, w.mla_heads, w.topk, row_bytes=row_bytes)
         wi1 = accounting.index_score_work(lengths, 1, w.index_heads, w.index_dim)
         wt1 = accounting.topk_work(lengths, 1, w.topk)
         kern["draft_steps"] = dict(bytes=w.share_steps * (ws_["bytes"] + wi1["bytes"] + wt1["bytes"]),
@@ -454,7 +473,8 @@ def main():
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4)}
     roof["kernel"] = dom
-    roof["traffic"] = traffic_for(kd.get("file", ""), dom) if kd.get("file") else None
+    roof["traffic"] = (traffic_for(kd["file"], kd.get("traffic_key", dom))
+                       if kd.get("file") and not (fp8 and dom == "cache_write") else None)
 
     rows_step = T + w.share_steps * w.batch  # verify rows, plus one draft row per reuse step
     value = rows_step / (ms_step * 1e-3)
@@ -467,7 +487,7 @@ def main():
                    "index_heads": w.index_heads, "index_dim": w.index_dim, "topk": w.topk,
                    "mla_heads": w.mla_heads, "vocab": w.vocab, "global_batch": rows_step,
                    "seq_len": max_kv, "share_steps": w.share_steps, "topk_refine": refine,
-                   "topk_path": args.topk_path, "index_share": (not args.no_share) if w.share_steps else None,
+                   "topk_path": args.topk_path, "mla_cache": args.mla_cache, "index_share": (not args.no_share) if w.share_steps else None,
                    "accept": args.accept,
                    "parallelism": "single-gpu"},
         "step_includes": names,

@@ -35,6 +35,9 @@ SIGNATURES = {
     "dsa_sparse_mla_decode": ([P, P, P, I32, P, P, P, P, I32, I32, I32, I32, I32, F32, P, P, P, SZ, P],
                               ctypes.c_int),
     "dsa_sparse_mla_workspace_size": ([I32, I32, I32], SZ),
+    "dsa_sparse_mla_decode_fp8": ([P, P, P, I32, P, P, P, P, I32, I32, I32, I32, I32, F32, P, P, P, SZ,
+                                   P], ctypes.c_int),
+    "dsa_mla_fp8_pack": ([P, P, I64, P, P], ctypes.c_int),
     "greedy_accept": ([P, I32, I64, P, I32, I32, I32, P, P, P, P, SZ, P], ctypes.c_int),
     "greedy_accept_workspace_size": ([I32, I32, I32], SZ),
     "greedy_accept_noalloc": ([P, I32, I64, P, I32, I32, I32, P, P, P, P], ctypes.c_int),

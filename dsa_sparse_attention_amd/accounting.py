@@ -65,14 +65,19 @@ def index_topk_work(lengths, rows: int, heads: int, dim: int, k: int) -> dict:
                 pairs=wi["pairs"])
 
 
-def sparse_mla_work(n_rows: int, heads: int, k: int, selected_per_row=None) -> dict:
-    """Bytes/flops of dsa_sparse_mla_decode.
+FP8_ROW_BYTES = 656  # FP8 latent cache row ("GLM-5.3 推理全链路(十四)": 656 B/token/layer)
 
-    bytes: one 1152-byte latent row per selected position, q and out per (row, head),
-    4-byte indices and the fp32 lse. flops: QK^T over 576 dims plus PV over 512.
+
+def sparse_mla_work(n_rows: int, heads: int, k: int, selected_per_row=None,
+                    row_bytes: int = DQK * 2) -> dict:
+    """Bytes/flops of dsa_sparse_mla_decode (row_bytes 1152, bf16 rows) or of
+    dsa_sparse_mla_decode_fp8 (row_bytes FP8_ROW_BYTES).
+
+    bytes: one latent row per selected position, q and out per (row, head), 4-byte
+    indices and the fp32 lse. flops: QK^T over 576 dims plus PV over 512.
     """
     sel = n_rows * k if selected_per_row is None else int(selected_per_row)
-    bytes_ = sel * DQK * 2 + n_rows * heads * (DQK * 2 + LATENT * 2 + 4) + n_rows * k * 4
+    bytes_ = sel * row_bytes + n_rows * heads * (DQK * 2 + LATENT * 2 + 4) + n_rows * k * 4
     flops = 2 * heads * sel * (DQK + LATENT)
     return dict(bytes=bytes_, flops=flops)
 

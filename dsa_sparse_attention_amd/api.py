@@ -56,6 +56,9 @@ def _shape(t, name, shape):
     return t
 
 
+FP8_ROW_BYTES = 656  # FP8 latent cache row: 512 e4m3fn codes, 4 float32 scales, 64 bf16
+
+
 def abi_version() -> int:
     return _lib.load().dsa_abi_version()
 
@@ -278,6 +281,69 @@ def sparse_mla_decode(q, kv, topk_idx, q_row_offsets, kv_row_offsets, max_q_rows
         _p(q), _p(kv), _p(topk_idx), topk_idx.shape[0], _p(share_base), _p(num_accepted), _p(q_row_offsets),
         _p(kv_row_offsets), B, T, max_q_rows, H, k, float(sm_scale), _p(out), _p(lse),
         _p(workspace), wsb, _stream()))
+    return out, lse
+
+
+def mla_fp8_pack(latent, kv_fp8=None, dst_rows=None):
+    """FP8 latent cache rows [N, 656] u8 from bf16 latent rows [n, 576]: row dst_rows[i]
+    (row i without dst_rows) of kv_fp8 packs latent[i]. Returns kv_fp8."""
+    _dev(latent, "latent", torch.bfloat16)
+    if latent.shape[-1] != 576:
+        raise ValueError("latent rows must be 576 wide (512 latent + 64 rope)")
+    n = latent.numel() // 576
+    if kv_fp8 is None:
+        if dst_rows is not None:
+            raise ValueError("dst_rows needs the kv_fp8 cache it indexes")
+        kv_fp8 = torch.empty(latent.shape[:-1] + (FP8_ROW_BYTES,), dtype=torch.uint8,
+                             device=latent.device)
+    _dev(kv_fp8, "kv_fp8", torch.uint8)
+    if kv_fp8.shape[-1] != FP8_ROW_BYTES:
+        raise ValueError(f"kv_fp8 rows must be {FP8_ROW_BYTES} bytes")
+    if dst_rows is not None:
+        _dev(dst_rows, "dst_rows", torch.int64)
+        _shape(dst_rows, "dst_rows", (n,))
+    elif kv_fp8.numel() // FP8_ROW_BYTES < n:
+        raise ValueError("kv_fp8 holds fewer rows than latent")
+    _check(_lib.load().dsa_mla_fp8_pack(_p(latent), _p(dst_rows), n, _p(kv_fp8), _stream()))
+    return kv_fp8
+
+
+def sparse_mla_decode_fp8(q, kv_fp8, topk_idx, q_row_offsets, kv_row_offsets, max_q_rows: int,
+                          sm_scale: float, share_base=None, num_accepted=None, out=None, lse=None,
+                          workspace=None, want_lse: bool = True):
+    """Sparse MLA over an FP8 latent cache [N, 656] u8 (rows of mla_fp8_pack):
+    (out [T,H,512] bf16, lse [T,H] f32)."""
+    _dev(q, "q", torch.bfloat16)
+    _dev(kv_fp8, "kv_fp8", torch.uint8)
+    _dev(topk_idx, "topk", torch.int32)
+    _dev(q_row_offsets, "q_row_offsets", torch.int32)
+    _dev(kv_row_offsets, "kv_row_offsets", torch.int64)
+    if share_base is not None:
+        _dev(share_base, "share_base", torch.int32)
+        _dev(num_accepted, "num_accepted", torch.int32)
+    T, H, dq = q.shape
+    if dq != 576 or kv_fp8.shape[-1] != FP8_ROW_BYTES:
+        raise ValueError(f"q rows must be 576 wide and kv_fp8 rows {FP8_ROW_BYTES} bytes")
+    k = topk_idx.shape[1]
+    B = q_row_offsets.numel() - 1
+    if out is None:
+        out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=q.device)
+    _dev(out, "out", torch.bfloat16)
+    _shape(out, "out", (T, H, 512))
+    if lse is None and want_lse:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+        _shape(lse, "lse", (T, H))
+    lib = _lib.load()
+    need = lib.dsa_sparse_mla_workspace_size(T, H, k)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.dsa_sparse_mla_decode_fp8(
+        _p(q), _p(kv_fp8), _p(topk_idx), topk_idx.shape[0], _p(share_base), _p(num_accepted),
+        _p(q_row_offsets), _p(kv_row_offsets), B, T, max_q_rows, H, k, float(sm_scale), _p(out),
+        _p(lse), _p(workspace), wsb, _stream()))
     return out, lse
 
 

@@ -126,8 +126,66 @@ __global__ __launch_bounds__(256) void verify_write_kernel(
   reinterpret_cast<i32x4*>(kv_cache + dst_rows[t] * LATENT)[piece] = val;
 }
 
+// FP8 latent cache rows ("GLM-5.3 推理全链路(十四)", the draft layer's KV pool: 656 bytes
+// per token per layer): bytes [0, 512) e4m3fn codes of the 512 latent values, [512, 528)
+// the float32 scale of each 128-value block (amax / 448, 1 when amax == 0), [528, 656) the
+// 64 rope values copied as bf16. One wave per row: lane l quantises latent values
+// 8l .. 8l+7 (its 16-lane group is one scale block); lanes 0..7 copy the rope.
+constexpr int RB8 = 656;
+
+__global__ __launch_bounds__(256) void mla_fp8_pack_kernel(const uint16_t* __restrict__ latent,
+                                                           const int64_t* __restrict__ dst_rows,
+                                                           int64_t n, uint8_t* __restrict__ out) {
+  const int lane = threadIdx.x % 64;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / 64;
+  const bool live = r < n;
+  const int64_t rr = live ? r : 0;
+  const uint16_t* src = latent + rr * LATENT;
+  const i32x4 v = reinterpret_cast<const i32x4*>(src)[lane];
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf16_bits_to_f32(static_cast<uint16_t>(v[i] & 0xFFFF));
+    x[2 * i + 1] = bf16_bits_to_f32(static_cast<uint16_t>(static_cast<uint32_t>(v[i]) >> 16));
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+  const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+  if (!live) return;
+  uint8_t* dst = out + (dst_rows ? dst_rows[r] : r) * RB8;
+  uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    w0 |= e4m3_rne_sat(x[i] / s) << (8 * i);
+    w1 |= e4m3_rne_sat(x[4 + i] / s) << (8 * i);
+  }
+  reinterpret_cast<uint2*>(dst)[lane] = make_uint2(w0, w1);
+  if ((lane & 15) == 0) reinterpret_cast<float*>(dst + 512)[lane >> 4] = s;
+  if (lane < 8)
+    reinterpret_cast<i32x4*>(dst + 528)[lane] = reinterpret_cast<const i32x4*>(src + 512)[lane];
+}
+
 }  // namespace
 }  // namespace dsa
+
+extern "C" dsa_status dsa_mla_fp8_pack(const uint16_t* latent, const int64_t* dst_rows, int64_t n,
+                                       uint8_t* kv_fp8, void* stream) {
+  using namespace dsa;
+  DSA_REQUIRE(n >= 0, "dsa_mla_fp8_pack: n must be >= 0 (got %lld)", (long long)n);
+  if (n == 0) return ok();
+  DSA_REQUIRE(latent && kv_fp8, "dsa_mla_fp8_pack: null pointer");
+  DSA_REQUIRE((reinterpret_cast<uintptr_t>(latent) & 15) == 0 &&
+                  (reinterpret_cast<uintptr_t>(kv_fp8) & 15) == 0,
+              "dsa_mla_fp8_pack: latent and kv_fp8 must be 16-byte aligned");
+  const int64_t blocks = ceil_div(n, 4);
+  DSA_REQUIRE(blocks <= 0x7FFFFFFF, "dsa_mla_fp8_pack: too many rows");
+  hipLaunchKernelGGL(mla_fp8_pack_kernel, dim3((unsigned)blocks), dim3(256), 0, as_stream(stream),
+                     latent, dst_rows, n, kv_fp8);
+  return check_launch("dsa_mla_fp8_pack");
+}
 
 extern "C" dsa_status dsa_quantize_fp8(const float* x, int64_t n_vec, int32_t dim,
                                        uint8_t* x_fp8, float* scale, void* stream) {

@@ -51,6 +51,7 @@ KERNELS = {
     "topk_kernel": ("topk", "topk.hip"),
     "sample_tau_kernel": ("index_topk", "index_score.hip"),
     "fused_select_kernel": ("index_topk", "index_score.hip"),
+    "mla_fp8_pack_kernel": ("cache_write", "quantize.hip"),
     "mla_decode_kernel": ("sparse_mla", "sparse_mla.hip"),
     "mla_combine_kernel": ("sparse_mla", "sparse_mla.hip"),
     "argmax_slices_kernel": ("greedy_accept", "greedy_accept.hip"),
@@ -127,10 +128,14 @@ def dispatch_table(path: str):
     return out
 
 
-def classify(name: str):
-    """(call entry, source) of a kernel; index_score_kernel's fused modes belong to index_topk."""
+def classify(name: str, fp8_mla: bool = False):
+    """(call entry, source) of a kernel; index_score_kernel's fused modes belong to index_topk,
+    and the FP8 decode (mla_decode_kernel<true>, with the combine of its run: fp8_mla) to
+    sparse_mla_fp8."""
     if "index_score_kernel" in name and index_score_mode(name) != 0:
         return "index_topk", "+".join(SOURCES["index_topk"])
+    if "mla_decode_kernel<true>" in name or (fp8_mla and "mla_combine_kernel" in name):
+        return "sparse_mla_fp8", "sparse_mla.hip"
     for key, (entry, src) in KERNELS.items():
         if key in name:
             if entry in SOURCES:
@@ -165,17 +170,18 @@ def traffic(fetch_csvs, write_csvs, cal_fetch_csv: str, cal_write_csv: str):
     for fetch_csv, write_csv in zip(fetch_csvs, write_csvs):
         fetch = per_dispatch(fetch_csv, "FETCH_SIZE")
         write = per_dispatch(write_csv, "WRITE_SIZE")
+        fp8 = any("mla_decode_kernel<true>" in n for n, _ in fetch.values())
         # sum the kernels of one API call (the MLA is decode + combine), averaged per call
         fsum, wsum, nlaunch, srcs = (collections.defaultdict(float), collections.defaultdict(float),
                                      collections.defaultdict(int), {})
         for d, (n, v) in fetch.items():
-            e, src = classify(n)
+            e, src = classify(n, fp8)
             if e:
                 fsum[e] += v * 1024.0 * f_factor
                 srcs[e] = src
                 nlaunch[e] += primary(n)
         for d, (n, v) in write.items():
-            e, _ = classify(n)
+            e, _ = classify(n, fp8)
             if e:
                 wsum[e] += v * 1024.0 * w_factor
         for e in fsum:

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 5
+#define DSA_ABI_VERSION 6
 
 typedef enum {
   DSA_OK = 0,
@@ -300,6 +300,46 @@ dsa_status dsa_sparse_mla_decode(const uint16_t* q, const uint16_t* kv, const in
                                  size_t ws_bytes, void* stream);
 
 size_t dsa_sparse_mla_workspace_size(int32_t T, int32_t H, int32_t k);
+
+/*
+ * dsa_mla_fp8_pack -- FP8 latent cache rows from bf16 latent rows.
+ * ("GLM-5.3 推理全链路(十四)", the draft-layer section: the KV pool holds 656 bytes per
+ * token per layer in the fp8_ds_mla layout; "MAX Pipeline 中的 DeepSeek-V3.2 架构实现解析",
+ * "配置体系": float8_e4m3fn caches with float32 scales.)
+ *
+ * Row layout, 656 bytes (rows are 16-byte aligned when the array is):
+ *   bytes [0, 512)   e4m3fn code of latent value c = 0..511
+ *   bytes [512, 528) float32 scale of latent block b = 0..3 (values 128b .. 128b+127):
+ *                    amax_b / 448 rounded to float32, 1 when amax_b == 0
+ *   bytes [528, 656) the 64 rope values (latent dims 512..575), bf16 copied bit for bit
+ * code = e4m3fn(x / scale_b): float32 division, round to nearest even, saturating at
+ * +-448. A code stands for decode(code) * scale_b.
+ * For i < n: row dst_rows[i] (row i when dst_rows is NULL) of kv_fp8 = pack(latent[i]).
+ *   latent [n, 576] bf16; dst_rows [n] int64 device array or NULL (distinct rows,
+ *   trusted); kv_fp8 [N, 656] u8. latent and kv_fp8 16-byte aligned.
+ * Errors: DSA_ERR_INVALID_ARGUMENT (n < 0, null or misaligned pointers).
+ */
+dsa_status dsa_mla_fp8_pack(const uint16_t* latent, const int64_t* dst_rows, int64_t n,
+                            uint8_t* kv_fp8, void* stream);
+
+/*
+ * dsa_sparse_mla_decode_fp8 -- dsa_sparse_mla_decode over an FP8 latent cache.
+ * (The passages of dsa_sparse_mla_decode; the rows are those of dsa_mla_fp8_pack.)
+ *
+ * Same arguments, results, workspace and errors as dsa_sparse_mla_decode, with
+ * kv_fp8 [N, 656] u8 (16-byte aligned) in place of kv: a row stands for
+ * decode(code) * scale_b in its 512 latent dims and for its bf16 rope in the last 64.
+ * The codes enter the bf16 MFMAs exactly; the scales are applied in float32, to each
+ * block's partial logit and to the PV weights (which are rounded to bf16 after the
+ * scale, as the bf16 path rounds its weights).
+ */
+dsa_status dsa_sparse_mla_decode_fp8(const uint16_t* q, const uint8_t* kv_fp8,
+                                     const int32_t* topk, int32_t topk_rows,
+                                     const int32_t* share_base, const int32_t* num_accepted,
+                                     const int32_t* q_row_offsets, const int64_t* kv_row_offsets,
+                                     int32_t B, int32_t T, int32_t max_q_rows, int32_t H, int32_t k,
+                                     float sm_scale, uint16_t* out, float* lse, void* ws,
+                                     size_t ws_bytes, void* stream);
 
 /*
  * greedy_accept -- greedy acceptance of a chain of K drafts per request.

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_workspace_queries():
     lib = _lib.load()
-    assert lib.dsa_abi_version() == 5
+    assert lib.dsa_abi_version() == 6
     assert lib.dsa_last_error() in (b"", None)
     assert lib.dsa_topk_workspace_size(32, 192, 65536, 2048, 0) == 0
     # the refine keeps one key-scale maximum per 2048 positions of every request
