@@ -455,10 +455,11 @@ __device__ __forceinline__ i32x4 digit_plane(const uint32_t (&wd)[16], int p) {
 // evaluated in float64 with one rounding per product and per sum.
 // The head dots are exact integer arithmetic on the int8 MFMA: every e4m3fn value times 2^9
 // is an integer below 2^18, split into three base-128 digits; the nine digit-plane products
-// (v_mfma_i32_16x16x64_i8, int32 accumulation, |sum| < 2^21 per plane pair) recombine
-// exactly in float64 (|d| 2^18 < 2^43). A wave takes one tile of 16 heads x 16 band keys
-// per round; the u_j max(d_j, 0) terms of a round go to LDS, and one thread per key then
-// adds them in ascending head order.
+// (v_mfma_i32_16x16x64_i8) chain into five int32 accumulators, one per digit-weight 2^(7s)
+// (s = a + b, |sum| < 3 * 2^21), which recombine exactly in float64 (|d| 2^18 < 2^43). A
+// wave takes one tile of 16 heads x 16 band keys per round, with the next round's key codes
+// already loading; the u_j max(d_j, 0) terms of a round go to LDS, and one thread per key
+// then adds them in ascending head order.
 __device__ __forceinline__ double rescore_band(const RowRef& rr, const float* __restrict__ srow,
                                                int nb, RefineLds& L, bool table_ready,
                                                float* band_sk, float* band_f32) {
@@ -528,7 +529,6 @@ __device__ __forceinline__ double rescore_band(const RowRef& rr, const float* __
   }
   double worst = 0.0;
   for (int base = 0; base < nb; base += KPR) {  // block-uniform rounds
-    if (base > 0) load_keys(base, kc);
     if (base + 16 * kt < nb) {  // wave-uniform: the tile holds at least one band key
       i32x4 kb[2][3];
 #pragma unroll
@@ -538,17 +538,23 @@ __device__ __forceinline__ double rescore_band(const RowRef& rr, const float* __
 #pragma unroll
         for (int p = 0; p < 3; ++p) kb[h][p] = digit_plane(wd, p);
       }
-      double d[4] = {0.0, 0.0, 0.0, 0.0};  // exact dots times 2^18, heads 4 g + i, key c16
+      if (base + KPR < nb) load_keys(base + KPR, kc);  // the next round's codes, in flight
+      i32x4 acc[5];  // digit weight 2^(7s): sum of the (a, b) plane products with a + b = s
+#pragma unroll
+      for (int sw = 0; sw < 5; ++sw) acc[sw] = (i32x4){0, 0, 0, 0};
 #pragma unroll
       for (int a = 0; a < 3; ++a)
 #pragma unroll
         for (int b = 0; b < 3; ++b) {
-          i32x4 acc = {0, 0, 0, 0};
-          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[0][a], kb[0][b], acc, 0, 0, 0);
-          if (halves > 1) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[1][a], kb[1][b], acc, 0, 0, 0);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) d[i] += __builtin_ldexp(static_cast<double>(acc[i]), 7 * (a + b));
+          acc[a + b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[0][a], kb[0][b], acc[a + b], 0, 0, 0);
+          if (halves > 1)
+            acc[a + b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[1][a], kb[1][b], acc[a + b], 0, 0, 0);
         }
+      double d[4] = {0.0, 0.0, 0.0, 0.0};  // exact dots times 2^18, heads 4 g + i, key c16
+#pragma unroll
+      for (int sw = 0; sw < 5; ++sw)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) d[i] += __builtin_ldexp(static_cast<double>(acc[sw][i]), 7 * sw);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int head = 16 * ht + 4 * g + i;
