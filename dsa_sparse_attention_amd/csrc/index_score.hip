@@ -30,8 +30,9 @@
 //     of a tile at once.
 //  3. Each compute wave stores its row's 32 scores of the tile (key scale applied)
 //     with one coalesced 128-byte store.
-// One barrier per tile hands a landed tile to the compute waves and the slot of the
-// previous tile back to the producer.
+// One barrier per tile hands the tile after the current one to the compute waves (so a
+// wave reads the next tile's first B operand before the barrier, and its MFMAs issue right
+// after it) and the slot of the tile before the previous one back to the producer.
 #include <atomic>
 
 #include "common.hpp"
@@ -165,9 +166,12 @@ __device__ __forceinline__ void producer_segment(
       lds_dma4(sreq + pos_of(key), (const lds_void*)(slot + TILE_K));
     }
   };
-  // Tile it+NBUF-2 goes into the slot of tile it-2, which every compute wave finished
-  // reading before barrier it-1: the producer issues it before barrier it, overlapped
-  // with the compute of tile it-1, and reaches the barrier as soon as tile it is in.
+  // Barrier it hands over tile it+1 (tiles 0 and 1 at barrier 0): the compute waves read
+  // a tile's sub-tile 0 between the barriers before it and its own, and the rest between its
+  // own barrier and the next. Tile it+NBUF-2 goes into the slot of tile it-2, which every
+  // compute wave finished reading before barrier it-1: the producer issues it before
+  // barrier it, overlapped with the compute, and reaches the barrier as soon as tile it+1
+  // is in.
   // Retire every load the compiler issued so far: its own wait bookkeeping does not see
   // the DMAs, and a wait it placed for one of its loads inside the loop would count them
   // wrongly and drain the whole DMA pipeline.
@@ -177,10 +181,11 @@ __device__ __forceinline__ void producer_segment(
 #pragma unroll 1
   for (int it = 0; it < ntiles; ++it) {
     if (it + NBUF - 2 < ntiles) issue_tile(it + NBUF - 2);
-    // tile `it` has landed when at most the DMAs of the tiles after it are in flight
-    const int after = ntiles - 1 - it < NBUF - 2 ? ntiles - 1 - it : NBUF - 2;
-    wait_vm_at_most<(NBUF - 2) * DMAS>(after * DMAS);
-    __syncthreads();  // hand tile `it` over; every compute wave is done with tile it-1
+    // tile it+1 has landed when at most the DMAs of the tiles after it are in flight
+    const int last = it + NBUF - 2 < ntiles ? it + NBUF - 2 : ntiles - 1;  // last issued
+    const int need = it + 1 < ntiles ? it + 1 : ntiles - 1;
+    wait_vm_at_most<(NBUF - 3) * DMAS>((last - need) * DMAS);
+    __syncthreads();  // hand tile it+1 over; every compute wave is done with tile it-1
   }
 }
 
@@ -259,28 +264,27 @@ __device__ __forceinline__ void compute_segment(
 
   // Software pipeline over 16-key sub-tiles (each wave owns sub-tiles 0 and 1 of its
   // 32-key half of every tile): the MFMAs of the next sub-tile are issued before the
-  // current one is reduced, so the MFMA pipe and the VALU reduction overlap. Every read of
-  // a tile's slot (keys and scale) happens before the barrier that lets the producer
-  // refill it.
+  // current one is reduced. A tile's sub-tile 0 is read between the barrier that hands it
+  // over and the tile's own barrier, the rest (sub-tile 1, key scales) before the barrier
+  // after that, which is before the producer refills its slot.
   const bool live = row_live;
   auto live_tile = [&](int it) { return live && it * KT + 32 * kh < nstore; };  // wave-uniform
   // this lane's piece addresses in the current tile's slot (carried from sub-tile 0 of a
   // tile to its sub-tile 1)
   const uint8_t* a_lo = ring[0] + off_lo;
   const uint8_t* a_hi = ring[0] + off_hi;
-  auto set_tile = [&](int it) {
-    a_lo = ring[it % NBUF] + off_lo;
-    a_hi = ring[it % NBUF] + off_hi;
-  };
-  auto mfma_sub = [&](int sb, f32x4 (&acc)[HT]) {
-    // (for D = 128 every lane group holds 32 of the key's dims: the load is unconditional,
-    // with no zero fill on the VALU)
+  // B operand of sub-tile sb of the tile at a_lo / a_hi (for D = 128 every lane group holds
+  // 32 of the key's dims: the load is unconditional, with no zero fill on the VALU)
+  auto load_b = [&](int sb) {
     i32x8 bfrag = {0, 0, 0, 0, 0, 0, 0, 0};
     if (D >= 128 || 32 * g < D) {
       const i32x4 lo = *reinterpret_cast<const i32x4*>(a_lo + sb * 16 * D);
       const i32x4 hi = *reinterpret_cast<const i32x4*>(a_hi + sb * 16 * D);
       bfrag = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
+    return bfrag;
+  };
+  auto mfma_sub = [&](const i32x8& bfrag, f32x4 (&acc)[HT]) {
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
       const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -328,22 +332,31 @@ __device__ __forceinline__ void compute_segment(
 
   f32x4 acc0[HT], acc1[HT];  // sub-tile 0 / sub-tile 1 of the current tile
   if (ntiles > 0) {
-    __syncthreads();  // tile 0 is in LDS (the producer waited for it)
-    if (live_tile(0)) mfma_sub(0, acc0);
+    __syncthreads();  // tiles 0 and 1 are in LDS (the producer waited for them)
+    if (live_tile(0)) mfma_sub(load_b(0), acc0);
   }
-#pragma unroll 1
-  for (int it = 0; it < ntiles; ++it) {
+  // One tile: `slot` = it % NBUF. The loop below unrolls NBUF steps so that every slot
+  // address is a constant offset from the ring's base.
+  auto step = [&](const int it, const int slot) {
+    const int nslot = (slot + 1) % NBUF;
     const bool lv = live_tile(it);
     float sc = 0.0f, p0 = 0.0f;
+    const i32x8 b1 = load_b(1);
+    if (lv) sc = reinterpret_cast<const float*>(ring[slot] + TILE_K)[kt];
+    // sub-tile 0 of tile it+1, landed at the last barrier, read before the next one
+    i32x8 bn = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (it + 1 < ntiles) {
+      a_lo = ring[nslot] + off_lo;
+      a_hi = ring[nslot] + off_hi;
+      bn = load_b(0);
+    }
     if (lv) {
-      mfma_sub(1, acc1);
-      sc = reinterpret_cast<const float*>(ring[it % NBUF] + TILE_K)[kt];
+      mfma_sub(b1, acc1);
       p0 = partial(acc0);
     }
     if (it + 1 < ntiles) {
-      __syncthreads();  // tile it+1 is in LDS; every wave is done reading tile it
-      set_tile(it + 1);
-      if (live_tile(it + 1)) mfma_sub(0, acc0);
+      __syncthreads();  // tile it+2 is in LDS; every wave is done reading tile it
+      if (live_tile(it + 1)) mfma_sub(bn, acc0);
     }
     if (live_tile(it)) {  // recomputed (scalar) rather than carried across the barrier
       const float sum = combine(p0, partial(acc1));
@@ -366,6 +379,12 @@ __device__ __forceinline__ void compute_segment(
         if (mine) tile_row[kt] = sum * sc;
       }
     }
+  };
+#pragma unroll 1
+  for (int base = 0; base < ntiles; base += NBUF) {
+#pragma unroll
+    for (int k = 0; k < NBUF; ++k)
+      if (base + k < ntiles) step(base + k, k);
   }
   if constexpr (MODE == COMPACT) {
     if (live) {
