@@ -51,6 +51,7 @@ constexpr int DMA_BLOCKS = CHUNK_BYTES / 1024;   // 36 wave-wide (64 x 16 B) DMA
 constexpr int LEAD = 2;                          // chunks in flight ahead of the S waves
 constexpr int NBUF = LEAD + 2;                   // chunk ring: S, O, and LEAD in flight
 constexpr int MAX_KPS = 2048;                    // top-k entries per slice (LDS staging)
+constexpr int MAX_SPLITS = 16;                   // slices per row (k <= 16 * MAX_KPS)
 constexpr int HPB = 64;                          // heads per block
 constexpr int NSW = 8, NOW = 8, NWAVE = NSW + NOW, NT = NWAVE * 64;
 constexpr int KS = DQK / 32;                     // 18 k-steps of the S product
@@ -147,8 +148,9 @@ __global__ __launch_bounds__(NT, 1) void mla_decode_kernel(
     const int32_t* __restrict__ topk, const int32_t* __restrict__ share_base,
     const int32_t* __restrict__ num_acc, const int32_t* __restrict__ q_off,
     const int64_t* __restrict__ kv_off, int H, int nhg, int k, int topk_rows, float c2,
-    int nsplit, int keys_per_split, uint16_t* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+    int nsplit, int keys_per_split, int max_q_rows, int nwork, int per_xcd,
+    uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ ws_o,
+    float* __restrict__ ws_ml) {
   constexpr int PER_T = MAX_KPS / NT;  // index entries per thread
   constexpr int SLOT = F8 ? F8_SLOT : CHUNK_BYTES;
   constexpr int NB = NBUF, LD = LEAD;
@@ -163,8 +165,15 @@ __global__ __launch_bounds__(NT, 1) void mla_decode_kernel(
   __shared__ int sh_resc[2][4];       // head quarter moved its reference, chunk parity
   __shared__ float sh_m[HPB], sh_l[2][HPB];
 
-  const int hg = blockIdx.x % nhg, split = blockIdx.x / nhg;
-  const int r_row = blockIdx.y, b = blockIdx.z;
+  // Work item w = (split * nhg + hg) + nsplit * nhg * (row + max_q_rows * request): the
+  // blocks of one query row (its head groups and slices) are consecutive. Block L goes to
+  // XCD L % 8 (round-robin dispatch), and XCD x takes items x * per_xcd .. + per_xcd - 1, so
+  // a row's blocks share one L2: the head groups' gathers of the same latent rows hit it.
+  const int w = static_cast<int>(blockIdx.x % 8) * per_xcd + static_cast<int>(blockIdx.x / 8);
+  if (w >= nwork) return;
+  const int gx = nsplit * nhg;
+  const int hg = (w % gx) % nhg, split = (w % gx) / nhg;
+  const int r_row = (w / gx) % max_q_rows, b = (w / gx) / max_q_rows;
   const RowInfo ri = load_row_info(q_off, kv_off, b);
   if (r_row >= ri.R) return;
   const int64_t t = ri.t0 + r_row;
@@ -550,59 +559,69 @@ __global__ __launch_bounds__(NT, 1) void mla_decode_kernel(
       if (hd >= H) continue;
       const float mh = sh_m[32 * ht + r];
       const float lh = sh_l[0][32 * ht + r] + sh_l[1][32 * ht + r];
+      // the normalised output (bf16): the row's result, or with several slices this slice's
+      // partial, which the combine kernel weighs by its (max, sum)
+      const int64_t slot = (t * nsplit + split) * H + hd;
+      const float inv = lh > 0.0f ? 1.0f / lh : 0.0f;
+      uint16_t* orow = (nsplit == 1 ? out + (t * H + hd) * DV : ws_o + slot * DV) + 64 * ow + 4 * h;
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const f32x16& a = o[dt][ht];
+          const uint32_t lo = f32_to_bf16_bits(a[4 * qd] * inv) |
+                              (static_cast<uint32_t>(f32_to_bf16_bits(a[4 * qd + 1] * inv)) << 16);
+          const uint32_t hi = f32_to_bf16_bits(a[4 * qd + 2] * inv) |
+                              (static_cast<uint32_t>(f32_to_bf16_bits(a[4 * qd + 3] * inv)) << 16);
+          *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * qd) = make_uint2(lo, hi);
+        }
       if (nsplit == 1) {
-        const float inv = lh > 0.0f ? 1.0f / lh : 0.0f;
-        uint16_t* orow = out + (t * H + hd) * DV + 64 * ow + 4 * h;
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-          for (int qd = 0; qd < 4; ++qd) {
-            const f32x16& a = o[dt][ht];
-            const uint32_t lo = f32_to_bf16_bits(a[4 * qd] * inv) |
-                                (static_cast<uint32_t>(f32_to_bf16_bits(a[4 * qd + 1] * inv)) << 16);
-            const uint32_t hi = f32_to_bf16_bits(a[4 * qd + 2] * inv) |
-                                (static_cast<uint32_t>(f32_to_bf16_bits(a[4 * qd + 3] * inv)) << 16);
-            *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * qd) = make_uint2(lo, hi);
-          }
         if (lse && ow == 0 && h == 0)
           lse[t * H + hd] = lh > 0.0f ? (mh + __log2f(lh)) * 0.69314718055994531f : -INFINITY;
-      } else {
-        const int64_t slot = (t * nsplit + split) * H + hd;
-        float* orow = ws_o + slot * DV + 64 * ow + 4 * h;
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-          for (int qd = 0; qd < 4; ++qd)
-            *reinterpret_cast<float4*>(orow + 32 * dt + 8 * qd) =
-                make_float4(o[dt][ht][4 * qd], o[dt][ht][4 * qd + 1], o[dt][ht][4 * qd + 2],
-                            o[dt][ht][4 * qd + 3]);
-        if (ow == 0 && h == 0) {
-          ws_ml[2 * slot] = mh;
-          ws_ml[2 * slot + 1] = lh;
-        }
+      } else if (ow == 0 && h == 0) {
+        ws_ml[2 * slot] = mh;
+        ws_ml[2 * slot + 1] = lh;
       }
     }
   }
 }
 
-// Merge split partials of one (row, head): 128 threads x 4 dims.
-__global__ __launch_bounds__(128) void mla_combine_kernel(const float* __restrict__ ws_o,
+// Merge the slices' normalised partials of one (row, head): 128 threads x 4 dims. Slice s
+// (reference max m_s, row sum l_s) weighs l_s 2^(m_s - M), M the largest m_s.
+__global__ __launch_bounds__(128) void mla_combine_kernel(const uint16_t* __restrict__ ws_o,
                                                           const float* __restrict__ ws_ml,
                                                           int H, int nsplit,
                                                           uint16_t* __restrict__ out,
                                                           float* __restrict__ lse) {
   const int64_t t = blockIdx.x;
   const int head = blockIdx.y;
+  // every slice's (max, sum) and 4 outputs are loaded at once (at most MAX_SPLITS slices)
+  float2 ml[MAX_SPLITS];
+  uint2 v[MAX_SPLITS];
+#pragma unroll
+  for (int s = 0; s < MAX_SPLITS; ++s) {
+    if (s < nsplit) {
+      const int64_t slot = (t * nsplit + s) * H + head;
+      ml[s] = reinterpret_cast<const float2*>(ws_ml)[slot];
+      v[s] = reinterpret_cast<const uint2*>(ws_o + slot * DV)[threadIdx.x];
+    }
+  }
   float M = M_INIT;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ws_ml[2 * ((t * nsplit + s) * H + head)]);
+#pragma unroll
+  for (int s = 0; s < MAX_SPLITS; ++s)
+    if (s < nsplit) M = fmaxf(M, ml[s].x);
   float L = 0.0f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < nsplit; ++s) {
-    const int64_t slot = (t * nsplit + s) * H + head;
-    const float f = exp2f(ws_ml[2 * slot] - M);  // 0 for a slice without valid keys
-    L += ws_ml[2 * slot + 1] * f;
-    const float4 v = reinterpret_cast<const float4*>(ws_o + slot * DV)[threadIdx.x];
-    acc.x += v.x * f; acc.y += v.y * f; acc.z += v.z * f; acc.w += v.w * f;
+#pragma unroll
+  for (int s = 0; s < MAX_SPLITS; ++s) {
+    if (s < nsplit) {
+      const float f = ml[s].y * exp2f(ml[s].x - M);  // 0: no valid keys
+      L += f;
+      acc.x += bf16_bits_to_f32(static_cast<uint16_t>(v[s].x)) * f;
+      acc.y += bf16_bits_to_f32(static_cast<uint16_t>(v[s].x >> 16)) * f;
+      acc.z += bf16_bits_to_f32(static_cast<uint16_t>(v[s].y)) * f;
+      acc.w += bf16_bits_to_f32(static_cast<uint16_t>(v[s].y >> 16)) * f;
+    }
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   const uint32_t lo = f32_to_bf16_bits(acc.x * inv) | (static_cast<uint32_t>(f32_to_bf16_bits(acc.y * inv)) << 16);
@@ -613,15 +632,18 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(const float* __restric
 }
 
 constexpr int64_t TARGET_BLOCKS = 160;  // grids below this many blocks take more slices
+constexpr int64_t GRID_CUS = 256;       // compute units of the MI355X: one block each
 
-// Slices per row: at least ceil(k / 2048) (LDS index staging), then doubled while the
-// grid is below TARGET_BLOCKS blocks (one per CU) and each slice keeps >= 256
-// entries.
+// Slices per row: at least ceil(k / 2048) (LDS index staging). A grid below TARGET_BLOCKS
+// blocks takes as many slices as still fit one block per CU (at most 16, each with >= 256
+// entries).
 int choose_splits(int64_t blocks_per_split, int k) {
   int s = static_cast<int>(ceil_div(k, MAX_KPS));
-  while (s < 16 && blocks_per_split * s < TARGET_BLOCKS && ceil_div(k, 2 * s) >= 256)
-    s *= 2;
-  return s;
+  if (blocks_per_split * s >= TARGET_BLOCKS) return s;
+  int64_t fit = GRID_CUS / blocks_per_split;
+  fit = fit < MAX_SPLITS ? fit : MAX_SPLITS;
+  fit = fit < k / 256 ? fit : k / 256;
+  return fit > s ? static_cast<int>(fit) : s;
 }
 
 int64_t keys_per_split(int k, int s) { return ceil_div(ceil_div(k, s), KC) * KC; }
@@ -634,7 +656,7 @@ extern "C" size_t dsa_sparse_mla_workspace_size(int32_t T, int32_t H, int32_t k)
   if (T <= 0 || H <= 0 || k <= 0) return 0;
   const int s = choose_splits(static_cast<int64_t>(T) * ceil_div(H, HPB), k);
   if (s == 1) return 0;
-  return static_cast<size_t>(T) * s * H * (DV + 2) * sizeof(float);
+  return static_cast<size_t>(T) * s * H * (DV * sizeof(uint16_t) + 2 * sizeof(float));
 }
 
 namespace dsa {
@@ -652,8 +674,8 @@ dsa_status sparse_mla_launch(const char* name, const uint16_t* q, const void* kv
                              void* stream) {
   if (H < 16 || H > 128 || H % 16)
     return fail(DSA_ERR_UNSUPPORTED, "%s: H must be a multiple of 16 in [16, 128] (got %d)", name, H);
-  DSA_REQUIRE(k >= 1 && k <= 16 * MAX_KPS, "%s: k must be in [1, %d] (got %d)", name,
-              16 * MAX_KPS, k);
+  DSA_REQUIRE(k >= 1 && k <= MAX_SPLITS * MAX_KPS, "%s: k must be in [1, %d] (got %d)", name,
+              MAX_SPLITS * MAX_KPS, k);
   DSA_REQUIRE(topk_rows >= 0, "%s: topk_rows must be >= 0", name);
   DSA_REQUIRE(B >= 0 && T >= 0 && max_q_rows >= 0, "%s: negative size", name);
   DSA_REQUIRE((share_base == nullptr) == (num_accepted == nullptr),
@@ -676,14 +698,19 @@ dsa_status sparse_mla_launch(const char* name, const uint16_t* q, const void* kv
               "%s: workspace must be 16-byte aligned", name);
   const int kps = static_cast<int>(keys_per_split(k, s));
   const int nsplit = static_cast<int>(ceil_div(k, kps));
-  float* ws_o = static_cast<float*>(ws);
-  float* ws_ml = need ? ws_o + static_cast<size_t>(T) * nsplit * H * DV : nullptr;
+  uint16_t* ws_o = static_cast<uint16_t*>(ws);
+  float* ws_ml = need ? reinterpret_cast<float*>(ws_o + static_cast<size_t>(T) * nsplit * H * DV)
+                      : nullptr;
+  // one block per work item (slice, head group, row, request), XCD-ordered (see the kernel)
+  const int64_t nwork = static_cast<int64_t>(nsplit) * nhg * max_q_rows * B;
+  DSA_REQUIRE(nwork <= (int64_t{1} << 30), "%s: too many (row, head group, slice) blocks", name);
+  const int per_xcd = static_cast<int>(ceil_div(nwork, 8));
   const float c2 = sm_scale * 1.4426950408889634f;  // natural -> base-2 logits
   hipStream_t st = as_stream(stream);
-  hipLaunchKernelGGL(mla_decode_kernel<F8>,
-                     dim3((unsigned)(nsplit * nhg), (unsigned)max_q_rows, (unsigned)B), dim3(NT),
-                     0, st, q, kv, topk, share_base, num_accepted, q_row_offsets, kv_row_offsets,
-                     H, nhg, k, topk_rows, c2, nsplit, kps, out, lse, ws_o, ws_ml);
+  hipLaunchKernelGGL(mla_decode_kernel<F8>, dim3(static_cast<unsigned>(8 * per_xcd)), dim3(NT), 0,
+                     st, q, kv, topk, share_base, num_accepted, q_row_offsets, kv_row_offsets, H,
+                     nhg, k, topk_rows, c2, nsplit, kps, max_q_rows, static_cast<int>(nwork),
+                     per_xcd, out, lse, ws_o, ws_ml);
   dsa_status stt = check_launch(name);
   if (stt != DSA_OK || nsplit == 1) return stt;
   hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)T, (unsigned)H), dim3(128), 0, st, ws_o,

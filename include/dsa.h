@@ -288,7 +288,9 @@ size_t dsa_index_topk_workspace_size(int32_t B, int32_t T, int32_t max_q_rows, i
  *   without a share map; a share map entry outside [0, topk_rows) selects nothing)
  *   out [T, H, 512] bf16; lse [T, H] float32 or NULL
  * H must be a multiple of 16, at most 128.
- * Workspace: dsa_sparse_mla_workspace_size() bytes (split-K partials).
+ * Workspace: dsa_sparse_mla_workspace_size() bytes, 0 unless a row's list is cut into
+ * slices (small grids, or k > 2048): per (row, slice, head) the slice's normalised
+ * output in bf16 and its (max, sum) in float32, merged by a second launch.
  * Errors: DSA_ERR_INVALID_ARGUMENT, DSA_ERR_UNSUPPORTED,
  * DSA_ERR_WORKSPACE_TOO_SMALL.
  */

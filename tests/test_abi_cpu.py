@@ -40,14 +40,16 @@ def test_version_and_workspace_queries():
     assert lib.dsa_topk_workspace_size(4, 24, 262144, 2048, 0) == (24 * 4 * 2048 + 24 * 8192) * 4
     assert lib.dsa_topk_workspace_size(4, 24, 262144, 2048, 1) == (24 * 4 * 2048 + 24 * 8192) * 4 + 4 * 128 * 4
     assert lib.dsa_topk_workspace_size(3, 5, 100, 8, 1) == 16  # padded to 16 bytes
-    # split-K partials: T * splits * H * (512 + 2) floats, or none when one split suffices
+    # split-K partials: per (row, split, head) 512 bf16 outputs and a float32 (max, sum),
+    # or none when one split suffices
+    per = 512 * 2 + 2 * 4
     ws = lib.dsa_sparse_mla_workspace_size(192, 64, 2048)
-    assert ws == 0 or ws % (192 * 64 * 514 * 4) == 0
+    assert ws == 0 or ws % (192 * 64 * per) == 0
     # a split holds at most 2048 top-k entries: k = 2048 over many rows needs no partials,
     # k = 4096 needs two splits; few rows are split further (>= 256 entries per split)
     assert lib.dsa_sparse_mla_workspace_size(1024, 64, 2048) == 0
-    assert lib.dsa_sparse_mla_workspace_size(1024, 64, 4096) == 1024 * 2 * 64 * 514 * 4
-    assert lib.dsa_sparse_mla_workspace_size(16, 128, 2048) == 16 * 8 * 128 * 514 * 4
+    assert lib.dsa_sparse_mla_workspace_size(1024, 64, 4096) == 1024 * 2 * 64 * per
+    assert lib.dsa_sparse_mla_workspace_size(16, 128, 2048) == 16 * 8 * 128 * per
     # greedy accept: one (max, index) pair per 4096-entry vocabulary slice per row
     assert lib.greedy_accept_workspace_size(32, 5, 151552) == 32 * 6 * 37 * 8
     assert lib.greedy_accept_workspace_size(0, 5, 10) == 0

@@ -418,6 +418,36 @@ def test_sparse_mla_many_rows_split_lists_and_workspace_reuse(heads):
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
 
 
+@pytest.mark.parametrize("batch,rows,heads,ctx,topk,slices", [
+    (8, 5, 128, 3000, 2048, 3), (4, 6, 128, 3000, 2048, 5), (6, 6, 64, 3000, 2048, 7),
+    (1, 6, 16, 3000, 2048, 8), (1, 6, 16, 5000, 4096, 16)])
+def test_sparse_mla_slice_counts(batch, rows, heads, ctx, topk, slices):
+    # Small grids cut each row's list into as many slices as fit one block per CU (any
+    # count up to 16): the slices' bf16 partials are merged by the combine kernel.
+    _say(f"sparse_mla slices={slices} (T={batch * rows}, H={heads}, k={topk})")
+    w = W.replace(W.scaled(W.MTP5_VERIFY, ctx=ctx, batch=batch, topk=topk), rows=rows,
+                  mla_heads=heads)
+    lens = synth.context_lengths(w)
+    qo, ko = synth.q_row_offsets(w), synth.kv_row_offsets(lens)
+    m = synth.mla_inputs(w, lens)
+    idx = synth.random_topk(w, lens, qo, w.topk, pad_frac=0.1)
+    idx[3, : topk // 2] = -1           # a row whose first slices hold nothing
+    T = int(qo[-1])
+    need = api.sparse_mla_workspace_size(T, heads, w.topk)
+    assert need == T * slices * heads * (512 * 2 + 8), "the case does not take the slices it names"
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    u16 = lambda x: x.view(torch.uint16).numpy()
+    ref_o, ref_l = oracle.sparse_mla(u16(m["q"]), u16(m["kv"]), idx.numpy(), qo.numpy(),
+                                     ko.numpy(), w.sm_scale)
+    outs = []
+    for call in range(2):
+        out, lse = api.sparse_mla_decode(m["q"].to(DEV), m["kv"].to(DEV), idx.to(DEV), qo.to(DEV),
+                                         ko.to(DEV), w.rows, w.sm_scale, workspace=ws)
+        _say(f"  call {call}: worst err/bound = {mla_check(out, lse, ref_o, ref_l):.3f}")
+        outs.append((out.clone(), lse.clone()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
 def test_sparse_mla_dense_equals_full_visible_set():
     # k >= visible: sparse MLA over every visible position is dense causal attention
     _say("sparse_mla dense case")
