@@ -460,8 +460,9 @@ __device__ __forceinline__ i32x4 digit_plane(const uint32_t (&wd)[16], int p) {
 // wave takes one tile of 16 heads x 16 band keys per round, with the next round's key codes
 // already loading; the u_j max(d_j, 0) terms of a round go to LDS, and one thread per key
 // then adds them in ascending head order.
+template <class Lds>
 __device__ __forceinline__ double rescore_band(const RowRef& rr, const float* __restrict__ srow,
-                                               int nb, RefineLds& L, bool table_ready,
+                                               int nb, Lds& L, bool table_ready,
                                                float* band_sk, float* band_f32) {
   const Refine& rf = rr.rf;
   const int tid = threadIdx.x, lane = tid % 64;
@@ -1487,6 +1488,83 @@ __device__ __forceinline__ void refine_generic(const float* __restrict__ srow, i
   if (tid == 0 && status) status[rr.t] = refine_status(nb, worst, eps);
 }
 
+// ---------------------------------------------------------------------------------------
+// Long-row refine. Rows longer than FAST_MAX (up to LR_MAX_N positions) refine over three
+// more launches after the merge, so that the band, which massive exact ties can make
+// thousands of keys long, is classified and rescored by the whole GPU rather than by the
+// row's one block:
+//  - the merge kernel (one block per row) writes theta, eps and the band edges (LongRow);
+//  - topk_band_classify_kernel (LR_CLS positions per block) counts the kept keys and
+//    appends the band's positions (unordered) to the row's band list;
+//  - topk_band_rescore_kernel (one rescoring round of a row's band per block) writes the
+//    exact scores and the largest |I_f32 - I_exact|;
+//  - topk_band_finish_kernel (one block per row) picks the best `need` band keys by a radix
+//    select on (exact score desc, then position asc) and writes the kept and the chosen keys
+//    in ascending position order through LDS position bitmaps.
+// Longer rows keep the single-block refine (refine_generic) in the merge kernel.
+constexpr int64_t LR_MAX_N = int64_t{1} << 18;  // positions the finishing bitmaps cover
+constexpr int LR_CLS = 16384;                   // positions classified per block
+constexpr int LR_KPR_MIN = 32;                  // band keys per rescoring block at 128 heads
+constexpr int LR_ROUNDS = 2;                    // rescoring rounds per block
+constexpr int LR_RESCORE_X = BAND_CAP / (LR_KPR_MIN * LR_ROUNDS);  // rescoring blocks per row
+
+struct LongRow {  // per query row, in the workspace
+  double eps;
+  float theta, lo_f, hi_f;
+  int32_t state;             // 0: the row refines on this path; otherwise it does not
+  uint32_t nb;               // band keys found (atomic)
+  uint32_t kept;             // keys above the band (atomic)
+  unsigned long long worst;  // largest |I_f32 - I_exact| over the band, as double bits (atomic max)
+  uint32_t pad[2];
+};
+static_assert(sizeof(LongRow) == 48, "LongRow layout");
+
+struct LongRefine {   // kernel argument; rows == nullptr: no long-row path
+  LongRow* rows;      // [T]
+  int32_t* band_pos;  // [T, BAND_CAP] request-local positions
+  double* band_ex;    // [T, BAND_CAP] exact scores
+};
+
+// Long-row path, stage 1 (in the merge kernel, after the float32 selection is in out):
+// theta = the smallest selected score, eps and the band edges go to the row's LongRow, with
+// its counters cleared. pa / ps: refine_prefetch's partials; red: TK_WAVES doubles of LDS.
+__device__ __forceinline__ void long_row_open(const float* __restrict__ srow, int k,
+                                              const int32_t* __restrict__ out, const RowRef& rr,
+                                              LongRow& row, const double* pa, const float* ps,
+                                              double* red) {
+  const int tid = threadIdx.x;
+  constexpr int U = 8;  // loads in flight per thread
+  float th = __builtin_inff();
+  for (int i0 = tid; i0 < k; i0 += U * TK_THREADS) {
+    int32_t pp[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) pp[u] = i0 + u * TK_THREADS < k ? out[i0 + u * TK_THREADS] : -1;
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = pp[u] >= 0 ? srow[pp[u]] : __builtin_inff();
+#pragma unroll
+    for (int u = 0; u < U; ++u) th = fminf(th, v[u]);
+  }
+  th = static_cast<float>(-block_max_d(-static_cast<double>(th), red));
+  const double eps = refine_eps(rr.rf, th, pa, ps);
+  if (tid != 0) return;
+  row.nb = 0;
+  row.kept = 0;
+  row.worst = 0;
+  if (!__builtin_isfinite(th) || !__builtin_isfinite(eps)) {
+    row.state = 2;
+    if (rr.rf.status) rr.rf.status[rr.t] = -2;
+    return;
+  }
+  float lo_f, hi_f;
+  band_edges(th, eps, &lo_f, &hi_f);
+  row.eps = eps;
+  row.theta = th;
+  row.lo_f = lo_f;
+  row.hi_f = hi_f;
+  row.state = 0;
+}
+
 __device__ __forceinline__ RowRef row_ref(const Refine& rf, int64_t t, int b, int64_t kv_base) {
   RowRef rr;
   rr.rf = rf;
@@ -1561,7 +1639,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ q_off,
     const int64_t* __restrict__ kv_off, int64_t ld, int k, int nchunk, int64_t cstride,
     const int32_t* __restrict__ widx, const float* __restrict__ cand_s,
-    int32_t* __restrict__ topk, Refine rf) {
+    int32_t* __restrict__ topk, Refine rf, LongRefine lr) {
   __shared__ __attribute__((aligned(16))) TopkLds S;
   const int b = blockIdx.y, r = blockIdx.x;
   const RowInfo ri = load_row_info(q_off, kv_off, b);
@@ -1583,8 +1661,267 @@ __global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(
   if (rf.q_fp8 != nullptr) {
     refine_prefetch(rr, n, S.rf_a, S.rf_s);
     __syncthreads();
-    refine_generic(scores + t * ld, n, k, out, rr, *reinterpret_cast<RefineLds*>(S.regA), S.tmp,
-                   S.rf_a, S.rf_s);
+    if (lr.rows != nullptr && n <= LR_MAX_N) {
+      long_row_open(scores + t * ld, k, out, rr, lr.rows[t], S.rf_a, S.rf_s,
+                    reinterpret_cast<double*>(S.regA));
+    } else {
+      if (lr.rows != nullptr && threadIdx.x == 0) lr.rows[t].state = 1;
+      refine_generic(scores + t * ld, n, k, out, rr, *reinterpret_cast<RefineLds*>(S.regA), S.tmp,
+                     S.rf_a, S.rf_s);
+    }
+  }
+}
+
+// Long-row path, stage 2 (every position chunk of every long row): the kept keys are
+// counted and the band's positions appended to the row's list.
+__global__ __launch_bounds__(TK_THREADS) void topk_band_classify_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ q_off,
+    const int64_t* __restrict__ kv_off, int64_t ld, int ncls, LongRefine lr) {
+  __shared__ int32_t bpos[LR_CLS];
+  __shared__ uint32_t cnt[2], base_s;
+  const int c = static_cast<int>(blockIdx.x) % ncls, r = static_cast<int>(blockIdx.x) / ncls;
+  const int b = blockIdx.y;
+  const RowInfo ri = load_row_info(q_off, kv_off, b);
+  if (r >= ri.R) return;
+  const int64_t t = ri.t0 + r;
+  int64_t n = visible_count(ri, r);
+  if (n > ld) n = ld;
+  if (n <= FAST_MAX || n > LR_MAX_N) return;
+  const LongRow& row = lr.rows[t];
+  if (row.state != 0) return;
+  const int64_t c0 = static_cast<int64_t>(c) * LR_CLS;
+  if (c0 >= n) return;
+  const int nc = static_cast<int>(n - c0 < LR_CLS ? n - c0 : LR_CLS);
+  const float lo_f = row.lo_f, hi_f = row.hi_f;
+  const int tid = threadIdx.x;
+  if (tid < 2) cnt[tid] = 0;
+  __syncthreads();
+  const float* srow = scores + t * ld + c0;
+  uint32_t kept = 0;
+  auto classify = [&](float x, int i) {
+    if (x > hi_f) {
+      ++kept;
+    } else if (x >= lo_f) {
+      bpos[atomicAdd(&cnt[0], 1u)] = static_cast<int32_t>(c0 + i);
+    }
+  };
+  constexpr int PER = LR_CLS / 4 / TK_THREADS;  // float4 loads per thread, all in flight
+  const int n4 = nc / 4;
+  float4 v[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int i = tid + u * TK_THREADS;
+    v[u] = i < n4 ? reinterpret_cast<const float4*>(srow)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int i = tid + u * TK_THREADS;
+    if (i < n4) {
+      classify(v[u].x, 4 * i);
+      classify(v[u].y, 4 * i + 1);
+      classify(v[u].z, 4 * i + 2);
+      classify(v[u].w, 4 * i + 3);
+    }
+  }
+  if (tid < nc - 4 * n4) classify(srow[4 * n4 + tid], 4 * n4 + tid);
+  kept = wave_sum(kept);
+  if (tid % 64 == 0 && kept) atomicAdd(&cnt[1], kept);
+  __syncthreads();
+  LongRow& rw = lr.rows[t];
+  if (tid == 0) {
+    base_s = cnt[0] ? atomicAdd(&rw.nb, cnt[0]) : 0u;
+    if (cnt[1]) atomicAdd(&rw.kept, cnt[1]);
+  }
+  __syncthreads();
+  int32_t* dst = lr.band_pos + t * BAND_CAP;
+  for (uint32_t i = tid; i < cnt[0]; i += TK_THREADS)
+    if (base_s + i < static_cast<uint32_t>(BAND_CAP)) dst[base_s + i] = bpos[i];
+}
+
+// LDS of one rescoring round (the members rescore_band uses)
+struct RescoreLds {
+  double band_val[256 * LR_ROUNDS];
+  double terms[RS_TERMS];
+  uint32_t digits[256];
+  int32_t band_pos[256 * LR_ROUNDS];
+  double redd[TK_WAVES];
+  float sk[256 * LR_ROUNDS], f32[256 * LR_ROUNDS];
+};
+
+// Long-row path, stage 3: block x rescores band keys x KR .. x KR + KR - 1 of its row, KR =
+// LR_ROUNDS rounds of rescore_band (KPR = 256 / head tiles keys each; the next round's key
+// codes load during the current one).
+__global__ __launch_bounds__(TK_THREADS) void topk_band_rescore_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ q_off,
+    const int64_t* __restrict__ kv_off, int64_t ld, Refine rf, LongRefine lr) {
+  __shared__ __attribute__((aligned(16))) RescoreLds L;
+  const int r = static_cast<int>(blockIdx.x) / LR_RESCORE_X, b = blockIdx.y;
+  const RowInfo ri = load_row_info(q_off, kv_off, b);
+  if (r >= ri.R) return;
+  const int64_t t = ri.t0 + r;
+  int64_t n = visible_count(ri, r);
+  if (n > ld) n = ld;
+  if (n <= FAST_MAX || n > LR_MAX_N) return;
+  LongRow& row = lr.rows[t];
+  if (row.state != 0) return;
+  const int nb = static_cast<int>(row.nb);
+  if (nb > BAND_CAP) return;  // the finishing stage reports the overflow
+  const int HT = rf.H <= 16 ? 1 : rf.H <= 32 ? 2 : rf.H <= 64 ? 4 : 8;
+  const int KR = LR_ROUNDS * (256 / HT);
+  const int base = static_cast<int>(blockIdx.x % LR_RESCORE_X) * KR;
+  if (base >= nb) return;
+  const int cnt = nb - base < KR ? nb - base : KR;
+  const int32_t* src = lr.band_pos + t * BAND_CAP + base;
+  for (int i = threadIdx.x; i < cnt; i += TK_THREADS) L.band_pos[i] = src[i];
+  __syncthreads();
+  const double worst = rescore_band(row_ref(rf, t, b, ri.kv_base), scores + t * ld, cnt, L, false,
+                                    L.sk, L.f32);
+  double* ex = lr.band_ex + t * BAND_CAP + base;
+  for (int i = threadIdx.x; i < cnt; i += TK_THREADS) ex[i] = L.band_val[i];
+  if (threadIdx.x == 0)
+    atomicMax(&row.worst, static_cast<unsigned long long>(__double_as_longlong(worst)));
+}
+
+// Order-preserving 64-bit key of a double (larger value, larger key).
+__device__ __forceinline__ uint64_t order_key64(double x) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(x == 0.0 ? 0.0 : x));
+  return (u >> 63) ? ~u : (u | (uint64_t{1} << 63));
+}
+
+struct FinishLds {
+  uint64_t key[BAND_CAP];
+  int32_t pos[BAND_CAP];
+  uint32_t sel[LR_MAX_N / 32];   // positions taken
+  uint32_t tie[LR_MAX_N / 32];   // band positions tied with the selection's last exact score
+  uint32_t hist[256];
+  uint32_t tmp[2 * TK_WAVES];
+  uint64_t prefix;
+  uint32_t want;
+  uint32_t kept2;
+};
+
+// Ordered walk over the first nw words of a position bitmap: each thread takes a contiguous
+// run of words; f(position, rank) is called for every set bit, rank = its order among them.
+// Returns the number of set bits (to every thread).
+template <class F>
+__device__ __forceinline__ uint32_t bitmap_walk(const uint32_t* bits, int nw, uint32_t* tmp, F f) {
+  const int tid = threadIdx.x;
+  const int per = (nw + TK_THREADS - 1) / TK_THREADS;
+  const int w0 = tid * per, w1 = w0 + per < nw ? w0 + per : nw;
+  uint32_t c = 0;
+  for (int w = w0; w < w1; ++w) c += static_cast<uint32_t>(__popc(bits[w]));
+  uint32_t total;
+  uint32_t rank = block_excl_scan(c, tmp, &total);
+  for (int w = w0; w < w1; ++w) {
+    uint32_t x = bits[w];
+    while (x) {
+      const int bit = __builtin_ctz(x);
+      x &= x - 1u;
+      f(32 * w + bit, rank++);
+    }
+  }
+  return total;
+}
+
+// Long-row path, stage 4 (one block per long row).
+__global__ __launch_bounds__(TK_THREADS) void topk_band_finish_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ q_off,
+    const int64_t* __restrict__ kv_off, int64_t ld, int k, int32_t* __restrict__ topk,
+    int32_t* __restrict__ status, LongRefine lr) {
+  __shared__ __attribute__((aligned(16))) FinishLds F;
+  const int r = blockIdx.x, b = blockIdx.y;
+  const RowInfo ri = load_row_info(q_off, kv_off, b);
+  if (r >= ri.R) return;
+  const int64_t t = ri.t0 + r;
+  int64_t n = visible_count(ri, r);
+  if (n > ld) n = ld;
+  if (n <= FAST_MAX || n > LR_MAX_N) return;
+  const LongRow& row = lr.rows[t];
+  if (row.state != 0) return;
+  const int tid = threadIdx.x;
+  const int nb = static_cast<int>(row.nb);
+  const int kept = static_cast<int>(row.kept);
+  const int need = k - kept;
+  if (nb > BAND_CAP || need < 1 || need > nb) {  // uniform: keep the float32 selection
+    if (tid == 0 && status) status[t] = nb > BAND_CAP ? -1 : -2;
+    return;
+  }
+  const float* srow = scores + t * ld;
+  int32_t* out = topk + t * k;
+  const int nw = static_cast<int>((n + 31) / 32);
+  for (int i = tid; i < nb; i += TK_THREADS) {
+    F.key[i] = order_key64(lr.band_ex[t * BAND_CAP + i]);
+    F.pos[i] = lr.band_pos[t * BAND_CAP + i];
+  }
+  for (int w = tid; w < nw; w += TK_THREADS) {
+    F.sel[w] = 0u;
+    F.tie[w] = 0u;
+  }
+  if (tid == 0) {
+    F.prefix = 0;
+    F.want = static_cast<uint32_t>(need);
+    F.kept2 = 0;
+  }
+  __syncthreads();
+  // the need-th largest exact key, eight bits at a time from the top: bin 255 - d holds
+  // digit d, so that bin 0 holds the largest keys
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += TK_THREADS) F.hist[i] = 0u;
+    __syncthreads();
+    const uint64_t prefix = F.prefix;
+    for (int i0 = 0; i0 < nb; i0 += TK_THREADS) {  // wave-aggregated: exact ties share a bin
+      const int i = i0 + tid;
+      const uint64_t x = i < nb ? F.key[i] : 0;
+      const bool act = i < nb && (shift == 56 || (x >> (shift + 8)) == (prefix >> (shift + 8)));
+      hist_add(F.hist, act, 255u - static_cast<uint32_t>((x >> shift) & 255u));
+    }
+    __syncthreads();
+    if (tid < 64) {
+      uint32_t bin = 0, above = 0;
+      wave_select<256>(F.hist, F.want, &bin, &above);
+      if (tid == 0) {
+        F.prefix = prefix | (static_cast<uint64_t>(255u - bin) << shift);
+        F.want -= above;
+      }
+    }
+    __syncthreads();
+  }
+  const uint64_t thk = F.prefix;  // the need-th largest exact key; F.want of its ties are taken
+  const uint32_t want = F.want;
+  // band keys above it are taken, its ties wait for the position order
+  for (int i = tid; i < nb; i += TK_THREADS) {
+    const int32_t p = F.pos[i];
+    if (F.key[i] > thk) atomicOr(&F.sel[p >> 5], 1u << (p & 31));
+    else if (F.key[i] == thk) atomicOr(&F.tie[p >> 5], 1u << (p & 31));
+  }
+  // the kept keys: the float32 selection's entries above the band
+  const float hi_f = row.hi_f;
+  uint32_t kc = 0;
+  for (int i = tid; i < k; i += TK_THREADS) {
+    const int32_t p = out[i];
+    if (p >= 0 && srow[p] > hi_f) {
+      atomicOr(&F.sel[p >> 5], 1u << (p & 31));
+      ++kc;
+    }
+  }
+  kc = wave_sum(kc);
+  if (tid % 64 == 0 && kc) atomicAdd(&F.kept2, kc);
+  __syncthreads();
+  if (F.kept2 != static_cast<uint32_t>(kept)) {  // uniform; cannot happen for a correct selection
+    if (tid == 0 && status) status[t] = -3;
+    return;
+  }
+  // the first `want` ties in position order
+  bitmap_walk(F.tie, nw, F.tmp, [&](int p, uint32_t rank) {
+    if (rank < want) atomicOr(&F.sel[p >> 5], 1u << (p & 31));
+  });
+  __syncthreads();
+  const uint32_t total = bitmap_walk(F.sel, nw, F.tmp, [&](int p, uint32_t rank) {
+    if (rank < static_cast<uint32_t>(k)) out[rank] = p;
+  });
+  if (tid == 0 && status) {
+    const double worst = __longlong_as_double(static_cast<long long>(row.worst));
+    status[t] = total == static_cast<uint32_t>(k) ? refine_status(nb, worst, row.eps) : -3;
   }
 }
 
@@ -2054,6 +2391,16 @@ int64_t topk_chunk_bytes(int32_t T, int64_t max_kv_len, int32_t k) {
   return ((static_cast<int64_t>(T) * nc * k + 3) / 4 * 4 + static_cast<int64_t>(T) * topk_cstride(nc, k)) * 4;
 }
 int64_t topk_nsc(int64_t max_kv_len) { return max_kv_len > 0 ? ceil_div(max_kv_len, SC_CHUNK) : 1; }
+// Bytes of the refine's scale maxima (16-byte multiple).
+int64_t topk_kmax_bytes(int32_t B, int64_t max_kv_len) {
+  return (static_cast<int64_t>(B) * topk_nsc(max_kv_len) * 4 + 15) / 16 * 16;
+}
+// Bytes of the long-row refine: LongRow[T], band positions [T, BAND_CAP] and exact scores
+// [T, BAND_CAP] (grids with rows longer than FAST_MAX only).
+int64_t topk_long_bytes(int32_t T, int64_t max_kv_len) {
+  if (topk_nchunk(max_kv_len) <= 1) return 0;
+  return static_cast<int64_t>(T) * (static_cast<int64_t>(sizeof(LongRow)) + BAND_CAP * (4 + 8));
+}
 }  // namespace
 }  // namespace dsa
 
@@ -2062,7 +2409,7 @@ extern "C" size_t dsa_topk_workspace_size(int32_t B, int32_t T, int64_t max_kv_l
   using namespace dsa;
   if (B <= 0 || T <= 0 || k <= 0 || max_kv_len < 0) return 0;
   int64_t bytes = topk_chunk_bytes(T, max_kv_len, k);
-  if (refine) bytes += (static_cast<int64_t>(B) * topk_nsc(max_kv_len) * 4 + 15) / 16 * 16;
+  if (refine) bytes += topk_kmax_bytes(B, max_kv_len) + topk_long_bytes(T, max_kv_len);
   return static_cast<size_t>(bytes);
 }
 
@@ -2103,9 +2450,13 @@ extern "C" dsa_status dsa_topk(const float* scores, int64_t score_ld,
               "dsa_topk: ws must be 16-byte aligned");
   const int64_t nchunk = topk_nchunk(max_kv_len);
   DSA_REQUIRE(max_q_rows * nchunk <= 0x7FFFFFFF, "dsa_topk: too many chunks");
+  DSA_REQUIRE(static_cast<int64_t>(max_q_rows) * (LR_MAX_N / LR_CLS > LR_RESCORE_X ? LR_MAX_N / LR_CLS
+                                                                                 : LR_RESCORE_X) <= 0x7FFFFFFF,
+              "dsa_topk: max_q_rows too large");
   const int64_t chunk_bytes = topk_chunk_bytes(T, max_kv_len, k);
   hipStream_t st = as_stream(stream);
   Refine rf{};
+  LongRefine lr{nullptr, nullptr, nullptr};
   if (refine) {
     const int64_t nsc = topk_nsc(max_kv_len);
     DSA_REQUIRE(nsc <= 65535, "dsa_topk: max_kv_len too large for the refine");
@@ -2122,6 +2473,13 @@ extern "C" dsa_status dsa_topk(const float* scores, int64_t score_ld,
     rf.nsc = static_cast<int>(nsc);
     hipLaunchKernelGGL(topk_scale_max_kernel, dim3((unsigned)nsc, (unsigned)B), dim3(256), 0, st,
                        refine->k_scale, kv_row_offsets, (int)nsc, const_cast<float*>(rf.kmax));
+    if (nchunk > 1) {
+      uint8_t* p = static_cast<uint8_t*>(ws) + chunk_bytes + topk_kmax_bytes(B, max_kv_len);
+      lr.rows = reinterpret_cast<LongRow*>(p);
+      lr.band_pos = reinterpret_cast<int32_t*>(p + static_cast<int64_t>(T) * sizeof(LongRow));
+      lr.band_ex = reinterpret_cast<double*>(p + static_cast<int64_t>(T) * sizeof(LongRow) +
+                                             static_cast<int64_t>(T) * BAND_CAP * 4);
+    }
   }
   dim3 grid((unsigned)max_q_rows, (unsigned)B);
   if (nchunk > 1) {
@@ -2132,7 +2490,19 @@ extern "C" dsa_status dsa_topk(const float* scores, int64_t score_ld,
                        dim3(TK_THREADS), 0, st, scores, score_ld, q_row_offsets, kv_row_offsets, k,
                        (int)nchunk, cstride, widx, cand_s, topk, rf);
     hipLaunchKernelGGL(topk_merge_kernel, grid, dim3(TK_THREADS), 0, st, scores, q_row_offsets,
-                       kv_row_offsets, score_ld, k, (int)nchunk, cstride, widx, cand_s, topk, rf);
+                       kv_row_offsets, score_ld, k, (int)nchunk, cstride, widx, cand_s, topk, rf, lr);
+    if (lr.rows) {
+      const int64_t ncls = ceil_div(max_kv_len < LR_MAX_N ? max_kv_len : LR_MAX_N, LR_CLS);
+      hipLaunchKernelGGL(topk_band_classify_kernel,
+                         dim3((unsigned)(ncls * max_q_rows), (unsigned)B), dim3(TK_THREADS), 0, st,
+                         scores, q_row_offsets, kv_row_offsets, score_ld, (int)ncls, lr);
+      hipLaunchKernelGGL(topk_band_rescore_kernel,
+                         dim3((unsigned)(static_cast<int64_t>(LR_RESCORE_X) * max_q_rows), (unsigned)B),
+                         dim3(TK_THREADS), 0, st, scores, q_row_offsets, kv_row_offsets, score_ld, rf,
+                         lr);
+      hipLaunchKernelGGL(topk_band_finish_kernel, grid, dim3(TK_THREADS), 0, st, scores,
+                         q_row_offsets, kv_row_offsets, score_ld, k, topk, rf.status, lr);
+    }
   } else {
     hipLaunchKernelGGL(topk_kernel, grid, dim3(TK_THREADS), 0, st, scores, score_ld, q_row_offsets,
                        kv_row_offsets, k, topk, rf);

@@ -216,10 +216,12 @@ typedef struct dsa_topk_refine {
  * Rows of up to 65536 visible scores take one block each. When max_kv_len
  * exceeds 65536, every row is first cut into 65536-position chunks whose own
  * top-k are selected in parallel (the row's top-k lies in their union), then
- * merged.
+ * merged; with the refine, rows of up to 2^18 positions then classify and
+ * rescore their band over many blocks (three more launches) before one block
+ * per row ranks it.
  * Workspace: dsa_topk_workspace_size(B, T, max_kv_len, k, refine != NULL)
  * bytes, 16-byte aligned (0 bytes for rows of at most 65536 positions without a
- * refine; ws may then be NULL).
+ * refine; ws may then be NULL). Its contents need no initialisation.
  * Errors: DSA_ERR_INVALID_ARGUMENT (k < 1, k > 8192, refine with k > 4096,
  * D_I not 64/128, H_I not in [1, 128], ...), DSA_ERR_WORKSPACE_TOO_SMALL.
  */

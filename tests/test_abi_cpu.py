@@ -38,7 +38,10 @@ def test_version_and_workspace_queries():
     assert lib.dsa_topk_workspace_size(32, 192, 65536, 2048, 1) == 32 * 32 * 4
     # 262144-position rows: 4 chunks of 2048 indices, then compact scores and positions
     assert lib.dsa_topk_workspace_size(4, 24, 262144, 2048, 0) == (24 * 4 * 2048 + 24 * 8192) * 4
-    assert lib.dsa_topk_workspace_size(4, 24, 262144, 2048, 1) == (24 * 4 * 2048 + 24 * 8192) * 4 + 4 * 128 * 4
+    # with the refine: the scale maxima, then per row the long-row refine's record (48
+    # bytes), band positions and exact band scores (4096 x (4 + 8) bytes)
+    assert lib.dsa_topk_workspace_size(4, 24, 262144, 2048, 1) == (
+        (24 * 4 * 2048 + 24 * 8192) * 4 + 4 * 128 * 4 + 24 * (48 + 4096 * 12))
     assert lib.dsa_topk_workspace_size(3, 5, 100, 8, 1) == 16  # padded to 16 bytes
     # split-K partials: per (row, split, head) 512 bf16 outputs and a float32 (max, sum),
     # or none when one split suffices

@@ -214,6 +214,41 @@ def test_topk_long_rows_chunked(levels):
             assert np.array_equal(got[t], ref), f"k={k} row {t} (visible {n})"
 
 
+@pytest.mark.parametrize("ctx,batch,rows,topk", [(100000, 2, 3, 2048), (100000, 2, 3, 512),
+                                                  (300000, 1, 2, 512)])
+def test_refined_topk_long_rows(ctx, batch, rows, topk):
+    # Rows above 65536 positions: the chunked float32 selection, then the refine. Up to 2^18
+    # positions the band is classified and rescored over many blocks and ranked by a radix
+    # select; longer rows refine in one block. 1% identical spike keys per request: with
+    # top-k 2048 they are all kept above a small band, with 512 every spike ties in the band
+    # (1000 and 3000 keys) and the lowest positions must win. Every row against the oracle.
+    _say(f"refined top-k long rows ctx={ctx} topk={topk}")
+    w = W.replace(W.scaled(W.LONG_CTX, ctx=ctx, batch=batch, topk=topk), rows=rows)
+    case = Case(w, with_mla=False, with_accept=False)
+    gi = gpu_indexer(case)
+    qc, qs, kc, ks, ko = oracle_quant(case)
+    rows_all = np.arange(case.T)
+    ref_s = oracle.index_score(qc, qs, case.host("w_f32"), kc, ks, case.qo.numpy(), ko,
+                               rows=rows_all, width=case.max_kv)
+    nvis = np.array([case.visible(int(t)) for t in rows_all])
+    assert nvis.min() > 65536
+    ref_k = oracle.topk(ref_s, nvis, w.topk)
+    ra = refine_args(gi, case)
+    ws = torch.zeros(api.topk_workspace_size(w.batch, case.T, case.max_kv, w.topk, True),
+                     dtype=torch.uint8, device=DEV)
+    for call in range(2):  # the workspace is reused as it comes
+        got = api.topk(gi["scores"], case.qo_d, case.ko_d, w.rows, case.max_kv, w.topk,
+                       refine=ra, workspace=ws)
+        st = ra["status"].cpu().numpy()
+        _say(f"  call {call}: band sizes {st.tolist()}")
+        assert st.min() >= 0
+        assert np.array_equal(got.cpu().numpy(), ref_k)
+    if topk < len(case.spike_pos[0]):
+        for t in rows_all:  # every spike ties: the lowest spike positions
+            b = int(t) // w.rows
+            assert list(got[t].cpu().numpy()) == list(case.spike_pos[b][:w.topk].numpy())
+
+
 @pytest.mark.parametrize("cluster", [2500, 600, 0])
 def test_topk_identical_clusters_across_row_lengths(cluster):
     # Rows at each register-path size class (up to 8192, 16384 and 65536 positions, with
