@@ -1505,8 +1505,11 @@ __device__ __forceinline__ void refine_generic(const float* __restrict__ srow, i
 constexpr int64_t LR_MAX_N = int64_t{1} << 18;  // positions the finishing bitmaps cover
 constexpr int LR_CLS = 16384;                   // positions classified per block
 constexpr int LR_KPR_MIN = 32;                  // band keys per rescoring block at 128 heads
-constexpr int LR_ROUNDS = 2;                    // rescoring rounds per block
-constexpr int LR_RESCORE_X = BAND_CAP / (LR_KPR_MIN * LR_ROUNDS);  // rescoring blocks per row
+// Rescoring rounds per block: a block's first round waits on a chain of dependent loads
+// (band positions, then scattered key rows, scales and scores) that costs several times a
+// later round, whose key codes load during the previous one, so a block takes five.
+constexpr int LR_ROUNDS = 5;
+constexpr int LR_RESCORE_X = (BAND_CAP + LR_KPR_MIN * LR_ROUNDS - 1) / (LR_KPR_MIN * LR_ROUNDS);
 
 struct LongRow {  // per query row, in the workspace
   double eps;
