@@ -48,6 +48,9 @@ KERNELS = {
     "topk_scale_max_kernel": ("topk", "topk.hip"),
     "topk_chunk_kernel": ("topk", "topk.hip"),
     "topk_merge_kernel": ("topk", "topk.hip"),
+    "topk_band_classify_kernel": ("topk", "topk.hip"),
+    "topk_band_rescore_kernel": ("topk", "topk.hip"),
+    "topk_band_finish_kernel": ("topk", "topk.hip"),
     "topk_kernel": ("topk", "topk.hip"),
     "sample_tau_kernel": ("index_topk", "index_score.hip"),
     "fused_select_kernel": ("index_topk", "index_score.hip"),
