@@ -249,6 +249,22 @@ def test_refined_topk_long_rows(ctx, batch, rows, topk):
             assert list(got[t].cpu().numpy()) == list(case.spike_pos[b][:w.topk].numpy())
 
 
+def test_refined_topk_long_rows_band_overflow():
+    # 5% identical spike keys in 100K-position rows: every row's band holds 5000 exact ties,
+    # more than the refine rescores (4096). The row reports -1 and keeps the float32
+    # selection, which ties resolve by position just as the exact order does.
+    _say("refined top-k long rows, band overflow")
+    w = W.replace(W.scaled(W.LONG_CTX, ctx=100000, batch=1, topk=512), rows=2, spike_frac=0.05)
+    case = Case(w, with_mla=False, with_accept=False)
+    gi = gpu_indexer(case)
+    ra = refine_args(gi, case)
+    got = api.topk(gi["scores"], case.qo_d, case.ko_d, w.rows, case.max_kv, w.topk, refine=ra)
+    assert ra["status"].cpu().tolist() == [-1, -1]
+    assert torch.equal(got, gi["topk"])
+    for t in range(case.T):
+        assert list(got[t].cpu().numpy()) == list(case.spike_pos[0][:w.topk].numpy())
+
+
 @pytest.mark.parametrize("cluster", [2500, 600, 0])
 def test_topk_identical_clusters_across_row_lengths(cluster):
     # Rows at each register-path size class (up to 8192, 16384 and 65536 positions, with
