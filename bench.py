@@ -102,6 +102,9 @@ class Inputs:
         # writes the verify rows' keys and latent rows again (cache rows `dst`)
         self.dst = synth.verify_cache_rows(lengths, w.rows).to(dev)
         self.k_fp8, self.k_scale = api.quantize_fp8(ix["k"])
+        # the key-scale table kept beside the index cache (the refine's eps reads it); each
+        # step's cache write raises its entries for the rows it writes
+        self.k_smax = api.key_scale_max(self.k_scale)
         self.k_new = ix["k"][self.dst].contiguous()
         self.k_f32_sample = ix["k"][: lengths[0]].cpu() if copy == 0 else None
         del ix
@@ -328,10 +331,10 @@ def main():
         mark()
         if not fp8:
             api.verify_cache_write(inp.k_new, inp.dst, inp.k_fp8, inp.k_scale, inp.latent_new, inp.kv,
-                                   q=inp.q_f32, q_fp8=qc, q_scale=qs)
+                                   q=inp.q_f32, q_fp8=qc, q_scale=qs, k_scale_max=inp.k_smax)
         else:  # index keys and queries, then the verify rows' latent rows packed to FP8
             api.verify_cache_write(inp.k_new, inp.dst, inp.k_fp8, inp.k_scale, q=inp.q_f32, q_fp8=qc,
-                                   q_scale=qs)
+                                   q_scale=qs, k_scale_max=inp.k_smax)
             api.mla_fp8_pack(inp.latent_new, inp.kv8, dst_rows=inp.dst)
         mark()
         if fused:
@@ -343,7 +346,8 @@ def main():
             api.index_score(qc, qs, inp.w, inp.k_fp8, inp.k_scale, qo, ko, w.rows, max_kv, scores=scores)
             mark()
             rf = (dict(q_fp8=qc, q_scale=qs, w=inp.w, k_fp8=inp.k_fp8, k_scale=inp.k_scale,
-                       status=status, err_scale=args.err_scale) if refine else None)
+                       status=status, err_scale=args.err_scale, k_scale_max=inp.k_smax)
+                  if refine else None)
             api.topk(scores, qo, ko, w.rows, max_kv, w.topk, out=topk, refine=rf, workspace=ws_tk)
             mark()
         mla(inp.q_mla, inp, topk, qo, w.rows, out, lse, ws_mla)
@@ -365,7 +369,8 @@ def main():
                             scores=scores1)
             api.topk(scores1, qo1, ko, 1, max_kv, w.topk, out=top1, workspace=ws_tk1,
                      refine=dict(q_fp8=qc1, q_scale=qs1, w=ixd["w"], k_fp8=inp.k_fp8,
-                                 k_scale=inp.k_scale, status=status1, err_scale=args.err_scale))
+                                 k_scale=inp.k_scale, status=status1, err_scale=args.err_scale,
+                                 k_scale_max=inp.k_smax))
             mla(qd, inp, top1, qo1, 1, out1, lse1, ws1)
         if inp.q_draft:
             mark()

@@ -15,16 +15,19 @@ P = ctypes.c_void_p
 I32, I64, F32, SZ = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 
 class TopkRefine(ctypes.Structure):
-    """dsa_topk_refine of include/dsa.h (device pointers, head count and width, error scale)."""
+    """dsa_topk_refine of include/dsa.h (device pointers, head count and width, error scale,
+    optional key-scale table)."""
     _fields_ = [("q_fp8", P), ("q_scale", P), ("w", P), ("k_fp8", P), ("k_scale", P),
-                ("H_I", I32), ("D_I", I32), ("err_scale", ctypes.c_double), ("status", P)]
+                ("H_I", I32), ("D_I", I32), ("err_scale", ctypes.c_double), ("status", P),
+                ("k_scale_max", P), ("k_scale_max_len", I64)]
 
 
 SIGNATURES = {
     "dsa_abi_version": ([], ctypes.c_int),
     "dsa_last_error": ([], ctypes.c_char_p),
     "dsa_quantize_fp8": ([P, I64, I32, P, P, P], ctypes.c_int),
-    "dsa_verify_cache_write": ([P, P, P, I32, I32, P, P, P, P, I32, P, P, P], ctypes.c_int),
+    "dsa_verify_cache_write": ([P, P, P, I32, I32, P, P, P, P, I32, P, P, P, P], ctypes.c_int),
+    "dsa_key_scale_max": ([P, I64, I64, I64, P, P], ctypes.c_int),
     "dsa_index_score": ([P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I64, P, I64, P],
                         ctypes.c_int),
     "dsa_topk": ([P, I64, P, P, I32, I32, I32, I64, I32, P, P, P, SZ, P], ctypes.c_int),

@@ -77,10 +77,33 @@ def quantize_fp8(x: torch.Tensor, out: torch.Tensor | None = None,
     return out, scale
 
 
+KEY_SCALE_CHUNK = 2048  # cache rows per entry of the key-scale table (DSA_KEY_SCALE_CHUNK)
+
+
+def key_scale_table_len(N: int) -> int:
+    return (N + KEY_SCALE_CHUNK - 1) // KEY_SCALE_CHUNK
+
+
+def key_scale_max(k_scale, out: torch.Tensor | None = None, row_begin: int = 0,
+                  row_end: int | None = None):
+    """The key-scale table [ceil(N / 2048)] float32: entry c = the largest scale of cache rows
+    2048c .. 2048c + 2047 (every chunk that meets [row_begin, row_end) is recomputed)."""
+    _dev(k_scale, "k_scale", torch.float32)
+    N = k_scale.numel()
+    if out is None:
+        out = torch.zeros(key_scale_table_len(N), dtype=torch.float32, device=k_scale.device)
+    _dev(out, "out", torch.float32)
+    _shape(out, "out", (key_scale_table_len(N),))
+    _check(_lib.load().dsa_key_scale_max(_p(k_scale), N, row_begin,
+                                         N if row_end is None else row_end, _p(out), _stream()))
+    return out
+
+
 def verify_cache_write(k_new, dst_rows, k_cache, k_scale, latent_new=None, kv_cache=None,
-                       q=None, q_fp8=None, q_scale=None):
+                       q=None, q_fp8=None, q_scale=None, k_scale_max=None):
     """The verify rows' new index keys (quantised) and latent rows into the caches at
-    dst_rows, and optionally the queries quantised into q_fp8/q_scale, in one launch."""
+    dst_rows, and optionally the queries quantised into q_fp8/q_scale, in one launch.
+    k_scale_max: the key-scale table (key_scale_max) to keep up to date, or None."""
     _dev(k_new, "k_new", torch.float32)
     _dev(dst_rows, "dst_rows", torch.int64)
     _dev(k_cache, "k_cache", torch.uint8)
@@ -107,9 +130,12 @@ def verify_cache_write(k_new, dst_rows, k_cache, k_scale, latent_new=None, kv_ca
             q_scale = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
         _dev(q_fp8, "q_fp8", torch.uint8)
         _dev(q_scale, "q_scale", torch.float32)
+    if k_scale_max is not None:
+        _dev(k_scale_max, "k_scale_max", torch.float32)
+        _shape(k_scale_max, "k_scale_max", (key_scale_table_len(k_scale.numel()),))
     _check(_lib.load().dsa_verify_cache_write(
         _p(k_new), _p(latent_new), _p(dst_rows), T, D, _p(k_cache), _p(k_scale), _p(kv_cache),
-        _p(q), H, _p(q_fp8), _p(q_scale), _stream()))
+        _p(q), H, _p(q_fp8), _p(q_scale), _p(k_scale_max), _stream()))
     return q_fp8, q_scale
 
 
@@ -147,7 +173,8 @@ def topk(scores, q_row_offsets, kv_row_offsets, max_q_rows: int, max_kv_len: int
     """Per-row top-k positions [T, k] (ascending, -1 padded).
 
     refine: the scored FP8 inputs, dict(q_fp8, q_scale, w, k_fp8, k_scale) plus optional
-    err_scale (float) and status (int32 [T]); the selection then follows the exact scores
+    err_scale (float), status (int32 [T]) and k_scale_max (the key-scale table of
+    key_scale_max over k_scale); the selection then follows the exact scores
     (exact-boundary refine, see dsa_topk in include/dsa.h).
     """
     _dev(scores, "scores", torch.float32)
@@ -178,9 +205,15 @@ def topk(scores, q_row_offsets, kv_row_offsets, max_q_rows: int, max_kv_len: int
         if st is not None:
             _dev(st, "status", torch.int32)
             _shape(st, "status", (T,))
+        ktab = refine.get("k_scale_max")
+        if ktab is not None:
+            _dev(ktab, "k_scale_max", torch.float32)
+            if ktab.dim() != 1 or ktab.numel() < 1:
+                raise ValueError("k_scale_max must be a non-empty 1-d table")
         rf = _lib.TopkRefine(_p(q), _p(refine["q_scale"]), _p(refine["w"]), _p(refine["k_fp8"]),
                              _p(refine["k_scale"]), q.shape[1], q.shape[2],
-                             float(refine.get("err_scale", 0.0)), _p(st))
+                             float(refine.get("err_scale", 0.0)), _p(st), _p(ktab),
+                             0 if ktab is None else ktab.numel())
     wsb = lib.dsa_topk_workspace_size(B, T, max_kv_len, k, 1 if refine is not None else 0)
     ws = workspace
     if ws is None and wsb:

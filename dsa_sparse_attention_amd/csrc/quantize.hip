@@ -46,7 +46,8 @@ template <int D>
 __device__ __forceinline__ void quantize_vector(const float* __restrict__ src, bool live,
                                                 int lane_in_vec, float rsqrt_d,
                                                 uint8_t* __restrict__ codes,
-                                                float* __restrict__ scale) {
+                                                float* __restrict__ scale,
+                                                unsigned int* smax = nullptr) {
   constexpr int LPV = D / 4;  // lanes per vector
   float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
   if (live) y = reinterpret_cast<const float4*>(src)[lane_in_vec];
@@ -74,7 +75,11 @@ __device__ __forceinline__ void quantize_vector(const float* __restrict__ src, b
   uint32_t packed = e4m3_rne_sat(e0 / s) | (e4m3_rne_sat(e1 / s) << 8) |
                     (e4m3_rne_sat(e2 / s) << 16) | (e4m3_rne_sat(e3 / s) << 24);
   reinterpret_cast<uint32_t*>(codes)[lane_in_vec] = packed;
-  if (lane_in_vec == 0) *scale = s;
+  if (lane_in_vec == 0) {
+    *scale = s;
+    // s > 0, so its bits order as the value does
+    if (smax) atomicMax(smax, __float_as_uint(s));
+  }
 }
 
 template <int D>
@@ -100,8 +105,9 @@ __global__ __launch_bounds__(256) void verify_write_kernel(
     const float* __restrict__ q, int64_t nq, uint8_t* __restrict__ q_fp8,
     float* __restrict__ q_scale, const float* __restrict__ k_new,
     const int64_t* __restrict__ dst_rows, int T, uint8_t* __restrict__ k_cache,
-    float* __restrict__ k_scale, const uint16_t* __restrict__ latent_new,
-    uint16_t* __restrict__ kv_cache, int nbq, int nbk, float rsqrt_d) {
+    float* __restrict__ k_scale, unsigned int* __restrict__ k_scale_max,
+    const uint16_t* __restrict__ latent_new, uint16_t* __restrict__ kv_cache, int nbq, int nbk,
+    float rsqrt_d) {
   constexpr int LPV = D / 4;
   const int blk = blockIdx.x;
   if (blk < nbq + nbk) {
@@ -114,7 +120,8 @@ __global__ __launch_bounds__(256) void verify_write_kernel(
     } else {
       const int64_t d = live ? dst_rows[vv] : 0;
       quantize_vector<D>(k_new + vv * D, live, threadIdx.x % LPV, rsqrt_d, k_cache + d * D,
-                         k_scale + d);
+                         k_scale + d,
+                         k_scale_max ? k_scale_max + d / DSA_KEY_SCALE_CHUNK : nullptr);
     }
     return;
   }
@@ -216,7 +223,7 @@ extern "C" dsa_status dsa_verify_cache_write(const float* k_new, const uint16_t*
                                              const int64_t* dst_rows, int32_t T, int32_t D_I,
                                              uint8_t* k_cache, float* k_scale, uint16_t* kv_cache,
                                              const float* q, int32_t H_I, uint8_t* q_fp8,
-                                             float* q_scale, void* stream) {
+                                             float* q_scale, float* k_scale_max, void* stream) {
   using namespace dsa;
   DSA_REQUIRE(T >= 0, "dsa_verify_cache_write: T must be >= 0 (got %d)", T);
   if (D_I != 64 && D_I != 128)
@@ -226,6 +233,8 @@ extern "C" dsa_status dsa_verify_cache_write(const float* k_new, const uint16_t*
   DSA_REQUIRE(!latent_new == !kv_cache, "dsa_verify_cache_write: latent_new and kv_cache go together");
   DSA_REQUIRE(!q || (q_fp8 && q_scale && H_I >= 1),
               "dsa_verify_cache_write: q needs q_fp8, q_scale and H_I >= 1");
+  DSA_REQUIRE((reinterpret_cast<uintptr_t>(k_scale_max) & 3) == 0,
+              "dsa_verify_cache_write: k_scale_max must be 4-byte aligned");
   DSA_REQUIRE((reinterpret_cast<uintptr_t>(k_new) & 15) == 0 &&
                   (reinterpret_cast<uintptr_t>(k_cache) & 3) == 0 &&
                   (!q || ((reinterpret_cast<uintptr_t>(q) & 15) == 0 &&
@@ -243,11 +252,13 @@ extern "C" dsa_status dsa_verify_cache_write(const float* k_new, const uint16_t*
   const dim3 grid(static_cast<unsigned>(nbq + nbk + nbl));
   if (D_I == 128)
     hipLaunchKernelGGL(verify_write_kernel<128>, grid, dim3(256), 0, as_stream(stream), q, nq, q_fp8,
-                       q_scale, k_new, dst_rows, T, k_cache, k_scale, latent_new, kv_cache,
+                       q_scale, k_new, dst_rows, T, k_cache, k_scale,
+                       reinterpret_cast<unsigned int*>(k_scale_max), latent_new, kv_cache,
                        static_cast<int>(nbq), static_cast<int>(nbk), rsqrt_d);
   else
     hipLaunchKernelGGL(verify_write_kernel<64>, grid, dim3(256), 0, as_stream(stream), q, nq, q_fp8,
-                       q_scale, k_new, dst_rows, T, k_cache, k_scale, latent_new, kv_cache,
+                       q_scale, k_new, dst_rows, T, k_cache, k_scale,
+                       reinterpret_cast<unsigned int*>(k_scale_max), latent_new, kv_cache,
                        static_cast<int>(nbq), static_cast<int>(nbk), rsqrt_d);
   return check_launch("dsa_verify_cache_write");
 }

@@ -255,11 +255,14 @@ __device__ __forceinline__ void hist_add(uint32_t* h, bool act, uint32_t bin) {
 //    over them marks the kept keys in a position bitmap and lists the band.
 //  - Every other path (rows whose sample missed, rows longer than 64K) runs the generic
 //    refine after its float32 selection is written: one more read of the row.
-// eps needs the largest key scale among the row's visible keys; a pre-pass stores the
-// maximum of every SC_CHUNK consecutive scales of each request, so no row rescans them.
+// eps needs the largest key scale among the row's visible keys (an upper bound of it serves
+// too: the band only widens). No row rescans them: either the caller keeps a table of the
+// maxima of every SC_CHUNK consecutive cache rows (dsa_key_scale_max, updated by the cache
+// write), or a pre-pass stores the maximum of every SC_CHUNK scales of each request.
 constexpr int BAND_CAP = 4096;   // band keys rescored per row
 constexpr int RF_MAXK = 4096;    // k supported by the refine
 constexpr int SC_CHUNK = 2048;   // key scales per stored maximum
+static_assert(SC_CHUNK == DSA_KEY_SCALE_CHUNK, "the caller's table uses the header's chunk");
 
 struct Refine {  // kernel argument; q_fp8 == nullptr: no refine
   const uint8_t* q_fp8;
@@ -267,11 +270,14 @@ struct Refine {  // kernel argument; q_fp8 == nullptr: no refine
   const float* w;
   const uint8_t* k_fp8;
   const float* k_scale;
-  const float* kmax;  // [B, nsc] maxima of SC_CHUNK key scales each, or nullptr: smax_given
+  const float* kmax;  // [B, nsc] maxima of SC_CHUNK key scales each, or nullptr
+  const float* kglob; // maxima of SC_CHUNK consecutive cache rows' scales (kept by the
+                      // caller), or nullptr
+  int64_t kglob_len;  // entries of kglob
   int32_t* status;    // [T] or nullptr
   double C;
   int H, D, nsc;
-  float smax_given;   // the row's largest visible key scale when kmax is nullptr
+  float smax_given;   // the row's largest visible key scale when kmax and kglob are nullptr
 };
 
 struct RowRef {  // one row of a refine
@@ -357,7 +363,16 @@ __device__ __forceinline__ void refine_prefetch(const RowRef& rr, int64_t n, dou
     }
   }
   float sm = 0.0f;
-  if (rf.kmax) {
+  if (rf.kglob) {
+    // the table entries of cache rows kv_base .. kv_base + n - 1; a row outside the table
+    // makes eps infinite (the float32 selection is kept)
+    if (n > 0) {
+      const int64_t c0 = rr.kv_base >= 0 ? rr.kv_base / SC_CHUNK : -1;
+      const int64_t c1 = rr.kv_base >= 0 ? (rr.kv_base + n - 1) / SC_CHUNK : -1;
+      for (int64_t c = c0 + tid; c <= c1; c += TK_THREADS)
+        sm = fmaxf(sm, c >= 0 && c < rf.kglob_len ? rf.kglob[c] : __builtin_inff());
+    }
+  } else if (rf.kmax) {
     int nc = static_cast<int>((n + SC_CHUNK - 1) / SC_CHUNK);
     if (nc > rf.nsc) nc = rf.nsc;  // rows are clipped to the score stride; stay in the table
     for (int c = tid; c < nc; c += TK_THREADS)
@@ -1962,6 +1977,30 @@ __global__ __launch_bounds__(256) void topk_scale_max_kernel(const float* __rest
 
 
 
+// Key-scale table kept beside the cache: kglob[c] = the largest |k_scale| of cache rows
+// [c SC_CHUNK, (c+1) SC_CHUNK) below N, for chunks c0 + blockIdx.x.
+__global__ __launch_bounds__(256) void key_scale_table_kernel(const float* __restrict__ k_scale,
+                                                              int64_t N, int64_t c0,
+                                                              float* __restrict__ kglob) {
+  constexpr int PER = SC_CHUNK / 256;
+  __shared__ float red[4];
+  const int64_t c = c0 + blockIdx.x;
+  const int64_t r0 = c * SC_CHUNK + threadIdx.x;
+  float v[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {  // rows past N load row N - 1 (in bounds) and are masked
+    const int64_t r = r0 + 256 * u;
+    v[u] = k_scale[r < N ? r : N - 1];
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) m = fmaxf(m, r0 + 256 * u < N ? fabsf(v[u]) : 0.0f);
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if (threadIdx.x % 64 == 0) red[threadIdx.x / 64] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) kglob[c] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
 // The need-th largest of the order keys key[0..PER) of every thread (entries with live false
 // excluded), by the whole block: the 16-bit class (key >> 16) counted below the largest class
 // (2048 bins, the last one gathering every class 2047 or more below; keys drawn from the top of
@@ -2416,6 +2455,23 @@ extern "C" size_t dsa_topk_workspace_size(int32_t B, int32_t T, int64_t max_kv_l
   return static_cast<size_t>(bytes);
 }
 
+extern "C" dsa_status dsa_key_scale_max(const float* k_scale, int64_t N, int64_t row_begin,
+                                        int64_t row_end, float* k_scale_max, void* stream) {
+  using namespace dsa;
+  DSA_REQUIRE(N >= 0 && row_begin >= 0 && row_begin <= row_end && row_end <= N,
+              "dsa_key_scale_max: need 0 <= row_begin <= row_end <= N");
+  if (row_begin == row_end) return ok();
+  DSA_REQUIRE(k_scale && k_scale_max, "dsa_key_scale_max: null pointer");
+  DSA_REQUIRE((reinterpret_cast<uintptr_t>(k_scale_max) & 3) == 0 &&
+                  (reinterpret_cast<uintptr_t>(k_scale) & 3) == 0,
+              "dsa_key_scale_max: k_scale and k_scale_max must be 4-byte aligned");
+  const int64_t c0 = row_begin / SC_CHUNK, c1 = (row_end - 1) / SC_CHUNK;
+  DSA_REQUIRE(c1 - c0 < 0x7FFFFFFF, "dsa_key_scale_max: too many rows");
+  hipLaunchKernelGGL(key_scale_table_kernel, dim3(static_cast<unsigned>(c1 - c0 + 1)), dim3(256), 0,
+                     as_stream(stream), k_scale, N, c0, k_scale_max);
+  return check_launch("dsa_key_scale_max");
+}
+
 extern "C" dsa_status dsa_topk(const float* scores, int64_t score_ld,
                                const int32_t* q_row_offsets, const int64_t* kv_row_offsets,
                                int32_t B, int32_t T, int32_t max_q_rows, int64_t max_kv_len,
@@ -2436,6 +2492,10 @@ extern "C" dsa_status dsa_topk(const float* scores, int64_t score_ld,
     DSA_REQUIRE(refine->H_I >= 1 && refine->H_I <= 128, "dsa_topk: refine H_I must be in [1, 128]");
     DSA_REQUIRE(refine->err_scale >= 0.0 && refine->err_scale < 1e30,
                 "dsa_topk: refine err_scale must be in [0, 1e30)");
+    DSA_REQUIRE(!refine->k_scale_max || refine->k_scale_max_len >= 1,
+                "dsa_topk: refine k_scale_max needs k_scale_max_len >= 1");
+    DSA_REQUIRE((reinterpret_cast<uintptr_t>(refine->k_scale_max) & 3) == 0,
+                "dsa_topk: refine k_scale_max must be 4-byte aligned");
   }
   if (B == 0 || T == 0 || max_q_rows == 0) return ok();
   DSA_REQUIRE(scores && q_row_offsets && kv_row_offsets && topk, "dsa_topk: null pointer");
@@ -2468,14 +2528,19 @@ extern "C" dsa_status dsa_topk(const float* scores, int64_t score_ld,
     rf.w = refine->w;
     rf.k_fp8 = refine->k_fp8;
     rf.k_scale = refine->k_scale;
-    rf.kmax = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + chunk_bytes);
     rf.status = refine->status;
     rf.C = refine->err_scale;
     rf.H = refine->H_I;
     rf.D = refine->D_I;
     rf.nsc = static_cast<int>(nsc);
-    hipLaunchKernelGGL(topk_scale_max_kernel, dim3((unsigned)nsc, (unsigned)B), dim3(256), 0, st,
-                       refine->k_scale, kv_row_offsets, (int)nsc, const_cast<float*>(rf.kmax));
+    if (refine->k_scale_max) {  // the caller's table: no pre-pass
+      rf.kglob = refine->k_scale_max;
+      rf.kglob_len = refine->k_scale_max_len;
+    } else {
+      rf.kmax = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + chunk_bytes);
+      hipLaunchKernelGGL(topk_scale_max_kernel, dim3((unsigned)nsc, (unsigned)B), dim3(256), 0, st,
+                         refine->k_scale, kv_row_offsets, (int)nsc, const_cast<float*>(rf.kmax));
+    }
     if (nchunk > 1) {
       uint8_t* p = static_cast<uint8_t*>(ws) + chunk_bytes + topk_kmax_bytes(B, max_kv_len);
       lr.rows = reinterpret_cast<LongRow*>(p);

@@ -53,7 +53,10 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 6
+#define DSA_ABI_VERSION 7
+
+/* Cache rows per entry of the key-scale table (dsa_key_scale_max). */
+#define DSA_KEY_SCALE_CHUNK 2048
 
 typedef enum {
   DSA_OK = 0,
@@ -106,11 +109,15 @@ dsa_status dsa_quantize_fp8(const float* x, int64_t n_vec, int32_t dim, uint8_t*
  *   kv_cache[d, :] = latent_new[t, :]  (576 bf16 copied bit for bit; skipped when
  *                                      latent_new is NULL)
  * and, when q is not NULL, q_fp8 / q_scale = dsa_quantize_fp8 of the T*H_I query
- * vectors q[t, j, :].
+ * vectors q[t, j, :]. When k_scale_max is not NULL (the key-scale table of
+ * dsa_key_scale_max), entry d / DSA_KEY_SCALE_CHUNK is raised to k_scale[d] if
+ * below it (an atomic maximum), so the table stays an upper bound of its
+ * chunks' scales.
  *   k_new [T, D_I] float32 (16-byte aligned); latent_new [T, 576] bf16 (16-byte
  *   aligned rows); dst_rows [T] int64 device array (distinct rows, trusted);
  *   k_cache [N, D_I] u8; k_scale [N] f32; kv_cache [N, 576] bf16;
- *   q [T, H_I, D_I] float32; q_fp8 [T, H_I, D_I] u8; q_scale [T, H_I] f32.
+ *   q [T, H_I, D_I] float32; q_fp8 [T, H_I, D_I] u8; q_scale [T, H_I] f32;
+ *   k_scale_max [ceil(N / DSA_KEY_SCALE_CHUNK)] f32 (4-byte aligned) or NULL.
  * The caller decides the rows: under the ragged layout of dsa_index_score, row
  * t = q_off[b] + r is position L_b - R_b + r of request b, cache row
  * kv_row_offsets[b] + L_b - R_b + r.
@@ -121,7 +128,7 @@ dsa_status dsa_verify_cache_write(const float* k_new, const uint16_t* latent_new
                                   const int64_t* dst_rows, int32_t T, int32_t D_I,
                                   uint8_t* k_cache, float* k_scale, uint16_t* kv_cache,
                                   const float* q, int32_t H_I, uint8_t* q_fp8, float* q_scale,
-                                  void* stream);
+                                  float* k_scale_max, void* stream);
 
 /*
  * dsa_index_score -- lightning-indexer scores of every verify row against
@@ -166,6 +173,11 @@ dsa_status dsa_index_score(const uint8_t* q_fp8, const float* q_scale, const flo
  *                      farther than eps_t / 2 from its exact value, so the margin
  *                      the bound relies on is thinner than measured (treat the
  *                      set as possibly inexact)
+ *   k_scale_max, k_scale_max_len  the caller's key-scale table (nullable). Set,
+ *              smax_t below is taken from its entries covering cache rows
+ *              kv_row_offsets[b] .. + p_t (an entry past the table gives an
+ *              infinite eps_t, status -2); NULL, a pre-pass launch computes the
+ *              per-request maxima in the workspace on every call.
  */
 typedef struct dsa_topk_refine {
   const uint8_t* q_fp8;
@@ -177,6 +189,8 @@ typedef struct dsa_topk_refine {
   int32_t D_I;
   double err_scale;
   int32_t* status;
+  const float* k_scale_max;  /* key-scale table (dsa_key_scale_max) or NULL */
+  int64_t k_scale_max_len;   /* its entries (>= 1 when k_scale_max is set) */
 } dsa_topk_refine;
 
 /*
@@ -199,8 +213,8 @@ typedef struct dsa_topk_refine {
  *   eps_t = C * 2^-16 * 448 * smax_t * sum_j |u_j| * max_c |q_hat[t,j,c]|
  *           + (H_I + 3) * 2^-23 * |theta_t|
  * of its exact value (smax_t: the largest key scale of the 2048-position
- * chunks holding the row's visible keys; theta_t: the k-th largest float32
- * score). The first term bounds the FP8 MFMA's accumulation error of each head
+ * chunks holding the row's visible keys, or an upper bound of it from the
+ * key-scale table; theta_t: the k-th largest float32 score). The first term bounds the FP8 MFMA's accumulation error of each head
  * dot by C times 2^-16 of the largest possible product; the second, the float32
  * epilogue for nonnegative weights. EXACTNESS IS CONDITIONAL: with the default
  * C = 4 the bound is not derived but checked by measurement (the largest
@@ -232,6 +246,29 @@ dsa_status dsa_topk(const float* scores, int64_t score_ld, const int32_t* q_row_
 
 size_t dsa_topk_workspace_size(int32_t B, int32_t T, int64_t max_kv_len, int32_t k,
                                int32_t refine);
+
+/*
+ * dsa_key_scale_max -- the key-scale table the refine of dsa_topk reads its
+ * smax_t from, kept beside the index-key cache so that no call rescans the
+ * scales. (The bound eps_t of dsa_topk needs the largest key scale among a
+ * row's visible keys; "MAX Pipeline 中的 DeepSeek-V3.2 架构实现解析", "Indexer 的结构与计算流程":
+ * the indexer K cache holds one fp32 scale per token.)
+ *
+ * For every chunk c = r / DSA_KEY_SCALE_CHUNK of a row r in [row_begin, row_end):
+ *   k_scale_max[c] = max |k_scale[i]| over rows i of chunk c below N
+ * (the whole chunk is recomputed, also rows outside [row_begin, row_end)).
+ * Build it once over [0, N) after the cache is filled, again over a range after
+ * writing that range in some other way; dsa_verify_cache_write with the table
+ * keeps it up to date (raising entries only). Any entry at or above the true
+ * maximum keeps the refine exact; a larger one only widens its band. Rows that
+ * hold no key count with the scale stored there (0 keeps them out).
+ *   k_scale [N] f32; k_scale_max [ceil(N / DSA_KEY_SCALE_CHUNK)] f32, both
+ *   device pointers, 4-byte aligned; caller-owned.
+ * Errors: DSA_ERR_INVALID_ARGUMENT (null pointers, not 0 <= row_begin <=
+ * row_end <= N).
+ */
+dsa_status dsa_key_scale_max(const float* k_scale, int64_t N, int64_t row_begin, int64_t row_end,
+                             float* k_scale_max, void* stream);
 
 /*
  * dsa_index_topk -- the indexer scores and the refined top-k of every row in one call, with

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_workspace_queries():
     lib = _lib.load()
-    assert lib.dsa_abi_version() == 6
+    assert lib.dsa_abi_version() == 7
     assert lib.dsa_last_error() in (b"", None)
     assert lib.dsa_topk_workspace_size(32, 192, 65536, 2048, 0) == 0
     # the refine keeps one key-scale maximum per 2048 positions of every request
@@ -56,3 +56,19 @@ def test_version_and_workspace_queries():
     # greedy accept: one (max, index) pair per 4096-entry vocabulary slice per row
     assert lib.greedy_accept_workspace_size(32, 5, 151552) == 32 * 6 * 37 * 8
     assert lib.greedy_accept_workspace_size(0, 5, 10) == 0
+
+
+def test_key_scale_table_argument_checks_before_launch():
+    # rejected on the host, before any HIP call (so this runs without a GPU)
+    lib = _lib.load()
+    assert lib.dsa_key_scale_max(None, 100, 10, 101, None, None) == 1  # row_end > N
+    assert lib.dsa_key_scale_max(None, 100, 20, 10, None, None) == 1   # row_begin > row_end
+    assert lib.dsa_key_scale_max(None, 100, 5, 5, None, None) == 0     # empty range: nothing
+    assert lib.dsa_key_scale_max(None, 100, 0, 100, None, None) == 1   # null pointers
+    assert b"null" in lib.dsa_last_error()
+    # a refine with a table needs its length
+    rf = _lib.TopkRefine(1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 8, 64, 0.0, None,
+                         1 << 20, 0)
+    st = lib.dsa_topk(1 << 20, 64, 1 << 20, 1 << 20, 1, 2, 2, 64, 8, ctypes.byref(rf), 1 << 20,
+                      None, 0, None)
+    assert st == 1 and b"k_scale_max_len" in lib.dsa_last_error()

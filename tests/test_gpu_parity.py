@@ -401,6 +401,91 @@ def test_topk_refine_rejects_bad_arguments():
         api.topk(s, qo, ko, 2, 64, 4097, refine=ra)       # k above the refine's limit
 
 
+def _chunk_max(ks: np.ndarray) -> np.ndarray:
+    """Largest scale of every 2048 consecutive rows (the last chunk ragged)."""
+    n = len(ks)
+    return np.array([np.abs(ks[c:c + 2048]).max() for c in range(0, n, 2048)], np.float32)
+
+
+def test_key_scale_table_build_range_and_cache_write():
+    # the table's entries are the chunk maxima; a range rebuild recomputes only the chunks it
+    # meets; a cache write with the table raises each chunk's entry to the new rows' scales
+    _say("key-scale table")
+    rng = np.random.default_rng(7)
+    N = 3 * 2048 + 777
+    ks = (np.abs(rng.standard_normal(N)) * 0.01 + 1e-3).astype(np.float32)
+    ks_d = torch.from_numpy(ks).to(DEV)
+    tab = api.key_scale_max(ks_d)
+    assert np.array_equal(tab.cpu().numpy(), _chunk_max(ks))
+    ks[4100:4110] = 5.0
+    ks_d[4100:4110] = 5.0
+    before = tab.cpu().numpy()
+    api.key_scale_max(ks_d, out=tab, row_begin=4100, row_end=4110)
+    after = tab.cpu().numpy()
+    assert after[2] == 5.0 and np.array_equal(np.delete(after, 2), np.delete(before, 2))
+    assert np.array_equal(after, _chunk_max(ks))
+    # the verify rows' keys: some far larger than any cached key, some smaller
+    T = 37
+    dst = rng.choice(N, T, replace=False).astype(np.int64)
+    k_new = rng.standard_normal((T, 128)).astype(np.float32)
+    k_new[::3] *= 1000.0
+    kc_d = torch.zeros((N, 128), dtype=torch.uint8, device=DEV)
+    api.verify_cache_write(torch.from_numpy(k_new).to(DEV), torch.from_numpy(dst).to(DEV), kc_d,
+                           ks_d, k_scale_max=tab)
+    _, new_s = oracle.quantize(k_new)
+    want = after.copy()
+    for d, sc in zip(dst, new_s):
+        want[d // 2048] = max(want[d // 2048], sc)
+    got = tab.cpu().numpy()
+    assert np.array_equal(got, want)
+    assert (got > after).any()  # the scaled-up keys raised some entries
+    assert np.array_equal(ks_d.cpu().numpy()[dst], new_s)
+    with pytest.raises(api.DsaError, match="INVALID_ARGUMENT"):
+        api.key_scale_max(ks_d, out=tab, row_begin=10, row_end=N + 1)
+
+
+@pytest.mark.parametrize("name", ["mtp5_verify@6000", "decode_verify@4096", "long100k"])
+def test_refined_topk_with_key_scale_table(name):
+    # smax_t from the caller's table (global 2048-row chunks, which straddle the requests'
+    # boundaries here, so it can only exceed the per-request maxima): every row is refined
+    # and its set equals the oracle's, as with the pre-pass
+    _say(f"refined top-k with the key-scale table, {name}")
+    if name == "long100k":
+        w = W.replace(W.scaled(W.LONG_CTX, ctx=100000, batch=2, topk=512), rows=3)
+    else:
+        w = SMALL[name]
+    case = Case(w, with_mla=False, with_accept=False)
+    gi = gpu_indexer(case)
+    qc, qs, kc, ks, ko = oracle_quant(case)
+    rows = np.arange(case.T)
+    ref_s = oracle.index_score(qc, qs, case.host("w_f32"), kc, ks, case.qo.numpy(), ko,
+                               rows=rows, width=case.max_kv)
+    nvis = np.array([case.visible(int(t)) for t in rows])
+    ref_k = oracle.topk(ref_s, nvis, w.topk)
+    ra = refine_args(gi, case)
+    ra["k_scale_max"] = api.key_scale_max(gi["ks"])
+    assert np.array_equal(ra["k_scale_max"].cpu().numpy(), _chunk_max(gi["ks"].cpu().numpy()))
+    got = api.topk(gi["scores"], case.qo_d, case.ko_d, w.rows, case.max_kv, w.topk, refine=ra)
+    st = ra["status"].cpu().numpy()
+    _say(f"  band sizes: max {st.max()}, mean {st.mean():.1f}")
+    assert st.min() >= 0
+    assert np.array_equal(got.cpu().numpy(), ref_k)
+
+
+def test_refined_topk_short_key_scale_table_keeps_float32():
+    # a table that ends before a row's cache rows gives that row an infinite eps: status -2
+    # and the float32 selection
+    _say("refined top-k, key-scale table too short")
+    w = SMALL["mtp5_verify@6000"]
+    case = Case(w, with_mla=False, with_accept=False)
+    gi = gpu_indexer(case)
+    ra = refine_args(gi, case)
+    ra["k_scale_max"] = api.key_scale_max(gi["ks"])[:1].contiguous()
+    got = api.topk(gi["scores"], case.qo_d, case.ko_d, w.rows, case.max_kv, w.topk, refine=ra)
+    assert ra["status"].cpu().tolist() == [-2] * case.T
+    assert torch.equal(got, gi["topk"])
+
+
 # ---------------------------------------------------------------- sparse MLA
 @pytest.mark.parametrize("heads,pad", [(16, 0.0), (64, 0.1), (128, 0.0), (48, 0.5)])
 def test_sparse_mla_matches_oracle(heads, pad):
