@@ -449,15 +449,17 @@ __device__ __forceinline__ void digit_words(i32x4 codes, const uint32_t* table, 
 }
 
 // Digit plane p of sixteen codes as an int8 MFMA operand: byte i of the operand is digit p of
-// code i.
-__device__ __forceinline__ i32x4 digit_plane(const uint32_t (&wd)[16], int p) {
+// code i. Three byte permutes per word: v_perm_b32(x, y, sel) picks byte sel_i of the eight
+// bytes {x, y} (y bytes 0..3, x bytes 4..7; selector 0x0c gives 0).
+template <int P>
+__device__ __forceinline__ i32x4 digit_plane(const uint32_t (&wd)[16]) {
+  constexpr uint32_t pair = P | ((4 + P) << 8) | 0x0c0c0000u;  // [y byte P, x byte P, 0, 0]
   i32x4 out;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    uint32_t packed = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) packed |= ((wd[4 * w + b] >> (8 * p)) & 0xFFu) << (8 * b);
-    out[w] = static_cast<int>(packed);
+    const uint32_t lo = __builtin_amdgcn_perm(wd[4 * w + 1], wd[4 * w], pair);
+    const uint32_t hi = __builtin_amdgcn_perm(wd[4 * w + 3], wd[4 * w + 2], pair);
+    out[w] = static_cast<int>(__builtin_amdgcn_perm(hi, lo, 0x05040100u));
   }
   return out;
 }
@@ -471,7 +473,9 @@ __device__ __forceinline__ i32x4 digit_plane(const uint32_t (&wd)[16], int p) {
 // The head dots are exact integer arithmetic on the int8 MFMA: every e4m3fn value times 2^9
 // is an integer below 2^18, split into three base-128 digits; the nine digit-plane products
 // (v_mfma_i32_16x16x64_i8) chain into five int32 accumulators, one per digit-weight 2^(7s)
-// (s = a + b, |sum| < 3 * 2^21), which recombine exactly in float64 (|d| 2^18 < 2^43). A
+// (s = a + b, |sum| < 3 * 2^21). They recombine exactly: lo = acc_0 + 2^7 acc_1 and
+// hi = acc_2 + 2^7 acc_3 + 2^14 acc_4 stay below 2^30 in int32 (the top digits are below 16),
+// and d 2^18 = lo + 2^14 hi (|d| 2^18 < 2^44) is one exact float64 fma. A
 // wave takes one tile of 16 heads x 16 band keys per round, with the next round's key codes
 // already loading; the u_j max(d_j, 0) terms of a round go to LDS, and one thread per key
 // then adds them in ascending head order.
@@ -540,8 +544,9 @@ __device__ __forceinline__ double rescore_band(const RowRef& rr, const float* __
   for (int h = 0; h < 2; ++h) {
     uint32_t wd[16];
     digit_words(qc[h], L.digits, wd);
-#pragma unroll
-    for (int p = 0; p < 3; ++p) qa[h][p] = digit_plane(wd, p);
+    qa[h][0] = digit_plane<0>(wd);
+    qa[h][1] = digit_plane<1>(wd);
+    qa[h][2] = digit_plane<2>(wd);
   }
   double worst = 0.0;
   for (int base = 0; base < nb; base += KPR) {  // block-uniform rounds
@@ -551,46 +556,55 @@ __device__ __forceinline__ double rescore_band(const RowRef& rr, const float* __
       for (int h = 0; h < 2; ++h) {
         uint32_t wd[16];
         digit_words(kc[h], L.digits, wd);
-#pragma unroll
-        for (int p = 0; p < 3; ++p) kb[h][p] = digit_plane(wd, p);
+        kb[h][0] = digit_plane<0>(wd);
+        kb[h][1] = digit_plane<1>(wd);
+        kb[h][2] = digit_plane<2>(wd);
       }
       if (base + KPR < nb) load_keys(base + KPR, kc);  // the next round's codes, in flight
       i32x4 acc[5];  // digit weight 2^(7s): sum of the (a, b) plane products with a + b = s
 #pragma unroll
       for (int sw = 0; sw < 5; ++sw) acc[sw] = (i32x4){0, 0, 0, 0};
+      // both halves unconditionally: with D = 64 the second half's codes are all 0
 #pragma unroll
       for (int a = 0; a < 3; ++a)
 #pragma unroll
         for (int b = 0; b < 3; ++b) {
           acc[a + b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[0][a], kb[0][b], acc[a + b], 0, 0, 0);
-          if (halves > 1)
-            acc[a + b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[1][a], kb[1][b], acc[a + b], 0, 0, 0);
+          acc[a + b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[1][a], kb[1][b], acc[a + b], 0, 0, 0);
         }
-      double d[4] = {0.0, 0.0, 0.0, 0.0};  // exact dots times 2^18, heads 4 g + i, key c16
-#pragma unroll
-      for (int sw = 0; sw < 5; ++sw)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) d[i] += __builtin_ldexp(static_cast<double>(acc[sw][i]), 7 * sw);
+      // heads past H (padding of the last tile) have u = 0 and so a +0 term
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int head = 16 * ht + 4 * g + i;
-        if (head < H) {
-          const double dj = __builtin_ldexp(d[i], -18);
-          L.terms[head * KPR + slot] = __dmul_rn(u[i], dj > 0.0 ? dj : 0.0);
-        }
+        // the exact dot of head 4 g + i and key c16 (2^18 d = lo + 2^14 hi, exact)
+        const int32_t lo = acc[0][i] + acc[1][i] * 128;
+        const int32_t hi = acc[2][i] + acc[3][i] * 128 + acc[4][i] * 16384;
+        const double d = __builtin_fma(static_cast<double>(hi), 16384.0, static_cast<double>(lo));
+        const double dj = __builtin_ldexp(d, -18);
+        L.terms[head * KPR + slot] = __dmul_rn(u[i], dj > 0.0 ? dj : 0.0);
       }
     }
     __syncthreads();
     if (tid < KPR && base + tid < nb) {  // one thread per key: heads in ascending order
       const float sk = band_sk[base + tid], f32 = band_f32[base + tid];
+      // all 16 HT heads: the sum starts at +0 and so never is -0, and the +0 terms of the
+      // padding heads at its end leave it unchanged. Eight terms are read ahead of the
+      // eight being added.
+      const int nh = 16 * HT;
       double acc = 0.0;
-      for (int j0 = 0; j0 < H; j0 += 8) {  // eight terms read ahead, added in order
-        double tv[8];
+      double tv[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) tv[j] = j0 + j < H ? L.terms[(j0 + j) * KPR + tid] : 0.0;
+      for (int j = 0; j < 8; ++j) tv[j] = L.terms[j * KPR + tid];
+      for (int j0 = 0; j0 < nh; j0 += 8) {
+        double nx[8];
+        if (j0 + 8 < nh) {  // block-uniform
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (j0 + j < H) acc = __dadd_rn(acc, tv[j]);
+          for (int j = 0; j < 8; ++j) nx[j] = L.terms[(j0 + 8 + j) * KPR + tid];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc = __dadd_rn(acc, tv[j]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) tv[j] = nx[j];
       }
       const double ex = __dmul_rn(acc, static_cast<double>(sk));
       L.band_val[base + tid] = ex;
@@ -1768,12 +1782,20 @@ struct RescoreLds {
 
 // Long-row path, stage 3: block x rescores band keys x KR .. x KR + KR - 1 of its row, KR =
 // LR_ROUNDS rounds of rescore_band (KPR = 256 / head tiles keys each; the next round's key
-// codes load during the current one).
+// codes load during the current one). Blocks are numbered piece-major: launch order
+// L = x + gridDim.x y holds piece L / (rows B) of row (L % rows, request (L / rows) % B),
+// so a band's first pieces, which every row has, are the first blocks dispatched and the
+// blocks past a short band (which return at once) come last instead of between them.
 __global__ __launch_bounds__(TK_THREADS) void topk_band_rescore_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ q_off,
-    const int64_t* __restrict__ kv_off, int64_t ld, Refine rf, LongRefine lr) {
+    const int64_t* __restrict__ kv_off, int64_t ld, int max_q_rows, int B, Refine rf,
+    LongRefine lr) {
   __shared__ __attribute__((aligned(16))) RescoreLds L;
-  const int r = static_cast<int>(blockIdx.x) / LR_RESCORE_X, b = blockIdx.y;
+  const int64_t lin = blockIdx.x + static_cast<int64_t>(gridDim.x) * blockIdx.y;
+  const int64_t per_piece = static_cast<int64_t>(max_q_rows) * B;
+  const int piece = static_cast<int>(lin / per_piece);
+  const int r = static_cast<int>(lin % per_piece % max_q_rows);
+  const int b = static_cast<int>(lin % per_piece / max_q_rows);
   const RowInfo ri = load_row_info(q_off, kv_off, b);
   if (r >= ri.R) return;
   const int64_t t = ri.t0 + r;
@@ -1786,7 +1808,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_band_rescore_kernel(
   if (nb > BAND_CAP) return;  // the finishing stage reports the overflow
   const int HT = rf.H <= 16 ? 1 : rf.H <= 32 ? 2 : rf.H <= 64 ? 4 : 8;
   const int KR = LR_ROUNDS * (256 / HT);
-  const int base = static_cast<int>(blockIdx.x % LR_RESCORE_X) * KR;
+  const int base = piece * KR;
   if (base >= nb) return;
   const int cnt = nb - base < KR ? nb - base : KR;
   const int32_t* src = lr.band_pos + t * BAND_CAP + base;
@@ -2566,8 +2588,8 @@ extern "C" dsa_status dsa_topk(const float* scores, int64_t score_ld,
                          scores, q_row_offsets, kv_row_offsets, score_ld, (int)ncls, lr);
       hipLaunchKernelGGL(topk_band_rescore_kernel,
                          dim3((unsigned)(static_cast<int64_t>(LR_RESCORE_X) * max_q_rows), (unsigned)B),
-                         dim3(TK_THREADS), 0, st, scores, q_row_offsets, kv_row_offsets, score_ld, rf,
-                         lr);
+                         dim3(TK_THREADS), 0, st, scores, q_row_offsets, kv_row_offsets, score_ld,
+                         max_q_rows, B, rf, lr);
       hipLaunchKernelGGL(topk_band_finish_kernel, grid, dim3(TK_THREADS), 0, st, scores,
                          q_row_offsets, kv_row_offsets, score_ld, k, topk, rf.status, lr);
     }
