@@ -1523,13 +1523,14 @@ __device__ __forceinline__ void refine_generic(const float* __restrict__ srow, i
 // thousands of keys long, is classified and rescored by the whole GPU rather than by the
 // row's one block:
 //  - the merge kernel (one block per row) writes theta, eps and the band edges (LongRow);
-//  - topk_band_classify_kernel (LR_CLS positions per block) counts the kept keys and
-//    appends the band's positions (unordered) to the row's band list;
+//  - topk_band_classify_kernel (LR_CLS positions per block) counts the kept keys, writes
+//    their bitmap, and appends the band's positions (unordered) to the row's band list;
 //  - topk_band_rescore_kernel (one rescoring round of a row's band per block) writes the
 //    exact scores and the largest |I_f32 - I_exact|;
 //  - topk_band_finish_kernel (one block per row) picks the best `need` band keys by a radix
 //    select on (exact score desc, then position asc) and writes the kept and the chosen keys
-//    in ascending position order through LDS position bitmaps.
+//    in ascending position order through LDS position bitmaps (the kept bitmap from the
+//    classify stage, so the float32 selection is not read again).
 // Longer rows keep the single-block refine (refine_generic) in the merge kernel.
 constexpr int64_t LR_MAX_N = int64_t{1} << 18;  // positions the finishing bitmaps cover
 constexpr int LR_CLS = 16384;                   // positions classified per block
@@ -1555,6 +1556,7 @@ struct LongRefine {   // kernel argument; rows == nullptr: no long-row path
   LongRow* rows;      // [T]
   int32_t* band_pos;  // [T, BAND_CAP] request-local positions
   double* band_ex;    // [T, BAND_CAP] exact scores
+  uint32_t* kept;     // [T, LR_MAX_N / 32] bitmap of the keys above the band
 };
 
 // Long-row path, stage 1 (in the merge kernel, after the float32 selection is in out):
@@ -1705,11 +1707,12 @@ __global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(
 }
 
 // Long-row path, stage 2 (every position chunk of every long row): the kept keys are
-// counted and the band's positions appended to the row's list.
+// counted and marked in the row's kept bitmap, the band's positions appended to its list.
 __global__ __launch_bounds__(TK_THREADS) void topk_band_classify_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ q_off,
     const int64_t* __restrict__ kv_off, int64_t ld, int ncls, LongRefine lr) {
   __shared__ int32_t bpos[LR_CLS];
+  __shared__ uint32_t kbits[LR_CLS / 32];  // this block's words of the kept bitmap
   __shared__ uint32_t cnt[2], base_s;
   const int c = static_cast<int>(blockIdx.x) % ncls, r = static_cast<int>(blockIdx.x) / ncls;
   const int b = blockIdx.y;
@@ -1727,12 +1730,14 @@ __global__ __launch_bounds__(TK_THREADS) void topk_band_classify_kernel(
   const float lo_f = row.lo_f, hi_f = row.hi_f;
   const int tid = threadIdx.x;
   if (tid < 2) cnt[tid] = 0;
+  for (int w = tid; w < LR_CLS / 32; w += TK_THREADS) kbits[w] = 0u;
   __syncthreads();
   const float* srow = scores + t * ld + c0;
   uint32_t kept = 0;
   auto classify = [&](float x, int i) {
     if (x > hi_f) {
       ++kept;
+      atomicOr(&kbits[i >> 5], 1u << (i & 31));
     } else if (x >= lo_f) {
       bpos[atomicAdd(&cnt[0], 1u)] = static_cast<int32_t>(c0 + i);
     }
@@ -1768,6 +1773,9 @@ __global__ __launch_bounds__(TK_THREADS) void topk_band_classify_kernel(
   int32_t* dst = lr.band_pos + t * BAND_CAP;
   for (uint32_t i = tid; i < cnt[0]; i += TK_THREADS)
     if (base_s + i < static_cast<uint32_t>(BAND_CAP)) dst[base_s + i] = bpos[i];
+  // the block's words of the row's kept bitmap (c0 is a multiple of 32; bits past n are 0)
+  uint32_t* kdst = lr.kept + t * (LR_MAX_N / 32) + c0 / 32;
+  for (int w = tid; w < (nc + 31) / 32; w += TK_THREADS) kdst[w] = kbits[w];
 }
 
 // LDS of one rescoring round (the members rescore_band uses)
@@ -1834,6 +1842,7 @@ struct FinishLds {
   uint32_t sel[LR_MAX_N / 32];   // positions taken
   uint32_t tie[LR_MAX_N / 32];   // band positions tied with the selection's last exact score
   uint32_t hist[256];
+  uint64_t kmin[TK_WAVES], kmax[TK_WAVES];
   uint32_t tmp[2 * TK_WAVES];
   uint64_t prefix;
   uint32_t want;
@@ -1886,26 +1895,57 @@ __global__ __launch_bounds__(TK_THREADS) void topk_band_finish_kernel(
     if (tid == 0 && status) status[t] = nb > BAND_CAP ? -1 : -2;
     return;
   }
-  const float* srow = scores + t * ld;
   int32_t* out = topk + t * k;
   const int nw = static_cast<int>((n + 31) / 32);
+  // the band's keys, and the kept keys' bitmap from the classify stage (both contiguous)
+  uint64_t kmin = ~uint64_t{0}, kmax = 0;
   for (int i = tid; i < nb; i += TK_THREADS) {
-    F.key[i] = order_key64(lr.band_ex[t * BAND_CAP + i]);
+    const uint64_t x = order_key64(lr.band_ex[t * BAND_CAP + i]);
+    F.key[i] = x;
     F.pos[i] = lr.band_pos[t * BAND_CAP + i];
+    kmin = x < kmin ? x : kmin;
+    kmax = x > kmax ? x : kmax;
   }
+  uint32_t kc = 0;
+  const uint32_t* kbits = lr.kept + t * (LR_MAX_N / 32);
   for (int w = tid; w < nw; w += TK_THREADS) {
-    F.sel[w] = 0u;
+    const uint32_t x = kbits[w];
+    F.sel[w] = x;
     F.tie[w] = 0u;
+    kc += static_cast<uint32_t>(__popc(x));
   }
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint64_t a = __shfl_xor(kmin, o), c = __shfl_xor(kmax, o);
+    kmin = a < kmin ? a : kmin;
+    kmax = c > kmax ? c : kmax;
+  }
+  kc = wave_sum(kc);
+  if (tid % 64 == 0) {
+    F.kmin[tid / 64] = kmin;
+    F.kmax[tid / 64] = kmax;
+  }
+  if (tid == 0) F.kept2 = 0;
+  __syncthreads();
+  if (tid % 64 == 0 && kc) atomicAdd(&F.kept2, kc);
+  kmin = F.kmin[0];
+  kmax = F.kmax[0];
+  for (int w = 1; w < TK_WAVES; ++w) {
+    kmin = F.kmin[w] < kmin ? F.kmin[w] : kmin;
+    kmax = F.kmax[w] > kmax ? F.kmax[w] : kmax;
+  }
+  // Every key shares the bytes above the highest one where the smallest and largest keys
+  // differ, so the radix select starts at that byte with those bytes as its prefix; an
+  // all-tied band (kmin == kmax) needs no pass.
+  const uint64_t diff = kmin ^ kmax;
+  const int s0 = diff ? 8 * ((63 - __builtin_clzll(diff)) / 8) : -8;
   if (tid == 0) {
-    F.prefix = 0;
+    F.prefix = s0 < 0 ? kmax : s0 == 56 ? 0 : (kmax >> (s0 + 8)) << (s0 + 8);
     F.want = static_cast<uint32_t>(need);
-    F.kept2 = 0;
   }
   __syncthreads();
-  // the need-th largest exact key, eight bits at a time from the top: bin 255 - d holds
-  // digit d, so that bin 0 holds the largest keys
-  for (int shift = 56; shift >= 0; shift -= 8) {
+  // the need-th largest exact key, eight bits at a time from byte s0 down: bin 255 - d
+  // holds digit d, so that bin 0 holds the largest keys
+  for (int shift = s0; shift >= 0; shift -= 8) {
     for (int i = tid; i < 256; i += TK_THREADS) F.hist[i] = 0u;
     __syncthreads();
     const uint64_t prefix = F.prefix;
@@ -1934,18 +1974,6 @@ __global__ __launch_bounds__(TK_THREADS) void topk_band_finish_kernel(
     if (F.key[i] > thk) atomicOr(&F.sel[p >> 5], 1u << (p & 31));
     else if (F.key[i] == thk) atomicOr(&F.tie[p >> 5], 1u << (p & 31));
   }
-  // the kept keys: the float32 selection's entries above the band
-  const float hi_f = row.hi_f;
-  uint32_t kc = 0;
-  for (int i = tid; i < k; i += TK_THREADS) {
-    const int32_t p = out[i];
-    if (p >= 0 && srow[p] > hi_f) {
-      atomicOr(&F.sel[p >> 5], 1u << (p & 31));
-      ++kc;
-    }
-  }
-  kc = wave_sum(kc);
-  if (tid % 64 == 0 && kc) atomicAdd(&F.kept2, kc);
   __syncthreads();
   if (F.kept2 != static_cast<uint32_t>(kept)) {  // uniform; cannot happen for a correct selection
     if (tid == 0 && status) status[t] = -3;
@@ -2459,11 +2487,13 @@ int64_t topk_nsc(int64_t max_kv_len) { return max_kv_len > 0 ? ceil_div(max_kv_l
 int64_t topk_kmax_bytes(int32_t B, int64_t max_kv_len) {
   return (static_cast<int64_t>(B) * topk_nsc(max_kv_len) * 4 + 15) / 16 * 16;
 }
-// Bytes of the long-row refine: LongRow[T], band positions [T, BAND_CAP] and exact scores
-// [T, BAND_CAP] (grids with rows longer than FAST_MAX only).
+// Bytes of the long-row refine: LongRow[T], band positions [T, BAND_CAP], exact scores
+// [T, BAND_CAP] and the kept keys' bitmaps [T, LR_MAX_N / 32] (grids with rows longer than
+// FAST_MAX only).
 int64_t topk_long_bytes(int32_t T, int64_t max_kv_len) {
   if (topk_nchunk(max_kv_len) <= 1) return 0;
-  return static_cast<int64_t>(T) * (static_cast<int64_t>(sizeof(LongRow)) + BAND_CAP * (4 + 8));
+  return static_cast<int64_t>(T) *
+         (static_cast<int64_t>(sizeof(LongRow)) + BAND_CAP * (4 + 8) + LR_MAX_N / 32 * 4);
 }
 }  // namespace
 }  // namespace dsa
@@ -2541,7 +2571,7 @@ extern "C" dsa_status dsa_topk(const float* scores, int64_t score_ld,
   const int64_t chunk_bytes = topk_chunk_bytes(T, max_kv_len, k);
   hipStream_t st = as_stream(stream);
   Refine rf{};
-  LongRefine lr{nullptr, nullptr, nullptr};
+  LongRefine lr{nullptr, nullptr, nullptr, nullptr};
   if (refine) {
     const int64_t nsc = topk_nsc(max_kv_len);
     DSA_REQUIRE(nsc <= 65535, "dsa_topk: max_kv_len too large for the refine");
@@ -2569,6 +2599,8 @@ extern "C" dsa_status dsa_topk(const float* scores, int64_t score_ld,
       lr.band_pos = reinterpret_cast<int32_t*>(p + static_cast<int64_t>(T) * sizeof(LongRow));
       lr.band_ex = reinterpret_cast<double*>(p + static_cast<int64_t>(T) * sizeof(LongRow) +
                                              static_cast<int64_t>(T) * BAND_CAP * 4);
+      lr.kept = reinterpret_cast<uint32_t*>(p + static_cast<int64_t>(T) * sizeof(LongRow) +
+                                            static_cast<int64_t>(T) * BAND_CAP * 12);
     }
   }
   dim3 grid((unsigned)max_q_rows, (unsigned)B);

@@ -39,9 +39,10 @@ def test_version_and_workspace_queries():
     # 262144-position rows: 4 chunks of 2048 indices, then compact scores and positions
     assert lib.dsa_topk_workspace_size(4, 24, 262144, 2048, 0) == (24 * 4 * 2048 + 24 * 8192) * 4
     # with the refine: the scale maxima, then per row the long-row refine's record (48
-    # bytes), band positions and exact band scores (4096 x (4 + 8) bytes)
+    # bytes), band positions and exact band scores (4096 x (4 + 8) bytes) and the bitmap of
+    # the keys kept above the band (2^18 bits)
     assert lib.dsa_topk_workspace_size(4, 24, 262144, 2048, 1) == (
-        (24 * 4 * 2048 + 24 * 8192) * 4 + 4 * 128 * 4 + 24 * (48 + 4096 * 12))
+        (24 * 4 * 2048 + 24 * 8192) * 4 + 4 * 128 * 4 + 24 * (48 + 4096 * 12 + 32768))
     assert lib.dsa_topk_workspace_size(3, 5, 100, 8, 1) == 16  # padded to 16 bytes
     # split-K partials: per (row, split, head) 512 bf16 outputs and a float32 (max, sum),
     # or none when one split suffices
