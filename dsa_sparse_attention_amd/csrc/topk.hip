@@ -1559,26 +1559,13 @@ struct LongRefine {   // kernel argument; rows == nullptr: no long-row path
   uint32_t* kept;     // [T, LR_MAX_N / 32] bitmap of the keys above the band
 };
 
-// Long-row path, stage 1 (in the merge kernel, after the float32 selection is in out):
-// theta = the smallest selected score, eps and the band edges go to the row's LongRow, with
-// its counters cleared. pa / ps: refine_prefetch's partials; red: TK_WAVES doubles of LDS.
-__device__ __forceinline__ void long_row_open(const float* __restrict__ srow, int k,
-                                              const int32_t* __restrict__ out, const RowRef& rr,
-                                              LongRow& row, const double* pa, const float* ps,
-                                              double* red) {
+// Long-row path, stage 1 (in the merge kernel, after the float32 selection): theta = the
+// smallest selected score (th: this thread's share of the minimum), eps and the band edges
+// go to the row's LongRow, with its counters cleared. pa / ps: refine_prefetch's partials;
+// red: TK_WAVES doubles of LDS.
+__device__ __forceinline__ void long_row_open(float th, const RowRef& rr, LongRow& row,
+                                              const double* pa, const float* ps, double* red) {
   const int tid = threadIdx.x;
-  constexpr int U = 8;  // loads in flight per thread
-  float th = __builtin_inff();
-  for (int i0 = tid; i0 < k; i0 += U * TK_THREADS) {
-    int32_t pp[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) pp[u] = i0 + u * TK_THREADS < k ? out[i0 + u * TK_THREADS] : -1;
-    float v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = pp[u] >= 0 ? srow[pp[u]] : __builtin_inff();
-#pragma unroll
-    for (int u = 0; u < U; ++u) th = fminf(th, v[u]);
-  }
   th = static_cast<float>(-block_max_d(-static_cast<double>(th), red));
   const double eps = refine_eps(rr.rf, th, pa, ps);
   if (tid != 0) return;
@@ -1685,19 +1672,26 @@ __global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(
   const int64_t m = (n + FAST_MAX - 1) / FAST_MAX * k;  // this row's chunks
   int32_t* out = topk + t * k;
   const RowRef rr = row_ref(rf, t, b, ri.kv_base);
-  select_row(cand_s + t * cstride, m, k, out, S, rr, false);
+  // the refine's query-side loads overlap the selection (its partials stay in rf_a / rf_s)
+  if (rf.q_fp8 != nullptr) refine_prefetch(rr, n, S.rf_a, S.rf_s);
+  const float* crow = cand_s + t * cstride;
+  select_row(crow, m, k, out, S, rr, false);
   __syncthreads();
+  // candidate indices -> positions; theta's share of this thread from the candidates'
+  // scores (loaded in the same round as their positions)
   const int32_t* wrow = widx + t * nchunk * k;
+  float th = __builtin_inff();
   for (int i = threadIdx.x; i < k; i += TK_THREADS) {
     const int32_t j = out[i];
-    if (j >= 0) out[i] = (j / k) * FAST_MAX + wrow[j];
+    if (j >= 0) {
+      out[i] = (j / k) * FAST_MAX + wrow[j];
+      th = fminf(th, crow[j]);
+    }
   }
   if (rf.q_fp8 != nullptr) {
-    refine_prefetch(rr, n, S.rf_a, S.rf_s);
     __syncthreads();
     if (lr.rows != nullptr && n <= LR_MAX_N) {
-      long_row_open(scores + t * ld, k, out, rr, lr.rows[t], S.rf_a, S.rf_s,
-                    reinterpret_cast<double*>(S.regA));
+      long_row_open(th, rr, lr.rows[t], S.rf_a, S.rf_s, reinterpret_cast<double*>(S.regA));
     } else {
       if (lr.rows != nullptr && threadIdx.x == 0) lr.rows[t].state = 1;
       refine_generic(scores + t * ld, n, k, out, rr, *reinterpret_cast<RefineLds*>(S.regA), S.tmp,
