@@ -86,14 +86,30 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// 2^x by v_exp_f32 alone: results below 2^-126 flush to +0 (exp2f would rescale them into
+// denormals at five more instructions each). The softmax weights taken here never need
+// them: the key that set the reference max weighs exactly 1, so the row sum is at least 1
+// and a weight or a rescale factor below 2^-126 is below half an ulp of it, and of the
+// output's float32 accumulation as well.
+__device__ __forceinline__ float exp2_flush(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// The larger of two logits by one v_max_f32. fmaxf would first quiet each operand that the
+// compiler cannot prove canonical (lane swaps, selects), one more instruction per operand;
+// logits are never NaN here (-inf marks a padding row), so the plain instruction serves.
+__device__ __forceinline__ float max_logit(float a, float b) {
+  float r;
+  asm("v_max_f32_e32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // max / sum over lanes l, l^16, l^32, l^48 (the four lanes of one S^T column)
 __device__ __forceinline__ float max_xor16_xor32(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = max_logit(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return max_logit(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ float sum_xor16_xor32(float x) {
@@ -314,24 +330,27 @@ __global__ __launch_bounds__(NT, 1) void mla_decode_kernel(
             s[j] = v;
           }
         }
-        // keys 32i + 16kt + 4g + j, j = 0..3
+        // keys 32i + 16kt + 4g + j, j = 0..3; only the last chunk can hold padding rows
+        if (KC * (i + 1) <= nvalid) {  // block-uniform
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bool v = KC * i + 16 * kt + 4 * g + j < nvalid;
-          s[j] = v ? s[j] * c2 : -INFINITY;
-          cm = fmaxf(cm, s[j]);
+          for (int j = 0; j < 4; ++j) s[j] *= c2;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            s[j] = KC * i + 16 * kt + 4 * g + j < nvalid ? s[j] * c2 : -INFINITY;
         }
+        cm = max_logit(max_logit(s[0], s[1]), max_logit(s[2], s[3]));
         cm = max_xor16_xor32(cm);
         if (g == 0) sh_cm[kt][16 * hq + c16] = cm;
       }
       __syncthreads();  // B1: every S wave is done with chunk i's K (rope takes P^T)
       if (i < nch) {
-        cm = fmaxf(cm, sh_cm[kt ^ 1][16 * hq + c16]);
+        cm = max_logit(cm, sh_cm[kt ^ 1][16 * hq + c16]);
         const float mn = cm > m_ref + LAZY ? cm : m_ref;
         const bool resc = __any(mn != m_ref);  // wave-uniform; same in both key halves
         float alpha = 1.0f;
         if (resc) {
-          alpha = exp2f(m_ref - mn);  // 0 at the first chunk, 1 if unchanged
+          alpha = exp2_flush(m_ref - mn);  // 0 at the first chunk, 1 if unchanged
           lsum *= alpha;
           m_ref = mn;
         }
@@ -349,7 +368,7 @@ __global__ __launch_bounds__(NT, 1) void mla_decode_kernel(
         float ev[4];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {  // masked keys: exp2(-inf) = 0; bf16 round to nearest even
-          const float e0 = exp2f(s[2 * j] - m_ref), e1 = exp2f(s[2 * j + 1] - m_ref);
+          const float e0 = exp2_flush(s[2 * j] - m_ref), e1 = exp2_flush(s[2 * j + 1] - m_ref);
           const bf16x2 pp = __builtin_convertvector((f32x2){e0, e1}, bf16x2);
           psum += e0 + e1;
           pw[j] = __builtin_bit_cast(uint32_t, pp);
