@@ -32,7 +32,7 @@ import torch
 import oracle
 from dsa_sparse_attention_amd import api, synth, workloads
 from tests._pipeline import (DEV, check_topk_valid, kth_largest, mla_check, refine_eps,
-                             score_tolerance)
+                             score_tolerance, REFINE_MARGIN)
 
 pytestmark = pytest.mark.gpu
 
@@ -152,6 +152,7 @@ def test_full_index_score_sampled_within_bound(f):
         assert np.all(err <= tol), f"row {t}: score error above bound"
         worst = max(worst, float((err / tol).max()))
     _say(f"  worst |err|/bound = {worst:.3e}")
+    assert worst <= REFINE_MARGIN, "scores drift past the margin the default refine relies on"
 
 
 @pytest.mark.parametrize("levels", [0, 7, 2000])

@@ -16,7 +16,8 @@ import torch
 import oracle
 from dsa_sparse_attention_amd import api, synth, workloads
 from tests._pipeline import (DEV, Case, check_topk_valid, gpu_indexer, kth_largest, mla_check,
-                             oracle_quant, refine_args, refine_eps, score_tolerance)
+                             oracle_quant, refine_args, refine_eps, score_tolerance,
+                             REFINE_MARGIN)
 
 pytestmark = pytest.mark.gpu
 
@@ -112,6 +113,7 @@ def test_index_score_within_bound(name):
         assert np.all(err <= tol[t, :n]), f"row {t}: score error above bound"
         worst = max(worst, float((err / np.maximum(tol[t, :n], 1e-300)).max()))
     _say(f"  worst |err|/bound = {worst:.3e}")
+    assert worst <= REFINE_MARGIN, "scores drift past the margin the default refine relies on"
 
 
 def test_index_score_exact_grid_bitexact():
