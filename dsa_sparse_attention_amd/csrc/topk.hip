@@ -465,7 +465,7 @@ __device__ __forceinline__ i32x4 digit_plane(const uint32_t (&wd)[16]) {
 }
 
 // Exact scores of the nb band keys (positions in L.band_pos, request-local) into
-// L.band_val; returns (to every thread) the largest |I_f32 - I_exact| over the band, I_f32
+// L.band_val; returns (to thread 0) the largest |I_f32 - I_exact| over the band, I_f32
 // read from srow (or given in band_f32 when srow is null). band_sk and band_f32 are LDS
 // staging arrays of at least nb entries, free until the band is chosen.
 //   I_exact = s_k * sum_{j ascending} u_j * max(d_j, 0), d_j = q_hat[t,j] . k_hat (exact),
@@ -549,6 +549,10 @@ __device__ __forceinline__ double rescore_band(const RowRef& rr, const float* __
     qa[h][2] = digit_plane<2>(wd);
   }
   double worst = 0.0;
+  // A band of one round with at most 64 keys is summed, ranked and read back by wave 0 alone
+  // (thread i sums key i and writes band_val[i]): no barrier after its sums, and its error
+  // maximum is a wave reduction.
+  const bool one_wave = nb <= KPR && KPR <= 64;  // block-uniform
   for (int base = 0; base < nb; base += KPR) {  // block-uniform rounds
     if (base + 16 * kt < nb) {  // wave-uniform: the tile holds at least one band key
       i32x4 kb[2][3];
@@ -610,7 +614,12 @@ __device__ __forceinline__ double rescore_band(const RowRef& rr, const float* __
       L.band_val[base + tid] = ex;
       worst = fmax(worst, __builtin_fabs(static_cast<double>(f32) - ex));
     }
-    __syncthreads();
+    if (!one_wave) __syncthreads();
+  }
+  if (one_wave) {
+    if (wave == 0)
+      for (int o = 32; o >= 1; o >>= 1) worst = fmax(worst, __shfl_xor(worst, o));
+    return worst;
   }
   return block_max_d(worst, L.redd);
 }
