@@ -509,6 +509,45 @@ def test_sparse_mla_matches_oracle(heads, pad):
     _say(f"  worst err/bound = {worst:.3f}")
 
 
+@pytest.mark.parametrize("where", [0, 300])
+def test_sparse_mla_extreme_logit_spread(where):
+    # Every row's list holds, at list position `where`, a key whose logit lies about 185
+    # above the others in base 2 (its rope aligned with a shift of the queries' rope), and seven
+    # places later one as far below: the other keys' weights fall below 2^-126 of the
+    # dominant one, where the kernel's exponential flushes to zero. At position 300 the
+    # dominant key arrives after nine chunks, so the reference max jumps and the earlier
+    # accumulators are rescaled by a factor below 2^-126. The output dims carry no spike, so
+    # the tolerance stays at the scale of ordinary values. Both latent caches.
+    _say(f"sparse_mla extreme logit spread at list position {where}")
+    w = W.replace(W.scaled(W.MTP5_VERIFY, ctx=3000, batch=2, topk=512), mla_heads=16)
+    lens = synth.context_lengths(w)
+    qo, ko = synth.q_row_offsets(w), synth.kv_row_offsets(lens)
+    m = synth.mla_inputs(w, lens)
+    idx = synth.random_topk(w, lens, qo, w.topk, pad_frac=0.0)
+    q = m["q"].float()
+    kv = m["kv"].float()
+    q[:, :, 512:] += 4.0
+    T = int(qo[-1])
+    for t in range(T):
+        b = int(np.searchsorted(qo.numpy(), t, side="right") - 1)
+        kv[int(ko[b]) + int(idx[t, where]), 512:] = 12.0
+        kv[int(ko[b]) + int(idx[t, where + 7]), 512:] = -12.0
+    q, kv = q.to(torch.bfloat16), kv.to(torch.bfloat16)
+    u16 = lambda x: x.view(torch.uint16).numpy()
+    ref_o, ref_l = oracle.sparse_mla(u16(q), u16(kv), idx.numpy(), qo.numpy(), ko.numpy(),
+                                     w.sm_scale)
+    assert np.all(ref_l > 100.0), "the spike must dominate every row by more than 126 in base 2"
+    out, lse = api.sparse_mla_decode(q.to(DEV), kv.to(DEV), idx.to(DEV), qo.to(DEV), ko.to(DEV),
+                                     w.rows, w.sm_scale)
+    _say(f"  bf16 rows: worst err/bound = {mla_check(out, lse, ref_o, ref_l):.3f}")
+    kv8 = oracle.mla_fp8_pack(u16(kv))
+    ref8_o, ref8_l = oracle.sparse_mla_fp8(u16(q), kv8, idx.numpy(), qo.numpy(), ko.numpy(),
+                                           w.sm_scale)
+    out8, lse8 = api.sparse_mla_decode_fp8(q.to(DEV), torch.from_numpy(kv8).to(DEV), idx.to(DEV),
+                                           qo.to(DEV), ko.to(DEV), w.rows, w.sm_scale)
+    _say(f"  FP8 rows: worst err/bound = {mla_check(out8, lse8, ref8_o, ref8_l):.3f}")
+
+
 def test_sparse_mla_index_share_equals_compacted_copy():
     _say("sparse_mla index share")
     w = W.replace(W.scaled(W.DRAFT_SHARE, ctx=3000, batch=5, topk=256), rows=6)
