@@ -139,14 +139,16 @@ def test_index_score_exact_grid_bitexact():
         assert np.array_equal(got[t, :n], ref[t, :n])
 
 
-@pytest.mark.parametrize("H,D,seed", [(64, 128, 0), (128, 128, 1), (8, 64, 2)])
-def test_index_score_ragged_many_requests_exact_grid(H, D, seed):
+@pytest.mark.parametrize("H,D,seed,signed", [(64, 128, 0, False), (128, 128, 1, False), (8, 64, 2, False),
+                                              (1, 128, 3, True), (37, 128, 4, True), (100, 64, 5, True)])
+def test_index_score_ragged_many_requests_exact_grid(H, D, seed, signed):
     # Many requests with ragged lengths (empty ones, a few keys, tile multiples) and a
     # varying number of rows (up to 9, so rows split into row groups): the key ranges of
     # the blocks cross request boundaries at arbitrary points. Integer codes keep every
     # sum exact, so every visible score must equal the oracle's, and every entry past a
-    # row's visible prefix must keep its prefilled value.
-    _say(f"index_score ragged exact grid H={H} D={D}")
+    # row's visible prefix must keep its prefilled value. Head counts that fill no whole
+    # 16-head tile (1, 37, 100) and head weights of either sign are covered too.
+    _say(f"index_score ragged exact grid H={H} D={D} signed={signed}")
     rng = np.random.default_rng(100 + seed)
     B = 120
     lens = rng.integers(0, 300, B)
@@ -159,7 +161,7 @@ def test_index_score_ragged_many_requests_exact_grid(H, D, seed):
     vals = np.array([-4, -3, -2, -1, 0, 1, 2, 3, 4], np.float32)
     q = oracle.fp8_encode(rng.choice(vals, (T, H, D)))
     k = oracle.fp8_encode(rng.choice(vals, (N, D)))
-    w = (rng.integers(0, 16, (T, H)) / 16).astype(np.float32)
+    w = (rng.integers(-16 if signed else 0, 16, (T, H)) / 16).astype(np.float32)
     qs = np.ones((T, H), np.float32)
     ks = np.ones(N, np.float32)
     ref = oracle.index_score(q, qs, w, k, ks, qo, ko, width=L)
@@ -364,6 +366,38 @@ def test_end_to_end_topk_refined_equals_oracle(name):
     w = SMALL[name]
     _say(f"end-to-end refined top-k {name}")
     case = Case(w, with_mla=False, with_accept=False)
+    gi = gpu_indexer(case)
+    qc, qs, kc, ks, ko = oracle_quant(case)
+    rows = np.arange(case.T)
+    ref_s = oracle.index_score(qc, qs, case.host("w_f32"), kc, ks, case.qo.numpy(), ko,
+                               rows=rows, width=case.max_kv)
+    nvis = np.array([case.visible(int(t)) for t in rows])
+    ref_k = oracle.topk(ref_s, nvis, w.topk)
+    got_s = gi["scores"].cpu().numpy()[:, :case.max_kv].astype(np.float64)
+    eps = refine_eps(qc, qs, case.host("w_f32"), ks, case.qo.numpy(), ko, rows,
+                     kth_largest(got_s, nvis, w.topk))
+    ratio = max(float(np.abs(got_s[t, :nvis[t]] - ref_s[t, :nvis[t]]).max() / eps[t])
+                for t in rows if nvis[t])
+    _say(f"  max |I_f32 - I_exact| / eps = {ratio:.3f}")
+    assert ratio <= 0.5
+    ra = refine_args(gi, case)
+    got = api.topk(gi["scores"], case.qo_d, case.ko_d, w.rows, case.max_kv, w.topk, refine=ra)
+    st = ra["status"].cpu().numpy()
+    _say(f"  band sizes: max {st.max()}, mean {st.mean():.1f}")
+    assert st.min() >= 0
+    assert np.array_equal(got.cpu().numpy(), ref_k)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_end_to_end_topk_refined_signed_weights(name):
+    # head weights of either sign (w -> 2w - 1, so about half are negative): the scorer's
+    # weighted ReLU sum and the refine's bound (which takes |w_j q_scale_j|) must still give
+    # the oracle's exact sets
+    w = SMALL[name]
+    _say(f"end-to-end refined top-k, signed weights {name}")
+    case = Case(w, with_mla=False, with_accept=False)
+    case.w_f32 = 2.0 * case.w_f32 - 1.0
+    assert bool((case.w_f32 < 0).any()) and bool((case.w_f32 > 0).any())
     gi = gpu_indexer(case)
     qc, qs, kc, ks, ko = oracle_quant(case)
     rows = np.arange(case.T)
