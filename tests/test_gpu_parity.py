@@ -388,6 +388,32 @@ def test_end_to_end_topk_refined_equals_oracle(name):
     assert np.array_equal(got.cpu().numpy(), ref_k)
 
 
+@pytest.mark.parametrize("ctx", [2050, 8195, 16387, 65539])
+def test_refined_topk_row_lengths_at_path_boundaries(ctx):
+    # six verify rows of one request see ctx - 5 .. ctx keys. With k = 2048 at ctx 2050 they
+    # cross n < k (every visible key), n = k and n = k + 1; the other sizes straddle the
+    # register path's 8, 16 and 64 scores per lane (8192 and 16384 positions) and its end
+    # at 65536 (past it, the LDS selection and the generic refine). Every row's refined set
+    # must be the oracle's.
+    w = W.replace(W.scaled(W.MTP5_VERIFY, ctx=ctx, batch=1, topk=2048), ctx_min=0)
+    _say(f"refined top-k at row lengths {ctx - 5}..{ctx}")
+    case = Case(w, with_mla=False, with_accept=False)
+    gi = gpu_indexer(case)
+    qc, qs, kc, ks, ko = oracle_quant(case)
+    rows = np.arange(case.T)
+    ref_s = oracle.index_score(qc, qs, case.host("w_f32"), kc, ks, case.qo.numpy(), ko,
+                               rows=rows, width=case.max_kv)
+    nvis = np.array([case.visible(int(t)) for t in rows])
+    assert list(nvis) == list(range(ctx - 5, ctx + 1))
+    ref_k = oracle.topk(ref_s, nvis, w.topk)
+    ra = refine_args(gi, case)
+    got = api.topk(gi["scores"], case.qo_d, case.ko_d, w.rows, case.max_kv, w.topk, refine=ra)
+    st = ra["status"].cpu().numpy()
+    _say(f"  status per row: {list(st)}")
+    assert st.min() >= 0
+    assert np.array_equal(got.cpu().numpy(), ref_k)
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_end_to_end_topk_refined_signed_weights(name):
     # head weights of either sign (w -> 2w - 1, so about half are negative): the scorer's
