@@ -721,6 +721,42 @@ def test_greedy_accept_bitexact(name, batch, vocab, K):
     assert np.array_equal(rn, a["planted_n"].numpy())
 
 
+@pytest.mark.parametrize("dtype,pad", [(torch.bfloat16, 5), (torch.bfloat16, 8), (torch.float32, 3)])
+def test_greedy_accept_strided_rows_via_abi(dtype, pad):
+    # logits rows `pad` entries longer than the vocabulary (logits_ld = V + pad, so with an
+    # odd pad most bf16 rows start off a 16-byte boundary): the entries past V hold the
+    # row's largest value and must never be taken
+    _say(f"greedy_accept strided rows {dtype} pad={pad}")
+    from dsa_sparse_attention_amd import _lib
+    B, K, V = 5, 3, 5000
+    w = W.replace(W.TINY, batch=B, vocab=V, rows=K + 1)
+    a = synth.accept_inputs(w)
+    base = a["logits"].float()
+    wide = torch.empty((B * (K + 1), V + pad), dtype=torch.float32)
+    wide[:, :V] = base
+    wide[:, V:] = base.max() + 1.0
+    wide = wide.to(dtype)
+    host = wide[:, :V].contiguous()
+    host = host.view(torch.uint16).numpy() if dtype == torch.bfloat16 else host.numpy()
+    rn, rnx, ram = oracle.greedy_accept(host, a["draft"].numpy(), K)
+    lib = _lib.load()
+    dev = wide.to(DEV)
+    draft = a["draft"].to(DEV)
+    n = torch.empty(B, dtype=torch.int32, device=DEV)
+    nxt = torch.empty(B, dtype=torch.int32, device=DEV)
+    am = torch.empty((B, K + 1), dtype=torch.int32, device=DEV)
+    need = lib.greedy_accept_workspace_size(B, K, V)
+    ws = torch.empty(max(need, 4), dtype=torch.uint8, device=DEV)
+    dt = api.DSA_BF16 if dtype == torch.bfloat16 else api.DSA_F32
+    rc = lib.greedy_accept(dev.data_ptr(), dt, V + pad, draft.data_ptr(), B, K, V, n.data_ptr(),
+                           nxt.data_ptr(), am.data_ptr(), ws.data_ptr(), ws.numel(),
+                           torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, lib.dsa_last_error()
+    torch.cuda.synchronize()
+    assert np.array_equal(am.cpu().numpy(), ram)
+    assert np.array_equal(n.cpu().numpy(), rn) and np.array_equal(nxt.cpu().numpy(), rnx)
+
+
 def test_abi_rejects_bad_arguments_before_launch():
     _say("abi error paths")
     x = torch.zeros((4, 96), device=DEV)
