@@ -757,6 +757,36 @@ def test_greedy_accept_strided_rows_via_abi(dtype, pad):
     assert np.array_equal(n.cpu().numpy(), rn) and np.array_equal(nxt.cpu().numpy(), rnx)
 
 
+@pytest.mark.parametrize("name,pad", [("bf16", 5), ("f32", 3)])
+def test_rejection_accept_strided_rows_equal_contiguous(name, pad):
+    # logits rows `pad` entries longer than the vocabulary, the extra entries huge: the
+    # result must be the same as for the contiguous rows (which the oracle test covers)
+    _say(f"rejection_accept strided rows {name} pad={pad}")
+    from dsa_sparse_attention_amd import _lib
+    B, K, V = 6, 3, 5000
+    w = W.scaled(W.TINY, ctx=4096, batch=B, vocab=V, rows=K + 1,
+                 logits_dtype="f32" if name == "f32" else "bf16")
+    d = synth.rejection_inputs(w, draft_noise=0.3)
+    g = {k: v.to(DEV) for k, v in d.items()}
+    n0, x0 = api.rejection_accept(g["logits"], g["draft_probs"], g["draft"], g["u"], g["us"], K)
+    lg = g["logits"]
+    wide = torch.full((lg.shape[0], V + pad), 1.0e4, dtype=lg.dtype, device=DEV)
+    wide[:, :V] = lg
+    lib = _lib.load()
+    n = torch.empty(B, dtype=torch.int32, device=DEV)
+    nxt = torch.empty(B, dtype=torch.int32, device=DEV)
+    need = lib.rejection_accept_workspace_size(B, K, V)
+    ws = torch.empty(max(need, 8), dtype=torch.uint8, device=DEV)
+    dt = api.DSA_F32 if name == "f32" else api.DSA_BF16
+    rc = lib.rejection_accept(wide.data_ptr(), dt, V + pad, g["draft_probs"].data_ptr(),
+                              g["draft"].data_ptr(), g["u"].data_ptr(), g["us"].data_ptr(), B, K, V,
+                              n.data_ptr(), nxt.data_ptr(), ws.data_ptr(), ws.numel(),
+                              torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, lib.dsa_last_error()
+    torch.cuda.synchronize()
+    assert torch.equal(n, n0) and torch.equal(nxt, x0)
+
+
 def test_abi_rejects_bad_arguments_before_launch():
     _say("abi error paths")
     x = torch.zeros((4, 96), device=DEV)
