@@ -60,6 +60,28 @@ def test_fused_topk_equals_oracle(name):
             assert list(top[t]) == list(case.spike_pos[0][:w.topk].numpy())
 
 
+@pytest.mark.parametrize("ctx,k", [(2050, 2048), (8195, 2048), (65539, 2048), (300, 2048)])
+def test_fused_row_lengths_around_k_and_path_sizes(ctx, k):
+    # six verify rows of one request see ctx - 5 .. ctx keys: around k (n < k keeps every
+    # visible key, n = k, n = k + 1), around the register path's size steps and its end, and
+    # a context shorter than k; every row's set must be the oracle's, every row refined
+    w = W.replace(W.scaled(W.MTP5_VERIFY, ctx=ctx, batch=1, topk=k), ctx_min=0)
+    _say(f"fused index_topk at row lengths {ctx - 5}..{ctx}, k={k}")
+    case = Case(w, with_mla=False, with_accept=False)
+    gi = gpu_indexer(case)
+    top, st, path = _fused(gi, case, k)
+    qc, qs, kc, ks, ko = oracle_quant(case)
+    rows = np.arange(case.T)
+    ref_s = oracle.index_score(qc, qs, case.host("w_f32"), kc, ks, case.qo.numpy(), ko,
+                               rows=rows, width=case.max_kv)
+    nvis = np.array([case.visible(int(t)) for t in rows])
+    assert list(nvis) == list(range(ctx - 5, ctx + 1))
+    ref_k = oracle.topk(ref_s, nvis, k)
+    _say(f"  status {list(st)}, path {list(path)}")
+    assert st.min() >= 0
+    assert np.array_equal(top, ref_k)
+
+
 def test_fused_ragged_many_requests():
     # ragged requests, empty ones, rows before their request's first key: every row's set
     # equals the oracle's
