@@ -655,6 +655,30 @@ def test_sparse_mla_many_rows_split_lists_and_workspace_reuse(heads):
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
 
 
+@pytest.mark.parametrize("k", [1, 31, 33, 300, 2047])
+def test_sparse_mla_list_lengths_off_the_chunk_grid(k):
+    # top-k lists whose length is not a multiple of the 32-row chunk (one key, one short of
+    # and one past a chunk, and a list that the small grid cuts into slices with a ragged
+    # last chunk), on bf16 and FP8 rows
+    _say(f"sparse_mla list length k={k}")
+    w = W.replace(W.scaled(W.MTP5_VERIFY, ctx=3000, batch=2, topk=k), rows=3, mla_heads=64)
+    lens = synth.context_lengths(w)
+    qo, ko = synth.q_row_offsets(w), synth.kv_row_offsets(lens)
+    m = synth.mla_inputs(w, lens)
+    idx = synth.random_topk(w, lens, qo, k, pad_frac=0.1 if k > 1 else 0.0)
+    d = lambda x: (torch.from_numpy(x) if isinstance(x, np.ndarray) else x).to(DEV)
+    u16 = lambda x: x.view(torch.uint16).numpy()
+    out, lse = api.sparse_mla_decode(d(m["q"]), d(m["kv"]), d(idx), d(qo), d(ko), w.rows, w.sm_scale)
+    ref_o, ref_l = oracle.sparse_mla(u16(m["q"]), u16(m["kv"]), idx.numpy(), qo.numpy(), ko.numpy(),
+                                     w.sm_scale)
+    _say(f"  bf16 rows: worst err/bound = {mla_check(out, lse, ref_o, ref_l):.3f}")
+    kv8 = oracle.mla_fp8_pack(u16(m["kv"]))
+    out8, lse8 = api.sparse_mla_decode_fp8(d(m["q"]), d(kv8), d(idx), d(qo), d(ko), w.rows, w.sm_scale)
+    ref_o8, ref_l8 = oracle.sparse_mla_fp8(u16(m["q"]), kv8, idx.numpy(), qo.numpy(), ko.numpy(),
+                                           w.sm_scale)
+    _say(f"  FP8 rows: worst err/bound = {mla_check(out8, lse8, ref_o8, ref_l8):.3f}")
+
+
 @pytest.mark.parametrize("batch,rows,heads,ctx,topk,slices", [
     (8, 5, 128, 3000, 2048, 3), (4, 6, 128, 3000, 2048, 5), (6, 6, 64, 3000, 2048, 7),
     (1, 6, 16, 3000, 2048, 8), (1, 6, 16, 5000, 4096, 16)])
