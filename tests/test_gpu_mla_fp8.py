@@ -62,7 +62,7 @@ def _fp8_case(w, pad=0.0, rows=None, seed_offset=0):
     return lens, qo, ko, m["q"], kv8
 
 
-@pytest.mark.parametrize("heads,pad", [(16, 0.0), (64, 0.1), (128, 0.0), (48, 0.5)])
+@pytest.mark.parametrize("heads,pad", [(16, 0.0), (64, 0.1), (128, 0.0), (48, 0.5), (112, 0.1)])
 def test_sparse_mla_fp8_matches_oracle(heads, pad):
     _say(f"sparse_mla_fp8 heads={heads} pad={pad}")
     w = W.replace(W.scaled(W.MTP5_VERIFY, ctx=3000, batch=3, topk=512), mla_heads=heads)

@@ -549,7 +549,8 @@ def test_refined_topk_short_key_scale_table_keeps_float32():
 
 
 # ---------------------------------------------------------------- sparse MLA
-@pytest.mark.parametrize("heads,pad", [(16, 0.0), (64, 0.1), (128, 0.0), (48, 0.5)])
+@pytest.mark.parametrize("heads,pad", [(16, 0.0), (64, 0.1), (128, 0.0), (48, 0.5), (80, 0.1),
+                                       (112, 0.0)])
 def test_sparse_mla_matches_oracle(heads, pad):
     _say(f"sparse_mla heads={heads} pad={pad}")
     w = W.replace(W.scaled(W.MTP5_VERIFY, ctx=3000, batch=3, topk=512), mla_heads=heads)
