@@ -414,6 +414,49 @@ def test_refined_topk_row_lengths_at_path_boundaries(ctx):
     assert np.array_equal(got.cpu().numpy(), ref_k)
 
 
+@pytest.mark.parametrize("ctx", [5000, 20000])
+def test_refined_topk_largest_k(ctx):
+    # k = 4096, the largest the refine takes, through the separate and the fused path; at
+    # 20000 positions the register path's per-wave candidate regions overflow, so the rows
+    # take the LDS selection and the generic refine
+    k = 4096
+    w = W.replace(W.scaled(W.MTP5_VERIFY, ctx=ctx, batch=1, topk=k), ctx_min=0)
+    _say(f"refined top-k k={k} at row lengths {ctx - 5}..{ctx}")
+    case = Case(w, with_mla=False, with_accept=False)
+    gi = gpu_indexer(case)
+    qc, qs, kc, ks, ko = oracle_quant(case)
+    rows = np.arange(case.T)
+    ref_s = oracle.index_score(qc, qs, case.host("w_f32"), kc, ks, case.qo.numpy(), ko,
+                               rows=rows, width=case.max_kv)
+    nvis = np.array([case.visible(int(t)) for t in rows])
+    ref_k = oracle.topk(ref_s, nvis, k)
+    ra = refine_args(gi, case)
+    got = api.topk(gi["scores"], case.qo_d, case.ko_d, w.rows, case.max_kv, k, refine=ra)
+    st = ra["status"].cpu().numpy()
+    _say(f"  separate: status {list(st)}")
+    assert st.min() >= 0
+    assert np.array_equal(got.cpu().numpy(), ref_k)
+    fst = torch.full((case.T,), -9, dtype=torch.int32, device=DEV)
+    fused = api.index_topk(gi["qc"], gi["qs"], case.w_f32, gi["kc"], gi["ks"], case.qo_d,
+                           case.ko_d, w.rows, case.max_kv, k, status=fst)
+    _say(f"  fused: status {list(fst.cpu().numpy())}")
+    assert int(fst.min()) >= 0
+    assert np.array_equal(fused.cpu().numpy(), ref_k)
+
+
+def test_topk_largest_k_unrefined():
+    # k = 8192, the largest dsa_topk takes without the refine, on shared scores with ties:
+    # rows just below, at and past 8192 positions, a register-path row and a chunked row
+    _say("topk k=8192")
+    lens = [8190, 8192, 8193, 30000, 100000]
+    qo = torch.arange(len(lens) + 1, dtype=torch.int32)
+    ko = synth.kv_row_offsets(lens)
+    s = synth.random_scores(len(lens), max(lens), seed=21, tie_levels=50)
+    got = api.topk(s.to(DEV), qo.to(DEV), ko.to(DEV), 1, max(lens), 8192).cpu().numpy()
+    ref = oracle.topk(s.double().numpy(), lens, 8192)
+    assert np.array_equal(got, ref)
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_end_to_end_topk_refined_signed_weights(name):
     # head weights of either sign (w -> 2w - 1, so about half are negative): the scorer's
