@@ -673,6 +673,31 @@ def test_sparse_mla_index_share_equals_compacted_copy():
     mla_check(o_sh, l_sh, ref_o, ref_l)
 
 
+def test_sparse_mla_index_share_edges():
+    # share map edges: a request with no accepted draft (its bonus row's list), one that
+    # accepted every draft (its last verify row's list), and one whose map entry points past
+    # the top-k rows (it selects nothing: out 0, lse -inf)
+    _say("sparse_mla index share edges")
+    w = W.replace(W.scaled(W.DRAFT_SHARE, ctx=3000, batch=5, topk=256), rows=6)
+    lens = synth.context_lengths(w)
+    qo0, ko = synth.q_row_offsets(w), synth.kv_row_offsets(lens)
+    step0 = synth.random_topk(w, lens, qo0, w.topk, pad_frac=0.05)
+    n_acc = synth.accepted_lengths(w).clone()
+    n_acc[0], n_acc[1], n_acc[4] = 0, w.rows - 1, 10 ** 6
+    qo1 = torch.arange(w.batch + 1, dtype=torch.int32)
+    m = synth.mla_inputs(w, lens, rows=1, seed_offset=2)
+    d = lambda x: x.to(DEV)
+    out, lse = api.sparse_mla_decode(d(m["q"]), d(m["kv"]), d(step0), d(qo1), d(ko), 1, w.sm_scale,
+                                     share_base=d(qo0), num_accepted=d(n_acc))
+    assert torch.all(out[4] == 0) and torch.all(torch.isneginf(lse[4]))
+    ok = n_acc.clone()
+    ok[4] = 0  # the oracle is asked only about the requests with a valid map entry
+    u16 = lambda x: x.view(torch.uint16).numpy()
+    ref_o, ref_l = oracle.sparse_mla(u16(m["q"]), u16(m["kv"]), step0.numpy(), qo1.numpy(), ko.numpy(),
+                                     w.sm_scale, share_base=qo0.numpy(), num_accepted=ok.numpy())
+    mla_check(out[:4], lse[:4], ref_o[:4], ref_l[:4])
+
+
 @pytest.mark.parametrize("heads", [64, 128])
 def test_sparse_mla_many_rows_split_lists_and_workspace_reuse(heads):
     # 200 rows with k = 448 (ragged contexts, 20% padding): lists split over blocks whose
